@@ -1,0 +1,438 @@
+/*
+ * moe_oracle.c -- fp64 CPU oracle of the routed MoE FFN layer.  TEST INFRASTRUCTURE ONLY
+ * (see moe_oracle.h for who may use it and for the source abbreviations [MX] [BP] [C31] ...).
+ *
+ * Plain loops, IEEE binary64 throughout, no blocking or reordering beyond what each definition
+ * states.  OpenMP only distributes independent output elements over threads; every output element
+ * is still produced by one thread in index order, so results do not depend on the thread count.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------------ */
+/* Number formats                                                                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [MX]: an E2M1 code is one sign bit plus a magnitude from {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ * Reading (the page gives the set, not the bit assignment): bit 3 is the sign, bits 2..0 index
+ * the magnitudes in ascending order -- the standard E2M1 layout (2 exponent bits, bias 1, one
+ * mantissa bit).  Code 8 is negative zero. */
+static const double E2M1_MAGNITUDE[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1(int code) {
+  double mag = E2M1_MAGNITUDE[code & 7];
+  return (code & 8) ? -mag : mag;
+}
+
+/* [MX]: the block scale is the unsigned E8M0 code e; its value is 2^(e-127). */
+double orc_e8m0(int e) { return ldexp(1.0, e - 127); }
+
+/* [MX]: decoded weight w_hat = v(c) * 2^(e-127). */
+double orc_mxfp4(int code, int e) { return orc_e2m1(code) * orc_e8m0(e); }
+
+/* [MX]: a 32-weight block stores 32 four-bit codes and one 8-bit scale: 4 + 8/32 bits per weight. */
+double orc_mxfp4_bits_per_weight(void) { return (32.0 * 4.0 + 8.0) / 32.0; }
+
+int64_t orc_mxfp4_bytes(int64_t n_rows, int64_t k) {
+  return n_rows * (k / 2) + n_rows * (k / 32);
+}
+
+/* bfloat16: the top 16 bits of an IEEE binary32 value. */
+double orc_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double orc_f16(uint16_t bits) {
+  int sign = bits >> 15, ex = (bits >> 10) & 31, fr = bits & 1023;
+  double v;
+  if (ex == 0)
+    v = ldexp((double)fr, -24);                       /* zero and subnormals: fr * 2^-14 * 2^-10 */
+  else if (ex == 31)
+    v = fr ? NAN : INFINITY;
+  else
+    v = ldexp(1024.0 + (double)fr, ex - 25);          /* (1 + fr/1024) * 2^(ex-15) */
+  return sign ? -v : v;
+}
+
+static double act_value(const uint16_t *x, int x_fmt, int64_t i) {
+  return x_fmt == ORC_X_FP16 ? orc_f16(x[i]) : orc_bf16(x[i]);
+}
+
+/* Element (n, k) of expert e of one projection.  [MX]: element k of a packed row lives in byte
+ * k/2 (reading: even k in the low nibble) and uses the scale of block floor(k/32); rows are
+ * row-major with K contiguous, read in place with no repack. */
+double orc_weight(const orc_proj *p, int fmt, int e, int n, int k) {
+  if (fmt == ORC_W_FP16) {
+    const uint8_t *row = (const uint8_t *)p->w + (int64_t)e * p->w_expert_stride + (int64_t)n * p->w_row_stride;
+    uint16_t bits;
+    memcpy(&bits, row + 2 * (int64_t)k, 2);
+    return orc_f16(bits);
+  }
+  const uint8_t *row = (const uint8_t *)p->w + (int64_t)e * p->w_expert_stride + (int64_t)n * p->w_row_stride;
+  const uint8_t *srow = p->scales + (int64_t)e * p->s_expert_stride + (int64_t)n * p->s_row_stride;
+  uint8_t byte = row[k / 2];
+  int code = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+  return orc_mxfp4(code, srow[k / 32]);
+}
+
+/* SiLU(z) = z / (1 + e^-z).  For very negative z, e^-z overflows to +inf and the quotient is -0,
+ * which is the limit; no NaN can arise for finite z. */
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Router: logits, softmax, top-k, renormalise, append shared experts                         */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Per token t:
+ *   L[t,e] = sum_h x[t,h] W_r[e,h] + b[e]
+ *   p      = softmax(L[t,:]) = exp(L - max L) / sum exp(L - max L)
+ *   the k experts with the largest p, ordered by (p descending, index ascending)
+ *   w_j    = p_j / sum_{j'<k} p_j'      (routing weights renormalised to 1)
+ *   slots k .. k+S-1 hold the shared experts E .. E+S-1 with weight 1.
+ * [C31] routing produces expert ids and routing weights for the fused expert path, and shared
+ * experts are always-included selections after the routed ones.  The softmax -> top-k ->
+ * renormalise order, the lowest-index tie-break and the shared weight of 1 (outside the
+ * renormalisation) are readings: the pages print no softmax router.
+ * near_tie[t] = 1 when two neighbours among the first min(k+1, E) sorted probabilities differ by
+ * at most tie_eps; such tokens may legitimately come out in another order. */
+void orc_route(const uint16_t *x, int x_fmt, int T, int H, const float *w_router, const float *bias,
+               int E, int top_k, int n_shared, double tie_eps,
+               double *logits, double *probs, int32_t *ids, double *weights, uint8_t *near_tie) {
+  const int k_total = top_k + n_shared;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; ++t) {
+    double *L = (double *)malloc(sizeof(double) * (size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    int *order = (int *)malloc(sizeof(int) * (size_t)E);
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];
+      L[e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+    double mx = L[0];
+    for (int e = 1; e < E; ++e)
+      if (L[e] > mx) mx = L[e];
+    double den = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp(L[e] - mx);
+      den += p[e];
+    }
+    for (int e = 0; e < E; ++e) p[e] /= den;
+    /* Selection: repeatedly take the largest remaining p, lowest index first among equals. */
+    for (int e = 0; e < E; ++e) order[e] = e;
+    int n_sort = top_k + 1 < E ? top_k + 1 : E;
+    for (int j = 0; j < n_sort; ++j) {
+      int best = j;
+      for (int i = j + 1; i < E; ++i) {
+        int a = order[i], b = order[best];
+        if (p[a] > p[b] || (p[a] == p[b] && a < b)) best = i;
+      }
+      int tmp = order[j];
+      order[j] = order[best];
+      order[best] = tmp;
+    }
+    double sel = 0.0;
+    for (int j = 0; j < top_k; ++j) sel += p[order[j]];
+    for (int j = 0; j < top_k; ++j) {
+      ids[(int64_t)t * k_total + j] = order[j];
+      weights[(int64_t)t * k_total + j] = p[order[j]] / sel;
+    }
+    for (int s = 0; s < n_shared; ++s) {
+      ids[(int64_t)t * k_total + top_k + s] = E + s;
+      weights[(int64_t)t * k_total + top_k + s] = 1.0;
+    }
+    uint8_t tie = 0;
+    for (int j = 0; j + 1 < n_sort; ++j)
+      if (p[order[j]] - p[order[j + 1]] <= tie_eps) tie = 1;
+    if (near_tie) near_tie[t] = tie;
+    if (logits) memcpy(logits + (int64_t)t * E, L, sizeof(double) * (size_t)E);
+    if (probs) memcpy(probs + (int64_t)t * E, p, sizeof(double) * (size_t)E);
+    free(L);
+    free(p);
+    free(order);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Bucketing: group slots by expert                                                           */
+/* ------------------------------------------------------------------------------------------ */
+
+/* [C31]: the fused path executes only the selected experts' work, so slots are grouped by expert.
+ * counts[b] = number of slots s with ids[s] == b; offsets = exclusive prefix sum of counts with
+ * offsets[n_buckets] = number of valid slots; sorted_slot lists slot indices bucket by bucket,
+ * ascending slot index within a bucket (a stable counting sort); slot_pos is its inverse.
+ * A slot whose id is outside [0, n_buckets) is dropped: slot_pos = -1, and sorted_slot entries
+ * past the valid count are -1.  Returns the number of valid slots. */
+int orc_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *counts, int32_t *offsets,
+               int32_t *sorted_slot, int32_t *slot_pos) {
+  for (int b = 0; b < n_buckets; ++b) counts[b] = 0;
+  for (int s = 0; s < n_slots; ++s)
+    if (ids[s] >= 0 && ids[s] < n_buckets) counts[ids[s]]++;
+  offsets[0] = 0;
+  for (int b = 0; b < n_buckets; ++b) offsets[b + 1] = offsets[b] + counts[b];
+  int32_t *fill = (int32_t *)calloc((size_t)n_buckets + 1, sizeof(int32_t));
+  for (int s = 0; s < n_slots; ++s) sorted_slot[s] = -1;
+  for (int s = 0; s < n_slots; ++s) {
+    int b = ids[s];
+    if (b < 0 || b >= n_buckets) {
+      if (slot_pos) slot_pos[s] = -1;
+      continue;
+    }
+    int pos = offsets[b] + fill[b]++;
+    sorted_slot[pos] = s;
+    if (slot_pos) slot_pos[s] = pos;
+  }
+  free(fill);
+  return offsets[n_buckets];
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Expert FFN                                                                                 */
+/* ------------------------------------------------------------------------------------------ */
+
+/* One expert applied to one activation vector xv[H] (already in double):
+ *   g_n = sum_k W_g[n,k] x_k,  u_n = sum_k W_u[n,k] x_k,  h_n = SiLU(g_n) u_n,
+ *   out_m = sum_n W_d[m,n] h_n.
+ * [C31] gate/up projections, SwiGLU, down projection.  With MXFP4 weights each sum is the
+ * decode-in-reduction sum z_n = sum_k a_k v(c_{n,k}) 2^(e_{n,floor(k/32)}-127) of [MX]. */
+void orc_expert_apply(const orc_weights *W, int e, const double *xv, double *out) {
+  const int H = W->hidden, I = W->inter;
+  double *h = (double *)malloc(sizeof(double) * (size_t)I);
+  for (int n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int k = 0; k < H; ++k) {
+      g += orc_weight(&W->gate, W->fmt, e, n, k) * xv[k];
+      u += orc_weight(&W->up, W->fmt, e, n, k) * xv[k];
+    }
+    h[n] = orc_silu(g) * u;
+  }
+  for (int m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int n = 0; n < I; ++n) acc += orc_weight(&W->down, W->fmt, e, m, n) * h[n];
+    out[m] = acc;
+  }
+  free(h);
+}
+
+/* Grouped expert FFN over buckets: for every expert e and every row r in
+ * [offsets[e], offsets[e+1]), slot s = sorted_slot[r] of token t = s / k_total gets
+ * y_slots[s,:] = expert_e(x[t,:]).  Each expert's weight rows are decoded once per row and
+ * applied to all of its bucket's rows -- the same sums as orc_expert_apply, in the same k order.
+ * slot_mask (optional): only slots with slot_mask[s] != 0 are computed; other rows of y_slots are
+ * left untouched. */
+void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                    const int32_t *offsets, const int32_t *sorted_slot, const uint8_t *slot_mask,
+                    double *y_slots) {
+  const int H = W->hidden, I = W->inter, E2 = W->n_experts;
+  const int64_t n_slots = (int64_t)T * k_total;
+  for (int e = 0; e < E2; ++e) {
+    int r0 = offsets[e], r1 = offsets[e + 1];
+    int n_rows = 0;
+    int *slot = (int *)malloc(sizeof(int) * (size_t)(r1 - r0 + 1));
+    for (int r = r0; r < r1; ++r) {
+      int s = sorted_slot[r];
+      if (s < 0 || s >= n_slots) continue;
+      if (slot_mask && !slot_mask[s]) continue;
+      slot[n_rows++] = s;
+    }
+    if (n_rows == 0) {
+      free(slot);
+      continue;
+    }
+    double *xs = (double *)malloc(sizeof(double) * (size_t)n_rows * H);
+    double *hs = (double *)malloc(sizeof(double) * (size_t)n_rows * I);
+    for (int i = 0; i < n_rows; ++i) {
+      int t = slot[i] / k_total;
+      for (int k = 0; k < H; ++k) xs[(int64_t)i * H + k] = act_value(x, x_fmt, (int64_t)t * H + k);
+    }
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < I; ++n) {
+      double *wg = (double *)malloc(sizeof(double) * (size_t)H);
+      double *wu = (double *)malloc(sizeof(double) * (size_t)H);
+      for (int k = 0; k < H; ++k) {
+        wg[k] = orc_weight(&W->gate, W->fmt, e, n, k);
+        wu[k] = orc_weight(&W->up, W->fmt, e, n, k);
+      }
+      for (int i = 0; i < n_rows; ++i) {
+        const double *xv = xs + (int64_t)i * H;
+        double g = 0.0, u = 0.0;
+        for (int k = 0; k < H; ++k) {
+          g += wg[k] * xv[k];
+          u += wu[k] * xv[k];
+        }
+        hs[(int64_t)i * I + n] = orc_silu(g) * u;
+      }
+      free(wg);
+      free(wu);
+    }
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < H; ++m) {
+      double *wd = (double *)malloc(sizeof(double) * (size_t)I);
+      for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, m, n);
+      for (int i = 0; i < n_rows; ++i) {
+        const double *hv = hs + (int64_t)i * I;
+        double acc = 0.0;
+        for (int n = 0; n < I; ++n) acc += wd[n] * hv[n];
+        y_slots[(int64_t)slot[i] * H + m] = acc;
+      }
+      free(wd);
+    }
+    free(xs);
+    free(hs);
+    free(slot);
+  }
+}
+
+/* Weighted reduction [C31]: y[t,:] = sum_{j = 0..k_total-1, ascending} w[t,j] * y_slots[t*k_total+j,:].
+ * token_mask (optional): only tokens with token_mask[t] != 0 are computed. */
+void orc_combine(const double *y_slots, const double *weights, int T, int k_total, int H,
+                 const uint8_t *token_mask, double *y) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    if (token_mask && !token_mask[t]) continue;
+    for (int m = 0; m < H; ++m) {
+      double acc = 0.0;
+      for (int j = 0; j < k_total; ++j)
+        acc += weights[(int64_t)t * k_total + j] * y_slots[((int64_t)t * k_total + j) * H + m];
+      y[(int64_t)t * H + m] = acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Cross-check forms                                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Dense decode of one packed MXFP4 matrix [n_rows][k], walking bytes rather than elements:
+ * byte j of a row gives elements 2j (low nibble) and 2j+1 (high nibble), both in block
+ * floor(2j/32). */
+void orc_mxfp4_decode_matrix(const uint8_t *codes, const uint8_t *scales, int n_rows, int k,
+                             double *out) {
+  for (int n = 0; n < n_rows; ++n) {
+    const uint8_t *row = codes + (int64_t)n * (k / 2);
+    const uint8_t *srow = scales + (int64_t)n * (k / 32);
+    for (int j = 0; j < k / 2; ++j) {
+      double s = orc_e8m0(srow[(2 * j) / 32]);
+      out[(int64_t)n * k + 2 * j] = orc_e2m1(row[j] & 0x0F) * s;
+      out[(int64_t)n * k + 2 * j + 1] = orc_e2m1(row[j] >> 4) * s;
+    }
+  }
+}
+
+static void dense_expert(const orc_weights *W, int e, double *g, double *u, double *d) {
+  const int H = W->hidden, I = W->inter;
+  for (int n = 0; n < I; ++n)
+    for (int k = 0; k < H; ++k) {
+      g[(int64_t)n * H + k] = orc_weight(&W->gate, W->fmt, e, n, k);
+      u[(int64_t)n * H + k] = orc_weight(&W->up, W->fmt, e, n, k);
+    }
+  for (int m = 0; m < H; ++m)
+    for (int n = 0; n < I; ++n) d[(int64_t)m * I + n] = orc_weight(&W->down, W->fmt, e, m, n);
+}
+
+static void dense_apply(const double *g, const double *u, const double *d, int H, int I,
+                        const double *xv, double *out) {
+  double *h = (double *)malloc(sizeof(double) * (size_t)I);
+  for (int n = 0; n < I; ++n) {
+    double a = 0.0, b = 0.0;
+    for (int k = 0; k < H; ++k) {
+      a += g[(int64_t)n * H + k] * xv[k];
+      b += u[(int64_t)n * H + k] * xv[k];
+    }
+    h[n] = orc_silu(a) * b;
+  }
+  for (int m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int n = 0; n < I; ++n) acc += d[(int64_t)m * I + n] * h[n];
+    out[m] = acc;
+  }
+  free(h);
+}
+
+/* Form B: per token, decode each selected expert densely and accumulate w * expert(x) -- no
+ * bucketing, no slot buffer. */
+void orc_layer_bruteforce(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                          const int32_t *ids, const double *weights, double *y) {
+  const int H = W->hidden, I = W->inter;
+  double *g = (double *)malloc(sizeof(double) * (size_t)I * H);
+  double *u = (double *)malloc(sizeof(double) * (size_t)I * H);
+  double *d = (double *)malloc(sizeof(double) * (size_t)H * I);
+  double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+  double *o = (double *)malloc(sizeof(double) * (size_t)H);
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < H; ++k) xv[k] = act_value(x, x_fmt, (int64_t)t * H + k);
+    for (int m = 0; m < H; ++m) y[(int64_t)t * H + m] = 0.0;
+    for (int j = 0; j < k_total; ++j) {
+      int e = ids[(int64_t)t * k_total + j];
+      dense_expert(W, e, g, u, d);
+      dense_apply(g, u, d, H, I, xv, o);
+      for (int m = 0; m < H; ++m) y[(int64_t)t * H + m] += weights[(int64_t)t * k_total + j] * o[m];
+    }
+  }
+  free(g); free(u); free(d); free(xv); free(o);
+}
+
+/* Form C: a dense mixture over every expert, gate g_e = w_j when e = ids[t,j], else 0. */
+void orc_layer_dense_mixture(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                             const int32_t *ids, const double *weights, double *y) {
+  const int H = W->hidden, E2 = W->n_experts;
+  double *xv = (double *)malloc(sizeof(double) * (size_t)H);
+  double *o = (double *)malloc(sizeof(double) * (size_t)H);
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < H; ++k) xv[k] = act_value(x, x_fmt, (int64_t)t * H + k);
+    for (int m = 0; m < H; ++m) y[(int64_t)t * H + m] = 0.0;
+    for (int e = 0; e < E2; ++e) {
+      double gate = 0.0;
+      for (int j = 0; j < k_total; ++j)
+        if (ids[(int64_t)t * k_total + j] == e) gate = weights[(int64_t)t * k_total + j];
+      orc_expert_apply(W, e, xv, o);
+      for (int m = 0; m < H; ++m) y[(int64_t)t * H + m] += gate * o[m];
+    }
+  }
+  free(xv); free(o);
+}
+
+/* Form D [C34]: the unsliced dense SwiGLU FFN with binary16 weights wg, wu [I][H] and wd [H][I]:
+ * y = W_d [SiLU(W_g x) (.) W_u x]. */
+void orc_dense_ffn_f16(const uint16_t *x, int x_fmt, int T, int H, int I, const uint16_t *wg,
+                       const uint16_t *wu, const uint16_t *wd, double *y) {
+  for (int t = 0; t < T; ++t) {
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < I; ++n) {
+      double a = 0.0, b = 0.0;
+      for (int k = 0; k < H; ++k) {
+        double xv = act_value(x, x_fmt, (int64_t)t * H + k);
+        a += orc_f16(wg[(int64_t)n * H + k]) * xv;
+        b += orc_f16(wu[(int64_t)n * H + k]) * xv;
+      }
+      h[n] = orc_silu(a) * b;
+    }
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < H; ++m) {
+      double acc = 0.0;
+      for (int n = 0; n < I; ++n) acc += orc_f16(wd[(int64_t)m * I + n]) * h[n];
+      y[(int64_t)t * H + m] = acc;
+    }
+    free(h);
+  }
+}

@@ -1,0 +1,92 @@
+/*
+ * moe_oracle.h -- plain, slow fp64 CPU oracle of the routed Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * may load or call it.  It shares no code, header, table or helper with the HIP library, and the
+ * library never calls it.
+ *
+ * Sources (cited by page title and section):
+ *  [MX]  "DeepSeek-V4-Flash on a four-GPU Ampere workstation" (FreeToken blog post), section
+ *        "MXFP4 is not NVFP4, and the difference matters on Ampere": E2M1 codes, E8M0 block
+ *        scales, decoded weight v(c) 2^(e-127), 4.25 bits per weight, the decode-in-reduction
+ *        sum z_n, row-major packed banks.
+ *  [BP]  same post, section "Why it would not run": quantised partitioning must preserve blocks.
+ *  [C31] "Cascadia: Resident 975B MoE Inference on Eleven AI PCs", Sec. 3.1: expert-major banks,
+ *        gate/up projections, SwiGLU, down projection, weighted reduction; routing yields expert
+ *        ids and routing weights; shared experts are always-included selections.
+ *  [C32] Cascadia Sec. 3.2: a call supplies rows, expert ids and weights; FP32 output.
+ *  [C34] Cascadia Sec. 3.4, Eq. 2: a dense FFN equals the sum of its all-active slices.
+ *
+ * Where the pages leave a step open the reading used here is stated next to the function.
+ * Every floating-point value is computed in IEEE binary64 with plain loops in index order.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_W_MXFP4 = 0, ORC_W_FP16 = 1 };
+enum { ORC_X_BF16 = 0, ORC_X_FP16 = 1 };
+
+/* One projection of every expert, logical [n_experts][N][K] with K contiguous.
+ * MXFP4: w holds bytes, element k of a row in byte k/2, even k in the low nibble; scales hold one
+ *        E8M0 byte per 32 elements along K.  FP16: w holds binary16 words, scales unused.
+ * Strides are in bytes, so slices of a larger matrix can be described. */
+typedef struct {
+  const void *w;
+  const uint8_t *scales;
+  int64_t w_expert_stride, w_row_stride, s_expert_stride, s_row_stride;
+} orc_proj;
+
+typedef struct {
+  int fmt;        /* ORC_W_MXFP4 or ORC_W_FP16 */
+  int n_experts;  /* E' = routed + shared */
+  int hidden;     /* H */
+  int inter;      /* I */
+  orc_proj gate;  /* N = I, K = H */
+  orc_proj up;    /* N = I, K = H */
+  orc_proj down;  /* N = H, K = I */
+} orc_weights;
+
+/* ---- number formats ---- */
+double orc_e2m1(int code);                  /* v(c), c in [0,16) */
+double orc_e8m0(int e);                     /* 2^(e-127), e in [0,256) */
+double orc_mxfp4(int code, int e);          /* v(c) 2^(e-127) */
+double orc_bf16(uint16_t bits);
+double orc_f16(uint16_t bits);
+double orc_weight(const orc_proj *p, int fmt, int e, int n, int k);
+double orc_mxfp4_bits_per_weight(void);     /* storage cost of one block, per weight */
+int64_t orc_mxfp4_bytes(int64_t n_rows, int64_t k);  /* codes + scales of an [n_rows][k] matrix */
+
+/* ---- the layer ---- */
+void orc_route(const uint16_t *x, int x_fmt, int T, int H, const float *w_router, const float *bias,
+               int E, int top_k, int n_shared, double tie_eps,
+               double *logits, double *probs, int32_t *ids, double *weights, uint8_t *near_tie);
+int orc_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *counts, int32_t *offsets,
+               int32_t *sorted_slot, int32_t *slot_pos);
+void orc_expert_apply(const orc_weights *W, int e, const double *xv, double *out);
+void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                    const int32_t *offsets, const int32_t *sorted_slot, const uint8_t *slot_mask,
+                    double *y_slots);
+void orc_combine(const double *y_slots, const double *weights, int T, int k_total, int H,
+                 const uint8_t *token_mask, double *y);
+
+/* ---- cross-check forms ---- */
+void orc_layer_bruteforce(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                          const int32_t *ids, const double *weights, double *y);
+void orc_layer_dense_mixture(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                             const int32_t *ids, const double *weights, double *y);
+void orc_dense_ffn_f16(const uint16_t *x, int x_fmt, int T, int H, int I, const uint16_t *wg,
+                       const uint16_t *wu, const uint16_t *wd, double *y);
+void orc_mxfp4_decode_matrix(const uint8_t *codes, const uint8_t *scales, int n_rows, int k,
+                             double *out);
+double orc_silu(double z);
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,439 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each check takes a loaded oracle.Oracle and raises AssertionError when the oracle disagrees with
+what the pages, a closed form, a library routine or brute force fixes.  test_oracle_pins.py runs
+them on the real oracle; test_oracle_mutants.py runs them on copies of the oracle with a planted
+mistake and requires that every mutant fails at least one of them.
+
+Independent references used here (none calls the oracle):
+  * minifloat(): a generic sign/exponent/fraction decoder, itself checked against numpy's binary16
+    and binary32 conversions over every bit pattern, then used with (2 exponent bits, 1 fraction
+    bit, bias 1) -- the E2M1 layout -- and compared with the page's magnitude set.
+  * np_decode(): numpy nibble unpacking and block scales built from binary32 bit patterns.
+  * numpy matmul, scipy softmax/expit, numpy lexsort/argsort/bincount.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+
+import synth
+from oracle import ExpertWeights, X_BF16, X_FP16, W_MXFP4, W_FP16
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------------------------------------
+# independent references
+# ------------------------------------------------------------------------------------------------
+def minifloat(bits: int, e_bits: int, m_bits: int, bias: int, inf_nan: bool) -> float:
+    sign = (bits >> (e_bits + m_bits)) & 1
+    ex = (bits >> m_bits) & ((1 << e_bits) - 1)
+    fr = bits & ((1 << m_bits) - 1)
+    if ex == 0:
+        v = math.ldexp(fr, 1 - bias - m_bits)
+    elif inf_nan and ex == (1 << e_bits) - 1:
+        v = math.nan if fr else math.inf
+    else:
+        v = math.ldexp((1 << m_bits) + fr, ex - bias - m_bits)
+    return -v if sign else v
+
+
+E2M1_REF = np.array([minifloat(c, 2, 1, 1, False) for c in range(16)])
+
+
+def scale_ref(e: np.ndarray) -> np.ndarray:
+    """2^(e-127) built from binary32 bit patterns (exponent field e, or the subnormal 2^-127 for
+    e = 0); e = 255 has no binary32 power of two and is handled by the caller."""
+    e = np.asarray(e, np.uint32)
+    bits = np.where(e == 0, np.uint32(0x00400000), e << np.uint32(23)).astype(np.uint32)
+    return bits.view(np.float32).astype(np.float64)
+
+
+def np_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[N][K/2] packed bytes + [N][K/32] scale codes -> [N][K] float64 (low nibble first)."""
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    c = np.stack([codes & 0x0F, codes >> 4], axis=-1).reshape(N, K)
+    return E2M1_REF[c] * np.repeat(scale_ref(scales), 32, axis=1)
+
+
+def np_act(x_bits: np.ndarray, fmt: int) -> np.ndarray:
+    if fmt == X_FP16:
+        return x_bits.view(np.float16).astype(np.float64)
+    return (x_bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def np_weights(L):
+    """Dense float64 [E'][N][K] gate, up, down for synth.LayerInputs L."""
+    if L.wl.weight_format == "mxfp4":
+        dec = lambda c, s: np.stack([np_decode(c[e], s[e]) for e in range(c.shape[0])])
+        return dec(L.gate_codes, L.gate_scales), dec(L.up_codes, L.up_scales), dec(L.down_codes, L.down_scales)
+    f = lambda c: np.ascontiguousarray(c).view(np.float16).astype(np.float64)
+    return f(L.gate_codes), f(L.up_codes), f(L.down_codes)
+
+
+def np_silu(z):
+    return z * scipy.special.expit(z)
+
+
+def np_expert(Wg, Wu, Wd, X):
+    """X [n][H] -> [n][H]: the SwiGLU expert on each row."""
+    g = X @ Wg.T
+    u = X @ Wu.T
+    return (np_silu(g) * u) @ Wd.T
+
+
+def np_route(x, fmt, router, bias, k):
+    X = np_act(x, fmt)
+    logits = X @ router.astype(np.float64).T
+    if bias is not None:
+        logits = logits + bias.astype(np.float64)
+    p = scipy.special.softmax(logits, axis=1)
+    T, E = p.shape
+    order = np.stack([np.lexsort((np.arange(E), -p[t])) for t in range(T)])
+    return logits, p, order
+
+
+def close(a, b, rel=1e-10, what=""):
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    scale = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= rel * scale, f"{what}: max abs err {err:.3e} > {rel:.1e} * {scale:.3e}"
+
+
+def small_layer(T=6, H=64, E=5, k=2, S=0, I=96, seed=3, zipf=0.0, router_std=0.3, fmt="mxfp4", scale=(118, 127)):
+    wl = synth.custom(hidden=H, n_routed=E, top_k=k, n_shared=S, inter=I, weight_format=fmt,
+                      act_dtype="bf16" if fmt == "mxfp4" else "fp16", router_std=router_std, zipf_s=zipf,
+                      weight_std=0.05, scale_lo=scale[0], scale_hi=scale[1])
+    return synth.make_layer(wl, T, seed=seed)
+
+
+# ------------------------------------------------------------------------------------------------
+# number formats
+# ------------------------------------------------------------------------------------------------
+def check_minifloat_reference(o):
+    """The generic decoder agrees with numpy on every binary16 and bfloat16 pattern."""
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        f16 = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+        bf = (bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    for b in range(0, 65536, 7):  # every 7th pattern keeps this quick; all exponent fields are hit
+        r16 = minifloat(b, 5, 10, 15, True)
+        rbf = minifloat(b, 8, 7, 127, True)
+        assert (math.isnan(r16) and math.isnan(f16[b])) or r16 == f16[b], b
+        assert (math.isnan(rbf) and math.isnan(bf[b])) or rbf == bf[b], b
+
+
+def check_e2m1(o):
+    """v(c) for all 16 codes: the E2M1 layout, magnitudes equal to the page's set, bit 3 = sign."""
+    g = golden("mxfp4_format.json")
+    assert sorted(set(abs(v) for v in E2M1_REF)) == g["e2m1_magnitudes"]
+    for c in range(16):
+        v = o.e2m1(c)
+        assert v == E2M1_REF[c] and math.copysign(1, v) == math.copysign(1, E2M1_REF[c]), (c, v)
+    assert sorted(abs(o.e2m1(c)) for c in range(8)) == [abs(o.e2m1(c)) for c in range(8)]
+
+
+def check_e8m0(o):
+    """2^(e-127) against binary32 bit patterns (e in 0..254) and the closed form at e = 255."""
+    ref = scale_ref(np.arange(255))
+    for e in range(255):
+        assert o.e8m0(e) == ref[e], e
+    assert o.e8m0(255) == 2.0 ** 128
+
+
+def check_mxfp4_table(o):
+    """All 16 x 256 (code, scale) pairs against v(c) * 2^(e-127) evaluated two other ways."""
+    g = golden("mxfp4_format.json")
+    bias = g["scale_bias"]
+    for e in range(256):
+        s = 2.0 ** (e - bias)
+        for c in range(16):
+            v = o.mxfp4(c, e)
+            assert v == E2M1_REF[c] * s == math.ldexp(E2M1_REF[c], e - bias), (c, e, v)
+
+
+def check_bf16_f16(o):
+    for b in list(range(0, 65536, 11)) + [0x0001, 0x03FF, 0x0400, 0x7BFF, 0x7C00, 0x8001, 0xFC00, 0x3C00]:
+        r16 = minifloat(b, 5, 10, 15, True)
+        v = o.f16(b)
+        assert (math.isnan(v) and math.isnan(r16)) or v == r16, (b, v, r16)
+        rbf = minifloat(b, 8, 7, 127, True)
+        v = o.bf16(b)
+        assert (math.isnan(v) and math.isnan(rbf)) or v == rbf, (b, v, rbf)
+
+
+def check_storage(o):
+    """4 + 8/32 = 4.25 bits per weight, and the byte counts of the workloads."""
+    g = golden("mxfp4_format.json")
+    assert o.bits_per_weight() == g["bits_per_weight"]
+    for n, k in [(1, 32), (7, 96), (2048, 7168), (4096, 1536)]:
+        assert o.mxfp4_bytes(n, k) * 8 == n * k * g["bits_per_weight"], (n, k)
+    for case in golden("storage_sizes.json")["cases"]:
+        H, I, E = case["hidden"], case["inter"], case["experts"]
+        total = E * (2 * o.mxfp4_bytes(I, H) + o.mxfp4_bytes(H, I))
+        assert total == case["bytes"], case
+        if "code_bytes" in case:
+            assert E * 3 * I * H // 2 == case["code_bytes"] and E * 3 * I * H // 32 == case["scale_bytes"]
+
+
+def check_nibble_order(o):
+    """Hand-packed row: low nibble first, sign in bit 3."""
+    g = golden("nibble_order.json")
+    codes = np.frombuffer(bytes.fromhex(g["bytes_hex"]), np.uint8).reshape(1, 16)
+    scales = np.array([[g["scale_code"]]], np.uint8)
+    got = o.decode_matrix(codes, scales)[0]
+    want = np.array(g["values"])
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want)), got
+    # element access used by the FFN: expert 0's gate = this row, in a 1-row, 32-column matrix
+    gate = codes.reshape(1, 1, 16); gs = scales.reshape(1, 1, 1)
+    down = np.zeros((1, 32, 1), np.uint8); ds = np.full((1, 32, 1), 127, np.uint8)
+    W = ExpertWeights(W_MXFP4, gate, gs, gate, gs, down, ds)
+    for k in range(32):
+        v = o.weight(W, "gate", 0, 0, k)
+        assert v == want[k] and np.signbit(v) == np.signbit(want[k]), (k, v)
+
+
+def check_weight_access(o):
+    """orc_weight equals the numpy decode at every element, for strided (sliced) views too."""
+    L = small_layer(T=1, H=64, I=96, E=3)
+    W = ExpertWeights.from_layer(L)
+    Wg, Wu, Wd = np_weights(L)
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        e = int(rng.integers(3)); n = int(rng.integers(96)); k = int(rng.integers(64))
+        assert o.weight(W, "gate", e, n, k) == Wg[e, n, k]
+        assert o.weight(W, "up", e, n, k) == Wu[e, n, k]
+        assert o.weight(W, "down", e, k, n) == Wd[e, k, n]
+    # a column slice of the down projection (as in the all-active-slices layout)
+    big = L.down_codes  # [3][64][48]
+    view = big[:, :, 16:32]  # columns 32..63 of each expert: bytes 16..31, blocks 1..1
+    sv = L.down_scales[:, :, 1:2]
+    Wv = ExpertWeights(W_MXFP4, L.gate_codes, L.gate_scales, L.up_codes, L.up_scales, view, sv)
+    for e in range(3):
+        for m in range(0, 64, 9):
+            for n in range(32):
+                assert o.weight(Wv, "down", e, m, n) == Wd[e, m, 32 + n]
+
+
+def check_silu(o):
+    for z in [-1000.0, -50.0, -3.5, -1e-9, 0.0, 1e-9, 0.7, 2.0, 30.0, 700.0, 1000.0]:
+        v = o.silu(z)
+        assert not math.isnan(v)
+        ref = z * scipy.special.expit(z)
+        assert abs(v - ref) <= 1e-15 * max(1.0, abs(ref)), (z, v, ref)
+    assert o.silu(-1000.0) == 0.0
+
+
+def check_decode_matrix(o):
+    L = small_layer(T=1, H=96, I=64, E=2, scale=(0, 254))
+    for e in range(2):
+        assert np.array_equal(o.decode_matrix(L.gate_codes[e], L.gate_scales[e]),
+                              np_decode(L.gate_codes[e], L.gate_scales[e]))
+
+
+# ------------------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------------------
+def check_router_vs_numpy(o):
+    for (T, H, E, k, zipf) in [(9, 64, 7, 3, 0.0), (5, 96, 16, 4, 1.2), (4, 32, 3, 1, 0.0)]:
+        L = small_layer(T=T, H=H, E=E, k=k, zipf=zipf, router_std=0.4)
+        r = o.route(L.x, X_BF16, L.router, L.bias, k)
+        logits, p, order = np_route(L.x, X_BF16, L.router, L.bias, k)
+        close(r["logits"], logits, 1e-12, "logits")
+        close(r["probs"], p, 1e-12, "probs")
+        for t in range(T):
+            if not r["near_tie"][t]:
+                assert list(r["ids"][t]) == list(order[t, :k]), (t, r["ids"][t], order[t, :k])
+            sel = p[t, r["ids"][t]]
+            close(r["weights"][t], sel / sel.sum(), 1e-12, "weights")
+            assert abs(r["weights"][t].sum() - 1.0) <= 1e-12
+
+
+def check_router_tiebreak(o):
+    """Equal probabilities: lowest index first; the token is flagged as a near tie."""
+    H, E = 32, 6
+    router = np.zeros((E, H), np.float32)
+    router[1] = 0.25; router[4] = 0.25; router[2] = 0.5  # experts 1 and 4 tie, 2 leads
+    x = synth.to_bf16_bits(np.ones((1, H)))
+    r = o.route(x, X_BF16, router, None, 3)
+    assert list(r["ids"][0]) == [2, 1, 4], r["ids"]
+    r2 = o.route(x, X_BF16, router, None, 2)
+    assert list(r2["ids"][0]) == [2, 1]
+    assert r["near_tie"][0] == 1 and r2["near_tie"][0] == 1
+    # a clear gap is not flagged
+    router[4] = 0.0
+    r3 = o.route(x, X_BF16, router, None, 2)
+    assert list(r3["ids"][0]) == [2, 1] and r3["near_tie"][0] == 0
+
+
+def check_router_k_equals_E(o):
+    """k = E: every expert is selected, in descending-probability order, and w = p."""
+    L = small_layer(T=5, H=64, E=6, k=6)
+    r = o.route(L.x, X_BF16, L.router, None, 6)
+    _, p, order = np_route(L.x, X_BF16, L.router, None, 6)
+    for t in range(5):
+        assert sorted(r["ids"][t]) == list(range(6))
+        close(r["weights"][t], p[t, r["ids"][t]], 1e-12, "w=p")
+        if not r["near_tie"][t]:
+            assert list(r["ids"][t]) == list(order[t])
+
+
+def check_router_shift_invariance(o):
+    """Adding one constant to every logit (through the bias) changes neither p nor the choice."""
+    L = small_layer(T=7, H=64, E=9, k=3, zipf=1.2)
+    a = o.route(L.x, X_BF16, L.router, L.bias, 3)
+    b = o.route(L.x, X_BF16, L.router, (L.bias + np.float32(2.5)).astype(np.float32), 3)
+    close(a["probs"], b["probs"], 1e-12, "shift")
+    assert np.array_equal(a["ids"], b["ids"])
+    # the bias shapes the choice: without it the routing differs on this input
+    c = o.route(L.x, X_BF16, L.router, None, 3)
+    assert not np.array_equal(a["ids"], c["ids"])
+
+
+def check_router_shared(o):
+    """Cascadia's 6 routed + 2 shared = 8 selections per row; shared ids follow the routed ones."""
+    g = golden("cascadia_routing.json")
+    E, k = g["routed_experts"], g["top_k"]
+    S = len(g["shared_ids"])
+    L = small_layer(T=3, H=32, E=E, k=k, S=S)
+    r = o.route(L.x, X_BF16, L.router, None, k, S)
+    assert r["ids"].shape[1] == g["selections_per_row"]
+    for t in range(3):
+        assert list(r["ids"][t, k:]) == g["shared_ids"]
+        assert all(0 <= i < E for i in r["ids"][t, :k])
+        assert list(r["weights"][t, k:]) == [1.0] * S
+        assert abs(r["weights"][t, :k].sum() - 1.0) <= 1e-12
+
+
+# ------------------------------------------------------------------------------------------------
+# bucketing
+# ------------------------------------------------------------------------------------------------
+def check_bucket(o):
+    rng = np.random.default_rng(1)
+    for n, nb in [(1, 1), (40, 7), (300, 33), (1000, 257)]:
+        ids = rng.integers(0, nb, n).astype(np.int32)
+        b = o.bucket(ids, nb)
+        assert np.array_equal(b["counts"], np.bincount(ids, minlength=nb))
+        assert np.array_equal(b["offsets"], np.concatenate([[0], np.cumsum(np.bincount(ids, minlength=nb))]))
+        assert np.array_equal(b["sorted_slot"], np.argsort(ids, kind="stable"))
+        assert np.array_equal(b["slot_pos"][b["sorted_slot"]], np.arange(n))
+        assert b["n_valid"] == n
+
+
+def check_bucket_invalid(o):
+    ids = np.array([3, -1, 0, 9, 3, 2, 100], np.int32)
+    b = o.bucket(ids, 4)
+    assert list(b["counts"]) == [1, 0, 1, 2] and b["n_valid"] == 4
+    assert list(b["sorted_slot"]) == [2, 5, 0, 4, -1, -1, -1]
+    assert list(b["slot_pos"]) == [2, -1, 0, -1, 3, 1, -1]
+
+
+# ------------------------------------------------------------------------------------------------
+# expert FFN, combine, layer
+# ------------------------------------------------------------------------------------------------
+def check_expert_apply_vs_numpy(o):
+    """One expert on one vector: the decode-in-reduction sums equal numpy matmuls over the
+    numpy-decoded matrices (non-square H != I catches a transposed operand)."""
+    for fmt in ("mxfp4", "fp16"):
+        L = small_layer(T=3, H=64, I=96, E=3, fmt=fmt)
+        W = ExpertWeights.from_layer(L)
+        Wg, Wu, Wd = np_weights(L)
+        xf = X_BF16 if fmt == "mxfp4" else X_FP16
+        X = np_act(L.x, xf)
+        for e in range(3):
+            ref = np_expert(Wg[e], Wu[e], Wd[e], X)
+            for t in range(3):
+                close(o.expert_apply(W, e, X[t]), ref[t], 1e-11, f"expert {fmt} e={e}")
+
+
+def check_layer_vs_numpy(o):
+    """The whole oracle layer against numpy routing + per-token expert mixture."""
+    for (T, H, E, k, S, I) in [(8, 64, 5, 2, 0, 96), (6, 32, 4, 3, 1, 64)]:
+        L = small_layer(T=T, H=H, E=E, k=k, S=S, I=I)
+        out = o.layer(L)
+        _, p, order = np_route(L.x, X_BF16, L.router, L.bias, k)
+        Wg, Wu, Wd = np_weights(L)
+        X = np_act(L.x, X_BF16)
+        ref = np.zeros((T, H))
+        for t in range(T):
+            sel = order[t, :k]
+            w = p[t, sel] / p[t, sel].sum()
+            for j, e in enumerate(sel):
+                ref[t] += w[j] * np_expert(Wg[e], Wu[e], Wd[e], X[t:t + 1])[0]
+            for s in range(S):
+                e = E + s
+                ref[t] += np_expert(Wg[e], Wu[e], Wd[e], X[t:t + 1])[0]
+        keep = out["route"]["near_tie"] == 0
+        close(out["y"][keep], ref[keep], 1e-10, "layer")
+
+
+def check_layer_forms(o):
+    """Grouped path (bucket + slots + combine) == per-token brute force == dense mixture."""
+    L = small_layer(T=7, H=64, E=6, k=2, S=1, I=64)
+    out = o.layer(L)
+    r = out["route"]
+    yb = o.layer_bruteforce(L.x, X_BF16, out["weights"], r["ids"], r["weights"])
+    yc = o.layer_dense_mixture(L.x, X_BF16, out["weights"], r["ids"], r["weights"])
+    close(out["y"], yb, 1e-12, "grouped vs brute force")
+    close(out["y"], yc, 1e-12, "grouped vs dense mixture")
+
+
+def check_single_expert_swiglu(o):
+    """E = k = 1: the layer is the textbook SwiGLU FFN W_d[SiLU(W_g x) * W_u x]."""
+    L = small_layer(T=4, H=64, E=1, k=1, I=96)
+    out = o.layer(L)
+    Wg, Wu, Wd = np_weights(L)
+    X = np_act(L.x, X_BF16)
+    close(out["y"], np_expert(Wg[0], Wu[0], Wd[0], X), 1e-11, "swiglu")
+    assert np.all(out["route"]["weights"] == 1.0)
+
+
+def check_combine(o):
+    rng = np.random.default_rng(2)
+    T, kt, H = 5, 3, 16
+    ys = rng.standard_normal((T * kt, H))
+    w1 = rng.standard_normal((T, kt)); w2 = rng.standard_normal((T, kt))
+    ref = np.einsum("tj,tjh->th", w1, ys.reshape(T, kt, H))
+    close(o.combine(ys, w1), ref, 1e-13, "combine")
+    onehot = np.zeros((T, kt)); onehot[:, 1] = 1.0
+    assert np.array_equal(o.combine(ys, onehot), ys.reshape(T, kt, H)[:, 1])
+    close(o.combine(ys, 2.0 * w1 - 3.0 * w2), 2.0 * o.combine(ys, w1) - 3.0 * o.combine(ys, w2), 1e-12, "linear")
+
+
+def check_dense_slices(o):
+    """Eq. 2: the sum of 8 all-active unit-weight slices equals the unsliced dense FFN, and the
+    unsliced FFN equals numpy's."""
+    g = golden("dense_slices.json")
+    ns = g["n_slices"]
+    wl = synth.custom(hidden=64, n_routed=ns, top_k=ns, inter=32, weight_format="fp16", act_dtype="fp16",
+                      weight_std=0.05, dense_slices=True)
+    L = synth.make_layer(wl, 3, seed=5)
+    wg, wu, wd = synth.make_dense_fp16(wl, seed=5)
+    out = o.layer(L)
+    assert np.all(out["route"]["weights"] == g["slice_weight"])
+    dense = o.dense_ffn_f16(L.x, X_FP16, wg, wu, wd)
+    close(out["y"], dense, 1e-12, "slices vs dense")
+    f = lambda a: a.view(np.float16).astype(np.float64)
+    close(dense, np_expert(f(wg), f(wu), f(wd), np_act(L.x, X_FP16)), 1e-12, "dense vs numpy")
+
+
+ALL_CHECKS = [
+    check_minifloat_reference, check_e2m1, check_e8m0, check_mxfp4_table, check_bf16_f16, check_storage,
+    check_nibble_order, check_weight_access, check_silu, check_decode_matrix,
+    check_router_vs_numpy, check_router_tiebreak, check_router_k_equals_E, check_router_shift_invariance,
+    check_router_shared, check_bucket, check_bucket_invalid,
+    check_expert_apply_vs_numpy, check_layer_vs_numpy, check_layer_forms, check_single_expert_swiglu,
+    check_combine, check_dense_slices,
+]

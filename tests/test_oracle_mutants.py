@@ -1,0 +1,67 @@
+"""Every plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+Each mutant is a (search, replace) edit of oracle/moe_oracle.c; the search text must occur exactly
+once, so a mutant cannot silently stop applying when the oracle changes.  The mutated copy is
+compiled on the CPU into a temporary library and checked with the same pins as the real oracle.
+All mutants keep every memory access in bounds.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "nibble order swapped": ("int code = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                             "int code = (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);"),
+    "scale exponent off by one": ("return ldexp(1.0, e - 127);", "return ldexp(1.0, e - 126);"),
+    "sign bit dropped": ("return (code & 8) ? -mag : mag;", "return mag;"),
+    "magnitudes 3 and 4 swapped": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 4.0, 3.0, 6.0}"),
+    "wrong scale block": ("return orc_mxfp4(code, srow[k / 32]);", "return orc_mxfp4(code, srow[k / 64]);"),
+    "gate and up swapped in SwiGLU": ("hs[(int64_t)i * I + n] = orc_silu(g) * u;", "hs[(int64_t)i * I + n] = orc_silu(u) * g;"),
+    "SiLU sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "routing weights not renormalised": ("weights[(int64_t)t * k_total + j] = p[order[j]] / sel;",
+                                         "weights[(int64_t)t * k_total + j] = p[order[j]];"),
+    "router bias dropped": ("L[e] = acc + (bias ? (double)bias[e] : 0.0);", "L[e] = acc;"),
+    "tie-break to the highest index": ("(p[a] == p[b] && a < b)", "(p[a] == p[b] && a > b)"),
+    "last hidden term dropped in router": ("for (int h = 0; h < H; ++h)\n        acc += act_value",
+                                           "for (int h = 0; h < H - 1; ++h)\n        acc += act_value"),
+    "shared expert id off": ("ids[(int64_t)t * k_total + top_k + s] = E + s;",
+                             "ids[(int64_t)t * k_total + top_k + s] = E - 1 - s;"),
+    "bucket order not stable": ("int pos = offsets[b] + fill[b]++;",
+                                "int pos = offsets[b + 1] - 1 - fill[b]++;"),
+    "combine uses reversed weights": ("acc += weights[(int64_t)t * k_total + j] * y_slots",
+                                      "acc += weights[(int64_t)t * k_total + (k_total - 1 - j)] * y_slots"),
+    "down projection reads the wrong row": ("for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, m, n);",
+                                            "for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, (m + 1) % H, n);"),
+    "fp16 exponent bias": ("v = ldexp(1024.0 + (double)fr, ex - 25);", "v = ldexp(1024.0 + (double)fr, ex - 24);"),
+    "x row of the wrong token": ("int t = slot[i] / k_total;", "int t = slot[i] % T;"),
+    "probabilities mis-normalised by 1e-7": ("for (int e = 0; e < E; ++e) p[e] /= den;",
+                                               "for (int e = 0; e < E; ++e) p[e] /= den * 1.0000001;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(source, name, tmp_path):
+    search, replace = MUTANTS[name]
+    assert source.count(search) == 1, f"mutant '{name}' no longer applies"
+    src = tmp_path / "moe_oracle.c"
+    src.write_text(source.replace(search, replace))
+    lib = tmp_path / "liboracle_mutant.so"
+    oracle.build(str(src), str(lib))
+    mutant = oracle.Oracle(str(lib))
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"no pin catches the planted mistake '{name}'"

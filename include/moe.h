@@ -1,0 +1,187 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts feed-forward layer for AMD Instinct MI355X
+ * (gfx950).  Four calls make one layer: moe_route -> moe_bucket -> moe_expert_ffn -> moe_combine.
+ *
+ * Sources (cited by page title and section; the pages print no code):
+ *  [MX]  "DeepSeek-V4-Flash on a four-GPU Ampere workstation" (FreeToken blog post), section
+ *        "MXFP4 is not NVFP4, and the difference matters on Ampere": packed E2M1 codes with one
+ *        unsigned E8M0 scale per 32 values, decoded weight v(c) * 2^(e-127), 4.25 bits/weight,
+ *        decode inside the reduction with FP32 accumulation, row-major banks read with no repack.
+ *  [BP]  same post, section "Why it would not run": a partition that cuts an FP4 32-value block
+ *        is rejected instead of producing garbage; weights and scale grids are sliced together.
+ *  [C31] "Cascadia: Resident 975B MoE Inference on Eleven AI PCs", Sec. 3.1: expert-major banks;
+ *        gate/up projections, SwiGLU, down projection and weighted reduction over the selected
+ *        experts; routing yields expert ids and routing weights; shared experts are always-included
+ *        selections after the routed ones.
+ *  [C32] Cascadia Sec. 3.2: a layer call supplies rows, expert ids and routing weights; the
+ *        expert path returns FP32 output (Fig. 2).
+ *  [C34] Cascadia Sec. 3.4, Eq. 2: a dense FFN is the sum of its all-active, unit-weight slices,
+ *        cut at quantisation-group boundaries.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers of the current HIP device unless a comment says "host".
+ *    The caller owns and allocates every buffer; the library never allocates, frees or keeps
+ *    device memory, and keeps no state between calls.
+ *  - Calls only validate arguments on the host and enqueue work on `stream` (a hipStream_t, or
+ *    NULL for the default stream); they never synchronise and never read device memory on the
+ *    host.  Results are ready when the stream has reached that point.
+ *  - Validation happens before anything is enqueued; on any error nothing is launched and the
+ *    status says why.  T == 0 returns MOE_OK without touching any pointer.
+ *  - Inputs are read-only; outputs are overwritten (never accumulated into); buffers must not
+ *    alias each other.  Calls that share no output buffer may run concurrently on different
+ *    streams.
+ *  - Results are deterministic: the same inputs give bit-identical outputs on every run (no
+ *    floating-point atomics anywhere).
+ */
+#ifndef MOE_H
+#define MOE_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024  /* routed experts E, and buckets / experts E' of the later calls */
+#define MOE_MAX_SLOTS_PER_TOKEN 256  /* top_k + n_shared */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is negative, zero where it must not be, or beyond a limit */
+  MOE_ERR_BLOCK = 3,     /* an MXFP4 dimension, slice or stride cuts a 32-value block [BP] */
+  MOE_ERR_ALIGN = 4,     /* a pointer or byte stride is not 16-byte aligned */
+  MOE_ERR_DTYPE = 5,     /* an unknown enum value, or an activation dtype the format cannot take */
+  MOE_ERR_TOPK = 6,      /* top_k < 1 or top_k > E */
+  MOE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than the size query returns */
+  MOE_ERR_HIP = 8        /* a kernel launch failed (the HIP error is lost; nothing else ran) */
+} moe_status;
+
+typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_FP16 = 1 } moe_act_dtype;
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP16 = 1 } moe_w_format;
+
+/* One projection of every expert: logical [n_experts][N][K], K contiguous within a row [MX].
+ *  MXFP4: `w` holds two E2M1 codes per byte, element k of a row in byte k/2 with even k in the
+ *         low nibble (bits 3..0) and odd k in the high nibble; bit 3 of a code is its sign.
+ *         `scales` holds one E8M0 byte per 32 elements: scale of element k at byte k/32 of the
+ *         row.  Decoded weight = v(code) * 2^(scale - 127) [MX].  Scale codes 0..254 are
+ *         supported; 255 is outside the contract.
+ *  FP16:  `w` holds IEEE binary16 values; `scales` must be NULL.
+ *  Strides are in bytes between consecutive experts / rows, so a projection may be a slice of a
+ *  larger matrix [C34] -- e.g. columns [j*I, (j+1)*I) of a dense [H][8*I] down projection have
+ *  w = base + j*I*(bytes per element), w_expert_stride = I*(bytes per element),
+ *  w_row_stride = 8*I*(bytes per element).  w, w_expert_stride and w_row_stride must be
+ *  multiples of 16 bytes (for MXFP4 that is exactly one 32-code block, so an aligned slice never
+ *  cuts a block [BP]); scale pointers and strides have no alignment rule. */
+typedef struct {
+  const void *w;
+  const uint8_t *scales;
+  int64_t w_expert_stride, w_row_stride;
+  int64_t s_expert_stride, s_row_stride;
+} moe_proj;
+
+/* All expert weights of a layer [C31].  gate and up: N = inter, K = hidden; down: N = hidden,
+ * K = inter.  n_experts = E' = routed + shared experts (one bucket each).  hidden and inter must
+ * be positive multiples of 32.  The struct itself is a HOST struct holding device pointers. */
+typedef struct {
+  moe_w_format fmt;
+  int n_experts;
+  int hidden;
+  int inter;
+  moe_proj gate, up, down;
+} moe_expert_weights;
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_route -- router logits, softmax, top-k, renormalised weights, shared slots.
+ *
+ * Per token t (reading of [C31]; the pages print no softmax router, the order below is the
+ * method's statement): L[t,e] = sum_h x[t,h] * w_router[e,h] + logit_bias[e] (fp32 accumulation),
+ * p = softmax(L[t,:]); the top_k experts by (L descending, index ascending) -- i.e. by p with the
+ * lowest index winning exact ties -- fill slots j = 0..top_k-1 in that order with
+ * weights[t,j] = p_j / sum_{j'<top_k} p_j'; slots top_k .. top_k+n_shared-1 get the shared
+ * experts E .. E+n_shared-1 with weight 1.0.
+ *   x          [T][H] bf16 or fp16 (x_dtype), rows contiguous, 16-byte aligned
+ *   w_router   [E][H] fp32 (4-byte aligned, like every int32/fp32 array below)
+ *   logit_bias [E] fp32 added to the logits before the softmax, or NULL
+ *   ids        [T][top_k+n_shared] int32 out;  weights [T][top_k+n_shared] fp32 out
+ *   probs      [T][E] fp32 out (the full softmax), or NULL
+ *   workspace  moe_route_workspace_bytes(T, H, E) bytes, 16-byte aligned (NULL if that is 0)
+ * Errors: NULL, SHAPE (T<0, H<1, E<1, E>MOE_MAX_EXPERTS, n_shared<0), TOPK (also
+ * top_k+n_shared > MOE_MAX_SLOTS_PER_TOKEN), DTYPE, ALIGN, WORKSPACE, HIP. */
+size_t moe_route_workspace_bytes(int T, int H, int E);
+moe_status moe_route(const void *x, moe_act_dtype x_dtype, int T, int H, const float *w_router,
+                     const float *logit_bias, int E, int top_k, int n_shared, int32_t *ids,
+                     float *weights, float *probs, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_bucket -- group slots by expert (the fused path runs only the selected experts' work
+ * [C31]).  Slot s = t*k_total + j.
+ *   counts[b]      number of slots with ids[s] == b                         ([n_buckets])
+ *   offsets[b]     exclusive prefix sum of counts; offsets[n_buckets] = number of valid slots
+ *   sorted_slot[r] slot indices bucket by bucket, ascending slot index within a bucket (stable)
+ *   slot_pos[s]    inverse permutation: sorted_slot[slot_pos[s]] == s           (or NULL)
+ * A slot whose id is outside [0, n_buckets) is dropped: slot_pos = -1 and it is not counted;
+ * entries of sorted_slot past offsets[n_buckets] are -1.  (Ids live on the device, so this is
+ * the only possible check; the expert FFN then leaves that slot's y_slots row unwritten.)
+ *   workspace  moe_bucket_workspace_bytes(n_slots, n_buckets) bytes (NULL if that is 0)
+ * Errors: NULL, SHAPE (n_slots<0, n_buckets<1 or >MOE_MAX_EXPERTS), ALIGN, WORKSPACE, HIP. */
+size_t moe_bucket_workspace_bytes(int n_slots, int n_buckets);
+moe_status moe_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *counts,
+                      int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_expert_ffn -- grouped SwiGLU experts over the buckets [C31], decode inside the reduction
+ * with FP32 accumulation [MX].
+ * For every expert e and sorted row r in [offsets[e], offsets[e+1]) with slot s = sorted_slot[r]
+ * and token t = s / k_total:
+ *   g = W_gate[e] x_t,  u = W_up[e] x_t  (fp32 accumulation of exact products),
+ *   h = SiLU(g) * u     (fp32; fed to the down projection as a bf16 (fp16 for FP16 weights)
+ *                        high + low pair, i.e. about 16 significant bits),
+ *   y_slots[s,:] = W_down[e] h   (fp32).
+ *   x        [T][hidden] activations; MXFP4 weights need MOE_ACT_BF16, FP16 weights MOE_ACT_FP16
+ *   W        host pointer to the weight description (device pointers inside)
+ *   offsets  [W->n_experts + 1], sorted_slot [T*k_total] as written by moe_bucket
+ *   y_slots  [T*k_total][hidden] fp32 out; rows of dropped slots are left unwritten
+ *   workspace moe_expert_ffn_workspace_bytes(T, k_total, W) bytes, 16-byte aligned
+ * Sorted rows whose slot lies outside [0, T*k_total) are skipped, so corrupt device-side indices
+ * cannot cause out-of-bounds accesses.
+ * Errors: NULL, SHAPE, BLOCK (MXFP4 hidden or inter not a multiple of 32), ALIGN, DTYPE,
+ * WORKSPACE, HIP. */
+size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weights *W);
+moe_status moe_expert_ffn(const void *x, moe_act_dtype x_dtype, int T, int k_total,
+                          const moe_expert_weights *W, const int32_t *offsets,
+                          const int32_t *sorted_slot, float *y_slots, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_combine -- weighted reduction [C31] with FP32 output [C32]:
+ *   y[t,:] = sum_{j = 0 .. k_total-1, in ascending j} weights[t,j] * y_slots[t*k_total+j,:]
+ * Every output element has exactly one owner (no atomics).
+ *   y_slots [T*k_total][H] fp32, weights [T][k_total] fp32, y [T][H] fp32 out; H % 4 == 0,
+ *   y_slots and y 16-byte aligned.
+ * Errors: NULL, SHAPE, ALIGN, HIP. */
+moe_status moe_combine(const float *y_slots, const float *weights, int T, int k_total, int H,
+                       float *y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_mxfp4_dequant -- the device decode primitive of the expert FFN, exposed on its own: writes
+ * out[n][k] = bf16(v(code) * 2^(scale-127)) for an [n_rows][K] MXFP4 matrix [MX].  The value is
+ * exact in bf16 whenever it is finite (all scale codes 0..252; larger codes can overflow).
+ *   codes [n_rows] rows of K/2 bytes at code_row_stride; scales [n_rows] rows of K/32 bytes at
+ *   scale_row_stride; out [n_rows][K] bf16 (uint16 bits), 16-byte aligned.
+ * Errors: NULL, SHAPE, BLOCK (K % 32), ALIGN, HIP. */
+moe_status moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int n_rows, int K,
+                             int64_t code_row_stride, int64_t scale_row_stride, uint16_t *out,
+                             void *stream);
+
+/* Short text for a status code (host, static storage). */
+const char *moe_status_str(moe_status status);
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,287 @@
+"""Routed Mixture-of-Experts FFN layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/moe.h (libmoe.so, built from csrc/ by _build.py).  The
+functions keep the C names and only marshal arguments: torch tensors provide device memory and the
+current HIP stream; every step of the layer runs in the library's HIP kernels.  There is no CPU
+fallback -- importing works anywhere, but any call raises when libmoe.so is missing or no GPU is
+present.
+
+    ids, w, probs = moe_route(x, w_router, top_k, bias, n_shared)     # router
+    b = moe_bucket(ids, n_experts)                                     # group slots by expert
+    y_slots = moe_expert_ffn(x, W, b.offsets, b.sorted_slot, k_total)  # SwiGLU experts
+    y = moe_combine(y_slots, w)                                        # weighted combine, fp32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libmoe.so")
+ROOT = os.path.dirname(PKG)
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_ACT_BF16, MOE_ACT_FP16 = 0, 1
+MOE_W_MXFP4, MOE_W_FP16 = 0, 1
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_BLOCK", 4: "MOE_ERR_ALIGN",
+          5: "MOE_ERR_DTYPE", 6: "MOE_ERR_TOPK", 7: "MOE_ERR_WORKSPACE", 8: "MOE_ERR_HIP"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class moe_proj(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("w_expert_stride", ctypes.c_int64), ("w_row_stride", ctypes.c_int64),
+                ("s_expert_stride", ctypes.c_int64), ("s_row_stride", ctypes.c_int64)]
+
+
+class moe_expert_weights(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("n_experts", ctypes.c_int), ("hidden", ctypes.c_int),
+                ("inter", ctypes.c_int), ("gate", moe_proj), ("up", moe_proj), ("down", moe_proj)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with `python -m mxfp4_routed_expert_router_amd._build` "
+                               "(or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(LIBRARY)
+        vp, i, st, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int64
+        L.moe_status_str.restype = ctypes.c_char_p; L.moe_status_str.argtypes = [i]
+        L.moe_abi_version.restype = i; L.moe_abi_version.argtypes = []
+        L.moe_route_workspace_bytes.restype = st; L.moe_route_workspace_bytes.argtypes = [i, i, i]
+        L.moe_route.restype = i
+        L.moe_route.argtypes = [vp, i, i, i, vp, vp, i, i, i, vp, vp, vp, vp, st, vp]
+        L.moe_bucket_workspace_bytes.restype = st; L.moe_bucket_workspace_bytes.argtypes = [i, i]
+        L.moe_bucket.restype = i
+        L.moe_bucket.argtypes = [vp, i, i, vp, vp, vp, vp, vp, st, vp]
+        L.moe_expert_ffn_workspace_bytes.restype = st
+        L.moe_expert_ffn_workspace_bytes.argtypes = [i, i, ctypes.POINTER(moe_expert_weights)]
+        L.moe_expert_ffn.restype = i
+        L.moe_expert_ffn.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp, st, vp]
+        L.moe_combine.restype = i
+        L.moe_combine.argtypes = [vp, vp, i, i, i, vp, vp]
+        L.moe_mxfp4_dequant.restype = i
+        L.moe_mxfp4_dequant.argtypes = [vp, vp, i, i, i64, i64, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MoEError(status, where, lib().moe_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _act_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return MOE_ACT_BF16
+    if x.dtype == torch.float16:
+        return MOE_ACT_FP16
+    raise TypeError(f"activations must be bfloat16 or float16, got {x.dtype}")
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
+class ExpertWeights:
+    """Device weights of all experts of a layer, described for moe_expert_ffn.
+
+    MXFP4: gate/up codes uint8 [E'][I][H/2], scales uint8 [E'][I][H/32]; down codes [E'][H][I/2],
+    scales [E'][H][I/32].  FP16: gate/up float16 [E'][I][H], down [E'][H][I], scales None.
+    Any strided view whose last dimension is contiguous is accepted (slices of a larger matrix)."""
+
+    def __init__(self, gate, gate_scales, up, up_scales, down, down_scales):
+        fmt = MOE_W_FP16 if gate.dtype == torch.float16 else MOE_W_MXFP4
+        self.tensors = (gate, gate_scales, up, up_scales, down, down_scales)
+        E2, I = gate.shape[0], gate.shape[1]
+        H = down.shape[1]
+        self.fmt, self.n_experts, self.hidden, self.inter = fmt, E2, H, I
+
+        def proj(c, s):
+            p = moe_proj()
+            p.w = c.data_ptr()
+            es = c.element_size()
+            p.w_expert_stride, p.w_row_stride = c.stride(0) * es, c.stride(1) * es
+            if c.stride(2) != 1:
+                raise ValueError("weight rows must be contiguous")
+            if s is not None:
+                p.scales = s.data_ptr()
+                p.s_expert_stride, p.s_row_stride = s.stride(0), s.stride(1)
+            return p
+
+        self.c = moe_expert_weights(fmt, E2, H, I, proj(gate, gate_scales), proj(up, up_scales),
+                                    proj(down, down_scales))
+
+    @property
+    def device(self):
+        return self.tensors[0].device
+
+    def weight_bytes(self, experts=None) -> int:
+        """Logical bytes (codes + scales) of the given experts (all when None)."""
+        per = 0
+        for t in self.tensors:
+            if t is not None:
+                per += t[0].numel() * t.element_size()
+        n = self.n_experts if experts is None else len(experts)
+        return per * n
+
+
+# ----------------------------------------------------------------------------------------------------
+def moe_route_workspace_bytes(T: int, H: int, E: int) -> int:
+    return lib().moe_route_workspace_bytes(T, H, E)
+
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, top_k: int, logit_bias: Optional[torch.Tensor] = None,
+              n_shared: int = 0, want_probs: bool = False, out=None, workspace=None):
+    """-> (ids int32 [T][k'], weights fp32 [T][k'], probs fp32 [T][E] or None)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    kt = top_k + n_shared
+    dev = x.device
+    if out is None:
+        ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
+        w = torch.empty((T, kt), dtype=torch.float32, device=dev)
+        probs = torch.empty((T, E), dtype=torch.float32, device=dev) if want_probs else None
+    else:
+        ids, w, probs = out
+    need = moe_route_workspace_bytes(T, H, E)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_route(_ptr(x), _act_dtype(x), T, H, _ptr(w_router), _ptr(logit_bias), E, top_k, n_shared,
+                           _ptr(ids), _ptr(w), _ptr(probs), _ptr(ws), 0 if ws is None else ws.numel(),
+                           _stream(dev)), "moe_route")
+    return ids, w, probs
+
+
+@dataclass
+class Buckets:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    sorted_slot: torch.Tensor
+    slot_pos: Optional[torch.Tensor]
+
+
+def moe_bucket_workspace_bytes(n_slots: int, n_buckets: int) -> int:
+    return lib().moe_bucket_workspace_bytes(n_slots, n_buckets)
+
+
+def moe_bucket(ids: torch.Tensor, n_buckets: int, out: Optional[Buckets] = None, workspace=None) -> Buckets:
+    n = ids.numel()
+    dev = ids.device
+    if out is None:
+        out = Buckets(torch.empty(n_buckets, dtype=torch.int32, device=dev),
+                      torch.empty(n_buckets + 1, dtype=torch.int32, device=dev),
+                      torch.empty(n, dtype=torch.int32, device=dev),
+                      torch.empty(n, dtype=torch.int32, device=dev))
+    need = moe_bucket_workspace_bytes(n, n_buckets)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_bucket(_ptr(ids), n, n_buckets, _ptr(out.counts), _ptr(out.offsets), _ptr(out.sorted_slot),
+                            _ptr(out.slot_pos), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)),
+           "moe_bucket")
+    return out
+
+
+def moe_expert_ffn_workspace_bytes(T: int, k_total: int, W: ExpertWeights) -> int:
+    return lib().moe_expert_ffn_workspace_bytes(T, k_total, ctypes.byref(W.c))
+
+
+def moe_expert_ffn(x: torch.Tensor, W: ExpertWeights, offsets: torch.Tensor, sorted_slot: torch.Tensor,
+                   k_total: int, out: Optional[torch.Tensor] = None, workspace=None) -> torch.Tensor:
+    """-> y_slots fp32 [T*k_total][hidden] (rows of dropped slots are left as allocated)."""
+    T = x.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((T * k_total, W.hidden), dtype=torch.float32, device=dev)
+    need = moe_expert_ffn_workspace_bytes(T, k_total, W)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_expert_ffn(_ptr(x), _act_dtype(x), T, k_total, ctypes.byref(W.c), _ptr(offsets),
+                                _ptr(sorted_slot), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream(dev)), "moe_expert_ffn")
+    return y
+
+
+def moe_combine(y_slots: torch.Tensor, weights: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, kt = weights.shape
+    H = y_slots.shape[-1]
+    y = out if out is not None else torch.empty((T, H), dtype=torch.float32, device=y_slots.device)
+    _check(lib().moe_combine(_ptr(y_slots), _ptr(weights), T, kt, H, _ptr(y), _stream(y_slots.device)),
+           "moe_combine")
+    return y
+
+
+def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """[N][K/2] codes + [N][K/32] scales -> [N][K] bfloat16 (the FFN's decode primitive)."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=codes.device)
+    _check(lib().moe_mxfp4_dequant(_ptr(codes), _ptr(scales), N, K, codes.stride(0), scales.stride(0), _ptr(out),
+                                   _stream(codes.device)), "moe_mxfp4_dequant")
+    return out
+
+
+# ----------------------------------------------------------------------------------------------------
+class MoELayer:
+    """One routed-MoE layer with every intermediate buffer allocated once, so that forward() only
+    enqueues the four library calls (capturable in a HIP graph)."""
+
+    def __init__(self, W: ExpertWeights, T: int, top_k: int, n_shared: int = 0,
+                 w_router: Optional[torch.Tensor] = None, logit_bias: Optional[torch.Tensor] = None):
+        self.W, self.T, self.top_k, self.n_shared = W, T, top_k, n_shared
+        self.w_router, self.logit_bias = w_router, logit_bias
+        dev = W.device
+        kt = top_k + n_shared
+        self.k_total = kt
+        H = W.hidden
+        E = W.n_experts - n_shared
+        self.dense = w_router is None  # all-active slices: caller-fixed ids j, weights 1
+        if self.dense:
+            self.ids = torch.arange(kt, dtype=torch.int32, device=dev).repeat(T, 1).contiguous()
+            self.weights = torch.ones((T, kt), dtype=torch.float32, device=dev)
+            self.route_ws = None
+        else:
+            self.ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
+            self.weights = torch.empty((T, kt), dtype=torch.float32, device=dev)
+            self.route_ws = _workspace(moe_route_workspace_bytes(T, H, E), dev)
+        n = T * kt
+        self.buckets = Buckets(torch.empty(W.n_experts, dtype=torch.int32, device=dev),
+                               torch.empty(W.n_experts + 1, dtype=torch.int32, device=dev),
+                               torch.empty(n, dtype=torch.int32, device=dev),
+                               torch.empty(n, dtype=torch.int32, device=dev))
+        self.bucket_ws = _workspace(moe_bucket_workspace_bytes(n, W.n_experts), dev)
+        self.y_slots = torch.empty((n, H), dtype=torch.float32, device=dev)
+        self.ffn_ws = _workspace(moe_expert_ffn_workspace_bytes(T, kt, W), dev)
+        self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if not self.dense:
+            moe_route(x, self.w_router, self.top_k, self.logit_bias, self.n_shared,
+                      out=(self.ids, self.weights, None), workspace=self.route_ws)
+        moe_bucket(self.ids, self.W.n_experts, out=self.buckets, workspace=self.bucket_ws)
+        moe_expert_ffn(x, self.W, self.buckets.offsets, self.buckets.sorted_slot, self.k_total, out=self.y_slots,
+                       workspace=self.ffn_ws)
+        return moe_combine(self.y_slots, self.weights, out=self.y)
+
+
+__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine", "moe_mxfp4_dequant",
+           "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",
+           "ExpertWeights", "Buckets", "MoELayer", "MoEError", "lib"]

@@ -1,0 +1,177 @@
+// The C ABI (include/moe.h): synchronous host-side validation, then asynchronous launches on the
+// caller's stream.  Nothing here allocates, synchronises or reads device memory.
+#include <limits.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Checks of one projection; K is its reduction dimension.
+moe_status check_proj(const moe_proj& p, moe_w_format fmt, int n_experts, int N, int K) {
+  if (!p.w) return MOE_ERR_NULL;
+  if (fmt == MOE_W_MXFP4) {
+    if (!p.scales) return MOE_ERR_NULL;
+    if (K % 32 != 0) return MOE_ERR_BLOCK;
+    if (p.w_row_stride < K / 2 || p.s_row_stride < K / 32 || p.w_expert_stride < 0 || p.s_expert_stride < 0)
+      return MOE_ERR_SHAPE;
+  } else {
+    if (p.scales) return MOE_ERR_DTYPE;
+    if (K % 32 != 0) return MOE_ERR_SHAPE;
+    if (p.w_row_stride < 2 * (int64_t)K || p.w_expert_stride < 0) return MOE_ERR_SHAPE;
+  }
+  if (!al16(p.w) || p.w_row_stride % 16 != 0 || p.w_expert_stride % 16 != 0) return MOE_ERR_ALIGN;
+  (void)n_experts;
+  (void)N;
+  return MOE_OK;
+}
+
+moe::ProjDev dev(const moe_proj& p) {
+  moe::ProjDev d;
+  d.w = (const uint8_t*)p.w;
+  d.s = p.scales;
+  d.we = p.w_expert_stride;
+  d.wr = p.w_row_stride;
+  d.se = p.s_expert_stride;
+  d.sr = p.s_row_stride;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid size or shape";
+    case MOE_ERR_BLOCK: return "MXFP4 dimension or slice cuts a 32-value block";
+    case MOE_ERR_ALIGN: return "pointer or stride not aligned";
+    case MOE_ERR_DTYPE: return "unsupported dtype or format combination";
+    case MOE_ERR_TOPK: return "invalid top_k";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_route_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  const int s = moe::route_splits(T, H, E);
+  return round_up(sizeof(float) * (size_t)s * (size_t)T * (size_t)E, 256);
+}
+
+moe_status moe_route(const void* x, moe_act_dtype x_dtype, int T, int H, const float* w_router,
+                     const float* logit_bias, int E, int top_k, int n_shared, int32_t* ids, float* weights,
+                     float* probs, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (T < 0 || H < 1 || E < 1 || E > MOE_MAX_EXPERTS || n_shared < 0) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
+  if (top_k < 1 || top_k > E || top_k + n_shared > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_TOPK;
+  if (!x || !w_router || !ids || !weights) return MOE_ERR_NULL;
+  if ((int64_t)T * (top_k + n_shared) > INT_MAX || (int64_t)T * E > INT_MAX) return MOE_ERR_SHAPE;
+  if (!al16(x) || !al4(w_router) || !al4(ids) || !al4(weights) || (probs && !al4(probs)) ||
+      (logit_bias && !al4(logit_bias)))
+    return MOE_ERR_ALIGN;
+  const size_t need = moe_route_workspace_bytes(T, H, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k, n_shared,
+                                      ids, weights, probs, (float*)workspace, moe::route_splits(T, H, E),
+                                      (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_bucket_workspace_bytes(int n_slots, int n_buckets) {
+  if (n_slots <= moe::kBucketChunk || n_buckets <= 0) return 0;
+  const size_t chunks = (size_t)(n_slots + moe::kBucketChunk - 1) / moe::kBucketChunk;
+  return round_up(sizeof(int32_t) * ((size_t)n_slots + chunks * (size_t)n_buckets), 256);
+}
+
+moe_status moe_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,
+                      int32_t* sorted_slot, int32_t* slot_pos, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (n_slots == 0) return MOE_OK;
+  if (n_slots < 0 || n_buckets < 1 || n_buckets > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (!ids || !counts || !offsets || !sorted_slot) return MOE_ERR_NULL;
+  if (!al4(ids) || !al4(counts) || !al4(offsets) || !al4(sorted_slot) || (slot_pos && !al4(slot_pos)))
+    return MOE_ERR_ALIGN;
+  const size_t need = moe_bucket_workspace_bytes(n_slots, n_buckets);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_bucket(ids, n_slots, n_buckets, counts, offsets, sorted_slot, slot_pos,
+                                       (int32_t*)workspace, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weights* W) {
+  if (!W || T <= 0 || k_total <= 0 || W->inter <= 0) return 0;
+  // h as a high plane and a low plane of 16-bit values, one row of `inter` per sorted slot
+  const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
+  return 2 * plane;
+}
+
+moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                          const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (!W) return MOE_ERR_NULL;
+  if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_SHAPE;
+  if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
+  if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
+  if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
+  if ((W->fmt == MOE_W_MXFP4) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
+  if (!x || !offsets || !sorted_slot || !y_slots) return MOE_ERR_NULL;
+  const int H = W->hidden, I = W->inter;
+  moe_status st;
+  if ((st = check_proj(W->gate, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->up, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->down, W->fmt, W->n_experts, H, I)) != MOE_OK) return st;
+  if (!al16(x) || !al16(y_slots) || !al4(offsets) || !al4(sorted_slot)) return MOE_ERR_ALIGN;
+  const size_t need = moe_expert_ffn_workspace_bytes(T, k_total, W);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  uint16_t* h_hi = (uint16_t*)workspace;
+  uint16_t* h_lo = (uint16_t*)((uint8_t*)workspace + need / 2);
+  return hip_status(moe::launch_expert_ffn(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
+                                           dev(W->down), offsets, sorted_slot, y_slots, h_hi, h_lo,
+                                           (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+moe_status moe_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,
+                       void* stream) {
+  if (T == 0) return MOE_OK;
+  if (T < 0 || k_total < 1 || H < 1 || H % 4 != 0) return MOE_ERR_SHAPE;
+  if (!y_slots || !weights || !y) return MOE_ERR_NULL;
+  if (!al16(y_slots) || !al16(y) || !al4(weights)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine(y_slots, weights, T, k_total, H, y, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int n_rows, int K, int64_t code_row_stride,
+                             int64_t scale_row_stride, uint16_t* out, void* stream) {
+  if (n_rows == 0) return MOE_OK;
+  if (n_rows < 0 || K < 1) return MOE_ERR_SHAPE;
+  if (K % 32 != 0) return MOE_ERR_BLOCK;
+  if (!codes || !scales || !out) return MOE_ERR_NULL;
+  if (code_row_stride < K / 2 || scale_row_stride < K / 32) return MOE_ERR_SHAPE;
+  if (!al16(codes) || code_row_stride % 16 != 0 || !al16(out)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_dequant(codes, scales, n_rows, K, code_row_stride, scale_row_stride, out,
+                                        (hipStream_t)stream));
+}
+
+}  // extern "C"

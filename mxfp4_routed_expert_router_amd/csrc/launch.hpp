@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family), called by the C ABI after it
+// has validated every argument.  Each returns the launch status (hipGetLastError after enqueue).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- router ----
+int route_splits(int T, int H, int E);
+hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias,
+                        int E, int top_k, int n_shared, int32_t* ids, float* weights, float* probs,
+                        float* partial, int splits, hipStream_t stream);
+
+// ---- bucketing ----
+constexpr int kBucketChunk = 512;
+hipError_t launch_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_slot, int32_t* slot_pos, int32_t* ws, hipStream_t stream);
+
+// ---- expert FFN ----
+struct ProjDev {
+  const uint8_t* w;
+  const uint8_t* s;
+  int64_t we, wr, se, sr;
+};
+hipError_t launch_expert_ffn(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I,
+                             ProjDev gate, ProjDev up, ProjDev down, const int32_t* offsets,
+                             const int32_t* sorted_slot, float* y_slots, uint16_t* h_hi, uint16_t* h_lo,
+                             hipStream_t stream);
+
+// ---- combine ----
+hipError_t launch_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,
+                          hipStream_t stream);
+
+// ---- decode primitive ----
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n_rows, int K, int64_t code_stride,
+                          int64_t scale_stride, uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

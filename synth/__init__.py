@@ -18,8 +18,10 @@ up scales 5, down codes 6, down scales 7 (FP16 weights use 2, 4, 6).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -46,8 +48,10 @@ def _gen(seed: int, stream: int, sub: int = 0) -> np.random.Generator:
 
 
 def random_bytes(seed: int, stream: int, n: int, sub: int = 0) -> np.ndarray:
-    """n independent uniform bytes (uint8)."""
-    return np.frombuffer(_gen(seed, stream, sub).bytes(int(n)), dtype=np.uint8).copy()
+    """n independent uniform bytes (uint8): the little-endian bytes of consecutive 64-bit outputs."""
+    n = int(n)
+    words = _gen(seed, stream, sub).bit_generator.random_raw((n + 7) // 8).astype("<u8")
+    return words.view(np.uint8)[:n].copy()
 
 
 def uniform_uint(seed: int, stream: int, n: int, lo: int, hi: int, sub: int = 0) -> np.ndarray:
@@ -224,11 +228,46 @@ def make_layer(wl: Workload, T: int, seed: int = 0, experts=None) -> LayerInputs
         shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
         codes = {k: np.zeros((E2, n, kk), np.uint16) for k, (n, kk) in shapes.items()}
         scales = {k: None for k in shapes}
-    for e in (range(E2) if experts is None else experts):
-        for k in shapes:
-            c, s = make_expert_matrix(wl, k, e, seed)
-            codes[k][e] = c
-            if s is not None:
-                scales[k][e] = s
+    def fill(job):
+        e, k = job
+        c, s = make_expert_matrix(wl, k, e, seed)
+        codes[k][e] = c
+        if s is not None:
+            scales[k][e] = s
+
+    jobs = [(e, k) for e in (range(E2) if experts is None else experts) for k in shapes]
+    # every (expert, matrix) has its own generator key, so the order of the jobs does not matter
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, jobs))
     return LayerInputs(wl, T, x, router, bias, codes["gate"], scales["gate"], codes["up"], scales["up"],
                        codes["down"], scales["down"])
+
+
+def to_torch(L: LayerInputs, device) -> dict:
+    """Upload LayerInputs to torch tensors on `device` (bf16/fp16 activations, uint8 codes and scales
+    or fp16 weights, fp32 router).  For the all-active-slices workload the expert views are slices
+    of the unsliced dense matrices: gate/up rows and down columns, exactly as stored densely."""
+    import torch
+
+    def t(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    act = torch.bfloat16 if L.wl.act_dtype == "bf16" else torch.float16
+    out = {"x": t(L.x).view(act), "router": t(L.router), "bias": t(L.bias)}
+    if L.wl.dense_slices:
+        E2, I, H = L.gate_codes.shape
+        g = t(L.gate_codes.reshape(E2 * I, H)).view(torch.float16)
+        u = t(L.up_codes.reshape(E2 * I, H)).view(torch.float16)
+        d = t(np.ascontiguousarray(L.down_codes.transpose(1, 0, 2)).reshape(H, E2 * I)).view(torch.float16)
+        out.update(dense_gate=g, dense_up=u, dense_down=d,
+                   gate=g.view(E2, I, H), up=u.view(E2, I, H),
+                   down=d.as_strided((E2, H, I), (I, E2 * I, 1)),
+                   gate_scales=None, up_scales=None, down_scales=None)
+        return out
+    if L.wl.weight_format == "fp16":
+        out.update(gate=t(L.gate_codes).view(torch.float16), up=t(L.up_codes).view(torch.float16),
+                   down=t(L.down_codes).view(torch.float16), gate_scales=None, up_scales=None, down_scales=None)
+    else:
+        out.update(gate=t(L.gate_codes), up=t(L.up_codes), down=t(L.down_codes), gate_scales=t(L.gate_scales),
+                   up_scales=t(L.up_scales), down_scales=t(L.down_scales))
+    return out

@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU parity tests: device uploads, the oracle cache and tolerances."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import mxfp4_routed_expert_router_amd as moe
+
+DEV = "cuda:0"
+LAYER_TOL = 2e-2   # max-abs error <= LAYER_TOL * RMS of the oracle output (bf16 activations)
+PROB_TOL = 1e-5    # router probabilities and routing weights, absolute
+
+
+def note(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: the gpu-marked tests need an MI355X")
+    moe.lib()  # raises when libmoe.so has not been built
+
+
+def expert_weights(t: dict) -> moe.ExpertWeights:
+    return moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+
+
+def x_fmt(wl) -> int:
+    return oracle.X_BF16 if wl.act_dtype == "bf16" else oracle.X_FP16
+
+
+@functools.lru_cache(maxsize=4)
+def host_layer(name: str, T: int) -> synth.LayerInputs:
+    return synth.make_layer(synth.WORKLOADS[name], T)
+
+
+def rms_ratio(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, np.float64); ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
+
+
+def check_route(r_orc: dict, ids: np.ndarray, w: np.ndarray, probs: np.ndarray, top_k: int):
+    """Router parity: probabilities within PROB_TOL everywhere; ids bit-exact and weights within
+    PROB_TOL on every token the oracle does not flag as a near tie; on flagged tokens the GPU's
+    choice must still be a valid top-k of the oracle probabilities (within the tie window)."""
+    p = r_orc["probs"]
+    assert np.max(np.abs(probs - p)) <= PROB_TOL, np.max(np.abs(probs - p))
+    flag = r_orc["near_tie"].astype(bool)
+    ok = ~flag
+    assert np.array_equal(ids[ok], r_orc["ids"][ok]), np.argwhere(ids[ok] != r_orc["ids"][ok])[:5]
+    assert np.max(np.abs(w[ok] - r_orc["weights"][ok]), initial=0.0) <= PROB_TOL
+    for t in np.nonzero(flag)[0]:
+        sel = ids[t, :top_k]
+        assert len(set(sel.tolist())) == top_k
+        kth = np.sort(p[t])[::-1][top_k - 1]
+        assert np.all(p[t, sel] >= kth - 1e-6), (t, sel)
+        assert abs(w[t, :top_k].sum() - 1.0) <= 1e-5
+    return int(flag.sum())

@@ -1,0 +1,165 @@
+"""The C ABI on the host: the library loads, exports every entry point include/moe.h declares, and
+rejects bad arguments with the documented status before touching the GPU (no compute call here;
+device pointers are fake addresses that validation never dereferences)."""
+import ctypes
+import re
+
+import pytest
+
+import mxfp4_routed_expert_router_amd as m
+
+OK, NULL, SHAPE, BLOCK, ALIGN, DTYPE, TOPK, WORKSPACE = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x7F0000000000  # a 256-byte aligned fake device address
+
+
+def fake(off=0):
+    return ctypes.c_void_p(P + off)
+
+
+def declared_functions():
+    text = open(m.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = m.lib()
+    names = declared_functions()
+    assert {"moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+    for s in range(9):
+        assert L.moe_status_str(s)
+
+
+def test_route_validation():
+    L = m.lib()
+    ws = fake(0x1000)
+    r = lambda **k: L.moe_route(k.get("x", fake()), k.get("xdt", 0), k.get("T", 4), k.get("H", 64),
+                                k.get("wr", fake(0x100)), None, k.get("E", 8), k.get("k", 2), k.get("S", 0),
+                                k.get("ids", fake(0x200)), k.get("w", fake(0x300)), None, k.get("ws", ws),
+                                k.get("wsb", 1 << 20), None)
+    assert L.moe_route(None, 0, 0, 64, None, None, 8, 2, 0, None, None, None, None, 0, None) == OK  # T = 0
+    assert r(T=-1) == SHAPE
+    assert r(H=0) == SHAPE
+    assert r(E=0) == SHAPE
+    assert r(E=1025) == SHAPE
+    assert r(S=-1) == SHAPE
+    assert r(xdt=7) == DTYPE
+    assert r(k=0) == TOPK
+    assert r(k=9) == TOPK
+    assert r(E=512, k=250, S=7) == TOPK
+    assert r(x=None) == NULL
+    assert r(wr=None) == NULL
+    assert r(ids=None) == NULL
+    assert r(x=fake(8)) == ALIGN
+    assert r(wr=fake(0x102)) == ALIGN
+    assert r(ws=None) == WORKSPACE
+    need = L.moe_route_workspace_bytes(4, 64, 8)
+    assert need > 0
+    assert r(wsb=need - 1) == WORKSPACE
+    assert r(ws=fake(0x1004), wsb=need) == ALIGN
+
+
+def test_bucket_validation():
+    L = m.lib()
+    b = lambda **k: L.moe_bucket(k.get("ids", fake()), k.get("n", 100), k.get("nb", 8), k.get("c", fake(0x400)),
+                                 k.get("o", fake(0x800)), k.get("s", fake(0xC00)), None, k.get("ws", None),
+                                 k.get("wsb", 0), None)
+    assert L.moe_bucket(None, 0, 8, None, None, None, None, None, 0, None) == OK
+    assert b(n=-5) == SHAPE
+    assert b(nb=0) == SHAPE
+    assert b(nb=1025) == SHAPE
+    assert b(ids=None) == NULL
+    assert b(o=None) == NULL
+    assert b(ids=fake(2)) == ALIGN
+    assert L.moe_bucket_workspace_bytes(512, 8) == 0
+    need = L.moe_bucket_workspace_bytes(5000, 8)
+    assert need >= 4 * (5000 + 10 * 8)
+    assert b(n=5000) == WORKSPACE
+    assert b(n=5000, ws=fake(0x2000), wsb=need - 4) == WORKSPACE
+
+
+def weights(fmt=m.MOE_W_MXFP4, E=4, H=64, I=96, **over):
+    W = m.moe_expert_weights()
+    W.fmt, W.n_experts, W.hidden, W.inter = fmt, E, H, I
+    bpe = 2
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        p = getattr(W, name)
+        p.w = P + 0x10000
+        if fmt == m.MOE_W_MXFP4:
+            p.scales = P + 0x20000
+            p.w_row_stride, p.w_expert_stride = K // 2, N * K // 2
+            p.s_row_stride, p.s_expert_stride = K // 32, N * K // 32
+        else:
+            p.scales = None
+            p.w_row_stride, p.w_expert_stride = bpe * K, bpe * N * K
+    for k, v in over.items():
+        obj, field = k.split("__") if "__" in k else (None, k)
+        if obj:
+            setattr(getattr(W, obj), field, v)
+        else:
+            setattr(W, field, v)
+    return W
+
+
+def ffn(W, T=4, kt=2, xdt=0, x=None, ws=None, wsb=None):
+    L = m.lib()
+    need = L.moe_expert_ffn_workspace_bytes(T, kt, ctypes.byref(W))
+    return L.moe_expert_ffn(x if x is not None else fake(), xdt, T, kt, ctypes.byref(W), fake(0x100), fake(0x200),
+                            fake(0x300), ws if ws is not None else fake(0x4000), need if wsb is None else wsb, None)
+
+
+def test_expert_ffn_validation():
+    L = m.lib()
+    assert L.moe_expert_ffn(None, 0, 0, 2, None, None, None, None, None, 0, None) == OK
+    assert L.moe_expert_ffn(fake(), 0, 4, 2, None, fake(), fake(), fake(), fake(), 1 << 20, None) == NULL
+    assert ffn(weights(hidden=48)) == BLOCK          # MXFP4 hidden not a multiple of 32
+    assert ffn(weights(inter=80)) == BLOCK
+    assert ffn(weights(fmt=m.MOE_W_FP16, hidden=48), xdt=1) == SHAPE
+    assert ffn(weights(fmt=7)) == DTYPE
+    assert ffn(weights(), xdt=1) == DTYPE            # MXFP4 needs bf16 activations
+    assert ffn(weights(fmt=m.MOE_W_FP16), xdt=0) == DTYPE
+    Wf = weights(fmt=m.MOE_W_FP16)
+    Wf.gate.scales = P
+    assert ffn(Wf, xdt=1) == DTYPE                   # FP16 weights take no scales
+    assert ffn(weights(n_experts=0)) == SHAPE
+    assert ffn(weights(n_experts=2000)) == SHAPE
+    assert ffn(weights(), kt=0) == SHAPE
+    assert ffn(weights(), T=-3) == SHAPE
+    assert ffn(weights(gate__w=None)) == NULL
+    assert ffn(weights(down__scales=None)) == NULL
+    assert ffn(weights(up__w=P + 8)) == ALIGN
+    assert ffn(weights(gate__w_row_stride=40)) == ALIGN   # >= K/2 = 32 but not a multiple of 16
+    assert ffn(weights(down__w_expert_stride=100 * 16 + 8)) == ALIGN
+    assert ffn(weights(gate__w_row_stride=16)) == SHAPE   # rows would overlap
+    assert ffn(weights(), x=fake(4)) == ALIGN
+    assert ffn(weights(), ws=fake(0x4008)) == ALIGN
+    W = weights()
+    need = L.moe_expert_ffn_workspace_bytes(4, 2, ctypes.byref(W))
+    assert need >= 4 * 4 * 2 * 96
+    assert ffn(W, wsb=need - 1) == WORKSPACE
+    # a slice of a larger MXFP4 projection that starts mid-block (8 bytes = 16 codes) is refused
+    assert ffn(weights(down__w=P + 0x10000 + 8)) == ALIGN
+
+
+def test_combine_and_dequant_validation():
+    L = m.lib()
+    assert L.moe_combine(None, None, 0, 2, 64, None, None) == OK
+    assert L.moe_combine(fake(), fake(0x100), 4, 2, 66, fake(0x200), None) == SHAPE
+    assert L.moe_combine(fake(), fake(0x100), 4, 0, 64, fake(0x200), None) == SHAPE
+    assert L.moe_combine(None, fake(0x100), 4, 2, 64, fake(0x200), None) == NULL
+    assert L.moe_combine(fake(4), fake(0x100), 4, 2, 64, fake(0x200), None) == ALIGN
+    assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 48, 24, 2, fake(0x200), None) == BLOCK
+    assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 64, 16, 2, fake(0x200), None) == SHAPE
+    assert L.moe_mxfp4_dequant(fake(8), fake(0x100), 3, 64, 32, 2, fake(0x200), None) == ALIGN
+    assert L.moe_mxfp4_dequant(None, fake(0x100), 3, 64, 32, 2, fake(0x200), None) == NULL
+
+
+def test_workspace_queries_are_host_only():
+    L = m.lib()
+    assert L.moe_route_workspace_bytes(0, 64, 8) == 0
+    assert L.moe_route_workspace_bytes(8192, 7168, 256) >= 4 * 8192 * 256
+    W = weights(H=7168, I=2048, E=257)
+    assert L.moe_expert_ffn_workspace_bytes(8192, 9, ctypes.byref(W)) == 4 * 8192 * 9 * 2048

@@ -1,0 +1,320 @@
+"""HIP path against the fp64 oracle, stage by stage and end to end (needs an MI355X).
+
+Bars: routing ids and bucket permutations bit-exact (near ties flagged by the oracle are checked
+for validity instead); router probabilities and routing weights within 1e-5 absolute; expert FFN
+and layer outputs with max-abs error <= 2e-2 x RMS of the oracle output.  Workloads are the seeded
+synthetic layers of synth.WORKLOADS plus ragged and degenerate shapes; at the full prefill and
+sweep sizes the oracle computes a sample of tokens (all routing and bucketing is still whole).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import mxfp4_routed_expert_router_amd as moe
+from gpu_support import (DEV, LAYER_TOL, check_route, expert_weights, host_layer, note, require_gpu, rms_ratio,
+                         x_fmt)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def sync_np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------------------------
+# decode primitive
+# ------------------------------------------------------------------------------------------------
+def test_dequant_every_code_and_scale(orc):
+    """All 256 byte values (every code in both nibbles) under every scale code 0..252, bit-exact."""
+    K = 512
+    codes = np.tile(np.arange(256, dtype=np.uint8), (253, 1))          # [253][256] bytes
+    scales = np.repeat(np.arange(253, dtype=np.uint8)[:, None], K // 32, axis=1)
+    ref = orc.decode_matrix(codes, scales).astype(np.float32)           # exact in fp32
+    ref_bits = ref.view(np.uint32)
+    assert np.all(ref_bits & 0xFFFF == 0)                               # exact in bf16 too
+    note("dequant: 253 scale codes x 512 elements")
+    out = moe.moe_mxfp4_dequant(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    got = sync_np(out.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got, (ref_bits >> 16).astype(np.uint16))
+
+
+def test_dequant_strided_rows(orc):
+    rng = np.random.default_rng(7)
+    big = rng.integers(0, 256, (9, 48), dtype=np.uint8)                 # rows of 48 bytes
+    sc = rng.integers(118, 128, (9, 5), dtype=np.uint8)
+    dc = torch.from_numpy(big).to(DEV)[:, 16:48]                         # K = 64 codes, row stride 48 B
+    ds = torch.from_numpy(sc).to(DEV)[:, 1:3]
+    got = sync_np(moe.moe_mxfp4_dequant(dc, ds).float())
+    ref = orc.decode_matrix(np.ascontiguousarray(big[:, 16:48]), np.ascontiguousarray(sc[:, 1:3]))
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------------------------------------
+# router
+# ------------------------------------------------------------------------------------------------
+ROUTE_CASES = ([("tiny", 16)] + [("decode", t) for t in (1, 8, 32, 64)] + [("sweep", t) for t in (1, 15, 88, 176)]
+               + [("prefill", 8192)])
+
+
+def run_route(wl, x, router, bias):
+    return moe.moe_route(x, router, wl.top_k, bias, wl.n_shared, want_probs=True)
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES, ids=[f"{n}-T{t}" for n, t in ROUTE_CASES])
+def test_route(orc, name, T):
+    wl = synth.WORKLOADS[name]
+    note(f"route {name} T={T}")
+    x = synth.make_x(wl, T)
+    router, bias = synth.make_router(wl)
+    r = orc.route(x, x_fmt(wl), router, bias, wl.top_k, wl.n_shared)
+    xt = torch.from_numpy(x).to(DEV).view(torch.bfloat16)
+    ids, w, probs = run_route(wl, xt, torch.from_numpy(router).to(DEV),
+                              None if bias is None else torch.from_numpy(bias).to(DEV))
+    flagged = check_route(r, sync_np(ids), sync_np(w), sync_np(probs), wl.top_k)
+    note(f"  near ties flagged: {flagged} of {T}")
+
+
+ROUTE_EDGE = [  # (T, H, E, k, S, router_std, zipf)
+    (5, 64, 1, 1, 0, 0.3, 0.0),       # one expert
+    (9, 32, 7, 7, 0, 0.5, 0.0),       # k = E, E not a multiple of 64
+    (33, 96, 100, 5, 0, 0.3, 1.2),    # ragged H, biased logits
+    (4, 64, 1024, 8, 0, 0.3, 0.0),    # maximum expert count
+    (6, 64, 256, 6, 2, 0.3, 0.0),     # Cascadia: 6 routed + 2 shared selections
+    (3, 64, 300, 200, 0, 0.3, 0.0),   # k > 64: selections spread over several lanes' registers
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_EDGE, ids=[f"T{c[0]}-H{c[1]}-E{c[2]}-k{c[3]}-S{c[4]}" for c in ROUTE_EDGE])
+def test_route_edges(orc, case):
+    T, H, E, k, S, std, zipf = case
+    wl = synth.custom(hidden=H, n_routed=E, top_k=k, n_shared=S, inter=64, router_std=std, zipf_s=zipf)
+    note(f"route edge {case}")
+    x = synth.make_x(wl, T, seed=11)
+    router, bias = synth.make_router(wl, seed=11)
+    r = orc.route(x, oracle.X_BF16, router, bias, k, S)
+    ids, w, probs = moe.moe_route(torch.from_numpy(x).to(DEV).view(torch.bfloat16), torch.from_numpy(router).to(DEV),
+                                  k, None if bias is None else torch.from_numpy(bias).to(DEV), S, want_probs=True)
+    check_route(r, sync_np(ids), sync_np(w), sync_np(probs), k)
+    assert np.all(sync_np(ids)[:, k:] == np.arange(E, E + S))
+
+
+# ------------------------------------------------------------------------------------------------
+# bucketing
+# ------------------------------------------------------------------------------------------------
+def bucket_case_ids(kind):
+    rng = np.random.default_rng(5)
+    if kind == "prefill":
+        wl = synth.WORKLOADS["prefill"]
+        x = synth.make_x(wl, 8192)
+        router, bias = synth.make_router(wl)
+        return oracle.load().route(x, oracle.X_BF16, router, bias, wl.top_k, wl.n_shared)["ids"].reshape(-1), 257
+    n, nb = {"one": (7, 1), "exact-chunk": (512, 128), "ragged": (513, 33), "sweep": (1408, 256),
+             "max-buckets": (3000, 1024), "skew": (5000, 64)}[kind]
+    ids = rng.integers(0, nb, n).astype(np.int32)
+    if kind == "skew":
+        ids[rng.random(n) < 0.9] = 3
+    return ids, nb
+
+
+@pytest.mark.parametrize("kind", ["one", "exact-chunk", "ragged", "sweep", "max-buckets", "skew", "prefill"])
+def test_bucket(orc, kind):
+    ids, nb = bucket_case_ids(kind)
+    note(f"bucket {kind}: {ids.size} slots, {nb} buckets")
+    ref = orc.bucket(ids, nb)
+    b = moe.moe_bucket(torch.from_numpy(ids).to(DEV), nb)
+    for f in ("counts", "offsets", "sorted_slot", "slot_pos"):
+        assert np.array_equal(sync_np(getattr(b, f)), ref[f]), f
+
+
+def test_bucket_drops_invalid_ids(orc):
+    rng = np.random.default_rng(9)
+    for n in (300, 2000):
+        ids = rng.integers(0, 16, n).astype(np.int32)
+        ids[::7] = -3
+        ids[::11] = 99
+        ref = orc.bucket(ids, 16)
+        b = moe.moe_bucket(torch.from_numpy(ids).to(DEV), 16)
+        for f in ("counts", "offsets", "sorted_slot", "slot_pos"):
+            assert np.array_equal(sync_np(getattr(b, f)), ref[f]), (n, f)
+
+
+# ------------------------------------------------------------------------------------------------
+# expert FFN (fed the oracle's buckets) and combine (fed oracle slots and weights)
+# ------------------------------------------------------------------------------------------------
+def ffn_vs_oracle(orc, L, ids, sample_tokens=None):
+    """GPU moe_expert_ffn on the oracle's bucketing of `ids` vs the oracle's y_slots."""
+    wl = L.wl
+    T = L.T
+    kt = ids.shape[1]
+    W = oracle.ExpertWeights.from_layer(L)
+    b = orc.bucket(ids, wl.n_experts)
+    mask = None
+    if sample_tokens is not None:
+        mask = np.zeros(T, np.uint8); mask[sample_tokens] = 1
+        mask = np.repeat(mask, kt)
+    ref = orc.expert_ffn(L.x, x_fmt(wl), kt, W, b["offsets"], b["sorted_slot"], mask)
+    t = synth.to_torch(L, DEV)
+    y = moe.moe_expert_ffn(t["x"], expert_weights(t), torch.from_numpy(b["offsets"]).to(DEV),
+                           torch.from_numpy(b["sorted_slot"]).to(DEV), kt)
+    got = sync_np(y)
+    rows = np.arange(T * kt) if mask is None else np.nonzero(mask)[0]
+    return rms_ratio(got[rows], ref[rows])
+
+
+FFN_CASES = [("tiny", 16, None), ("decode", 1, None), ("decode", 8, None), ("decode", 64, None),
+             ("sweep", 1, None), ("sweep", 15, [0, 7, 14]), ("sweep", 176, [0, 5, 88, 175]),
+             ("dense_slices", 1, None), ("dense_slices", 16, [0, 9, 15]), ("dense_slices", 128, [0, 64, 127])]
+
+
+@pytest.mark.parametrize("name,T,sample", FFN_CASES, ids=[f"{c[0]}-T{c[1]}" for c in FFN_CASES])
+def test_expert_ffn(orc, name, T, sample):
+    note(f"expert ffn {name} T={T}")
+    L = host_layer(name, T)
+    wl = L.wl
+    if wl.dense_slices:
+        ids = np.tile(np.arange(wl.n_experts, dtype=np.int32), (T, 1))
+    else:
+        ids = orc.route(L.x, x_fmt(wl), L.router, L.bias, wl.top_k, wl.n_shared)["ids"]
+    err = ffn_vs_oracle(orc, L, ids, sample)
+    note(f"  max-abs / rms = {err:.3e}")
+    assert err <= LAYER_TOL
+
+
+FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
+    (37, 96, 160, 5, 2, "mxfp4", "routed"),      # ragged H and I (not multiples of 128 / 64)
+    (200, 64, 96, 4, 1, "mxfp4", "one-expert"),  # 200 rows in one expert: several tiles
+    (40, 64, 64, 3, 2, "mxfp4", "two-experts"),  # 40 rows per expert: 2-tile path
+    (23, 32, 32, 6, 3, "fp16", "routed"),        # smallest FP16 shapes
+    (64, 256, 128, 9, 8, "fp16", "routed"),
+    (3, 64, 64, 50, 2, "mxfp4", "routed"),       # most experts empty
+]
+
+
+@pytest.mark.parametrize("case", FFN_EDGE, ids=[f"T{c[0]}-H{c[1]}-I{c[2]}-E{c[3]}-k{c[4]}-{c[5]}-{c[6]}" for c in FFN_EDGE])
+def test_expert_ffn_edges(orc, case):
+    T, H, I, E, k, fmt, pattern = case
+    note(f"expert ffn edge {case}")
+    wl = synth.custom(hidden=H, n_routed=E, top_k=k, inter=I, weight_format=fmt,
+                      act_dtype="bf16" if fmt == "mxfp4" else "fp16", router_std=0.3, weight_std=0.05)
+    L = synth.make_layer(wl, T, seed=21)
+    if pattern == "routed":
+        ids = orc.route(L.x, x_fmt(wl), L.router, L.bias, k)["ids"]
+    elif pattern == "one-expert":
+        ids = np.full((T, 1), 2, np.int32)
+    else:
+        ids = np.tile(np.array([0, 2], np.int32), (T, 1))
+    err = ffn_vs_oracle(orc, L, ids)
+    note(f"  max-abs / rms = {err:.3e}")
+    assert err <= LAYER_TOL
+
+
+@pytest.mark.parametrize("T,kt,H", [(1, 8, 4096), (37, 3, 96), (176, 8, 7168)])
+def test_combine(orc, T, kt, H):
+    rng = np.random.default_rng(T)
+    ys = rng.standard_normal((T * kt, H)).astype(np.float32) * 1e3
+    w = rng.random((T, kt)).astype(np.float32)
+    ref = orc.combine(ys.astype(np.float64), w.astype(np.float64))
+    y = moe.moe_combine(torch.from_numpy(ys).to(DEV), torch.from_numpy(w).to(DEV))
+    assert rms_ratio(sync_np(y), ref) <= 1e-5
+
+
+# ------------------------------------------------------------------------------------------------
+# end to end
+# ------------------------------------------------------------------------------------------------
+def gpu_layer(L):
+    wl = L.wl
+    t = synth.to_torch(L, DEV)
+    layer = moe.MoELayer(expert_weights(t), L.T, wl.top_k if not wl.dense_slices else wl.n_experts,
+                         wl.n_shared, None if wl.dense_slices else t["router"], t["bias"])
+    return layer, t
+
+
+LAYER_CASES = ([("tiny", 16, None)] + [("decode", T, None) for T in (1, 8, 32, 64)]
+               + [("sweep", 1, None), ("sweep", 8, None), ("sweep", 32, [0, 31]), ("sweep", 88, [3, 50]),
+                  ("sweep", 176, [1, 100, 175]), ("prefill", 8192, "hot-cold")]
+               + [("dense_slices", T, None if T < 128 else [0, 127]) for T in (1, 16, 128)])
+
+
+@pytest.mark.parametrize("name,T,sample", LAYER_CASES, ids=[f"{c[0]}-T{c[1]}" for c in LAYER_CASES])
+def test_layer(orc, name, T, sample):
+    note(f"layer {name} T={T}")
+    L = host_layer(name, T)
+    wl = L.wl
+    layer, t = gpu_layer(L)
+    y = sync_np(layer.forward(t["x"]))
+    if wl.dense_slices:
+        rows = np.arange(T) if sample is None else np.array(sample)
+        g, u, d = synth.make_dense_fp16(wl)
+        ref = orc.dense_ffn_f16(L.x[rows], oracle.X_FP16, g, u, d)
+        err = rms_ratio(y[rows], ref)
+    else:
+        r = orc.route(L.x, x_fmt(wl), L.router, L.bias, wl.top_k, wl.n_shared)
+        if sample == "hot-cold":
+            # tokens routed to the hottest and to the least-loaded active routed experts
+            counts = np.bincount(r["ids"][:, :wl.top_k].reshape(-1), minlength=wl.n_routed)
+            hot, cold = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+            has = lambda e: np.nonzero((r["ids"][:, :wl.top_k] == e).any(axis=1))[0]
+            sample = sorted(set(has(hot)[:4].tolist() + has(cold)[:4].tolist() + [0, T - 1]))
+            note(f"  sampled tokens {sample} (hot expert {hot}: {counts[hot]} tokens, cold {cold}: {counts[cold]})")
+        mask = None
+        if sample is not None:
+            mask = np.zeros(T, np.uint8); mask[sample] = 1
+        out = orc.layer(L, token_mask=mask)
+        rows = np.arange(T) if sample is None else np.array(sample)
+        rows = rows[out["route"]["near_tie"][rows] == 0]
+        err = rms_ratio(y[rows], out["y"][rows])
+    note(f"  max-abs / rms = {err:.3e} over {len(rows)} tokens")
+    assert err <= LAYER_TOL
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("sweep", 176)])
+def test_deterministic(name, T):
+    L = host_layer(name, T)
+    layer, t = gpu_layer(L)
+    a = sync_np(layer.forward(t["x"])).copy()
+    b = sync_np(layer.forward(t["x"]))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_zero_tokens():
+    L = host_layer("tiny", 16)
+    t = synth.to_torch(L, DEV)
+    W = expert_weights(t)
+    x0 = t["x"][:0]
+    ids, w, _ = moe.moe_route(x0, t["router"], 2)
+    b = moe.moe_bucket(ids, 8)
+    y = moe.moe_expert_ffn(x0, W, b.offsets, b.sorted_slot, 2)
+    assert moe.moe_combine(y, w).shape == (0, 256)
+    torch.cuda.synchronize()
+
+
+def test_invalid_ids_are_dropped_safely(orc):
+    """Out-of-range ids: bucket drops them, the FFN skips them, valid slots are still exact."""
+    L = host_layer("tiny", 16)
+    r = orc.route(L.x, oracle.X_BF16, L.router, None, 2)
+    ids = r["ids"].copy()
+    ids[3, 1] = 8
+    ids[7, 0] = -1
+    t = synth.to_torch(L, DEV)
+    b = moe.moe_bucket(torch.from_numpy(ids).to(DEV), 8)
+    sentinel = torch.full((32, 256), 12345.0, device=DEV)
+    y = sync_np(moe.moe_expert_ffn(t["x"], expert_weights(t), b.offsets, b.sorted_slot, 2, out=sentinel))
+    ref_b = orc.bucket(ids, 8)
+    ref = orc.expert_ffn(L.x, oracle.X_BF16, 2, oracle.ExpertWeights.from_layer(L), ref_b["offsets"],
+                         ref_b["sorted_slot"])
+    assert np.all(y[3 * 2 + 1] == 12345.0) and np.all(y[7 * 2 + 0] == 12345.0)
+    valid = ref_b["slot_pos"] >= 0
+    assert rms_ratio(y[valid], ref[valid]) <= LAYER_TOL

@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+Workload: the concurrency-sweep MoE layer -- hidden 7168, 256 routed experts, top-8, expert SwiGLU
+intermediate 2048, MXFP4 expert weights (codes uniform, E8M0 in [118, 127]), bf16 activations
+~N(0,1), router weights ~N(0, 1/7168) so logits are ~N(0,1); seeded synthetic inputs (seed 0).
+One step = one layer call on T tokens (default 176): moe_route -> moe_bucket -> expert FFN
+(gate/up phase, down phase) -> moe_combine, inputs resident in HBM.  Weight sets are rotated so
+that the bytes touched between two visits of one set exceed the 256 MB Infinity Cache.
+
+Prints one JSON line: tokens/s (value), ms per layer call, the gate/up kernel's roofline (HIP-event
+duration and algorithmic bytes), the per-T sweep T = 1..176, and the fp64 CPU oracle timed on a
+bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+INFINITY_CACHE = 256 << 20
+MXFP4_BYTES_PER_WEIGHT = 17.0 / 32.0   # 4.25 bits
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--tokens", type=int, default=176, help="T of the headline step")
+    ap.add_argument("--sweep-steps", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens of the oracle's timed sample")
+    return ap.parse_args()
+
+
+class Runner:
+    """Preallocated buffers for one T; step(set) enqueues the five library calls on the current stream."""
+
+    def __init__(self, moe, sets, T, top_k, n_shared, n_experts, H, I):
+        import torch
+        dev = "cuda:0"
+        self.moe, self.sets, self.T, self.top_k, self.n_shared = moe, sets, T, top_k, n_shared
+        self.kt = top_k + n_shared
+        self.n_experts = n_experts
+        n = T * self.kt
+        W0 = sets[0]["W"]
+        self.ids = torch.empty((T, self.kt), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, self.kt), dtype=torch.float32, device=dev)
+        self.route_ws = self._ws(moe.moe_route_workspace_bytes(T, H, n_experts - n_shared))
+        self.b = moe.Buckets(torch.empty(n_experts, dtype=torch.int32, device=dev),
+                             torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+                             torch.empty(n, dtype=torch.int32, device=dev), None)
+        self.bucket_ws = self._ws(moe.moe_bucket_workspace_bytes(n, n_experts))
+        self.ffn_ws = self._ws(moe.moe_expert_ffn_workspace_bytes(T, self.kt, W0))
+        self.y_slots = torch.empty((n, H), dtype=torch.float32, device=dev)
+        self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    @staticmethod
+    def _ws(nbytes):
+        import torch
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda:0")
+
+    def step(self, i, events=None):
+        m, s = self.moe, self.sets[i % len(self.sets)]
+        rec = (lambda k: events[k].record()) if events is not None else (lambda k: None)
+        rec(0)
+        m.moe_route(s["x"][:self.T], s["router"], self.top_k, s["bias"], self.n_shared,
+                    out=(self.ids, self.w, None), workspace=self.route_ws)
+        rec(1)
+        m.moe_bucket(self.ids, self.n_experts, out=self.b, workspace=self.bucket_ws)
+        rec(2)
+        m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws)
+        rec(3)
+        m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws, self.y_slots)
+        rec(4)
+        m.moe_combine(self.y_slots, self.w, out=self.y)
+        rec(5)
+
+
+def time_steps(runner, steps, warmup):
+    """-> (ms per step from events around all steps, per-call mean ms from per-step events)."""
+    import torch
+    for i in range(warmup):
+        runner.step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        runner.step(i)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end) / steps
+    # second timed pass with events between the calls (same stream, same kernels)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for i in range(steps):
+        runner.step(i, evs[i])
+    torch.cuda.synchronize()
+    names = ["route", "bucket", "ffn_gateup", "ffn_down", "combine"]
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    return total_ms, per
+
+
+def active_experts(runner):
+    import torch
+    torch.cuda.synchronize()
+    return int((runner.b.counts.cpu() > 0).sum().item())
+
+
+def traffic_record(kernel_src):
+    """FETCH/WRITE bytes per launch of the gate/up kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "ffn_gateup_T176_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    digest = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this layer build has no "
+              "multi-GPU path: see the sharding design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import mxfp4_routed_expert_router_amd as moe
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    wl = synth.WORKLOADS["sweep"]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_routed, wl.top_k
+    Ts = sorted(set(([] if args.no_sweep else list(wl.tokens)) + [args.tokens]))
+    Tmax = max(Ts)
+    t0 = time.time()
+    L = synth.make_layer(wl, Tmax)
+    base = synth.to_torch(L, "cuda:0")
+    gen_s = time.time() - t0
+    expert_bytes = 3 * H * I * MXFP4_BYTES_PER_WEIGHT
+
+    def make_sets(T):
+        # enough independent copies (router + weights) that one pass over them exceeds 4x the cache
+        a = E * (1.0 - (1.0 - k / E) ** T)
+        r = max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes + 4 * H * E))))
+        sets = []
+        for j in range(r):
+            if j == 0:
+                t = base
+            else:
+                t = {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base.items()}
+            W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+            sets.append({"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t})
+        return sets
+
+    results = {}
+    for T in Ts:
+        sets = make_sets(T)
+        runner = Runner(moe, sets, T, k, 0, E, H, I)
+        steps = args.steps if T == args.tokens else args.sweep_steps
+        warm = args.warmup if T == args.tokens else min(args.warmup, 5)
+        ms, per = time_steps(runner, steps, warm)
+        A = active_experts(runner)
+        n_slots = T * k
+        w_bytes = A * expert_bytes
+        gateup_bytes = A * 2 * H * I * MXFP4_BYTES_PER_WEIGHT + n_slots * (2 * H + 4 * I)
+        results[T] = dict(T=T, ms=ms, per=per, active=A, weight_bytes=w_bytes, gateup_bytes=gateup_bytes,
+                          rotation_sets=len(sets), steps=steps)
+        del runner, sets
+        torch.cuda.empty_cache()
+
+    head = results[args.tokens]
+    t_gu = head["per"]["ffn_gateup"] / 1e3
+    achieved = head["gateup_bytes"] / t_gu
+    traffic = traffic_record(os.path.join(ROOT, "mxfp4_routed_expert_router_amd", "csrc", "ffn.hip"))
+    out = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (MXFP4 expert weights), T=1..176",
+        "value": args.tokens / (head["ms"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"moe_layer_sweep_H7168_E256_top8_I2048_mxfp4_T{args.tokens}",
+                   "tokens": args.tokens, "hidden": H, "routed_experts": E, "top_k": k, "inter": I,
+                   "weights": "mxfp4 (E2M1 + E8M0/32)", "activations": "bf16", "output": "fp32",
+                   "parallelism": "single GPU"},
+        "weight_GBps": head["weight_bytes"] / (head["ms"] / 1e3) / 1e9,
+        "weight_frac_of_hbm_peak": head["weight_bytes"] / (head["ms"] / 1e3) / HBM_PEAK,
+        "active_experts": head["active"],
+        "rotation_sets": head["rotation_sets"],
+        "per_call_ms": {kk: round(v, 5) for kk, v in head["per"].items()},
+        "roofline": {"kernel": "ffn_gateup_kernel (gate/up grouped GEMM + SwiGLU)", "bound": "hbm",
+                     "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": head["gateup_bytes"], "launch_ms": head["per"]["ffn_gateup"]},
+        "sweep": [{"T": r["T"], "us_per_layer": r["ms"] * 1e3, "tokens_per_s": r["T"] / (r["ms"] / 1e3),
+                   "active_experts": r["active"], "weight_GBps": r["weight_bytes"] / (r["ms"] / 1e3) / 1e9,
+                   "weight_frac_of_hbm_peak": r["weight_bytes"] / (r["ms"] / 1e3) / HBM_PEAK,
+                   "gateup_us": r["per"]["ffn_gateup"] * 1e3, "down_us": r["per"]["ffn_down"] * 1e3,
+                   "rotation_sets": r["rotation_sets"]} for r in (results[T] for T in Ts)],
+        "input_generation_s": gen_s,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(L, T, n):
+    """The fp64 oracle (as it stands) on the first n tokens of the same batch, run as one layer call
+    of n tokens: route, bucket, grouped expert FFN, combine."""
+    import dataclasses
+    import oracle
+    o = oracle.load()
+    sub = dataclasses.replace(L, T=n, x=L.x[:n])
+    t0 = time.perf_counter()
+    o.layer(sub)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of the {T}-token batch as one {n}-token layer call (route, bucket, expert FFN, "
+                      f"combine in fp64); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

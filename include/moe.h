@@ -155,6 +155,21 @@ moe_status moe_expert_ffn(const void *x, moe_act_dtype x_dtype, int T, int k_tot
                           const int32_t *sorted_slot, float *y_slots, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* The two phases of moe_expert_ffn as separate calls, for callers that time or overlap them.
+ * moe_expert_ffn_gateup computes h = SiLU(W_gate x) * (W_up x) for every sorted row into the
+ * workspace; moe_expert_ffn_down turns the workspace's h into y_slots.  Calling gateup then down
+ * on one stream with the same arguments and the same workspace gives exactly moe_expert_ffn's
+ * result (it launches the same two kernels).  x_dtype of the down call only selects the format
+ * check (it must match W->fmt as in moe_expert_ffn).  Errors as for moe_expert_ffn. */
+moe_status moe_expert_ffn_gateup(const void *x, moe_act_dtype x_dtype, int T, int k_total,
+                                 const moe_expert_weights *W, const int32_t *offsets,
+                                 const int32_t *sorted_slot, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total,
+                               const moe_expert_weights *W, const int32_t *offsets,
+                               const int32_t *sorted_slot, float *y_slots, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------------------------
  * moe_combine -- weighted reduction [C31] with FP32 output [C32]:
  *   y[t,:] = sum_{j = 0 .. k_total-1, in ascending j} weights[t,j] * y_slots[t*k_total+j,:]

@@ -123,10 +123,15 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weigh
   return 2 * plane;
 }
 
-moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
-                          const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (T == 0) return MOE_OK;
+}  // extern "C"
+
+namespace {
+
+// Validation shared by moe_expert_ffn and its two phases.  On success h_hi / h_lo point into the
+// workspace.
+moe_status check_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                     const int32_t* offsets, const int32_t* sorted_slot, const float* y_slots, bool need_x,
+                     bool need_y, void* workspace, size_t workspace_bytes, uint16_t** h_hi, uint16_t** h_lo) {
   if (!W) return MOE_ERR_NULL;
   if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_SHAPE;
   if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
@@ -134,21 +139,68 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
   if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
   if ((int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
   if ((W->fmt == MOE_W_MXFP4) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
-  if (!x || !offsets || !sorted_slot || !y_slots) return MOE_ERR_NULL;
+  if ((need_x && !x) || !offsets || !sorted_slot || (need_y && !y_slots)) return MOE_ERR_NULL;
   const int H = W->hidden, I = W->inter;
   moe_status st;
-  if ((st = check_proj(W->gate, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
-  if ((st = check_proj(W->up, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
-  if ((st = check_proj(W->down, W->fmt, W->n_experts, H, I)) != MOE_OK) return st;
-  if (!al16(x) || !al16(y_slots) || !al4(offsets) || !al4(sorted_slot)) return MOE_ERR_ALIGN;
+  if (need_x) {
+    if ((st = check_proj(W->gate, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+    if ((st = check_proj(W->up, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  }
+  if (need_y) {
+    if ((st = check_proj(W->down, W->fmt, W->n_experts, H, I)) != MOE_OK) return st;
+  }
+  if ((need_x && !al16(x)) || (need_y && !al16(y_slots)) || !al4(offsets) || !al4(sorted_slot))
+    return MOE_ERR_ALIGN;
   const size_t need = moe_expert_ffn_workspace_bytes(T, k_total, W);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (!al16(workspace)) return MOE_ERR_ALIGN;
-  uint16_t* h_hi = (uint16_t*)workspace;
-  uint16_t* h_lo = (uint16_t*)((uint8_t*)workspace + need / 2);
-  return hip_status(moe::launch_expert_ffn(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
-                                           dev(W->down), offsets, sorted_slot, y_slots, h_hi, h_lo,
-                                           (hipStream_t)stream));
+  *h_hi = (uint16_t*)workspace;
+  *h_lo = (uint16_t*)((uint8_t*)workspace + need / 2);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, int k_total,
+                                 const moe_expert_weights* W, const int32_t* offsets, const int32_t* sorted_slot,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  uint16_t *h_hi, *h_lo;
+  moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, nullptr, true, false, workspace,
+                            workspace_bytes, &h_hi, &h_lo);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->gate),
+                                           dev(W->up), offsets, sorted_slot, h_hi, h_lo, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                               const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  uint16_t *h_hi, *h_lo;
+  moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, false, true, workspace,
+                            workspace_bytes, &h_hi, &h_lo);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->down), offsets,
+                                         sorted_slot, y_slots, h_hi, h_lo, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                          const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  uint16_t *h_hi, *h_lo;
+  moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, true, true, workspace,
+                            workspace_bytes, &h_hi, &h_lo);
+  if (st != MOE_OK) return st;
+  const int H = W->hidden, I = W->inter;
+  hipError_t err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
+                                          offsets, sorted_slot, h_hi, h_lo, (hipStream_t)stream);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, H, I, dev(W->down), offsets, sorted_slot,
+                                         y_slots, h_hi, h_lo, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -26,10 +26,12 @@ struct ProjDev {
   const uint8_t* s;
   int64_t we, wr, se, sr;
 };
-hipError_t launch_expert_ffn(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I,
-                             ProjDev gate, ProjDev up, ProjDev down, const int32_t* offsets,
-                             const int32_t* sorted_slot, float* y_slots, uint16_t* h_hi, uint16_t* h_lo,
-                             hipStream_t stream);
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
+                             ProjDev up, const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi,
+                             uint16_t* h_lo, hipStream_t stream);
+hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
+                           const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi,
+                           const uint16_t* h_lo, hipStream_t stream);
 
 // ---- combine ----
 hipError_t launch_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,

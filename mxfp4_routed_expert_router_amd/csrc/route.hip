@@ -96,16 +96,27 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier follows
   float L[VPL];
+  // Sum the hidden-dimension slices in slice order; the loads of 8 slices are issued together.
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) L[v] = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float part[8][VPL];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = lane + 64 * v;
+        part[q][v] = (s0 + q < splits && e < E) ? partial[((int64_t)(s0 + q) * T + t) * E + e] : 0.0f;
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) L[v] += part[q][v];
+  }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
-    int e = lane + 64 * v;
-    float acc = -INFINITY;
-    if (e < E) {
-      acc = 0.0f;
-      for (int s = 0; s < splits; ++s) acc += partial[((int64_t)s * T + t) * E + e];
-      if (bias) acc += bias[e];
-    }
-    L[v] = acc;
+    const int e = lane + 64 * v;
+    L[v] = (e < E) ? L[v] + (bias ? bias[e] : 0.0f) : -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 
 int route_splits(int T, int H, int E) {
   const int tiles = ((E + kTE - 1) / kTE) * ((T + kTT - 1) / kTT);
-  const int max_splits = (H + 127) / 128;  // keep at least 128 hidden elements per slice
+  const int max_splits = min(16, (H + 255) / 256);  // at least 256 hidden elements per slice
   int s = (512 + tiles - 1) / tiles;
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;

@@ -318,3 +318,18 @@ def test_invalid_ids_are_dropped_safely(orc):
     assert np.all(y[3 * 2 + 1] == 12345.0) and np.all(y[7 * 2 + 0] == 12345.0)
     valid = ref_b["slot_pos"] >= 0
     assert rms_ratio(y[valid], ref[valid]) <= LAYER_TOL
+
+
+def test_split_phases_equal_fused_call():
+    """moe_expert_ffn_gateup then moe_expert_ffn_down == moe_expert_ffn, bit for bit."""
+    L = host_layer("decode", 8)
+    wl = L.wl
+    t = synth.to_torch(L, DEV)
+    W = expert_weights(t)
+    ids, w, _ = moe.moe_route(t["x"], t["router"], wl.top_k)
+    b = moe.moe_bucket(ids, wl.n_experts)
+    a = moe.moe_expert_ffn(t["x"], W, b.offsets, b.sorted_slot, wl.top_k)
+    ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(8, wl.top_k, W), dtype=torch.uint8, device=DEV)
+    moe.moe_expert_ffn_gateup(t["x"], W, b.offsets, b.sorted_slot, wl.top_k, ws)
+    c = moe.moe_expert_ffn_down(8, W, b.offsets, b.sorted_slot, wl.top_k, ws, torch.empty_like(a))
+    assert np.array_equal(sync_np(a).view(np.uint32), sync_np(c).view(np.uint32))

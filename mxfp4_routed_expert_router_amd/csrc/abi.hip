@@ -117,10 +117,11 @@ moe_status moe_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t* c
 
 // ---------------------------------------------------------------------------------------------
 size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weights* W) {
-  if (!W || T <= 0 || k_total <= 0 || W->inter <= 0) return 0;
-  // h as a high plane and a low plane of 16-bit values, one row of `inter` per sorted slot
+  if (!W || T <= 0 || k_total <= 0 || W->inter <= 0 || W->n_experts <= 0) return 0;
+  // h as a high plane and a low plane of 16-bit values, one row of `inter` per sorted slot,
+  // then the tile table shared by the two phases
   const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
-  return 2 * plane;
+  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts), 256);
 }
 
 }  // extern "C"
@@ -131,7 +132,8 @@ namespace {
 // workspace.
 moe_status check_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
                      const int32_t* offsets, const int32_t* sorted_slot, const float* y_slots, bool need_x,
-                     bool need_y, void* workspace, size_t workspace_bytes, uint16_t** h_hi, uint16_t** h_lo) {
+                     bool need_y, void* workspace, size_t workspace_bytes, uint16_t** h_hi, uint16_t** h_lo,
+                     void** table) {
   if (!W) return MOE_ERR_NULL;
   if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_SHAPE;
   if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
@@ -154,8 +156,10 @@ moe_status check_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, c
   const size_t need = moe_expert_ffn_workspace_bytes(T, k_total, W);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (!al16(workspace)) return MOE_ERR_ALIGN;
+  const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
   *h_hi = (uint16_t*)workspace;
-  *h_lo = (uint16_t*)((uint8_t*)workspace + need / 2);
+  *h_lo = (uint16_t*)((uint8_t*)workspace + plane);
+  *table = (uint8_t*)workspace + 2 * plane;
   return MOE_OK;
 }
 
@@ -168,11 +172,12 @@ moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, in
                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (T == 0) return MOE_OK;
   uint16_t *h_hi, *h_lo;
+  void* table;
   moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, nullptr, true, false, workspace,
-                            workspace_bytes, &h_hi, &h_lo);
+                            workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->gate),
-                                           dev(W->up), offsets, sorted_slot, h_hi, h_lo, (hipStream_t)stream));
+                                           dev(W->up), offsets, sorted_slot, h_hi, h_lo, table, (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
@@ -180,11 +185,12 @@ moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const 
                                size_t workspace_bytes, void* stream) {
   if (T == 0) return MOE_OK;
   uint16_t *h_hi, *h_lo;
+  void* table;
   moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, false, true, workspace,
-                            workspace_bytes, &h_hi, &h_lo);
+                            workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->down), offsets,
-                                         sorted_slot, y_slots, h_hi, h_lo, (hipStream_t)stream));
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->down),
+                                         sorted_slot, y_slots, h_hi, h_lo, table, (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
@@ -192,15 +198,16 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
                           size_t workspace_bytes, void* stream) {
   if (T == 0) return MOE_OK;
   uint16_t *h_hi, *h_lo;
+  void* table;
   moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, true, true, workspace,
-                            workspace_bytes, &h_hi, &h_lo);
+                            workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   const int H = W->hidden, I = W->inter;
   hipError_t err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
-                                          offsets, sorted_slot, h_hi, h_lo, (hipStream_t)stream);
+                                          offsets, sorted_slot, h_hi, h_lo, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, H, I, dev(W->down), offsets, sorted_slot,
-                                         y_slots, h_hi, h_lo, (hipStream_t)stream));
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, H, I, dev(W->down), sorted_slot, y_slots,
+                                         h_hi, h_lo, table, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -30,56 +30,66 @@ namespace moe {
 
 namespace {
 
+constexpr int kTileMaxExperts = 1024;  // == MOE_MAX_EXPERTS
+
 struct TileInfo {
   int e, r0, nr;  // expert, first sorted row, rows in this tile (0 => no tile)
 };
 
-// Tile j -> (expert, rows).  Wave 0 builds per-lane tile counts over the experts and a wave scan;
-// the result goes through LDS to the whole workgroup.  Offsets are clamped so corrupt device data
-// cannot produce rows outside [0, n_rows_max).
-__device__ TileInfo find_tile(const int32_t* __restrict__ offsets, int n_experts, int n_rows_max, int rows_per_tile,
-                              int j, int* s_info) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (n_experts + 63) / 64;
-    const int eb = min(lane * per, n_experts), ee = min(eb + per, n_experts);
-    int cnt = 0;
-    for (int e = eb; e < ee; ++e) {
-      int a = min(max(offsets[e], 0), n_rows_max), b = min(max(offsets[e + 1], 0), n_rows_max);
-      int n = max(b - a, 0);
-      cnt += (n + rows_per_tile - 1) / rows_per_tile;
+// Tile table, built once per expert-FFN call by ffn_tiles_kernel: entry t = (expert, first sorted
+// row, rows) of tile t, tiles numbered expert by expert (an expert with n rows owns
+// ceil(n / rows_per_tile) consecutive tiles); entries from the tile count up to the grid's bound
+// hold rows = 0.  The gate/up and down phases read the same table.
+struct TileEntry {
+  int e, r0, nr, pad;
+};
+
+__global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int n_experts,
+                                                         int n_rows_max, int rows_per_tile, int n_entries,
+                                                         TileEntry* __restrict__ table) {
+  __shared__ int wsum[16];
+  __shared__ int s_total;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // tiles of expert tid (offsets clamped, so corrupt device data cannot produce rows outside
+  // [0, n_rows_max))
+  int a = 0, n = 0, cnt = 0;
+  if (tid < n_experts) {
+    a = min(max(offsets[tid], 0), n_rows_max);
+    const int b = min(max(offsets[tid + 1], 0), n_rows_max);
+    n = max(b - a, 0);
+    cnt = (n + rows_per_tile - 1) / rows_per_tile;
+  }
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int v = wsum[w];
+      wsum[w] = run;
+      run += v;
     }
-    const int incl = wave_incl_scan(cnt);
-    const int excl = incl - cnt;
-    const int total = __shfl(incl, 63, kWave);
-    if (lane == 0 && j >= total) {
-      s_info[0] = -1;
-      s_info[1] = 0;
-      s_info[2] = 0;
-    }
-    if (j >= excl && j < incl) {
-      int acc = excl;
-      for (int e = eb; e < ee; ++e) {
-        int a = min(max(offsets[e], 0), n_rows_max), b = min(max(offsets[e + 1], 0), n_rows_max);
-        int n = max(b - a, 0);
-        int tiles = (n + rows_per_tile - 1) / rows_per_tile;
-        if (j < acc + tiles) {
-          const int r0 = a + (j - acc) * rows_per_tile;
-          s_info[0] = e;
-          s_info[1] = r0;
-          s_info[2] = min(rows_per_tile, b - r0);
-          break;
-        }
-        acc += tiles;
-      }
-    }
+    s_total = run;
   }
   __syncthreads();
-  TileInfo t;
-  t.e = s_info[0];
-  t.r0 = s_info[1];
-  t.nr = t.e < 0 ? 0 : s_info[2];
-  return t;
+  const int first = wsum[wave] + incl - cnt;
+  // (the bound on n_entries holds for offsets from moe_bucket; the guard keeps inconsistent offsets
+  // from writing past the table)
+  for (int p = 0; p < cnt && first + p < n_entries; ++p) {
+    const int r0 = a + p * rows_per_tile;
+    table[first + p] = TileEntry{tid, r0, min(rows_per_tile, a + n - r0), 0};
+  }
+  const int total = s_total;
+  for (int t = total + tid; t < n_entries; t += blockDim.x) table[t] = TileEntry{0, 0, 0, 0};
+}
+
+__device__ __forceinline__ TileInfo get_tile(const TileEntry* __restrict__ table, int tile) {
+  const TileEntry t = table[tile];
+  TileInfo r;
+  r.e = __builtin_amdgcn_readfirstlane(t.e);
+  r.r0 = __builtin_amdgcn_readfirstlane(t.r0);
+  r.nr = __builtin_amdgcn_readfirstlane(t.nr);
+  return r;
 }
 
 // Work item of workgroup b.  Workgroups are dispatched round-robin over the 8 XCDs (b % 8), and
@@ -172,15 +182,14 @@ __device__ __forceinline__ typename Op<FMT>::V decode_step(const RawW<FMT>& r, i
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int n_experts, int n_nblk,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   typedef typename Op<FMT>::V V;
-  __shared__ int s_info[4];
   __shared__ float s_red[NW][RT][2][256];
   const int n_slots = T * k_total;
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = find_tile(offsets, n_experts, n_slots, 16 * MT, tile, s_info);
+  const TileInfo ti = get_tile(tiles, tile);
   if (ti.nr <= 0) return;  // uniform across the workgroup
   // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -328,14 +337,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int n_experts, int n_nblk,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   typedef typename Op<FMT>::V V;
-  __shared__ int s_info[4];
   __shared__ float s_red[NW][RT][256];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = find_tile(offsets, n_experts, n_slots, 16 * MT, tile, s_info);
+  const TileInfo ti = get_tile(tiles, tile);
   if (ti.nr <= 0) return;
   // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -455,118 +463,93 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
 
 // ------------------------------------------------------------------------------------------------
 // Streaming variants for MXFP4 with 128-aligned K and 4-byte aligned scale rows (every workload
-// shape): each wave keeps a private LDS ring of S chunks filled by direct global->LDS loads
-// (global_load_lds_dwordx4 for codes, global_load_lds_dword for scales), so S-1 chunks of weights
-// are in flight per wave without holding them in VGPRs.  The ring is private to its wave, so the
-// loop has no barrier; completion is tracked with explicit vmcnt waits (loads return in issue
-// order).  64 (matrix, row) pairs per workgroup row block: gate/up use 2 matrices x 32 rows,
-// down 1 matrix x 64 rows, so one dword-load instruction fetches all scales of a chunk.
+// shape).  Weights, activations and h are read with MUBUF buffer loads into registers, two chunks
+// deep (ping-pong register sets, so no register copy forces an early wait); the loads go through
+// buffer descriptors whose ranges bound every access.  Each wave keeps the scale bytes of its K
+// share for the workgroup's 64 (matrix, row) pairs in a private LDS table filled once per work
+// item with row-contiguous dword loads, instead of one scale load per row and chunk.
 // ------------------------------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Ring reads go through inline asm: the compiler cannot tell which in-flight DMA targets which
-// stage and would otherwise wait for every outstanding load (vmcnt(0)) before each ring read.
-// lds_sync ties the results to an explicit lgkmcnt wait so no use is scheduled before it.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr)p; }
-__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-  return v;
-}
-__device__ __forceinline__ uint32_t lds_read8(uint32_t a) {
-  uint32_t v;
-  asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(a));
-  return v;
-}
-template <int RT>
-__device__ __forceinline__ void lds_sync(u32x4 (&q)[RT], uint32_t (&e)[RT]) {
-  if constexpr (RT == 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(q[0]), "+v"(q[1]), "+v"(e[0]), "+v"(e[1]));
-  } else {
-    static_assert(RT == 4, "lds_sync");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
-  }
-}
-
-// Buffer resources (raw, stride 0) over one expert's matrix or one activation tensor.  Loads through
-// them are MUBUF instructions: the compiler keeps exact vmcnt accounting for them (FLAT-encoded
-// global_load_lds would make it treat the queue as unordered and drain it), and the descriptor's
-// range bounds every access.
 constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
 }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, off, 0, 0, 0);
-}
 __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 
-// Per-wave LDS: a ring of S stages of NM*RT x 1 KB of codes, then a scale table holding, for each
-// of the 64 (matrix, row) pairs of the workgroup, the scale bytes of the wave's whole K share
-// (4 per chunk, as dwords).  The table is filled once per work item by dword DMAs whose
-// consecutive lanes read consecutive dwords of one row, so an instruction touches a few cache
-// lines instead of one line per row.
-template <int NM, int RT>
-struct Ring {
-  static constexpr int kStage = NM * RT * 1024;
-  static constexpr int kRows = NM * RT * 16;  // 64
-  static_assert(kRows == 64, "one scale row per lane");
-  static constexpr int kMaxChunksPerWave = 64;  // K share of a wave <= 8192
-  static constexpr int bytes(int S, int cpw) { return S * kStage + kRows * cpw * 4; }
-};
+// Two chunks in flight over the chunks [c0, c1) of a wave: register set A holds chunk c, B chunk
+// c+1, and A is refilled with c+2 right after chunk c is consumed.  The steady-state loop issues
+// its loads unconditionally (a load skipped on some path would make the compiler's vmcnt
+// bookkeeping at the loop header fall back to waiting for everything); the last 1-3 chunks are
+// peeled.
+template <typename Chunk, typename Load, typename Compute>
+__device__ __forceinline__ void run_pipeline_impl(int c0, int c1, Load& load, Compute& compute) {
+  if (c0 >= c1) return;
+  Chunk A, B;
+  load(c0, A);
+  if (c1 - c0 == 1) {
+    compute(c0, A);
+    return;
+  }
+  load(c0 + 1, B);
+  int c = c0;
+  for (; c + 3 < c1; c += 2) {
+    // scheduling barriers keep each refill right behind the compute that frees its registers
+    compute(c, A);
+    load(c + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c + 1, B);
+    load(c + 3, B);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  compute(c, A);
+  if (c + 2 < c1) load(c + 2, A);
+  compute(c + 1, B);
+  if (c + 2 < c1) compute(c + 2, A);
+}
 
-// Activation and h pointers are deliberately not __restrict__: their loads must stay in program
-// order relative to the explicit vmcnt waits (an asm memory clobber does not fence restrict loads).
-template <int NW, int MT, int S>
-__global__ __launch_bounds__(NW * 64) void ffn_gateup_ring_kernel(
-    const uint16_t* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int n_experts, int n_nblk,
+constexpr int kMaxChunksPerWave = 64;  // K share of one wave <= 8192
+// A buffer offset past every descriptor range (ranges are < 2^31; offsets added to it stay < 2^32).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Scale table of one wave: [pairs][cpw dwords]
+__host__ __device__ constexpr int stab_bytes(int pairs, int cpw) { return pairs * cpw * 4; }
+
+template <int NW, int MT, int RT>
+__global__ __launch_bounds__(NW * 64) void ffn_gateup_stream_kernel(
+    const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
-  constexpr int RT = 2, NM = 2;
-  typedef Ring<NM, RT> R;
+  constexpr int NM = 2, NP = NM * RT * 16;  // (matrix, row) pairs of the row block
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_info[4];
   const int n_slots = T * k_total;
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = find_tile(offsets, n_experts, n_slots, 16 * MT, tile, s_info);
+  const TileInfo ti = get_tile(tiles, tile);
   if (ti.nr <= 0) return;
-  // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = nblk * 16 * RT;
   const int e = __builtin_amdgcn_readfirstlane(ti.e);
 
-  // activation rows of this lane's tokens (padded lanes read the tile's first token)
+  // activations: rows of this lane's tokens.  Padded token lanes get an offset past the
+  // descriptor's range: their loads are still issued (a uniform instruction count keeps the
+  // compiler's vmcnt accounting exact) but return zeros without touching memory; their output
+  // columns are never stored anyway.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
   uint32_t xoff[MT];
-  {
-    const int s_first = sorted_slot[ti.r0];
-    const int t_first = (s_first >= 0 && s_first < n_slots) ? s_first / k_total : 0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + l16;
-      bool ok = m < ti.nr;
-      const int sl = ok ? sorted_slot[ti.r0 + m] : -1;
-      ok = ok && sl >= 0 && sl < n_slots;
-      xoff[mt] = (uint32_t)(ok ? sl / k_total : t_first) * (uint32_t)H * 2u + 64u * lq;
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + l16;
+    bool ok = m < ti.nr;
+    const int sl = ok ? sorted_slot[ti.r0 + m] : -1;
+    ok = ok && sl >= 0 && sl < n_slots;
+    xoff[mt] = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 64u * lq : kOutOfRange;
   }
-  // this expert's gate and up matrices and scale grids
   const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
                                          make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
   const __amdgpu_buffer_rsrc_t sr[NM] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
@@ -574,47 +557,24 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_ring_kernel(
   uint32_t coff[NM][RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int n = min(n0 + rt * 16 + l16, I - 1);
+    const int n = min(n0 + rt * 16 + l16, I - 1);  // rows past I repeat the last row; never stored
     coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
     coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
   }
+
   const int n_chunks = H >> 7;
   const int cpw = (n_chunks + NW - 1) / NW;
   const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
-  uint8_t* ring = lds + wave * R::bytes(S, cpw);
-  uint8_t* stab = ring + S * R::kStage;  // [64 pairs][cpw dwords]; pair = matrix * 32 + row
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + wave * stab_bytes(NP, cpw));
 
-  // scale table: dword f = pair * cpw + j holds blocks 4*(c0+j) .. +3 of that pair's row
-  auto load_scales = [&]() {
-    for (int f0 = 0; f0 < 64 * cpw; f0 += 64) {
-      const int f = min(f0 + lane, 64 * cpw - 1);
-      const int pair = f / cpw, j = f - pair * cpw;
-      const int m = pair >> 5, n = min(n0 + (pair & 31), I - 1);
-      const uint32_t off = (uint32_t)(n * (m == 0 ? gate.sr : up.sr)) + 4u * (c0 + j);
-      // one descriptor per instruction: lanes of the other matrix are masked off by exec
-      if (m == 0) dma4(sr[0], off, stab + f0 * 4);
-      else dma4(sr[1], off, stab + f0 * 4);
-    }
-  };
-
-  // Fill ring stage `stage` with chunk c.  Every step issues the same loads (past the end of the
-  // wave's range it re-reads its last, L2-resident chunk into the free stage), so the vmcnt
-  // bookkeeping is the same in every step.
-  auto issue = [&](int stage, int c) {
-    // the stage being refilled was read in an earlier step; its LDS reads have returned
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    uint8_t* st = ring + stage * R::kStage;
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) dma16(wr[m], coff[m][rt] + 64u * c, st + (m * RT + rt) * 1024);
-  };
-  auto load_x = [&](int c, V (&dst)[MT][4]) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dst[mt][s] = bitcast<V>(bld16(xr, xoff[mt] + 256u * c + 16u * s));
-  };
+  // scale table: dword f = pair * cpw + j holds the scales of blocks 4*(c0+j) .. +3 of the pair's
+  // row (pair = matrix * 16*RT + row); consecutive lanes read consecutive dwords of one row.
+  for (int f = lane; f < NP * cpw; f += 64) {
+    const int pair = f / cpw, j = f - pair * cpw;
+    const int m = pair / (16 * RT), n = min(n0 + pair % (16 * RT), I - 1);
+    const int c = min(c0 + j, n_chunks - 1);
+    stab[f] = m == 0 ? bld4(sr[0], (uint32_t)(n * gate.sr) + 4u * c) : bld4(sr[1], (uint32_t)(n * up.sr) + 4u * c);
+  }
 
   f32x4 accg[MT][RT], accu[MT][RT];
 #pragma unroll
@@ -625,58 +585,44 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_ring_kernel(
       accu[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // Per step: refill the stage freed by the previous step, wait for chunk c (its stage and the
-  // activations loaded at the end of the previous step -- everything issued before this step's
-  // DMAs), multiply, then load the next chunk's activations into the same registers.
-  V xb[MT][4];
-  if (c0 < c1) {
-    load_scales();  // issued first: landed once the first chunk has
+  struct Chunk {
+    u32x4 q[NM][RT];
+    V xb[MT][4];
+  };
+  auto load = [&](int c, Chunk& d) {
 #pragma unroll
-    for (int j = 0; j < S - 1; ++j) issue((c0 + j) % S, min(c0 + j, c1 - 1));
-    load_x(c0, xb);
-  }
-  const uint32_t stab_a = lds_addr(stab);
-  for (int c = c0; c < c1; ++c) {
-    issue((c + S - 1) % S, min(c + S - 1, c1 - 1));
-    wait_vmcnt<NM * RT>();
-    const uint32_t st = lds_addr(ring + (c % S) * R::kStage);
-    const uint32_t sc = stab_a + 4u * (c - c0) + lq;
-    u32x4 qg[RT], qu[RT];
-    uint32_t eg[RT], eu[RT];
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) d.q[m][rt] = bld16(wr[m], coff[m][rt] + 64u * c);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) d.xb[mt][s] = bitcast<V>(bld16(xr, xoff[mt] + 256u * c + 16u * s));
+  };
+  auto compute = [&](int c, const Chunk& d) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      qg[rt] = lds_read16(st + (0 * RT + rt) * 1024 + lane * 16);
-      qu[rt] = lds_read16(st + (1 * RT + rt) * 1024 + lane * 16);
-      eg[rt] = lds_read8(sc + 4u * cpw * (0 * 32 + rt * 16 + l16));
-      eu[rt] = lds_read8(sc + 4u * cpw * (1 * 32 + rt * 16 + l16));
-    }
-    lds_sync<RT>(qg, eg);
-    lds_sync<RT>(qu, eu);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float sg = e8m0_to_f32(eg[rt]), su = e8m0_to_f32(eu[rt]);
-      // Padded rows (n >= I) and padded tokens read valid, finite data; an MFMA output element
-      // depends only on its own row of A and column of B, so they only fill output rows and
-      // columns that are never stored -- no zeroing is needed in the loop.
+      const float sg = e8m0_to_f32(sc[4 * cpw * (0 * 16 * RT + rt * 16 + l16)]);
+      const float su = e8m0_to_f32(sc[4 * cpw * (1 * 16 * RT + rt * 16 + l16)]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const V ag = decode8_bf16(qg[rt][s], sg), au = decode8_bf16(qu[rt][s], su);
+        const V ag = decode8_bf16(d.q[0][rt][s], sg), au = decode8_bf16(d.q[1][rt][s], su);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          accg[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[mt][s], accg[mt][rt], 0, 0, 0);
-          accu[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[mt][s], accu[mt][rt], 0, 0, 0);
+          accg[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, d.xb[mt][s], accg[mt][rt], 0, 0, 0);
+          accu[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, d.xb[mt][s], accu[mt][rt], 0, 0, 0);
         }
       }
     }
-    load_x(min(c + 1, c1 - 1), xb);
-  }
-  wait_vmcnt<0>();  // the last (re-read) DMAs have landed before the ring memory is reused
+  };
+  run_pipeline_impl<Chunk>(c0, c1, load, compute);
 
-  // cross-wave reduction (reuses the ring memory once every wave has left its loop)
-  float* red = reinterpret_cast<float*>(lds);  // [NW][RT][2][256]
+  // cross-wave reduction of the K shares, then SwiGLU
+  float* red = reinterpret_cast<float*>(lds + NW * stab_bytes(NP, cpw));  // [NW][RT][2][256]
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    __syncthreads();
+    if (mt > 0) __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -707,34 +653,30 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_ring_kernel(
   }
 }
 
-template <int NW, int MT, int S>
-__global__ __launch_bounds__(NW * 64) void ffn_down_ring_kernel(
-    const uint16_t* h_hi, const uint16_t* h_lo, int n_slots, int H, int I, ProjDev down,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slot, int n_experts, int n_nblk,
+template <int NW, int MT, int RT>
+__global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
-  constexpr int RT = 4, NM = 1;
-  typedef Ring<NM, RT> R;
+  constexpr int NP = RT * 16;  // rows of the row block
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int s_info[4];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = find_tile(offsets, n_experts, n_slots, 16 * MT, tile, s_info);
+  const TileInfo ti = get_tile(tiles, tile);
   if (ti.nr <= 0) return;
-  // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = nblk * 16 * RT;
-
   const int ex = __builtin_amdgcn_readfirstlane(ti.e);
+
   const __amdgpu_buffer_rsrc_t hr_hi = make_rsrc(h_hi, (int64_t)n_slots * I * 2);
   const __amdgpu_buffer_rsrc_t hr_lo = make_rsrc(h_lo, (int64_t)n_slots * I * 2);
-  uint32_t hoff[MT];
+  uint32_t hoff[MT];  // padded token lanes: out-of-range offsets (see the gate/up kernel)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + l16;
-    const int r = m < ti.nr ? ti.r0 + m : ti.r0;  // padded tokens read the tile's first row
-    hoff[mt] = (uint32_t)r * (uint32_t)I * 2u + 64u * lq;
+    hoff[mt] = m < ti.nr ? (uint32_t)(ti.r0 + m) * (uint32_t)I * 2u + 64u * lq : kOutOfRange;
   }
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
@@ -745,32 +687,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_ring_kernel(
   const int n_chunks = I >> 7;
   const int cpw = (n_chunks + NW - 1) / NW;
   const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
-  uint8_t* ring = lds + wave * R::bytes(S, cpw);
-  uint8_t* stab = ring + S * R::kStage;  // [64 rows][cpw dwords]
-
-  auto load_scales = [&]() {
-    for (int f0 = 0; f0 < 64 * cpw; f0 += 64) {
-      const int f = min(f0 + lane, 64 * cpw - 1);
-      const int row = f / cpw, j = f - row * cpw;
-      dma4(sr, (uint32_t)(min(n0 + row, H - 1) * down.sr) + 4u * (c0 + j), stab + f0 * 4);
-    }
-  };
-
-  auto issue = [&](int stage, int c) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    uint8_t* st = ring + stage * R::kStage;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) dma16(wr, coff[rt] + 64u * c, st + rt * 1024);
-  };
-  auto load_h = [&](int c, V (&hi)[MT][4], V (&lo)[MT][4]) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        hi[mt][s] = bitcast<V>(bld16(hr_hi, hoff[mt] + 256u * c + 16u * s));
-        lo[mt][s] = bitcast<V>(bld16(hr_lo, hoff[mt] + 256u * c + 16u * s));
-      }
-  };
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + wave * stab_bytes(NP, cpw));
+  for (int f = lane; f < NP * cpw; f += 64) {
+    const int row = f / cpw, j = f - row * cpw;
+    const int c = min(c0 + j, n_chunks - 1);
+    stab[f] = bld4(sr, (uint32_t)(min(n0 + row, H - 1) * down.sr) + 4u * c);
+  }
 
   f32x4 acc[MT][RT];
 #pragma unroll
@@ -778,48 +700,43 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_ring_kernel(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  V bh[MT][4], bl[MT][4];
-  if (c0 < c1) {
-    load_scales();
-#pragma unroll
-    for (int j = 0; j < S - 1; ++j) issue((c0 + j) % S, min(c0 + j, c1 - 1));
-    load_h(c0, bh, bl);
-  }
-  const uint32_t stab_a = lds_addr(stab);
-  for (int c = c0; c < c1; ++c) {
-    issue((c + S - 1) % S, min(c + S - 1, c1 - 1));
-    wait_vmcnt<RT>();
-    const uint32_t st = lds_addr(ring + (c % S) * R::kStage);
-    const uint32_t sc = stab_a + 4u * (c - c0) + lq;
+  struct Chunk {
     u32x4 q[RT];
-    uint32_t e[RT];
+    V hi[MT][4], lo[MT][4];
+  };
+  auto load = [&](int c, Chunk& d) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      q[rt] = lds_read16(st + rt * 1024 + lane * 16);
-      e[rt] = lds_read8(sc + 4u * cpw * (rt * 16 + l16));
-    }
-    lds_sync<RT>(q, e);
+    for (int rt = 0; rt < RT; ++rt) d.q[rt] = bld16(wr, coff[rt] + 64u * c);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float sc = e8m0_to_f32(e[rt]);
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const V a = decode8_bf16(q[rt][s], sc);  // padded rows / tokens: see the gate/up kernel
+        d.hi[mt][s] = bitcast<V>(bld16(hr_hi, hoff[mt] + 256u * c + 16u * s));
+        d.lo[mt][s] = bitcast<V>(bld16(hr_lo, hoff[mt] + 256u * c + 16u * s));
+      }
+  };
+  auto compute = [&](int c, const Chunk& d) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float scale = e8m0_to_f32(sc[4 * cpw * (rt * 16 + l16)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const V a = decode8_bf16(d.q[rt][s], scale);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[mt][s], acc[mt][rt], 0, 0, 0);
-          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt][s], acc[mt][rt], 0, 0, 0);
+          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, d.hi[mt][s], acc[mt][rt], 0, 0, 0);
+          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, d.lo[mt][s], acc[mt][rt], 0, 0, 0);
         }
       }
     }
-    load_h(min(c + 1, c1 - 1), bh, bl);
-  }
-  wait_vmcnt<0>();
+  };
+  run_pipeline_impl<Chunk>(c0, c1, load, compute);
 
-  float* red = reinterpret_cast<float*>(lds);  // [NW][RT][256]
+  float* red = reinterpret_cast<float*>(lds + NW * stab_bytes(NP, cpw));  // [NW][RT][256]
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    __syncthreads();
+    if (mt > 0) __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -849,120 +766,127 @@ int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {
 
 constexpr int kNW = 4, kRT1 = 2, kRT2 = 4;
 
-// Tokens per tile from the mean rows per active expert (known on the host without a sync); both
-// phases derive it from the same arguments, so they always agree on the tile numbering.
-int pick_mt(int T, int k_total, int n_experts) {
-  const int64_t rows = (int64_t)T * k_total;
-  const int64_t active = rows < n_experts ? rows : n_experts;
-  const double mean = (double)rows / (double)(active > 0 ? active : 1);
-  return mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4);
-}
-
-constexpr int kRingStages = 3;
-
-// Allows a kernel more than the default 64 KB of dynamic LDS (gfx950 has 160 KB per CU); done once
-// per kernel and device.
-template <typename K>
-hipError_t allow_lds(K kernel, size_t bytes) {
-  static int done_for_device[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (done_for_device[dev]) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done_for_device[dev] = 1;
-  return e;
-}
-
 inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
-// The streaming kernels need whole 128-wide chunks and dword-aligned scale rows.
-inline bool ring_ok(const ProjDev& p, int K) {
-  return K % 128 == 0 && K <= 4 * 128 * Ring<1, 4>::kMaxChunksPerWave && al4(p.s) && p.se % 4 == 0 &&
-         p.sr % 4 == 0;
+// The streaming kernels need whole 128-wide chunks, dword-aligned scale rows, a K share per wave
+// within the scale table, and 32-bit buffer offsets.
+inline bool stream_ok(const ProjDev& p, int K, int64_t rows) {
+  return K % 128 == 0 && K <= 4 * 128 * kMaxChunksPerWave && al4(p.s) && p.se % 4 == 0 && p.sr % 4 == 0 &&
+         rows * p.wr < INT32_MAX;
+}
+
+// Streaming kernels: RT 16-row tiles per workgroup (2 for gate/up -- 32 rows of each matrix --
+// and 4 for down).  Wider blocks amortise each activation chunk over more weight rows but cost
+// occupancy; measured on the sweep workload, these were the best.
+template <int MT, int RT>
+void launch_gateup_stream(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate,
+                          ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+                          const TileEntry* tiles, hipStream_t stream) {
+  const int nb = (I + 16 * RT - 1) / (16 * RT);
+  const int cpw = (H / 128 + kNW - 1) / kNW;
+  const size_t lds = (size_t)kNW * stab_bytes(2 * 16 * RT, cpw) + (size_t)kNW * RT * 2 * 256 * 4;
+  ffn_gateup_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
+      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb, h_hi, h_lo);
+}
+template <int MT, int RT>
+void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
+                        float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
+                        hipStream_t stream) {
+  const int nb = (H + 16 * RT - 1) / (16 * RT);
+  const int cpw = (I / 128 + kNW - 1) / kNW;
+  const size_t lds = (size_t)kNW * stab_bytes(16 * RT, cpw) + (size_t)kNW * RT * 256 * 4;
+  ffn_down_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
+      h_hi, h_lo, T * k_total, H, I, down, tiles, sorted_slot, nb, y_slots);
 }
 
 template <int FMT, int MT>
-hipError_t gateup_mt(const void* x, int T, int k_total, int n_experts, int H, int I, ProjDev gate, ProjDev up,
-                     const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+                     const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
-  const int64_t tiles = (max_tiles((int64_t)T * k_total, n_experts, 16 * MT) + kXcds - 1) / kXcds * kXcds;
-  const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
-  const dim3 grid((unsigned)(tiles * nb));
-  if (FMT == MOE_W_MXFP4 && ring_ok(gate, H) && ring_ok(up, H) && (int64_t)T * H * 2 < INT32_MAX &&
-      (int64_t)I * gate.wr < INT32_MAX && (int64_t)I * up.wr < INT32_MAX) {
-    const int cpw = (H / 128 + kNW - 1) / kNW;
-    const size_t lds = (size_t)kNW * Ring<2, 2>::bytes(kRingStages, cpw);
-    hipError_t e = allow_lds(ffn_gateup_ring_kernel<kNW, MT, kRingStages>, lds);
-    if (e != hipSuccess) return e;
-    ffn_gateup_ring_kernel<kNW, MT, kRingStages><<<grid, kNW * 64, lds, stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, offsets, sorted_slot, n_experts, nb, h_hi, h_lo);
+  if (FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX) {
+    launch_gateup_stream<MT, kRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {
-    ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<grid, kNW * 64, 0, stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, offsets, sorted_slot, n_experts, nb, h_hi, h_lo);
+    const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
+    ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb, h_hi, h_lo);
   }
   return hipGetLastError();
 }
 
 template <int FMT, int MT>
-hipError_t down_mt(int T, int k_total, int n_experts, int H, int I, ProjDev down, const int32_t* offsets,
-                   const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
+hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
+                   float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                    hipStream_t stream) {
   const int n_slots = T * k_total;
-  const int64_t tiles = (max_tiles(n_slots, n_experts, 16 * MT) + kXcds - 1) / kXcds * kXcds;
-  const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
-  const dim3 grid((unsigned)(tiles * nb));
-  if (FMT == MOE_W_MXFP4 && ring_ok(down, I) && (int64_t)n_slots * I * 2 < INT32_MAX &&
-      (int64_t)H * down.wr < INT32_MAX) {
-    const int cpw = (I / 128 + kNW - 1) / kNW;
-    const size_t lds = (size_t)kNW * Ring<1, 4>::bytes(kRingStages, cpw);
-    hipError_t e = allow_lds(ffn_down_ring_kernel<kNW, MT, kRingStages>, lds);
-    if (e != hipSuccess) return e;
-    ffn_down_ring_kernel<kNW, MT, kRingStages><<<grid, kNW * 64, lds, stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, offsets, sorted_slot, n_experts, nb, y_slots);
+  if (FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX) {
+    launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {
-    ffn_down_kernel<FMT, kNW, kRT2, MT><<<grid, kNW * 64, 0, stream>>>(h_hi, h_lo, n_slots, H, I, down, offsets,
-                                                                      sorted_slot, n_experts, nb, y_slots);
+    const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
+    ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
+        h_hi, h_lo, n_slots, H, I, down, tiles, sorted_slot, nb, y_slots);
   }
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t gateup_fmt(const void* x, int T, int k_total, int n_experts, int H, int I, ProjDev gate, ProjDev up,
-                      const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+hipError_t gateup_fmt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+                      const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                       hipStream_t stream) {
-  switch (pick_mt(T, k_total, n_experts)) {
-    case 1: return gateup_mt<FMT, 1>(x, T, k_total, n_experts, H, I, gate, up, offsets, sorted_slot, h_hi, h_lo, stream);
-    case 2: return gateup_mt<FMT, 2>(x, T, k_total, n_experts, H, I, gate, up, offsets, sorted_slot, h_hi, h_lo, stream);
-    default: return gateup_mt<FMT, 4>(x, T, k_total, n_experts, H, I, gate, up, offsets, sorted_slot, h_hi, h_lo, stream);
+  switch (pl.mt) {
+    case 1: return gateup_mt<FMT, 1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+    case 2: return gateup_mt<FMT, 2>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+    default: return gateup_mt<FMT, 4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   }
 }
 
 template <int FMT>
-hipError_t down_fmt(int T, int k_total, int n_experts, int H, int I, ProjDev down, const int32_t* offsets,
-                    const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
+hipError_t down_fmt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
+                    float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                     hipStream_t stream) {
-  switch (pick_mt(T, k_total, n_experts)) {
-    case 1: return down_mt<FMT, 1>(T, k_total, n_experts, H, I, down, offsets, sorted_slot, y_slots, h_hi, h_lo, stream);
-    case 2: return down_mt<FMT, 2>(T, k_total, n_experts, H, I, down, offsets, sorted_slot, y_slots, h_hi, h_lo, stream);
-    default: return down_mt<FMT, 4>(T, k_total, n_experts, H, I, down, offsets, sorted_slot, y_slots, h_hi, h_lo, stream);
+  switch (pl.mt) {
+    case 1: return down_mt<FMT, 1>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+    case 2: return down_mt<FMT, 2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+    default: return down_mt<FMT, 4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   }
 }
 
 }  // namespace
 
+FfnPlan ffn_plan(int T, int k_total, int n_experts) {
+  // Tokens per tile from the mean rows per active expert (known on the host without a sync).
+  const int64_t rows = (int64_t)T * k_total;
+  const int64_t active = rows < n_experts ? rows : n_experts;
+  const double mean = (double)rows / (double)(active > 0 ? active : 1);
+  FfnPlan p;
+  p.mt = mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4);
+  p.tiles = (max_tiles(rows, n_experts, 16 * p.mt) + kXcds - 1) / kXcds * kXcds;
+  return p;
+}
+
+size_t ffn_table_bytes(int T, int k_total, int n_experts) {
+  return (size_t)ffn_plan(T, k_total, n_experts).tiles * sizeof(TileEntry);
+}
+
 hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
                              ProjDev up, const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi,
-                             uint16_t* h_lo, hipStream_t stream) {
+                             uint16_t* h_lo, void* table, hipStream_t stream) {
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  TileEntry* tiles = (TileEntry*)table;
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, 16 * pl.mt, (int)pl.tiles, tiles);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   if (fmt == MOE_W_FP16)
-    return gateup_fmt<MOE_W_FP16>(x, T, k_total, n_experts, H, I, gate, up, offsets, sorted_slot, h_hi, h_lo, stream);
-  return gateup_fmt<MOE_W_MXFP4>(x, T, k_total, n_experts, H, I, gate, up, offsets, sorted_slot, h_hi, h_lo, stream);
+    return gateup_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+  return gateup_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
 }
 
 hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
-                           const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi,
-                           const uint16_t* h_lo, hipStream_t stream) {
+                           const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
+                           const void* table, hipStream_t stream) {
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  const TileEntry* tiles = (const TileEntry*)table;
   if (fmt == MOE_W_FP16)
-    return down_fmt<MOE_W_FP16>(T, k_total, n_experts, H, I, down, offsets, sorted_slot, y_slots, h_hi, h_lo, stream);
-  return down_fmt<MOE_W_MXFP4>(T, k_total, n_experts, H, I, down, offsets, sorted_slot, y_slots, h_hi, h_lo, stream);
+    return down_fmt<MOE_W_FP16>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+  return down_fmt<MOE_W_MXFP4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
 }
 
 }  // namespace moe

@@ -26,12 +26,21 @@ struct ProjDev {
   const uint8_t* s;
   int64_t we, wr, se, sr;
 };
+// Tile plan of one expert-FFN call: 16*mt sorted rows per tile, `tiles` entries in the tile table
+// (an upper bound, padded to a multiple of the XCD count).
+struct FfnPlan {
+  int mt;  // 16*mt sorted rows (tokens) per tile
+  int64_t tiles;
+};
+FfnPlan ffn_plan(int T, int k_total, int n_experts);
+size_t ffn_table_bytes(int T, int k_total, int n_experts);
+// The gate/up phase builds the tile table in `table` and writes h; the down phase reads both.
 hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
                              ProjDev up, const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi,
-                             uint16_t* h_lo, hipStream_t stream);
+                             uint16_t* h_lo, void* table, hipStream_t stream);
 hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
-                           const int32_t* offsets, const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi,
-                           const uint16_t* h_lo, hipStream_t stream);
+                           const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
+                           const void* table, hipStream_t stream);
 
 // ---- combine ----
 hipError_t launch_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,

@@ -1,9 +1,12 @@
 // Router: logits, softmax, top-k with renormalised weights, shared-expert slots.
 //
 // Stage 1 (route_logits_kernel): partial[s][t][e] = sum over the s-th slice of the hidden dim of
-//   x[t,h] * w_router[e,h], fp32 FMA.  A workgroup owns a 32-token x 64-expert tile and one
-//   hidden slice; both operand tiles are staged through LDS in 32-wide k steps.  Splitting the
-//   hidden dimension spreads the router-weight read over many CUs when T is small (decode).
+//   x[t,h] * w_router[e,h] on the matrix cores.  w_router (fp32) is split exactly into three bf16
+//   terms, hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each difference is exact, so
+//   hi + mid + lo = w for every normal w); x is bf16 (or fp16) and exact; every product is exact in
+//   fp32 and v_mfma_f32_16x16x32 accumulates in fp32, so the logits are fp32-accurate.  One wave
+//   owns 16 experts x 16*MT tokens x one hidden slice; slices spread the router-weight read over
+//   many CUs when T is small.
 // Stage 2 (route_select_kernel): one wave per token sums the slices in slice order, adds the
 //   bias, takes max / exp / sum over the E logits held across the wave, then picks top_k rounds of
 //   (largest logit, lowest index) by wave argmax and writes ids, renormalised weights and probs.
@@ -16,73 +19,108 @@
 namespace moe {
 
 namespace {
-constexpr int kTT = 32;   // tokens per tile
-constexpr int kTE = 64;   // experts per tile
-constexpr int kBK = 32;   // hidden elements per LDS step
+constexpr int kMaxSplits = 16;
 
-template <int XF16>
-__device__ __forceinline__ float act_to_f32(uint16_t b) {
-  if constexpr (XF16) {
-    return (float)bitcast<_Float16>(b);
-  } else {
-    return __uint_as_float((uint32_t)b << 16);
-  }
+__device__ __forceinline__ bf16x8 to_bf16x8_rne(const float (&v)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = bitcast<__bf16>(f32_to_bf16_bits(v[j]));
+  return r;
 }
 
-template <int XF16>
-__global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
-                                                           const float* __restrict__ w, int E, int k_per_split,
-                                                           float* __restrict__ partial) {
-  __shared__ float xs[kBK][kTT + 1];
-  __shared__ float ws[kBK][kTE + 4];
-  const int tid = threadIdx.x;
-  const int e0 = blockIdx.x * kTE;
-  const int t0 = blockIdx.y * kTT;
+// XF16: activations are fp16 (converted exactly to fp32 and re-split into two bf16 terms, since an
+// fp16 value has 11 significant bits).  VEC: 16-byte loads (aligned w_router rows, H % 8 == 0).
+template <int XF16, int VEC, int MT>
+__global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                          const float* __restrict__ w, int E, int ks_per_split,
+                                                          float* __restrict__ partial) {
+  const int lane = threadIdx.x, l16 = lane & 15, lq = lane >> 4;
+  const int e = blockIdx.x * 16 + l16;
+  const int t0 = blockIdx.y * 16 * MT;
   const int split = blockIdx.z;
-  const int h_begin = split * k_per_split;
-  const int h_end = min(H, h_begin + k_per_split);
-  const int tx = tid & 15;   // experts tx*4 .. tx*4+3
-  const int ty = tid >> 4;   // tokens ty*2, ty*2+1
-  float acc[2][4] = {};
-  for (int h0 = h_begin; h0 < h_end; h0 += kBK) {
-    // x tile: 32 tokens x 32 hidden, 4 elements per thread, k fastest
+  const int nks = (H + 31) / 32;
+  const int ks0 = split * ks_per_split, ks1 = min(ks0 + ks_per_split, nks);
+  const float* wrow = w + (int64_t)(e < E ? e : 0) * H;
+  f32x4 acc[MT];
 #pragma unroll
-    for (int q = 0; q < (kTT * kBK) / 256; ++q) {
-      int idx = tid + q * 256;
-      int kk = idx % kBK, tt = idx / kBK;
-      int t = t0 + tt, h = h0 + kk;
-      xs[kk][tt] = (t < T && h < h_end) ? act_to_f32<XF16>(x[(int64_t)t * H + h]) : 0.0f;
-    }
-    // w tile: 64 experts x 32 hidden, 8 elements per thread
-#pragma unroll
-    for (int q = 0; q < (kTE * kBK) / 256; ++q) {
-      int idx = tid + q * 256;
-      int kk = idx % kBK, ee = idx / kBK;
-      int e = e0 + ee, h = h0 + kk;
-      ws[kk][ee] = (e < E && h < h_end) ? w[(int64_t)e * H + h] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kBK; ++kk) {
-      float a0 = xs[kk][ty * 2], a1 = xs[kk][ty * 2 + 1];
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int k = ks * 32 + 8 * lq;  // this lane's 8 hidden indices
+    float wv[8];
+    if (VEC && k + 8 <= H) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(wrow + k);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(wrow + k + 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float b = ws[kk][tx * 4 + j];
-        acc[0][j] += a0 * b;
-        acc[1][j] += a1 * b;
+        wv[j] = a[j];
+        wv[4 + j] = b[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = (k + j < H) ? wrow[k + j] : 0.f;
+    }
+    if (e >= E) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = 0.f;
+    }
+    float r[8];
+    const bf16x8 hi = to_bf16x8_rne(wv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = wv[j] - (float)hi[j];
+    const bf16x8 mid = to_bf16x8_rne(r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] -= (float)mid[j];
+    const bf16x8 lo = to_bf16x8_rne(r);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = t0 + mt * 16 + l16;
+      const uint16_t* xr = x + (int64_t)(t < T ? t : 0) * H;
+      uint16_t xv[8];
+      if (VEC && k + 8 <= H) {
+        const u32x4 q = ld16(xr + k);
+        __builtin_memcpy(xv, &q, 16);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = (k + j < H) ? xr[k + j] : 0;
+      }
+      if (XF16) {
+        // fp16 -> fp32 exactly, then two bf16 terms (8 + 8 >= 11 significant bits)
+        float xf[8], xr2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xf[j] = (float)bitcast<_Float16>(xv[j]);
+        const bf16x8 xh = to_bf16x8_rne(xf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xr2[j] = xf[j] - (float)xh[j];
+        const bf16x8 xl = to_bf16x8_rne(xr2);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xh, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xh, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xh, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xl, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xl, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xl, acc[mt], 0, 0, 0);
+      } else {
+        if (t >= T) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[j] = 0;
+        }
+        bf16x8 b;
+        __builtin_memcpy(&b, xv, 16);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[mt], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
+  // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16 of each 16-token tile
   float* out = partial + (int64_t)split * T * E;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int t = t0 + ty * 2 + i;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = t0 + mt * 16 + l16;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = e0 + tx * 4 + j;
-      if (e < E) out[(int64_t)t * E + e] = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int ee = blockIdx.x * 16 + 4 * lq + i;
+      if (ee < E) out[(int64_t)t * E + ee] = acc[mt][i];
     }
   }
 }
@@ -96,22 +134,20 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier follows
   float L[VPL];
-  // Sum the hidden-dimension slices in slice order; the loads of 8 slices are issued together.
+  // Sum the hidden-dimension slices in slice order (all loads issued together).
+  float part[kMaxSplits][VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) L[v] = 0.0f;
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    float part[8][VPL];
+  for (int q = 0; q < kMaxSplits; ++q)
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + 64 * v;
+      part[q][v] = (q < splits && e < E) ? partial[((int64_t)q * T + t) * E + e] : 0.0f;
+    }
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = lane + 64 * v;
-        part[q][v] = (s0 + q < splits && e < E) ? partial[((int64_t)(s0 + q) * T + t) * E + e] : 0.0f;
-      }
+  for (int v = 0; v < VPL; ++v) {
+    L[v] = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) L[v] += part[q][v];
+    for (int q = 0; q < kMaxSplits; ++q) L[v] += part[q][v];
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
@@ -122,10 +158,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 #pragma unroll
   for (int v = 0; v < VPL; ++v) mx = fmaxf(mx, L[v]);
   mx = wave_max(mx);
-  float part = 0.0f;
+  float esum = 0.0f;
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) part += (lane + 64 * v < E) ? expf(L[v] - mx) : 0.0f;
-  const float den = wave_sum(part);
+  for (int v = 0; v < VPL; ++v) esum += (lane + 64 * v < E) ? expf(L[v] - mx) : 0.0f;
+  const float den = wave_sum(esum);
   if (probs) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
@@ -193,25 +229,42 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 }
 }  // namespace
 
+int route_mt(int T) { return T <= 16 ? 1 : (T <= 64 ? 4 : 16); }
+
 int route_splits(int T, int H, int E) {
-  const int tiles = ((E + kTE - 1) / kTE) * ((T + kTT - 1) / kTT);
-  const int max_splits = min(16, (H + 255) / 256);  // at least 256 hidden elements per slice
-  int s = (512 + tiles - 1) / tiles;
-  if (s > max_splits) s = max_splits;
+  const int64_t groups = (int64_t)((E + 15) / 16) * ((T + 16 * route_mt(T) - 1) / (16 * route_mt(T)));
+  const int nks = (H + 31) / 32;
+  int s = (int)((512 + groups - 1) / groups);
+  const int cap = nks / 4 < 1 ? 1 : nks / 4;  // at least 4 k-steps of 32 per slice
+  if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return s;
+}
+
+template <int XF16, int VEC>
+void launch_logits(const void* x, int T, int H, const float* w, int E, int splits, float* partial, hipStream_t st) {
+  const int mt = route_mt(T);
+  const int nks = (H + 31) / 32;
+  const int per = (nks + splits - 1) / splits;
+  const dim3 g((E + 15) / 16, (T + 16 * mt - 1) / (16 * mt), splits);
+  const uint16_t* xx = (const uint16_t*)x;
+  if (mt == 1) route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else if (mt == 4) route_logits_kernel<XF16, VEC, 4><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else route_logits_kernel<XF16, VEC, 16><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
 }
 
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,
                         int top_k, int n_shared, int32_t* ids, float* weights, float* probs, float* partial,
                         int splits, hipStream_t stream) {
-  int per = (H + splits - 1) / splits;
-  per = (per + kBK - 1) / kBK * kBK;
-  dim3 g1((E + kTE - 1) / kTE, (T + kTT - 1) / kTT, splits);
-  if (x_fp16)
-    route_logits_kernel<1><<<g1, 256, 0, stream>>>((const uint16_t*)x, T, H, w_router, E, per, partial);
-  else
-    route_logits_kernel<0><<<g1, 256, 0, stream>>>((const uint16_t*)x, T, H, w_router, E, per, partial);
+  const bool vec = ((uintptr_t)w_router % 16 == 0) && (H % 8 == 0);
+  if (x_fp16) {
+    if (vec) launch_logits<1, 1>(x, T, H, w_router, E, splits, partial, stream);
+    else launch_logits<1, 0>(x, T, H, w_router, E, splits, partial, stream);
+  } else {
+    if (vec) launch_logits<0, 1>(x, T, H, w_router, E, splits, partial, stream);
+    else launch_logits<0, 0>(x, T, H, w_router, E, splits, partial, stream);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 g2((T + 3) / 4);

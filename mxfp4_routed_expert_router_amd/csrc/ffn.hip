@@ -757,6 +757,375 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Row-split streaming variants (many active experts).  The four waves of a workgroup own
+// different weight rows, each over the whole reduction dimension, so no cross-wave reduction is
+// needed; the activation (or h) chunk of the tile's tokens is shared: each wave loads a quarter
+// of it into registers, writes it to a 3-stage LDS buffer, and every wave reads its MFMA operands
+// from LDS.  This cuts the L1 accesses spent on activations 4x -- the L1 access rate, not HBM,
+// bounds these kernels.  One barrier per chunk: a stage written in step c is read in step c+1 and
+// rewritten in step c+3, and every wave passes the barriers of steps c+1 and c+2 in between.
+// ------------------------------------------------------------------------------------------------
+// One LDS stage holds a 16-token x 128-K chunk of 16-bit operands in PL planes (x: one plane;
+// h: hi and lo planes).  Rows are padded by 16 bytes so the MFMA operand reads spread over banks.
+constexpr int kRowsRT1 = 2, kRowsRT2 = 4;  // 16-row tiles per wave: gate/up (of each matrix), down
+constexpr int kScaleWin = 16;              // chunks per scale-table window (gate/up)
+
+template <int PL>
+struct XStage {
+  static constexpr int kRow = 128 * 2 + 16;
+  static constexpr int kBytes = PL * 16 * kRow;
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
+    const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+  constexpr int RT = kRowsRT1, NM = 2, NP = NM * RT * 16;
+  typedef bf16x8 V;
+  typedef XStage<1> XS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int n_slots = T * k_total;
+  int tile, nblk;
+  xcd_work(blockIdx.x, n_nblk, tile, nblk);
+  const TileInfo ti = get_tile(tiles, tile);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = (nblk * NW + wave) * 16 * RT;  // this wave's first row
+  const int e = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = H >> 7;
+
+  // The wave's scale table holds two 16-chunk windows: [window][pair][16] dwords (a dword is the
+  // four block scales of one row in one chunk).  Chunk j lives in window (j / 16) % 2, column
+  // j % 16.  While window w is in use, window w+1 is fetched in four 16-byte-per-lane loads (16
+  // pairs x 64 bytes each), one every four steps: scattered per-row dword loads would cost about
+  // as much L1 address work as the weight loads themselves.
+  uint8_t* xs = lds;  // [3][XS::kBytes]
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 3 * XS::kBytes + wave * stab_bytes(NP, 2 * kScaleWin));
+
+  // This wave's share of each activation chunk: lane-load q = 64*wave + lane -> token q/16,
+  // 16-byte column q%16.  Padded tokens get an out-of-range offset (no memory access).
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
+  const int q_tok = (64 * wave + lane) >> 4, q_col = lane & 15;
+  uint32_t xoff;
+  {
+    bool ok = q_tok < ti.nr;
+    const int sl = ok ? sorted_slot[ti.r0 + q_tok] : -1;
+    ok = ok && sl >= 0 && sl < n_slots;
+    xoff = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 16u * q_col : kOutOfRange;
+  }
+  const uint32_t xs_w = (uint32_t)(q_tok * XS::kRow + 16 * q_col);  // where this lane writes
+  const uint32_t xs_r = (uint32_t)(l16 * XS::kRow + 64 * lq);        // where this lane reads (+16*s)
+
+  const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
+                                         make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
+  const __amdgpu_buffer_rsrc_t sr[NM] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
+                                         make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
+  uint32_t coff[NM][RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = min(n0 + rt * 16 + l16, I - 1);
+    coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
+    coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
+  }
+  // Scale group g (0..3) of window w: lane l carries pair 16g + l/4, columns 4(l%4) .. 4(l%4)+3.
+  const int sg_pair = lane >> 2, sg_col = 4 * (lane & 3);
+  uint32_t sg_off[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int pair = 16 * g + sg_pair, row = min(n0 + pair % (16 * RT), I - 1);
+    sg_off[g] = (uint32_t)(row * (pair < 16 * RT ? gate.sr : up.sr)) + 4u * sg_col;
+  }
+  auto fetch_s = [&](int w, int g, u32x4& r) {
+    r = bld16(sr[g / 2], w * kScaleWin + sg_col < n_chunks ? sg_off[g] + 4u * kScaleWin * w : kOutOfRange);
+  };
+  auto put_s = [&](int w, int g, const u32x4& r) {
+    *reinterpret_cast<u32x4*>(stab + ((w & 1) * NP + 16 * g + sg_pair) * kScaleWin + sg_col) = r;
+  };
+  {  // window 0
+    u32x4 w0[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) fetch_s(0, g, w0[g]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) put_s(0, g, w0[g]);
+  }
+
+  f32x4 accg[RT], accu[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    accg[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  struct Chunk {
+    u32x4 q[NM][RT];
+  };
+  auto load = [&](int c, Chunk& d) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) d.q[m][rt] = bld16(wr[m], coff[m][rt] + 64u * c);
+  };
+  // Activation chunks are fetched two chunks ahead, like the weights: X[c % 2] holds chunk c
+  // until it is written to its stage, then is refilled with chunk c + 2 (an out-of-range offset,
+  // which reads zeros without touching memory, past the last chunk).
+  u32x4 X[2];
+  auto fetch_x = [&](int c, u32x4& r) { r = bld16(xr, c < n_chunks ? xoff + 256u * c : kOutOfRange); };
+  auto put_x = [&](int c, const u32x4& r) { *reinterpret_cast<u32x4*>(xs + (c % 3) * XS::kBytes + xs_w) = r; };
+  auto compute = [&](int c, const Chunk& d) {
+    const uint8_t* xst = xs + (c % 3) * XS::kBytes + xs_r;
+    V xb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const V*>(xst + 16 * s);
+    const uint8_t* sc =
+        reinterpret_cast<const uint8_t*>(stab) + 4 * (((c / kScaleWin) & 1) * NP * kScaleWin + c % kScaleWin) + lq;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float sg = e8m0_to_f32(sc[4 * kScaleWin * (0 * 16 * RT + rt * 16 + l16)]);
+      const float su = e8m0_to_f32(sc[4 * kScaleWin * (1 * 16 * RT + rt * 16 + l16)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const V ag = decode8_bf16(d.q[0][rt][s], sg), au = decode8_bf16(d.q[1][rt][s], su);
+        accg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[s], accg[rt], 0, 0, 0);
+        accu[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[s], accu[rt], 0, 0, 0);
+      }
+    }
+  };
+  // Step c: publish chunk c+1's activations (held in Xn), sync, compute chunk c from register set
+  // D, refill D with chunk c+2's weights and Xn with chunk c+3's activations.  In the 4-step loop,
+  // step 4i also fetches scale group i % 4 of window i / 4 + 1, which step 4i + 2 writes.  Every
+  // step issues its loads in one order (4 weights, 1 activation, then the scale group), and the
+  // prologue issues the same sequence, so the wait counts the compiler derives at the loop heads
+  // are the steady ones.
+  u32x4 SQ;
+  auto step = [&](int c, Chunk& D, u32x4& Xn, int smode) {  // smode: 0 none, 1 fetch, 2 write
+    put_x(c + 1, Xn);
+    if (smode == 2) put_s(c / 16 + 1, (c / 4) % 4, SQ);
+    __syncthreads();
+    compute(c, D);
+    load(c + 2, D);
+    __builtin_amdgcn_sched_barrier(0);  // keep the load order fixed
+    fetch_x(c + 3, Xn);
+    if (smode == 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_s(c / 16 + 1, (c / 4) % 4, SQ);
+    }
+  };
+  Chunk A, B;
+  fetch_x(0, X[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load(0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_x(1, X[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  load(n_chunks > 1 ? 1 : 0, B);
+  __builtin_amdgcn_sched_barrier(0);
+  put_x(0, X[0]);
+  fetch_x(2, X[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  int c = 0;  // even: chunk c's weights in A, chunk c+1's in B
+  for (; c + 5 < n_chunks; c += 4) {
+    step(c, A, X[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 1, B, X[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 2, A, X[1], 2);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 3, B, X[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The 4-step loop has fetched every window that the remaining chunks read, except when it stops
+  // one iteration short of a window's last group (c % 16 == 12 with chunk c + 4 left): fetch that
+  // group here.
+  if (c % 16 == 12 && c + 4 < n_chunks) {
+    fetch_s(c / 16 + 1, 3, SQ);
+    put_s(c / 16 + 1, 3, SQ);
+  }
+  for (; c + 3 < n_chunks; c += 2) {
+    step(c, A, X[1], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 1, B, X[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // last 1-3 chunks: no loads past the end
+  if (c + 1 < n_chunks) put_x(c + 1, X[1]);
+  __syncthreads();
+  compute(c, A);
+  if (c + 2 < n_chunks) load(c + 2, A);
+  if (c + 1 < n_chunks) {
+    if (c + 2 < n_chunks) put_x(c + 2, X[0]);
+    __syncthreads();
+    compute(c + 1, B);
+  }
+  if (c + 2 < n_chunks) {
+    __syncthreads();
+    compute(c + 2, A);
+  }
+
+  // SwiGLU on the wave's own rows: lane holds rows n0 + rt*16 + 4*lq + i of token l16
+  const int m = l16;
+  if (m < ti.nr) {
+    const int64_t base = (int64_t)(ti.r0 + m) * I;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + rt * 16 + 4 * lq + i;
+        if (n < I) {
+          const float g = accg[rt][i], u = accu[rt][i];
+          const float h = (g / (1.0f + expf(-g))) * u;
+          uint16_t hi, lo;
+          Op<MOE_W_MXFP4>::split(h, hi, lo);
+          h_hi[base + n] = hi;
+          h_lo[base + n] = lo;
+        }
+      }
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
+    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    float* __restrict__ y_slots) {
+  constexpr int RT = kRowsRT2, NP = RT * 16;
+  typedef bf16x8 V;
+  typedef XStage<2> XS;  // hi plane then lo plane
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  int tile, nblk;
+  xcd_work(blockIdx.x, n_nblk, tile, nblk);
+  const TileInfo ti = get_tile(tiles, tile);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = (nblk * NW + wave) * 16 * RT;
+  const int ex = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = I >> 7;
+
+  uint8_t* xs = lds;  // [3][XS::kBytes]
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 3 * XS::kBytes + wave * stab_bytes(NP, n_chunks));
+
+  // h chunk = 16 tokens x 128 K x (hi, lo): 512 lane-loads, 128 per wave: lane-load q covers
+  // plane q / 256, token (q % 256) / 16, column q % 16
+  const __amdgpu_buffer_rsrc_t hr[2] = {make_rsrc(h_hi, (int64_t)n_slots * I * 2), make_rsrc(h_lo, (int64_t)n_slots * I * 2)};
+  uint32_t hoff[2], hs_w[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = 128 * wave + 64 * j + lane;
+    const int plane = q >> 8, tok = (q & 255) >> 4, col = q & 15;
+    hoff[j] = tok < ti.nr ? (uint32_t)(ti.r0 + tok) * (uint32_t)I * 2u + 16u * col : kOutOfRange;
+    hs_w[j] = (uint32_t)(plane * 16 * XS::kRow + tok * XS::kRow + 16 * col);
+  }
+  const int plane_of_j0 = (128 * wave) >> 8;  // both lane-loads of a wave hit one plane
+  const uint32_t hs_r = (uint32_t)(l16 * XS::kRow + 64 * lq);
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
+  uint32_t coff[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) coff[rt] = (uint32_t)(min(n0 + rt * 16 + l16, H - 1) * down.wr) + 16u * lq;
+  for (int f = lane; f < NP * n_chunks; f += 64) {
+    const int row = f / n_chunks, j = f - row * n_chunks;
+    stab[f] = bld4(sr, (uint32_t)(min(n0 + row, H - 1) * down.sr) + 4u * j);
+  }
+
+  f32x4 acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Chunk {
+    u32x4 q[RT];
+  };
+  auto load = [&](int c, Chunk& d) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) d.q[rt] = bld16(wr, coff[rt] + 64u * c);
+  };
+  u32x4 Hc[2][2];  // [chunk parity][lane-load]: fetched two chunks ahead, as in gate/up
+  auto fetch_h = [&](int c, u32x4 (&r)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r[j] = bld16(hr[plane_of_j0], c < n_chunks ? hoff[j] + 256u * c : kOutOfRange);
+  };
+  auto put_h = [&](int c, const u32x4 (&r)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(xs + (c % 3) * XS::kBytes + hs_w[j]) = r[j];
+  };
+  auto compute = [&](int c, const Chunk& d) {
+    const uint8_t* st = xs + (c % 3) * XS::kBytes + hs_r;
+    V bh[4], bl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bh[s] = *reinterpret_cast<const V*>(st + 16 * s);
+      bl[s] = *reinterpret_cast<const V*>(st + 16 * XS::kRow + 16 * s);
+    }
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float scale = e8m0_to_f32(sc[4 * n_chunks * (rt * 16 + l16)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const V a = decode8_bf16(d.q[rt][s], scale);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], acc[rt], 0, 0, 0);
+      }
+    }
+  };
+  auto step = [&](int c, Chunk& D, u32x4 (&Hn)[2]) {  // as in gate/up
+    put_h(c + 1, Hn);
+    __syncthreads();
+    compute(c, D);
+    load(c + 2, D);
+    fetch_h(c + 3, Hn);
+  };
+  Chunk A, B;
+  fetch_h(0, Hc[0]);
+  load(0, A);
+  fetch_h(1, Hc[1]);
+  load(n_chunks > 1 ? 1 : 0, B);
+  put_h(0, Hc[0]);
+  fetch_h(2, Hc[0]);
+  int c = 0;
+  for (; c + 3 < n_chunks; c += 2) {
+    step(c, A, Hc[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 1, B, Hc[0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (c + 1 < n_chunks) put_h(c + 1, Hc[1]);
+  __syncthreads();
+  compute(c, A);
+  if (c + 2 < n_chunks) load(c + 2, A);
+  if (c + 1 < n_chunks) {
+    if (c + 2 < n_chunks) put_h(c + 2, Hc[0]);
+    __syncthreads();
+    compute(c + 1, B);
+  }
+  if (c + 2 < n_chunks) {
+    __syncthreads();
+    compute(c + 2, A);
+  }
+
+  const int m = l16;
+  if (m < ti.nr) {
+    const int sl = sorted_slot[ti.r0 + m];
+    if (sl >= 0 && sl < n_slots) {
+      float* dst = y_slots + (int64_t)sl * H;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int n = n0 + rt * 16 + 4 * lq;
+        if ((H & 3) == 0 && n + 3 < H) {
+          *reinterpret_cast<f32x4*>(dst + n) = acc[rt];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n + i < H) dst[n + i] = acc[rt][i];
+        }
+      }
+    }
+  }
+}
+
 // Upper bound of the number of tiles: A active experts hold at least one row each, so
 // sum_e ceil(n_e / R) <= A + (rows - A) / R with A <= min(n_experts, rows).
 int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {
@@ -798,11 +1167,23 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
       h_hi, h_lo, T * k_total, H, I, down, tiles, sorted_slot, nb, y_slots);
 }
 
+// Row-split kernels: worth it once there are enough row blocks to fill the chip with full-K
+// streams; below that the K-split kernels spread each expert over more workgroups.
+constexpr int64_t kRowsMinBlocks = 1024;
+constexpr size_t kMaxLds = 160 * 1024;
+size_t gateup_rows_lds(int) { return 3 * (size_t)XStage<1>::kBytes + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, 2 * kScaleWin); }
+size_t down_rows_lds(int I) { return 3 * (size_t)XStage<2>::kBytes + kNW * (size_t)stab_bytes(16 * kRowsRT2, I / 128); }
+
 template <int FMT, int MT>
 hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                      const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
-  if (FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX) {
+  const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
+  const int nb_rows = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
+  if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
+    ffn_gateup_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, gateup_rows_lds(H), stream>>>(
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb_rows, h_hi, h_lo);
+  } else if (streamable) {
     launch_gateup_stream<MT, kRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
@@ -817,7 +1198,12 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
                    float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                    hipStream_t stream) {
   const int n_slots = T * k_total;
-  if (FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX) {
+  const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
+  const int nb_rows = (H + 16 * kRowsRT2 * kNW - 1) / (16 * kRowsRT2 * kNW);
+  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
+    ffn_down_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, down_rows_lds(I), stream>>>(
+        h_hi, h_lo, n_slots, H, I, down, tiles, sorted_slot, nb_rows, y_slots);
+  } else if (streamable) {
     launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);

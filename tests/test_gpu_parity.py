@@ -200,6 +200,17 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     (23, 32, 32, 6, 3, "fp16", "routed"),        # smallest FP16 shapes
     (64, 256, 128, 9, 8, "fp16", "routed"),
     (3, 64, 64, 50, 2, "mxfp4", "routed"),       # most experts empty
+    # many small tiles: the row-split streaming kernels (full-K streams per wave, shared LDS
+    # activation stages), at 1, 2, 3 and 5 chunks of 128 and with ragged row counts
+    (64, 128, 4096, 64, 4, "mxfp4", "routed"),
+    (64, 384, 4096, 64, 4, "mxfp4", "routed"),
+    (64, 4096, 256, 64, 4, "mxfp4", "routed"),
+    (64, 4096, 640, 64, 4, "mxfp4", "routed"),
+    (256, 1024, 992, 128, 8, "mxfp4", "routed"),
+    (256, 992, 1024, 256, 8, "mxfp4", "routed"),
+    # 17 and 21 chunks of 128: scale-table windows of 16 chunks, with the last one partly used
+    (128, 2176, 1024, 128, 4, "mxfp4", "routed"),
+    (128, 2688, 1024, 128, 4, "mxfp4", "routed"),
 ]
 
 

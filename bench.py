@@ -5,7 +5,7 @@ Workload: the concurrency-sweep MoE layer -- hidden 7168, 256 routed experts, to
 intermediate 2048, MXFP4 expert weights (codes uniform, E8M0 in [118, 127]), bf16 activations
 ~N(0,1), router weights ~N(0, 1/7168) so logits are ~N(0,1); seeded synthetic inputs (seed 0).
 One step = one layer call on T tokens (default 176): moe_route -> moe_bucket -> expert FFN
-(gate/up phase, down phase) -> moe_combine, inputs resident in HBM.  Weight sets are rotated so
+(tile plan, gate/up phase, down phase) -> moe_combine, inputs resident in HBM.  Weight sets are rotated so
 that the bytes touched between two visits of one set exceed the 256 MB Infinity Cache.
 
 Prints one JSON line: tokens/s (value), ms per layer call, the gate/up kernel's roofline (HIP-event
@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens of the oracle's timed sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain elementwise copy (torch.neg, fp32) of this many MiB three times, "
+                         "for scaling memory counters, and exit")
     return ap.parse_args()
 
 
@@ -79,12 +82,14 @@ class Runner:
         rec(1)
         m.moe_bucket(self.ids, self.n_experts, out=self.b, workspace=self.bucket_ws)
         rec(2)
-        m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws)
+        m.moe_expert_ffn_plan(self.T, s["W"], self.b.offsets, self.kt, self.ffn_ws)
         rec(3)
-        m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws, self.y_slots)
+        m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws)
         rec(4)
-        m.moe_combine(self.y_slots, self.w, out=self.y)
+        m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws, self.y_slots)
         rec(5)
+        m.moe_combine(self.y_slots, self.w, out=self.y)
+        rec(6)
 
 
 def time_steps(runner, steps, warmup):
@@ -101,11 +106,11 @@ def time_steps(runner, steps, warmup):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end) / steps
     # second timed pass with events between the calls (same stream, same kernels)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     for i in range(steps):
         runner.step(i, evs[i])
     torch.cuda.synchronize()
-    names = ["route", "bucket", "ffn_gateup", "ffn_down", "combine"]
+    names = ["route", "bucket", "ffn_plan", "ffn_gateup", "ffn_down", "combine"]
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     return total_ms, per
 
@@ -136,9 +141,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this layer build has no "
               "multi-GPU path: see the sharding design notes)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
+    if args.copy_calibration_mib:
+        return copy_calibration(args.copy_calibration_mib)
     import synth
     import mxfp4_routed_expert_router_amd as moe
 
@@ -172,6 +178,7 @@ def main():
 
     results = {}
     for T in Ts:
+        print(f"bench: T={T}", file=sys.stderr, flush=True)
         sets = make_sets(T)
         runner = Runner(moe, sets, T, k, 0, E, H, I)
         steps = args.steps if T == args.tokens else args.sweep_steps
@@ -212,7 +219,8 @@ def main():
         "active_experts": head["active"],
         "rotation_sets": head["rotation_sets"],
         "per_call_ms": {kk: round(v, 5) for kk, v in head["per"].items()},
-        "roofline": {"kernel": "ffn_gateup_kernel (gate/up grouped GEMM + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": "ffn_gateup_rows_kernel (moe_expert_ffn_gateup: grouped MXFP4 gate/up GEMM + SwiGLU)",
+                     "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "algorithmic_bytes_per_launch": head["gateup_bytes"], "launch_ms": head["per"]["ffn_gateup"]},
@@ -224,10 +232,24 @@ def main():
         "input_generation_s": gen_s,
     }
     if not args.no_cpu:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size (reads and writes mib MiB each), to scale FETCH_SIZE and
+    WRITE_SIZE readings into bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}), flush=True)
 
 
 def cpu_baseline(L, T, n):

@@ -155,12 +155,21 @@ moe_status moe_expert_ffn(const void *x, moe_act_dtype x_dtype, int T, int k_tot
                           const int32_t *sorted_slot, float *y_slots, void *workspace,
                           size_t workspace_bytes, void *stream);
 
-/* The two phases of moe_expert_ffn as separate calls, for callers that time or overlap them.
- * moe_expert_ffn_gateup computes h = SiLU(W_gate x) * (W_up x) for every sorted row into the
- * workspace; moe_expert_ffn_down turns the workspace's h into y_slots.  Calling gateup then down
- * on one stream with the same arguments and the same workspace gives exactly moe_expert_ffn's
- * result (it launches the same two kernels).  x_dtype of the down call only selects the format
- * check (it must match W->fmt as in moe_expert_ffn).  Errors as for moe_expert_ffn. */
+/* The three steps of moe_expert_ffn as separate calls, for callers that time or overlap them.
+ * moe_expert_ffn_plan writes the tile schedule (which expert and sorted rows each 16-row tile
+ * covers, from offsets) into the workspace; moe_expert_ffn_gateup computes
+ * h = SiLU(W_gate x) * (W_up x) for every sorted row into the workspace; moe_expert_ffn_down
+ * turns the workspace's h into y_slots.  Both phases read the schedule, so the plan must run first
+ * on the same workspace with the same T, k_total, W->n_experts and offsets contents; a schedule
+ * left from other arguments gives wrong rows, but the kernels check every schedule entry against
+ * the call's bounds and never access memory outside the buffers described.  Calling plan, gateup
+ * and down on one stream with the same arguments gives exactly moe_expert_ffn's result (it
+ * launches the same kernels).  x_dtype of the plan and down calls only selects the format check
+ * (it must match W->fmt as in moe_expert_ffn); the plan reads only W's sizes.  Errors as for
+ * moe_expert_ffn. */
+moe_status moe_expert_ffn_plan(moe_act_dtype x_dtype, int T, int k_total,
+                               const moe_expert_weights *W, const int32_t *offsets, void *workspace,
+                               size_t workspace_bytes, void *stream);
 moe_status moe_expert_ffn_gateup(const void *x, moe_act_dtype x_dtype, int T, int k_total,
                                  const moe_expert_weights *W, const int32_t *offsets,
                                  const int32_t *sorted_slot, void *workspace,

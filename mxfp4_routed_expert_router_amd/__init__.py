@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_workspace_bytes.argtypes = [i, i, ctypes.POINTER(moe_expert_weights)]
         L.moe_expert_ffn.restype = i
         L.moe_expert_ffn.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp, st, vp]
+        L.moe_expert_ffn_plan.restype = i
+        L.moe_expert_ffn_plan.argtypes = [i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, st, vp]
         L.moe_expert_ffn_gateup.restype = i
         L.moe_expert_ffn_gateup.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, st, vp]
         L.moe_expert_ffn_down.restype = i
@@ -225,9 +227,19 @@ def moe_expert_ffn(x: torch.Tensor, W: ExpertWeights, offsets: torch.Tensor, sor
     return y
 
 
+def moe_expert_ffn_plan(T: int, W: ExpertWeights, offsets: torch.Tensor, k_total: int,
+                        workspace: torch.Tensor) -> None:
+    """Step 1 of moe_expert_ffn: the tile schedule (from offsets) into `workspace`
+    (moe_expert_ffn_workspace_bytes bytes), read by the two phases below."""
+    xdt = MOE_ACT_FP16 if W.fmt == MOE_W_FP16 else MOE_ACT_BF16
+    _check(lib().moe_expert_ffn_plan(xdt, T, k_total, ctypes.byref(W.c), _ptr(offsets), _ptr(workspace),
+                                     workspace.numel(), _stream(offsets.device)),
+           "moe_expert_ffn_plan")
+
+
 def moe_expert_ffn_gateup(x: torch.Tensor, W: ExpertWeights, offsets: torch.Tensor, sorted_slot: torch.Tensor,
                           k_total: int, workspace: torch.Tensor) -> None:
-    """Phase 1 of moe_expert_ffn: h into `workspace` (moe_expert_ffn_workspace_bytes bytes)."""
+    """Phase 1 of moe_expert_ffn: h into `workspace`, after moe_expert_ffn_plan on it."""
     T = x.shape[0]
     _check(lib().moe_expert_ffn_gateup(_ptr(x), _act_dtype(x), T, k_total, ctypes.byref(W.c), _ptr(offsets),
                                        _ptr(sorted_slot), _ptr(workspace), workspace.numel(), _stream(x.device)),
@@ -305,6 +317,6 @@ class MoELayer:
         return moe_combine(self.y_slots, self.weights, out=self.y)
 
 
-__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_gateup", "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant",
+__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_plan", "moe_expert_ffn_gateup", "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",
            "ExpertWeights", "Buckets", "MoELayer", "MoEError", "lib"]

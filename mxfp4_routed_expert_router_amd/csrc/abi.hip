@@ -167,6 +167,18 @@ moe_status check_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, c
 
 extern "C" {
 
+moe_status moe_expert_ffn_plan(moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                               const int32_t* offsets, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  uint16_t *h_hi, *h_lo;
+  void* table;
+  // a non-null stand-in for sorted_slot: the plan reads only offsets
+  moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, offsets, nullptr, false, false, workspace,
+                            workspace_bytes, &h_hi, &h_lo, &table);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, offsets, table, (hipStream_t)stream));
+}
+
 moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, int k_total,
                                  const moe_expert_weights* W, const int32_t* offsets, const int32_t* sorted_slot,
                                  void* workspace, size_t workspace_bytes, void* stream) {
@@ -177,7 +189,7 @@ moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, in
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->gate),
-                                           dev(W->up), offsets, sorted_slot, h_hi, h_lo, table, (hipStream_t)stream));
+                                           dev(W->up), sorted_slot, h_hi, h_lo, table, (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
@@ -203,8 +215,10 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   const int H = W->hidden, I = W->inter;
-  hipError_t err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
-                                          offsets, sorted_slot, h_hi, h_lo, table, (hipStream_t)stream);
+  hipError_t err = moe::launch_ffn_plan(T, k_total, W->n_experts, offsets, table, (hipStream_t)stream);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up), sorted_slot,
+                               h_hi, h_lo, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, H, I, dev(W->down), sorted_slot, y_slots,
                                          h_hi, h_lo, table, (hipStream_t)stream));

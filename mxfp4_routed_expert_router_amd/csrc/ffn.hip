@@ -83,12 +83,17 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
   for (int t = total + tid; t < n_entries; t += blockDim.x) table[t] = TileEntry{0, 0, 0, 0};
 }
 
-__device__ __forceinline__ TileInfo get_tile(const TileEntry* __restrict__ table, int tile) {
+// Entry `tile`, checked against the launch: an entry naming an expert outside [0, n_experts), more
+// than max_rows rows or rows outside [0, n_rows) (a table not built for this call) reads as empty,
+// so the kernels never index outside their buffers.
+__device__ __forceinline__ TileInfo get_tile(const TileEntry* __restrict__ table, int tile, int n_experts, int n_rows,
+                                             int max_rows) {
   const TileEntry t = table[tile];
   TileInfo r;
   r.e = __builtin_amdgcn_readfirstlane(t.e);
   r.r0 = __builtin_amdgcn_readfirstlane(t.r0);
   r.nr = __builtin_amdgcn_readfirstlane(t.nr);
+  if (r.e < 0 || r.e >= n_experts || r.r0 < 0 || r.nr > max_rows || r.r0 > n_rows - r.nr) r.nr = 0;
   return r;
 }
 
@@ -182,14 +187,14 @@ __device__ __forceinline__ typename Op<FMT>::V decode_step(const RawW<FMT>& r, i
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   typedef typename Op<FMT>::V V;
   __shared__ float s_red[NW][RT][2][256];
   const int n_slots = T * k_total;
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16 * MT);
   if (ti.nr <= 0) return;  // uniform across the workgroup
   // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -337,13 +342,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   typedef typename Op<FMT>::V V;
   __shared__ float s_red[NW][RT][256];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16 * MT);
   if (ti.nr <= 0) return;
   // wave index in an SGPR: the K-share loop bounds are then wave-uniform (scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -521,7 +526,7 @@ __host__ __device__ constexpr int stab_bytes(int pairs, int cpw) { return pairs 
 template <int NW, int MT, int RT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_stream_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   constexpr int NM = 2, NP = NM * RT * 16;  // (matrix, row) pairs of the row block
   typedef bf16x8 V;
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_stream_kernel(
   const int n_slots = T * k_total;
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16 * MT);
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
@@ -656,14 +661,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_stream_kernel(
 template <int NW, int MT, int RT>
 __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   constexpr int NP = RT * 16;  // rows of the row block
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16 * MT);
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
@@ -760,53 +765,55 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
 // ------------------------------------------------------------------------------------------------
 // Row-split streaming variants (many active experts).  The four waves of a workgroup own
 // different weight rows, each over the whole reduction dimension, so no cross-wave reduction is
-// needed; the activation (or h) chunk of the tile's tokens is shared: each wave loads a quarter
-// of it into registers, writes it to a 3-stage LDS buffer, and every wave reads its MFMA operands
-// from LDS.  This cuts the L1 accesses spent on activations 4x -- the L1 access rate, not HBM,
-// bounds these kernels.  One barrier per chunk: a stage written in step c is read in step c+1 and
-// rewritten in step c+3, and every wave passes the barriers of steps c+1 and c+2 in between.
+// needed; the activation (or h) chunk of the tile's tokens is shared: each wave loads a part of
+// it into registers, writes it to an LDS stage, and every wave reads its MFMA operands from LDS.
+// This cuts the L1 requests spent on activations 4x (the L1 request rate, more than HBM, bounds
+// these kernels).  Each wave keeps the block scales of its rows over the whole reduction in an
+// LDS table filled once: refilling a smaller table in windows re-fetches the partial 128-byte
+// lines that straddle the windows (scale rows are 224 bytes for a 7168-wide matrix).
 // ------------------------------------------------------------------------------------------------
+constexpr int kRowsRT1 = 2, kRowsRT2 = 4;  // 16-row tiles per wave: gate/up (of each matrix), down
+
 // One LDS stage holds a 16-token x 128-K chunk of 16-bit operands in PL planes (x: one plane;
 // h: hi and lo planes).  Rows are padded by 16 bytes so the MFMA operand reads spread over banks.
-constexpr int kRowsRT1 = 2, kRowsRT2 = 4;  // 16-row tiles per wave: gate/up (of each matrix), down
-constexpr int kScaleWin = 16;              // chunks per scale-table window (gate/up)
-
 template <int PL>
 struct XStage {
   static constexpr int kRow = 128 * 2 + 16;
   static constexpr int kBytes = PL * 16 * kRow;
 };
 
+// Gate/up: a step covers two 128-K chunks, i.e. a whole 128-byte line of every weight row, so the
+// two halves of a line are requested together (one step apart, a line's second half was often
+// evicted from L2 and fetched again).  The activation ring has two stages of two chunks; with the
+// stage written right after the step's barrier, one barrier per step orders both the writes
+// before their reads (next step) and the reads before the stage's rewrite (the step after).
+constexpr int kGuXRow = 2 * 256 + 16;     // one token's two chunks of x + padding
+constexpr int kGuXStage = 16 * kGuXRow;  // bytes of one stage
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   constexpr int RT = kRowsRT1, NM = 2, NP = NM * RT * 16;
   typedef bf16x8 V;
-  typedef XStage<1> XS;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16);
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = (nblk * NW + wave) * 16 * RT;  // this wave's first row
   const int e = __builtin_amdgcn_readfirstlane(ti.e);
-  const int n_chunks = H >> 7;
+  const int n_chunks = H >> 7, n_steps = (n_chunks + 1) >> 1;
 
-  // The wave's scale table holds two 16-chunk windows: [window][pair][16] dwords (a dword is the
-  // four block scales of one row in one chunk).  Chunk j lives in window (j / 16) % 2, column
-  // j % 16.  While window w is in use, window w+1 is fetched in four 16-byte-per-lane loads (16
-  // pairs x 64 bytes each), one every four steps: scattered per-row dword loads would cost about
-  // as much L1 address work as the weight loads themselves.
-  uint8_t* xs = lds;  // [3][XS::kBytes]
-  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 3 * XS::kBytes + wave * stab_bytes(NP, 2 * kScaleWin));
+  uint8_t* xs = lds;  // [2][kGuXStage]
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kGuXStage + wave * stab_bytes(NP, n_chunks));
 
-  // This wave's share of each activation chunk: lane-load q = 64*wave + lane -> token q/16,
-  // 16-byte column q%16.  Padded tokens get an out-of-range offset (no memory access).
+  // Activations: thread q = 64*wave + lane moves token q/16, 16-byte column q%16 of both chunks of
+  // a step.  Padded tokens get an out-of-range offset (reads zeros, no memory access).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
   const int q_tok = (64 * wave + lane) >> 4, q_col = lane & 15;
   uint32_t xoff;
@@ -816,8 +823,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     ok = ok && sl >= 0 && sl < n_slots;
     xoff = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 16u * q_col : kOutOfRange;
   }
-  const uint32_t xs_w = (uint32_t)(q_tok * XS::kRow + 16 * q_col);  // where this lane writes
-  const uint32_t xs_r = (uint32_t)(l16 * XS::kRow + 64 * lq);        // where this lane reads (+16*s)
+  const uint32_t xs_w = (uint32_t)(q_tok * kGuXRow + 16 * q_col);  // + 256 * chunk of the step
+  const uint32_t xs_r = (uint32_t)(l16 * kGuXRow + 64 * lq);        // + 256 * chunk + 16 * s
 
   const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
                                          make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
@@ -830,26 +837,49 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
     coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
   }
-  // Scale group g (0..3) of window w: lane l carries pair 16g + l/4, columns 4(l%4) .. 4(l%4)+3.
-  const int sg_pair = lane >> 2, sg_col = 4 * (lane & 3);
-  uint32_t sg_off[4];
+
+  // Scale table [pair][n_chunks] dwords (a dword: the four block scales of one row in one chunk),
+  // pair = m * 16 * RT + row offset.  Filled per matrix, 8 loads in flight per lane, in 16-byte
+  // units when rows allow it.
+  {
+    const int rows = 16 * RT;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int pair = 16 * g + sg_pair, row = min(n0 + pair % (16 * RT), I - 1);
-    sg_off[g] = (uint32_t)(row * (pair < 16 * RT ? gate.sr : up.sr)) + 4u * sg_col;
-  }
-  auto fetch_s = [&](int w, int g, u32x4& r) {
-    r = bld16(sr[g / 2], w * kScaleWin + sg_col < n_chunks ? sg_off[g] + 4u * kScaleWin * w : kOutOfRange);
-  };
-  auto put_s = [&](int w, int g, const u32x4& r) {
-    *reinterpret_cast<u32x4*>(stab + ((w & 1) * NP + 16 * g + sg_pair) * kScaleWin + sg_col) = r;
-  };
-  {  // window 0
-    u32x4 w0[4];
+    for (int m = 0; m < NM; ++m) {
+      const ProjDev& p = m ? up : gate;
+      const bool vec = (n_chunks & 3) == 0 && (p.sr & 15) == 0 && ((uintptr_t)(p.s + (int64_t)e * p.se) & 15) == 0;
+      uint32_t* tm = stab + m * rows * n_chunks;
+      if (vec) {
+        const int upr = n_chunks >> 2, total = rows * upr;
+        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+          u32x4 v[8];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) fetch_s(0, g, w0[g]);
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
+            v[i] = bld16(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 16u * u : kOutOfRange);
+          }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) put_s(0, g, w0[g]);
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane;
+            if (f < total) *reinterpret_cast<u32x4*>(tm + 4 * f) = v[i];
+          }
+        }
+      } else {
+        const int total = rows * n_chunks;
+        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+          uint32_t v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
+            v[i] = bld4(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 4u * j : kOutOfRange);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane;
+            if (f < total) tm[f] = v[i];
+          }
+        }
+      }
+    }
   }
 
   f32x4 accg[RT], accu[RT];
@@ -859,109 +889,98 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     accu[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  struct Chunk {
-    u32x4 q[NM][RT];
+  struct Step {
+    u32x4 q[NM][RT][2];  // [matrix][row tile][chunk of the step]
   };
-  auto load = [&](int c, Chunk& d) {
+  // (the second chunk of the last step of an odd chunk count reads nothing)
+  auto load = [&](int s, Step& d) {
+    const bool two = 2 * s + 1 < n_chunks;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) d.q[m][rt] = bld16(wr[m], coff[m][rt] + 64u * c);
+      for (int rt = 0; rt < RT; ++rt) {
+        d.q[m][rt][0] = bld16(wr[m], coff[m][rt] + 128u * s);
+        d.q[m][rt][1] = bld16(wr[m], two ? coff[m][rt] + 128u * s + 64u : kOutOfRange);
+      }
   };
-  // Activation chunks are fetched two chunks ahead, like the weights: X[c % 2] holds chunk c
-  // until it is written to its stage, then is refilled with chunk c + 2 (an out-of-range offset,
-  // which reads zeros without touching memory, past the last chunk).
-  u32x4 X[2];
-  auto fetch_x = [&](int c, u32x4& r) { r = bld16(xr, c < n_chunks ? xoff + 256u * c : kOutOfRange); };
-  auto put_x = [&](int c, const u32x4& r) { *reinterpret_cast<u32x4*>(xs + (c % 3) * XS::kBytes + xs_w) = r; };
-  auto compute = [&](int c, const Chunk& d) {
-    const uint8_t* xst = xs + (c % 3) * XS::kBytes + xs_r;
+  // Activations are fetched two steps ahead, like the weights: X[s % 2] holds step s's chunks
+  // until they are written to their stage, then is refilled with step s + 2's.
+  u32x4 X[2][2];
+  auto fetch_x = [&](int s, u32x4 (&r)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r[j] = bld16(xr, 2 * s + j < n_chunks ? xoff + 512u * s + 256u * j : kOutOfRange);
+  };
+  auto put_x = [&](int s, const u32x4 (&r)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(xs + (s & 1) * kGuXStage + xs_w + 256 * j) = r[j];
+  };
+  auto compute_chunk = [&](int s, int j, const Step& d) {
+    const int c = 2 * s + j;
+    const uint8_t* xst = xs + (s & 1) * kGuXStage + xs_r + 256 * j;
     V xb[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xb[s] = *reinterpret_cast<const V*>(xst + 16 * s);
-    const uint8_t* sc =
-        reinterpret_cast<const uint8_t*>(stab) + 4 * (((c / kScaleWin) & 1) * NP * kScaleWin + c % kScaleWin) + lq;
+    for (int k = 0; k < 4; ++k) xb[k] = *reinterpret_cast<const V*>(xst + 16 * k);
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float sg = e8m0_to_f32(sc[4 * kScaleWin * (0 * 16 * RT + rt * 16 + l16)]);
-      const float su = e8m0_to_f32(sc[4 * kScaleWin * (1 * 16 * RT + rt * 16 + l16)]);
+      const float sg = e8m0_to_f32(sc[4 * n_chunks * (0 * 16 * RT + rt * 16 + l16)]);
+      const float su = e8m0_to_f32(sc[4 * n_chunks * (1 * 16 * RT + rt * 16 + l16)]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const V ag = decode8_bf16(d.q[0][rt][s], sg), au = decode8_bf16(d.q[1][rt][s], su);
-        accg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[s], accg[rt], 0, 0, 0);
-        accu[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[s], accu[rt], 0, 0, 0);
+      for (int k = 0; k < 4; ++k) {
+        const V ag = decode8_bf16(d.q[0][rt][j][k], sg), au = decode8_bf16(d.q[1][rt][j][k], su);
+        accg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[k], accg[rt], 0, 0, 0);
+        accu[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[k], accu[rt], 0, 0, 0);
       }
     }
   };
-  // Step c: publish chunk c+1's activations (held in Xn), sync, compute chunk c from register set
-  // D, refill D with chunk c+2's weights and Xn with chunk c+3's activations.  In the 4-step loop,
-  // step 4i also fetches scale group i % 4 of window i / 4 + 1, which step 4i + 2 writes.  Every
-  // step issues its loads in one order (4 weights, 1 activation, then the scale group), and the
-  // prologue issues the same sequence, so the wait counts the compiler derives at the loop heads
-  // are the steady ones.
-  u32x4 SQ;
-  auto step = [&](int c, Chunk& D, u32x4& Xn, int smode) {  // smode: 0 none, 1 fetch, 2 write
-    put_x(c + 1, Xn);
-    if (smode == 2) put_s(c / 16 + 1, (c / 4) % 4, SQ);
+  // Step s: sync, publish step s+1's activations (held in Xn), compute step s from register set D,
+  // refill D with step s+2's weights and Xn with step s+3's activations.  Every step issues its
+  // loads in one order (8 weights, then 2 activations) and the prologue issues the same sequence,
+  // so the wait counts the compiler derives at the loop head are the steady ones.
+  auto step = [&](int s, Step& D, u32x4 (&Xn)[2]) {
     __syncthreads();
-    compute(c, D);
-    load(c + 2, D);
+    put_x(s + 1, Xn);
+    compute_chunk(s, 0, D);
+    compute_chunk(s, 1, D);
+    load(s + 2, D);
     __builtin_amdgcn_sched_barrier(0);  // keep the load order fixed
-    fetch_x(c + 3, Xn);
-    if (smode == 1) {
-      __builtin_amdgcn_sched_barrier(0);
-      fetch_s(c / 16 + 1, (c / 4) % 4, SQ);
-    }
+    fetch_x(s + 3, Xn);
   };
-  Chunk A, B;
+  Step A, B;
   fetch_x(0, X[0]);
   __builtin_amdgcn_sched_barrier(0);
   load(0, A);
   __builtin_amdgcn_sched_barrier(0);
   fetch_x(1, X[1]);
   __builtin_amdgcn_sched_barrier(0);
-  load(n_chunks > 1 ? 1 : 0, B);
+  load(n_steps > 1 ? 1 : 0, B);
   __builtin_amdgcn_sched_barrier(0);
   put_x(0, X[0]);
   fetch_x(2, X[0]);
   __builtin_amdgcn_sched_barrier(0);
-  int c = 0;  // even: chunk c's weights in A, chunk c+1's in B
-  for (; c + 5 < n_chunks; c += 4) {
-    step(c, A, X[1], 1);
+  int s = 0;  // even: step s's weights in A, step s+1's in B
+  for (; s + 3 < n_steps; s += 2) {
+    step(s, A, X[1]);
     __builtin_amdgcn_sched_barrier(0);
-    step(c + 1, B, X[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    step(c + 2, A, X[1], 2);
-    __builtin_amdgcn_sched_barrier(0);
-    step(c + 3, B, X[0], 0);
+    step(s + 1, B, X[0]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // The 4-step loop has fetched every window that the remaining chunks read, except when it stops
-  // one iteration short of a window's last group (c % 16 == 12 with chunk c + 4 left): fetch that
-  // group here.
-  if (c % 16 == 12 && c + 4 < n_chunks) {
-    fetch_s(c / 16 + 1, 3, SQ);
-    put_s(c / 16 + 1, 3, SQ);
-  }
-  for (; c + 3 < n_chunks; c += 2) {
-    step(c, A, X[1], 0);
-    __builtin_amdgcn_sched_barrier(0);
-    step(c + 1, B, X[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // last 1-3 chunks: no loads past the end
-  if (c + 1 < n_chunks) put_x(c + 1, X[1]);
+  // last 1-3 steps: no loads past the end
   __syncthreads();
-  compute(c, A);
-  if (c + 2 < n_chunks) load(c + 2, A);
-  if (c + 1 < n_chunks) {
-    if (c + 2 < n_chunks) put_x(c + 2, X[0]);
+  if (s + 1 < n_steps) put_x(s + 1, X[1]);
+  compute_chunk(s, 0, A);
+  if (2 * s + 1 < n_chunks) compute_chunk(s, 1, A);
+  if (s + 2 < n_steps) load(s + 2, A);
+  if (s + 1 < n_steps) {
     __syncthreads();
-    compute(c + 1, B);
+    if (s + 2 < n_steps) put_x(s + 2, X[0]);
+    compute_chunk(s + 1, 0, B);
+    if (2 * s + 3 < n_chunks) compute_chunk(s + 1, 1, B);
   }
-  if (c + 2 < n_chunks) {
+  if (s + 2 < n_steps) {
     __syncthreads();
-    compute(c + 2, A);
+    compute_chunk(s + 2, 0, A);
+    if (2 * s + 5 < n_chunks) compute_chunk(s + 2, 1, A);
   }
 
   // SwiGLU on the wave's own rows: lane holds rows n0 + rt*16 + 4*lq + i of token l16
@@ -988,7 +1007,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
-    const TileEntry* __restrict__ tiles, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   constexpr int RT = kRowsRT2, NP = RT * 16;
   typedef bf16x8 V;
@@ -996,7 +1015,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
-  const TileInfo ti = get_tile(tiles, tile);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16);
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
@@ -1154,7 +1173,7 @@ void launch_gateup_stream(const FfnPlan& pl, const void* x, int T, int k_total, 
   const int cpw = (H / 128 + kNW - 1) / kNW;
   const size_t lds = (size_t)kNW * stab_bytes(2 * 16 * RT, cpw) + (size_t)kNW * RT * 2 * 256 * 4;
   ffn_gateup_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
-      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb, h_hi, h_lo);
+      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
 }
 template <int MT, int RT>
 void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
@@ -1164,14 +1183,14 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
   const int cpw = (I / 128 + kNW - 1) / kNW;
   const size_t lds = (size_t)kNW * stab_bytes(16 * RT, cpw) + (size_t)kNW * RT * 256 * 4;
   ffn_down_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
-      h_hi, h_lo, T * k_total, H, I, down, tiles, sorted_slot, nb, y_slots);
+      h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
 }
 
 // Row-split kernels: worth it once there are enough row blocks to fill the chip with full-K
 // streams; below that the K-split kernels spread each expert over more workgroups.
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
-size_t gateup_rows_lds(int) { return 3 * (size_t)XStage<1>::kBytes + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, 2 * kScaleWin); }
+size_t gateup_rows_lds(int H) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, H / 128); }
 size_t down_rows_lds(int I) { return 3 * (size_t)XStage<2>::kBytes + kNW * (size_t)stab_bytes(16 * kRowsRT2, I / 128); }
 
 template <int FMT, int MT>
@@ -1182,13 +1201,13 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
   const int nb_rows = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
   if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
     ffn_gateup_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, gateup_rows_lds(H), stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb_rows, h_hi, h_lo);
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
     launch_gateup_stream<MT, kRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
     ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, sorted_slot, nb, h_hi, h_lo);
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
   }
   return hipGetLastError();
 }
@@ -1202,13 +1221,13 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const int nb_rows = (H + 16 * kRowsRT2 * kNW - 1) / (16 * kRowsRT2 * kNW);
   if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
     ffn_down_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, down_rows_lds(I), stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, sorted_slot, nb_rows, y_slots);
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
     launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
     ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, sorted_slot, nb, y_slots);
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
   }
   return hipGetLastError();
 }
@@ -1243,6 +1262,7 @@ FfnPlan ffn_plan(int T, int k_total, int n_experts) {
   const int64_t active = rows < n_experts ? rows : n_experts;
   const double mean = (double)rows / (double)(active > 0 ? active : 1);
   FfnPlan p;
+  p.n_experts = n_experts;
   p.mt = mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4);
   p.tiles = (max_tiles(rows, n_experts, 16 * p.mt) + kXcds - 1) / kXcds * kXcds;
   return p;
@@ -1252,14 +1272,19 @@ size_t ffn_table_bytes(int T, int k_total, int n_experts) {
   return (size_t)ffn_plan(T, k_total, n_experts).tiles * sizeof(TileEntry);
 }
 
-hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
-                             ProjDev up, const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi,
-                             uint16_t* h_lo, void* table, hipStream_t stream) {
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, const int32_t* offsets, void* table,
+                           hipStream_t stream) {
   const FfnPlan pl = ffn_plan(T, k_total, n_experts);
-  TileEntry* tiles = (TileEntry*)table;
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, 16 * pl.mt, (int)pl.tiles, tiles);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, 16 * pl.mt, (int)pl.tiles,
+                                           (TileEntry*)table);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
+                             ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+                             const void* table, hipStream_t stream) {
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  const TileEntry* tiles = (const TileEntry*)table;
   if (fmt == MOE_W_FP16)
     return gateup_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   return gateup_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);

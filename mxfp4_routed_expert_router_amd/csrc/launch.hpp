@@ -31,13 +31,17 @@ struct ProjDev {
 struct FfnPlan {
   int mt;  // 16*mt sorted rows (tokens) per tile
   int64_t tiles;
+  int n_experts;
 };
 FfnPlan ffn_plan(int T, int k_total, int n_experts);
 size_t ffn_table_bytes(int T, int k_total, int n_experts);
-// The gate/up phase builds the tile table in `table` and writes h; the down phase reads both.
+// The plan builds the tile table in `table`; the gate/up phase reads it and writes h; the down
+// phase reads both.
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, const int32_t* offsets, void* table,
+                           hipStream_t stream);
 hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
-                             ProjDev up, const int32_t* offsets, const int32_t* sorted_slot, uint16_t* h_hi,
-                             uint16_t* h_lo, void* table, hipStream_t stream);
+                             ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+                             const void* table, hipStream_t stream);
 hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream);

@@ -144,6 +144,24 @@ def test_expert_ffn_validation():
     assert ffn(weights(down__w=P + 0x10000 + 8)) == ALIGN
 
 
+def test_expert_ffn_plan_validation():
+    L = m.lib()
+    W = weights()
+    need = L.moe_expert_ffn_workspace_bytes(4, 2, ctypes.byref(W))
+
+    def plan(W, T=4, kt=2, xdt=0, off=fake(0x100), ws=fake(0x4000), wsb=need):
+        return L.moe_expert_ffn_plan(xdt, T, kt, ctypes.byref(W), off, ws, wsb, None)
+
+    assert L.moe_expert_ffn_plan(0, 0, 2, None, None, None, 0, None) == OK
+    assert plan(W, off=None) == NULL
+    assert plan(W, wsb=need - 1) == WORKSPACE
+    assert plan(W, ws=fake(0x4008)) == ALIGN
+    assert plan(W, off=fake(0x102)) == ALIGN
+    assert plan(W, xdt=1) == DTYPE
+    assert plan(weights(n_experts=0)) == SHAPE
+    assert plan(W, kt=0) == SHAPE
+
+
 def test_combine_and_dequant_validation():
     L = m.lib()
     assert L.moe_combine(None, None, 0, 2, 64, None, None) == OK

@@ -332,7 +332,7 @@ def test_invalid_ids_are_dropped_safely(orc):
 
 
 def test_split_phases_equal_fused_call():
-    """moe_expert_ffn_gateup then moe_expert_ffn_down == moe_expert_ffn, bit for bit."""
+    """moe_expert_ffn_plan, moe_expert_ffn_gateup then moe_expert_ffn_down == moe_expert_ffn, bit for bit."""
     L = host_layer("decode", 8)
     wl = L.wl
     t = synth.to_torch(L, DEV)
@@ -341,6 +341,34 @@ def test_split_phases_equal_fused_call():
     b = moe.moe_bucket(ids, wl.n_experts)
     a = moe.moe_expert_ffn(t["x"], W, b.offsets, b.sorted_slot, wl.top_k)
     ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(8, wl.top_k, W), dtype=torch.uint8, device=DEV)
+    moe.moe_expert_ffn_plan(8, W, b.offsets, wl.top_k, ws)
     moe.moe_expert_ffn_gateup(t["x"], W, b.offsets, b.sorted_slot, wl.top_k, ws)
     c = moe.moe_expert_ffn_down(8, W, b.offsets, b.sorted_slot, wl.top_k, ws, torch.empty_like(a))
     assert np.array_equal(sync_np(a).view(np.uint32), sync_np(c).view(np.uint32))
+
+
+def test_stale_plan_stays_in_bounds():
+    """A tile schedule planned for a larger batch, then used for a smaller one: every entry that
+    names rows past the smaller batch reads as empty (no access outside the buffers), and the
+    properly planned call afterwards is exact again."""
+    L = host_layer("decode", 64)
+    wl = L.wl
+    t = synth.to_torch(L, DEV)
+    W = expert_weights(t)
+    ids, w, _ = moe.moe_route(t["x"], t["router"], wl.top_k)
+    b = moe.moe_bucket(ids, wl.n_experts)
+    ws = torch.empty(moe.moe_expert_ffn_workspace_bytes(64, wl.top_k, W), dtype=torch.uint8, device=DEV)
+    moe.moe_expert_ffn_plan(64, W, b.offsets, wl.top_k, ws)
+    T2 = 8
+    x2 = t["x"][:T2].contiguous()
+    ids2, _, _ = moe.moe_route(x2, t["router"], wl.top_k)
+    b2 = moe.moe_bucket(ids2, wl.n_experts)
+    out = torch.empty((T2 * wl.top_k, wl.hidden), dtype=torch.float32, device=DEV)
+    moe.moe_expert_ffn_gateup(x2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws)
+    moe.moe_expert_ffn_down(T2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws, out)
+    torch.cuda.synchronize()
+    ref = moe.moe_expert_ffn(x2, W, b2.offsets, b2.sorted_slot, wl.top_k)
+    moe.moe_expert_ffn_plan(T2, W, b2.offsets, wl.top_k, ws)
+    moe.moe_expert_ffn_gateup(x2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws)
+    moe.moe_expert_ffn_down(T2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws, out)
+    assert np.array_equal(sync_np(ref).view(np.uint32), sync_np(out).view(np.uint32))

@@ -1004,14 +1004,26 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   }
 }
 
-template <int NW>
+// Down: the same step structure as gate/up (CPS 128-K chunks per step, 2-stage ring written after
+// the step's barrier, scale table over the whole K).  A stage holds the hi and lo planes of h.
+template <int CPS>
+struct DnStage {
+  static constexpr int kRow = CPS * 256 + 16;     // one token's chunks of one h plane + padding
+  static constexpr int kBytes = 2 * 16 * kRow;    // hi plane, then lo plane
+};
+
+template <int NW, int CPS>
 __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   constexpr int RT = kRowsRT2, NP = RT * 16;
+  constexpr int LPT = CPS * 512 / (64 * NW);  // 16-byte lane-loads of h per thread per step
+  static_assert(LPT * 64 * NW == CPS * 512, "a step's h (2 planes x 16 tokens x CPS x 256 bytes)");
+  static_assert(CPS == 1 || CPS == 2, "one or two chunks per step");
+  constexpr int JB = CPS == 2 ? 1 : 0;  // bits of the chunk index within a step
+  constexpr int kDnXRow = DnStage<CPS>::kRow, kDnXStage = DnStage<CPS>::kBytes;
   typedef bf16x8 V;
-  typedef XStage<2> XS;  // hi plane then lo plane
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
@@ -1021,108 +1033,158 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = (nblk * NW + wave) * 16 * RT;
   const int ex = __builtin_amdgcn_readfirstlane(ti.e);
-  const int n_chunks = I >> 7;
+  const int n_chunks = I >> 7, n_steps = (n_chunks + CPS - 1) / CPS;
 
-  uint8_t* xs = lds;  // [3][XS::kBytes]
-  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 3 * XS::kBytes + wave * stab_bytes(NP, n_chunks));
+  uint8_t* xs = lds;  // [2][kDnXStage]
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kDnXStage + wave * stab_bytes(NP, n_chunks));
 
-  // h chunk = 16 tokens x 128 K x (hi, lo): 512 lane-loads, 128 per wave: lane-load q covers
-  // plane q / 256, token (q % 256) / 16, column q % 16
+  // Lane-load i of a thread: q = 64 * (NW * i + wave) + lane covers 16-byte column q % 16, chunk
+  // (q / 16) % CPS of the step, then token, then plane.  The plane is uniform over a wave's load,
+  // so each load uses one buffer descriptor.
   const __amdgpu_buffer_rsrc_t hr[2] = {make_rsrc(h_hi, (int64_t)n_slots * I * 2), make_rsrc(h_lo, (int64_t)n_slots * I * 2)};
-  uint32_t hoff[2], hs_w[2];
+  uint32_t hoff[LPT], hs_w[LPT];
+  int hplane[LPT];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = 128 * wave + 64 * j + lane;
-    const int plane = q >> 8, tok = (q & 255) >> 4, col = q & 15;
-    hoff[j] = tok < ti.nr ? (uint32_t)(ti.r0 + tok) * (uint32_t)I * 2u + 16u * col : kOutOfRange;
-    hs_w[j] = (uint32_t)(plane * 16 * XS::kRow + tok * XS::kRow + 16 * col);
+  for (int i = 0; i < LPT; ++i) {
+    const int q = 64 * (NW * i + wave) + lane;
+    const int plane = q >> (8 + JB), tok = (q >> (4 + JB)) & 15, j = (q >> 4) & (CPS - 1), col = q & 15;
+    hplane[i] = __builtin_amdgcn_readfirstlane(plane);
+    hoff[i] = tok < ti.nr ? (uint32_t)(ti.r0 + tok) * (uint32_t)I * 2u + 256u * j + 16u * col : kOutOfRange;
+    hs_w[i] = (uint32_t)(plane * 16 * kDnXRow + tok * kDnXRow + 256 * j + 16 * col);
   }
-  const int plane_of_j0 = (128 * wave) >> 8;  // both lane-loads of a wave hit one plane
-  const uint32_t hs_r = (uint32_t)(l16 * XS::kRow + 64 * lq);
+  const uint32_t hs_r = (uint32_t)(l16 * kDnXRow + 64 * lq);  // + 256 * chunk + 16 * k (+ lo plane)
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
   uint32_t coff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) coff[rt] = (uint32_t)(min(n0 + rt * 16 + l16, H - 1) * down.wr) + 16u * lq;
-  for (int f = lane; f < NP * n_chunks; f += 64) {
-    const int row = f / n_chunks, j = f - row * n_chunks;
-    stab[f] = bld4(sr, (uint32_t)(min(n0 + row, H - 1) * down.sr) + 4u * j);
+  {  // scale table [row][n_chunks] dwords, 8 loads in flight per lane, 16-byte units when possible
+    const bool vec = (n_chunks & 3) == 0 && (down.sr & 15) == 0 &&
+                     ((uintptr_t)(down.s + (int64_t)ex * down.se) & 15) == 0;
+    if (vec) {
+      const int upr = n_chunks >> 2, total = NP * upr;
+      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
+          v[i] = bld16(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 16u * u : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane;
+          if (f < total) *reinterpret_cast<u32x4*>(stab + 4 * f) = v[i];
+        }
+      }
+    } else {
+      const int total = NP * n_chunks;
+      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
+          v[i] = bld4(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 4u * j : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane;
+          if (f < total) stab[f] = v[i];
+        }
+      }
+    }
   }
 
   f32x4 acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  struct Chunk {
-    u32x4 q[RT];
+  struct Step {
+    u32x4 q[RT][CPS];  // [row tile][chunk of the step]
   };
-  auto load = [&](int c, Chunk& d) {
+  auto load = [&](int s, Step& d) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) d.q[rt] = bld16(wr, coff[rt] + 64u * c);
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int j = 0; j < CPS; ++j)
+        d.q[rt][j] = bld16(wr, CPS * s + j < n_chunks ? coff[rt] + 64u * (CPS * s + j) : kOutOfRange);
   };
-  u32x4 Hc[2][2];  // [chunk parity][lane-load]: fetched two chunks ahead, as in gate/up
-  auto fetch_h = [&](int c, u32x4 (&r)[2]) {
+  u32x4 Hc[2][LPT];  // [step parity][lane-load]: fetched two steps ahead
+  auto fetch_h = [&](int s, u32x4 (&r)[LPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) r[j] = bld16(hr[plane_of_j0], c < n_chunks ? hoff[j] + 256u * c : kOutOfRange);
-  };
-  auto put_h = [&](int c, const u32x4 (&r)[2]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(xs + (c % 3) * XS::kBytes + hs_w[j]) = r[j];
-  };
-  auto compute = [&](int c, const Chunk& d) {
-    const uint8_t* st = xs + (c % 3) * XS::kBytes + hs_r;
-    V bh[4], bl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bh[s] = *reinterpret_cast<const V*>(st + 16 * s);
-      bl[s] = *reinterpret_cast<const V*>(st + 16 * XS::kRow + 16 * s);
+    for (int i = 0; i < LPT; ++i) {
+      const int j = ((64 * (NW * i + wave) + lane) >> 4) & (CPS - 1);
+      r[i] = bld16(hr[hplane[i]], CPS * s + j < n_chunks ? hoff[i] + 256u * CPS * s : kOutOfRange);
     }
+  };
+  auto put_h = [&](int s, const u32x4 (&r)[LPT]) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(xs + (s & 1) * kDnXStage + hs_w[i]) = r[i];
+  };
+  auto compute_chunk = [&](int s, int j, const Step& d) {
+    const int c = CPS * s + j;
+    const uint8_t* st = xs + (s & 1) * kDnXStage + hs_r + 256 * j;
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
+    float scale[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float scale = e8m0_to_f32(sc[4 * n_chunks * (rt * 16 + l16)]);
+    for (int rt = 0; rt < RT; ++rt) scale[rt] = e8m0_to_f32(sc[4 * n_chunks * (rt * 16 + l16)]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const V a = decode8_bf16(d.q[rt][s], scale);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[s], acc[rt], 0, 0, 0);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[s], acc[rt], 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      const V bh = *reinterpret_cast<const V*>(st + 16 * k);
+      const V bl = *reinterpret_cast<const V*>(st + 16 * kDnXRow + 16 * k);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const V a = decode8_bf16(d.q[rt][j][k], scale[rt]);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[rt], 0, 0, 0);
       }
     }
   };
-  auto step = [&](int c, Chunk& D, u32x4 (&Hn)[2]) {  // as in gate/up
-    put_h(c + 1, Hn);
-    __syncthreads();
-    compute(c, D);
-    load(c + 2, D);
-    fetch_h(c + 3, Hn);
+  auto compute_step = [&](int s, const Step& d) {
+#pragma unroll
+    for (int j = 0; j < CPS; ++j)
+      if (j == 0 || CPS * s + j < n_chunks) compute_chunk(s, j, d);
   };
-  Chunk A, B;
+  auto step = [&](int s, Step& D, u32x4 (&Hn)[LPT]) {  // as in gate/up
+    __syncthreads();
+    put_h(s + 1, Hn);
+#pragma unroll
+    for (int j = 0; j < CPS; ++j) compute_chunk(s, j, D);
+    load(s + 2, D);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_h(s + 3, Hn);
+  };
+  Step A, B;
   fetch_h(0, Hc[0]);
+  __builtin_amdgcn_sched_barrier(0);
   load(0, A);
+  __builtin_amdgcn_sched_barrier(0);
   fetch_h(1, Hc[1]);
-  load(n_chunks > 1 ? 1 : 0, B);
+  __builtin_amdgcn_sched_barrier(0);
+  load(n_steps > 1 ? 1 : 0, B);
+  __builtin_amdgcn_sched_barrier(0);
   put_h(0, Hc[0]);
   fetch_h(2, Hc[0]);
-  int c = 0;
-  for (; c + 3 < n_chunks; c += 2) {
-    step(c, A, Hc[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s + 3 < n_steps; s += 2) {
+    step(s, A, Hc[1]);
     __builtin_amdgcn_sched_barrier(0);
-    step(c + 1, B, Hc[0]);
+    step(s + 1, B, Hc[0]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (c + 1 < n_chunks) put_h(c + 1, Hc[1]);
   __syncthreads();
-  compute(c, A);
-  if (c + 2 < n_chunks) load(c + 2, A);
-  if (c + 1 < n_chunks) {
-    if (c + 2 < n_chunks) put_h(c + 2, Hc[0]);
+  if (s + 1 < n_steps) put_h(s + 1, Hc[1]);
+  compute_step(s, A);
+  if (s + 2 < n_steps) load(s + 2, A);
+  if (s + 1 < n_steps) {
     __syncthreads();
-    compute(c + 1, B);
+    if (s + 2 < n_steps) put_h(s + 2, Hc[0]);
+    compute_step(s + 1, B);
   }
-  if (c + 2 < n_chunks) {
+  if (s + 2 < n_steps) {
     __syncthreads();
-    compute(c + 2, A);
+    compute_step(s + 2, A);
   }
 
   const int m = l16;
@@ -1191,7 +1253,11 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
 size_t gateup_rows_lds(int H) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, H / 128); }
-size_t down_rows_lds(int I) { return 3 * (size_t)XStage<2>::kBytes + kNW * (size_t)stab_bytes(16 * kRowsRT2, I / 128); }
+constexpr int kDnNW = 8;   // waves per down workgroup: 8 share each h stage
+constexpr int kDnCPS = 1;  // chunks per down step
+size_t down_rows_lds(int I) {
+  return 2 * (size_t)DnStage<kDnCPS>::kBytes + kDnNW * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
+}
 
 template <int FMT, int MT>
 hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
@@ -1218,9 +1284,9 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
                    hipStream_t stream) {
   const int n_slots = T * k_total;
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
-  const int nb_rows = (H + 16 * kRowsRT2 * kNW - 1) / (16 * kRowsRT2 * kNW);
-  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
-    ffn_down_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, down_rows_lds(I), stream>>>(
+  const int nb_rows = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
+  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
+    ffn_down_rows_kernel<kDnNW, kDnCPS><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I), stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
     launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);

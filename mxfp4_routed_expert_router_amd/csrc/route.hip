@@ -229,12 +229,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 }
 }  // namespace
 
-int route_mt(int T) { return T <= 16 ? 1 : (T <= 64 ? 4 : 16); }
-
+// Each wave computes one 16-expert x 16-token tile over a K slice.  The logits are latency-bound,
+// so many small waves (about 2048) beat fewer waves that reuse each router-weight fragment for
+// more tokens (measured).
 int route_splits(int T, int H, int E) {
-  const int64_t groups = (int64_t)((E + 15) / 16) * ((T + 16 * route_mt(T) - 1) / (16 * route_mt(T)));
+  const int64_t groups = (int64_t)((E + 15) / 16) * ((T + 15) / 16);
   const int nks = (H + 31) / 32;
-  int s = (int)((512 + groups - 1) / groups);
+  int s = (int)((2048 + groups - 1) / groups);
   const int cap = nks / 4 < 1 ? 1 : nks / 4;  // at least 4 k-steps of 32 per slice
   if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -244,14 +245,11 @@ int route_splits(int T, int H, int E) {
 
 template <int XF16, int VEC>
 void launch_logits(const void* x, int T, int H, const float* w, int E, int splits, float* partial, hipStream_t st) {
-  const int mt = route_mt(T);
   const int nks = (H + 31) / 32;
   const int per = (nks + splits - 1) / splits;
-  const dim3 g((E + 15) / 16, (T + 16 * mt - 1) / (16 * mt), splits);
+  const dim3 g((E + 15) / 16, (T + 15) / 16, splits);
   const uint16_t* xx = (const uint16_t*)x;
-  if (mt == 1) route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
-  else if (mt == 4) route_logits_kernel<XF16, VEC, 4><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
-  else route_logits_kernel<XF16, VEC, 16><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
 }
 
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,

@@ -8,9 +8,13 @@ One step = one layer call on T tokens (default 176): moe_route -> moe_bucket -> 
 (tile plan, gate/up phase, down phase) -> moe_combine, inputs resident in HBM.  Weight sets are rotated so
 that the bytes touched between two visits of one set exceed the 256 MB Infinity Cache.
 
-Prints one JSON line: tokens/s (value), ms per layer call, the gate/up kernel's roofline (HIP-event
-duration and algorithmic bytes), the per-T sweep T = 1..176, and the fp64 CPU oracle timed on a
-bounded token sample.
+Each T is timed twice: eager (the library calls issued from Python, HIP events around the steps and
+between the calls) and replayed from HIP graphs that hold one layer call each (the headline: the
+host's launch work is then out of the loop, which matters at small T).
+
+Prints one JSON line: tokens/s (value, graph replay), ms per layer call, the gate/up kernel's
+roofline (HIP-event duration and algorithmic bytes), the per-T sweep T = 1..176, and the fp64 CPU
+oracle timed on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -40,6 +44,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens of the oracle's timed sample")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the prefill layer instead (T=8192, 256 routed + 1 shared expert, top-8, "
+                         "log-Zipf routing bias) and print its own JSON line with MFMA utilisation")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain elementwise copy (torch.neg, fp32) of this many MiB three times, "
                          "for scaling memory counters, and exit")
@@ -115,6 +122,37 @@ def time_steps(runner, steps, warmup):
     return total_ms, per
 
 
+def time_graph(runner, steps, warmup):
+    """The same steps replayed from HIP graphs, one graph per rotated weight set (one layer call
+    each), so host-side launch work is out of the loop -> ms per step."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(len(runner.sets)):
+            runner.step(i)                      # eager pass on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(len(runner.sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            runner.step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record()
+    torch.cuda.synchronize()
+    del graphs
+    return start.elapsed_time(end) / steps
+
+
 def active_experts(runner):
     import torch
     torch.cuda.synchronize()
@@ -145,6 +183,8 @@ def main():
 
     if args.copy_calibration_mib:
         return copy_calibration(args.copy_calibration_mib)
+    if args.prefill:
+        return prefill_run(args)
     import synth
     import mxfp4_routed_expert_router_amd as moe
 
@@ -183,13 +223,15 @@ def main():
         runner = Runner(moe, sets, T, k, 0, E, H, I)
         steps = args.steps if T == args.tokens else args.sweep_steps
         warm = args.warmup if T == args.tokens else min(args.warmup, 5)
-        ms, per = time_steps(runner, steps, warm)
+        eager_ms, per = time_steps(runner, steps, warm)
+        graph_ms = time_graph(runner, steps, warm)
+        ms = graph_ms
         A = active_experts(runner)
         n_slots = T * k
         w_bytes = A * expert_bytes
         gateup_bytes = A * 2 * H * I * MXFP4_BYTES_PER_WEIGHT + n_slots * (2 * H + 4 * I)
-        results[T] = dict(T=T, ms=ms, per=per, active=A, weight_bytes=w_bytes, gateup_bytes=gateup_bytes,
-                          rotation_sets=len(sets), steps=steps)
+        results[T] = dict(T=T, ms=ms, eager_ms=eager_ms, per=per, active=A, weight_bytes=w_bytes,
+                          gateup_bytes=gateup_bytes, rotation_sets=len(sets), steps=steps)
         del runner, sets
         torch.cuda.empty_cache()
 
@@ -213,7 +255,8 @@ def main():
         "config": {"workload": f"moe_layer_sweep_H7168_E256_top8_I2048_mxfp4_T{args.tokens}",
                    "tokens": args.tokens, "hidden": H, "routed_experts": E, "top_k": k, "inter": I,
                    "weights": "mxfp4 (E2M1 + E8M0/32)", "activations": "bf16", "output": "fp32",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "timing": "HIP graph replay of whole layer calls"},
+        "eager_ms_per_step": head["eager_ms"],
         "weight_GBps": head["weight_bytes"] / (head["ms"] / 1e3) / 1e9,
         "weight_frac_of_hbm_peak": head["weight_bytes"] / (head["ms"] / 1e3) / HBM_PEAK,
         "active_experts": head["active"],
@@ -224,7 +267,8 @@ def main():
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
                      "algorithmic_bytes_per_launch": head["gateup_bytes"], "launch_ms": head["per"]["ffn_gateup"]},
-        "sweep": [{"T": r["T"], "us_per_layer": r["ms"] * 1e3, "tokens_per_s": r["T"] / (r["ms"] / 1e3),
+        "sweep": [{"T": r["T"], "us_per_layer": r["ms"] * 1e3, "eager_us_per_layer": r["eager_ms"] * 1e3,
+                   "tokens_per_s": r["T"] / (r["ms"] / 1e3),
                    "active_experts": r["active"], "weight_GBps": r["weight_bytes"] / (r["ms"] / 1e3) / 1e9,
                    "weight_frac_of_hbm_peak": r["weight_bytes"] / (r["ms"] / 1e3) / HBM_PEAK,
                    "gateup_us": r["per"]["ffn_gateup"] * 1e3, "down_us": r["per"]["ffn_down"] * 1e3,
@@ -236,6 +280,51 @@ def main():
         out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def prefill_run(args):
+    """The prefill layer (one weight set: its 6 GB of expert weights exceed the Infinity Cache many
+    times over).  Exact mode: weights decoded to bf16 in registers, bf16 MFMA with fp32
+    accumulation, h as a bf16 hi + lo pair (two MFMAs per down product)."""
+    import torch
+    import synth
+    import mxfp4_routed_expert_router_amd as moe
+    moe.lib()
+    wl = synth.WORKLOADS["prefill"]
+    T = wl.tokens[0]
+    H, I, E, k, S = wl.hidden, wl.inter, wl.n_routed, wl.top_k, wl.n_shared
+    t0 = time.time()
+    L = synth.make_layer(wl, T)
+    t = synth.to_torch(L, "cuda:0")
+    gen_s = time.time() - t0
+    W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+    sets = [{"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t}]
+    runner = Runner(moe, sets, T, k, S, E + S, H, I)
+    ms, per = time_steps(runner, args.steps, args.warmup)
+    counts = runner.b.counts.cpu()
+    A = int((counts > 0).sum().item())
+    kt = k + S
+    ffn_flops = 6.0 * H * I * T * kt
+    router_flops = 2.0 * T * H * E
+    bf16_peak = 2.5e15
+    gu_s, dn_s = per["ffn_gateup"] / 1e3, per["ffn_down"] / 1e3
+    out = {
+        "metric": "prefill MoE-layer tokens/s and MFMA utilisation (exact mode)",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"moe_layer_prefill_H{H}_E{E}+{S}_top{k}_I{I}_mxfp4_T{T}", "tokens": T,
+                   "zipf_s": wl.zipf_s},
+        "active_experts": A, "max_rows_per_expert": int(counts.max().item()),
+        "per_call_ms": {kk: round(v, 4) for kk, v in per.items()},
+        "ffn_tflops": ffn_flops / (gu_s + dn_s) / 1e12,
+        "gateup_tflops": 4.0 * H * I * T * kt / gu_s / 1e12,
+        "down_tflops": 2.0 * H * I * T * kt / dn_s / 1e12,
+        "frac_of_bf16_mfma_peak": ffn_flops / (gu_s + dn_s) / bf16_peak,
+        "frac_of_mxfp4_mfma_peak": ffn_flops / (gu_s + dn_s) / 10.1e15,
+        "layer_flops": ffn_flops + router_flops,
+        "input_generation_s": gen_s,
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -1207,6 +1207,338 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Tile kernels for calls with many rows per expert (prefill): 64-token tiles.  Each wave decodes
+// its 32 weight rows once per chunk and applies them to all four 16-token sub-tiles, so the work is
+// MFMA-bound rather than decode- or HBM-bound.  The tile's activations (or h) go through a
+// two-stage LDS ring, written right after each step's barrier.  Block scales are loaded with the
+// weights (one dword per row and chunk).  Workgroups are numbered tile-major with the row blocks
+// padded to a multiple of 8, so row block j of every tile runs on XCD j % 8: the tiles of a hot
+// expert that run together read each weight row from one L2.  Sub-tiles past the tile's rows are
+// computed on zero activations (branching around their MFMAs would split the scheduled loop).
+// ------------------------------------------------------------------------------------------------
+constexpr int kTileMT = 4;                     // 16-token sub-tiles per tile
+constexpr int kTileRow = 128 * 2 + 16;         // LDS bytes per token row of one plane of a stage
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
+    const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    int n_nblk_pad, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+  constexpr int RT = 2, NM = 2, MT = kTileMT, NTOK = 16 * MT;
+  constexpr int kStage = NTOK * kTileRow;
+  constexpr int LPT = NTOK * 16 / (64 * NW);  // 16-byte lane-loads of x per thread per chunk
+  typedef bf16x8 V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int n_slots = T * k_total;
+  const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
+  if (nblk >= n_nblk) return;
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, NTOK);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = (nblk * NW + wave) * 16 * RT;
+  const int e = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = H >> 7;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
+  uint32_t xoff[LPT], xs_w[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int q = threadIdx.x + 64 * NW * i, tok = q >> 4, col = q & 15;
+    bool ok = tok < ti.nr;
+    const int sl = ok ? sorted_slot[ti.r0 + tok] : -1;
+    ok = ok && sl >= 0 && sl < n_slots;
+    xoff[i] = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 16u * col : kOutOfRange;
+    xs_w[i] = (uint32_t)(tok * kTileRow + 16 * col);
+  }
+  const uint32_t xs_r = (uint32_t)(l16 * kTileRow + 64 * lq);
+
+  const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
+                                         make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
+  const __amdgpu_buffer_rsrc_t sr[NM] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
+                                         make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
+  uint32_t coff[NM][RT], soff[NM][RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = min(n0 + rt * 16 + l16, I - 1);
+    coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
+    coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
+    soff[0][rt] = (uint32_t)(n * gate.sr);
+    soff[1][rt] = (uint32_t)(n * up.sr);
+  }
+
+  f32x4 accg[RT][MT], accu[RT][MT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      accg[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accu[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  struct Step {
+    u32x4 q[NM][RT];
+    uint32_t sc[NM][RT];  // the four block scales of the row in this chunk; byte lq is this lane's
+  };
+  auto load = [&](int c, Step& d) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        d.q[m][rt] = bld16(wr[m], coff[m][rt] + 64u * c);
+        d.sc[m][rt] = bld4(sr[m], soff[m][rt] + 4u * c);
+      }
+  };
+  u32x4 X[2][LPT];
+  auto fetch_x = [&](int c, u32x4 (&r)[LPT]) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) r[i] = bld16(xr, c < n_chunks ? xoff[i] + 256u * c : kOutOfRange);
+  };
+  auto put_x = [&](int c, const u32x4 (&r)[LPT]) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(lds + (c & 1) * kStage + xs_w[i]) = r[i];
+  };
+  auto compute = [&](int c, const Step& d) {
+    const uint8_t* st = lds + (c & 1) * kStage + xs_r;
+    float scl[NM][RT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) scl[m][rt] = e8m0_to_f32((d.sc[m][rt] >> (8 * lq)) & 255u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      V xb[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xb[mt] = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const V ag = decode8_bf16(d.q[0][rt][k], scl[0][rt]), au = decode8_bf16(d.q[1][rt][k], scl[1][rt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          accg[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[mt], accg[rt][mt], 0, 0, 0);
+          accu[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[mt], accu[rt][mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto step = [&](int c, Step& D, u32x4 (&Xn)[LPT]) {
+    __syncthreads();
+    put_x(c + 1, Xn);
+    compute(c, D);
+    load(c + 2, D);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_x(c + 3, Xn);
+  };
+  Step A, B;
+  fetch_x(0, X[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load(0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_x(1, X[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  load(n_chunks > 1 ? 1 : 0, B);
+  __builtin_amdgcn_sched_barrier(0);
+  put_x(0, X[0]);
+  fetch_x(2, X[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  int c = 0;
+  for (; c + 3 < n_chunks; c += 2) {
+    step(c, A, X[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 1, B, X[0]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  if (c + 1 < n_chunks) put_x(c + 1, X[1]);
+  compute(c, A);
+  if (c + 2 < n_chunks) load(c + 2, A);
+  if (c + 1 < n_chunks) {
+    __syncthreads();
+    if (c + 2 < n_chunks) put_x(c + 2, X[0]);
+    compute(c + 1, B);
+  }
+  if (c + 2 < n_chunks) {
+    __syncthreads();
+    compute(c + 2, A);
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + l16;
+    if (m >= ti.nr) continue;
+    const int64_t base = (int64_t)(ti.r0 + m) * I;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + rt * 16 + 4 * lq + i;
+        if (n < I) {
+          const float g = accg[rt][mt][i], u = accu[rt][mt][i];
+          const float h = (g / (1.0f + expf(-g))) * u;
+          uint16_t hi, lo;
+          Op<MOE_W_MXFP4>::split(h, hi, lo);
+          h_hi[base + n] = hi;
+          h_lo[base + n] = lo;
+        }
+      }
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    int n_nblk_pad, float* __restrict__ y_slots) {
+  constexpr int RT = 2, MT = kTileMT, NTOK = 16 * MT;
+  constexpr int kStage = 2 * NTOK * kTileRow;     // hi plane, then lo plane
+  constexpr int LPT = 2 * NTOK * 16 / (64 * NW);  // 16-byte lane-loads of h per thread per chunk
+  typedef bf16x8 V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
+  if (nblk >= n_nblk) return;
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, NTOK);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = (nblk * NW + wave) * 16 * RT;
+  const int ex = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = I >> 7;
+
+  // lane-load q = threadIdx.x + 64 * NW * i: plane q / (16 * NTOK) (uniform per load), token
+  // (q / 16) % NTOK, column q % 16
+  const __amdgpu_buffer_rsrc_t hr[2] = {make_rsrc(h_hi, (int64_t)n_slots * I * 2), make_rsrc(h_lo, (int64_t)n_slots * I * 2)};
+  uint32_t hoff[LPT], hs_w[LPT];
+  int hplane[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int q = threadIdx.x + 64 * NW * i, plane = q / (16 * NTOK), tok = (q >> 4) % NTOK, col = q & 15;
+    hplane[i] = __builtin_amdgcn_readfirstlane(plane);
+    hoff[i] = tok < ti.nr ? (uint32_t)(ti.r0 + tok) * (uint32_t)I * 2u + 16u * col : kOutOfRange;
+    hs_w[i] = (uint32_t)(plane * NTOK * kTileRow + tok * kTileRow + 16 * col);
+  }
+  const uint32_t hs_r = (uint32_t)(l16 * kTileRow + 64 * lq);
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
+  uint32_t coff[RT], soff[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = min(n0 + rt * 16 + l16, H - 1);
+    coff[rt] = (uint32_t)(n * down.wr) + 16u * lq;
+    soff[rt] = (uint32_t)(n * down.sr);
+  }
+
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Step {
+    u32x4 q[RT];
+    uint32_t sc[RT];
+  };
+  auto load = [&](int c, Step& d) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      d.q[rt] = bld16(wr, coff[rt] + 64u * c);
+      d.sc[rt] = bld4(sr, soff[rt] + 4u * c);
+    }
+  };
+  // h is fetched one chunk ahead (its rows are shared by every row block of the tile and mostly
+  // come from L2)
+  u32x4 Hr[LPT];
+  auto fetch_h = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) Hr[i] = bld16(hr[hplane[i]], c < n_chunks ? hoff[i] + 256u * c : kOutOfRange);
+  };
+  auto put_h = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(lds + (c & 1) * kStage + hs_w[i]) = Hr[i];
+  };
+  auto compute = [&](int c, const Step& d) {
+    const uint8_t* st = lds + (c & 1) * kStage + hs_r;
+    float scl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) scl[rt] = e8m0_to_f32((d.sc[rt] >> (8 * lq)) & 255u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      V bh[MT], bl[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        bh[mt] = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
+        bl[mt] = *reinterpret_cast<const V*>(st + NTOK * kTileRow + mt * 16 * kTileRow + 16 * k);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const V a = decode8_bf16(d.q[rt][k], scl[rt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[mt], acc[rt][mt], 0, 0, 0);
+          acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt], acc[rt][mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto step = [&](int c, Step& D) {
+    __syncthreads();
+    put_h(c + 1);
+    fetch_h(c + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c, D);
+    load(c + 2, D);
+  };
+  Step A, B;
+  fetch_h(0);
+  load(0, A);
+  load(n_chunks > 1 ? 1 : 0, B);
+  put_h(0);
+  fetch_h(1);
+  __builtin_amdgcn_sched_barrier(0);
+  int c = 0;
+  for (; c + 3 < n_chunks; c += 2) {
+    step(c, A);
+    __builtin_amdgcn_sched_barrier(0);
+    step(c + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  if (c + 1 < n_chunks) put_h(c + 1);
+  if (c + 2 < n_chunks) fetch_h(c + 2);
+  compute(c, A);
+  if (c + 2 < n_chunks) load(c + 2, A);
+  if (c + 1 < n_chunks) {
+    __syncthreads();
+    if (c + 2 < n_chunks) put_h(c + 2);
+    compute(c + 1, B);
+  }
+  if (c + 2 < n_chunks) {
+    __syncthreads();
+    compute(c + 2, A);
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + l16;
+    if (m >= ti.nr) continue;
+    const int sl = sorted_slot[ti.r0 + m];
+    if (sl < 0 || sl >= n_slots) continue;
+    float* dst = y_slots + (int64_t)sl * H;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = n0 + rt * 16 + 4 * lq;
+      if ((H & 3) == 0 && n + 3 < H) {
+        *reinterpret_cast<f32x4*>(dst + n) = acc[rt][mt];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < H) dst[n + i] = acc[rt][mt][i];
+      }
+    }
+  }
+}
+
 // Upper bound of the number of tiles: A active experts hold at least one row each, so
 // sum_e ceil(n_e / R) <= A + (rows - A) / R with A <= min(n_experts, rows).
 int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {
@@ -1265,7 +1597,11 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
                      hipStream_t stream) {
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
   const int nb_rows = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
-  if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
+  if (MT == kTileMT && streamable) {
+    const int nb = (I + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+    ffn_gateup_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * kTileMT * 16 * kTileRow, stream>>>(
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
+  } else if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
     ffn_gateup_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, gateup_rows_lds(H), stream>>>(
         (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
@@ -1285,7 +1621,11 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const int n_slots = T * k_total;
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
   const int nb_rows = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
-  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
+  if (MT == kTileMT && streamable) {
+    const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+    ffn_down_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * 2 * kTileMT * 16 * kTileRow, stream>>>(
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, nbp, y_slots);
+  } else if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
     ffn_down_rows_kernel<kDnNW, kDnCPS><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I), stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {

@@ -30,97 +30,99 @@ __device__ __forceinline__ bf16x8 to_bf16x8_rne(const float (&v)[8]) {
 
 // XF16: activations are fp16 (converted exactly to fp32 and re-split into two bf16 terms, since an
 // fp16 value has 11 significant bits).  VEC: 16-byte loads (aligned w_router rows, H % 8 == 0).
-template <int XF16, int VEC, int MT>
+// A wave computes one 16-expert x 16-token tile over its K slice, kU k-steps of 32 at a time with
+// all of their loads issued first (the kernel is latency-bound: a load-then-use loop would wait a
+// full memory latency per k-step).
+constexpr int kU = 4;
+
+template <int XF16, int VEC>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ w, int E, int ks_per_split,
                                                           float* __restrict__ partial) {
   const int lane = threadIdx.x, l16 = lane & 15, lq = lane >> 4;
   const int e = blockIdx.x * 16 + l16;
-  const int t0 = blockIdx.y * 16 * MT;
+  const int t = blockIdx.y * 16 + l16;
   const int split = blockIdx.z;
   const int nks = (H + 31) / 32;
   const int ks0 = split * ks_per_split, ks1 = min(ks0 + ks_per_split, nks);
   const float* wrow = w + (int64_t)(e < E ? e : 0) * H;
-  f32x4 acc[MT];
+  const uint16_t* xrow = x + (int64_t)(t < T ? t : 0) * H;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ks = ks0; ks < ks1; ks += kU) {
+    float wv[kU][8];
+    uint16_t xv[kU][8];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int k = ks * 32 + 8 * lq;  // this lane's 8 hidden indices
-    float wv[8];
-    if (VEC && k + 8 <= H) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(wrow + k);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(wrow + k + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wv[j] = a[j];
-        wv[4 + j] = b[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = (k + j < H) ? wrow[k + j] : 0.f;
-    }
-    if (e >= E) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = 0.f;
-    }
-    float r[8];
-    const bf16x8 hi = to_bf16x8_rne(wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = wv[j] - (float)hi[j];
-    const bf16x8 mid = to_bf16x8_rne(r);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] -= (float)mid[j];
-    const bf16x8 lo = to_bf16x8_rne(r);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int t = t0 + mt * 16 + l16;
-      const uint16_t* xr = x + (int64_t)(t < T ? t : 0) * H;
-      uint16_t xv[8];
+    for (int u = 0; u < kU; ++u) {
+      // k-steps past the slice reload the slice's last step and are skipped below
+      const int k = min(ks + u, ks1 - 1) * 32 + 8 * lq;  // this lane's 8 hidden indices
       if (VEC && k + 8 <= H) {
-        const u32x4 q = ld16(xr + k);
-        __builtin_memcpy(xv, &q, 16);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(wrow + k);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(wrow + k + 4);
+        const u32x4 q = ld16(xrow + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wv[u][j] = a[j];
+          wv[u][4 + j] = b[j];
+        }
+        __builtin_memcpy(xv[u], &q, 16);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = (k + j < H) ? xr[k + j] : 0;
+        for (int j = 0; j < 8; ++j) {
+          wv[u][j] = (k + j < H) ? wrow[k + j] : 0.f;
+          xv[u][j] = (k + j < H) ? xrow[k + j] : 0;
+        }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (ks + u >= ks1) break;  // uniform
+      float r[8];
+      if (e >= E) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[u][j] = 0.f;
+      }
+      if (t >= T) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[u][j] = 0;
+      }
+      const bf16x8 hi = to_bf16x8_rne(wv[u]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = wv[u][j] - (float)hi[j];
+      const bf16x8 mid = to_bf16x8_rne(r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] -= (float)mid[j];
+      const bf16x8 lo = to_bf16x8_rne(r);
       if (XF16) {
         // fp16 -> fp32 exactly, then two bf16 terms (8 + 8 >= 11 significant bits)
         float xf[8], xr2[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xf[j] = (float)bitcast<_Float16>(xv[j]);
+        for (int j = 0; j < 8; ++j) xf[j] = (float)bitcast<_Float16>(xv[u][j]);
         const bf16x8 xh = to_bf16x8_rne(xf);
 #pragma unroll
         for (int j = 0; j < 8; ++j) xr2[j] = xf[j] - (float)xh[j];
         const bf16x8 xl = to_bf16x8_rne(xr2);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xh, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xh, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xh, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xl, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xl, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xl, acc[mt], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xl, acc, 0, 0, 0);
       } else {
-        if (t >= T) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xv[j] = 0;
-        }
         bf16x8 b;
-        __builtin_memcpy(&b, xv, 16);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[mt], 0, 0, 0);
+        __builtin_memcpy(&b, xv[u], 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);
       }
     }
   }
-  // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16 of each 16-token tile
-  float* out = partial + (int64_t)split * T * E;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int t = t0 + mt * 16 + l16;
-    if (t >= T) continue;
+  // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16
+  if (t < T) {
+    float* out = partial + ((int64_t)split * T + t) * E;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = blockIdx.x * 16 + 4 * lq + i;
-      if (ee < E) out[(int64_t)t * E + ee] = acc[mt][i];
+      if (ee < E) out[ee] = acc[i];
     }
   }
 }
@@ -249,7 +251,7 @@ void launch_logits(const void* x, int T, int H, const float* w, int E, int split
   const int per = (nks + splits - 1) / splits;
   const dim3 g((E + 15) / 16, (T + 15) / 16, splits);
   const uint16_t* xx = (const uint16_t*)x;
-  route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  route_logits_kernel<XF16, VEC><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
 }
 
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,

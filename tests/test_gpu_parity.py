@@ -211,6 +211,11 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     # 17 and 21 chunks of 128: scale-table windows of 16 chunks, with the last one partly used
     (128, 2176, 1024, 128, 4, "mxfp4", "routed"),
     (128, 2688, 1024, 128, 4, "mxfp4", "routed"),
+    # many rows per expert: the 64-token tile kernels, with partial sub-tiles and tiles
+    (512, 256, 384, 4, 2, "mxfp4", "routed"),
+    (300, 384, 256, 3, 2, "mxfp4", "routed"),
+    (200, 128, 256, 4, 1, "mxfp4", "one-expert"),
+    (70, 256, 128, 3, 2, "mxfp4", "two-experts"),
 ]
 
 
@@ -372,3 +377,34 @@ def test_stale_plan_stays_in_bounds():
     moe.moe_expert_ffn_gateup(x2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws)
     moe.moe_expert_ffn_down(T2, W, b2.offsets, b2.sorted_slot, wl.top_k, ws, out)
     assert np.array_equal(sync_np(ref).view(np.uint32), sync_np(out).view(np.uint32))
+
+
+@pytest.mark.parametrize("name,T", [("decode", 8), ("sweep", 176)])
+def test_graph_replay_equals_eager(name, T):
+    """One layer call captured in a HIP graph: each of several replays, with eager work and
+    synchronisations between them, reproduces the eager result bit for bit."""
+    note(f"graph replay {name} T={T}")
+    L = host_layer(name, T)
+    wl = L.wl
+    t = synth.to_torch(L, DEV)
+    layer = moe.MoELayer(expert_weights(t), T, wl.top_k, wl.n_shared, t["router"], t.get("bias"))
+    x = t["x"]
+    eager = sync_np(layer.forward(x)).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x)
+    for r in range(3):
+        layer.y.fill_(-1.0)                                   # eager work between replays
+        other = torch.randn(1 << 20, device=DEV).sum()        # a library reduction on the stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = sync_np(layer.y)
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {r}"
+        assert float(other) == float(other)

@@ -63,6 +63,69 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
+// Reductions through DPP moves (no LDS round trips): a running max / sum over 16-lane rows
+// (row_shr 1, 2, 4, 8), then row 0 -> 1 and row 2 -> 3 (row_bcast15), then rows 0-1 -> 2-3
+// (row_bcast31).  Lane 63 then holds the whole wave's result, read back as a uniform value.  A
+// lane whose DPP source is out of its row (or in a disabled row) keeps `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  uint32_t u = __float_as_uint(v);
+#define MOE_DPP_MAX(C, R) u = __float_as_uint(fmaxf(__uint_as_float(u), __uint_as_float(dpp_u32<C, R>(u, u))))
+  MOE_DPP_MAX(kDppRowShr1, 0xF);
+  MOE_DPP_MAX(kDppRowShr2, 0xF);
+  MOE_DPP_MAX(kDppRowShr4, 0xF);
+  MOE_DPP_MAX(kDppRowShr8, 0xF);
+  MOE_DPP_MAX(kDppRowBcast15, 0xA);
+  MOE_DPP_MAX(kDppRowBcast31, 0xC);
+#undef MOE_DPP_MAX
+  return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  uint32_t u = __float_as_uint(v);
+#define MOE_DPP_ADD(C, R) u = __float_as_uint(__uint_as_float(u) + __uint_as_float(dpp_u32<C, R>(0u, u)))
+  MOE_DPP_ADD(kDppRowShr1, 0xF);
+  MOE_DPP_ADD(kDppRowShr2, 0xF);
+  MOE_DPP_ADD(kDppRowShr4, 0xF);
+  MOE_DPP_ADD(kDppRowShr8, 0xF);
+  MOE_DPP_ADD(kDppRowBcast15, 0xA);
+  MOE_DPP_ADD(kDppRowBcast31, 0xC);
+#undef MOE_DPP_ADD
+  return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
+}
+// Maximum of a 64-bit key (hi, lo) over the wave, compared as unsigned; returns it uniform.
+__device__ __forceinline__ void wave_max_u64_dpp(uint32_t& hi, uint32_t& lo) {
+#define MOE_DPP_MAX64(C, R)                                                \
+  {                                                                        \
+    const uint32_t th = dpp_u32<C, R>(hi, hi), tl = dpp_u32<C, R>(lo, lo); \
+    const bool gt = th > hi || (th == hi && tl > lo);                      \
+    hi = gt ? th : hi;                                                     \
+    lo = gt ? tl : lo;                                                     \
+  }
+  MOE_DPP_MAX64(kDppRowShr1, 0xF);
+  MOE_DPP_MAX64(kDppRowShr2, 0xF);
+  MOE_DPP_MAX64(kDppRowShr4, 0xF);
+  MOE_DPP_MAX64(kDppRowShr8, 0xF);
+  MOE_DPP_MAX64(kDppRowBcast15, 0xA);
+  MOE_DPP_MAX64(kDppRowBcast31, 0xC);
+#undef MOE_DPP_MAX64
+  hi = __builtin_amdgcn_readlane(hi, 63);
+  lo = __builtin_amdgcn_readlane(lo, 63);
+}
+// Order-preserving map of a float (finite or infinite) onto uint32, and back.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Inclusive prefix sum over the lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);

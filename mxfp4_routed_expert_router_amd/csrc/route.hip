@@ -159,11 +159,11 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   float mx = -INFINITY;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) mx = fmaxf(mx, L[v]);
-  mx = wave_max(mx);
+  mx = wave_max_dpp(mx);
   float esum = 0.0f;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) esum += (lane + 64 * v < E) ? expf(L[v] - mx) : 0.0f;
-  const float den = wave_sum(esum);
+  const float den = wave_sum_dpp(esum);
   if (probs) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
@@ -171,34 +171,32 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
       if (e < E) probs[(int64_t)t * E + e] = expf(L[v] - mx) / den;
     }
   }
-  // k rounds of wave argmax over (logit desc, index asc).  The winner of round j is kept by lane
-  // j % 64 in register q = j / 64 (k_total <= MOE_MAX_SLOTS_PER_TOKEN = 4 * 64).
-  uint32_t taken = 0;
+  // k rounds of wave argmax over (logit desc, index asc), each one maximum of a 64-bit key
+  // (order key of the logit, then the complement of the index).  Taken and padded experts carry
+  // key 0, below every logit's key.  The winner of round j is kept by lane j % 64 in register
+  // q = j / 64 (k_total <= MOE_MAX_SLOTS_PER_TOKEN = 4 * 64).
+  uint32_t kh[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) kh[v] = (lane + 64 * v < E) ? f32_order_key(L[v]) : 0u;
   float psum = 0.0f;
   int my_id[4] = {0, 0, 0, 0};
   float my_p[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < top_k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    uint32_t bh = 0u, bl = 0u;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      int e = lane + 64 * v;
-      bool free_ = e < E && !((taken >> v) & 1u);
-      if (free_ && (L[v] > bv || (L[v] == bv && e < bi))) {
-        bv = L[v];
-        bi = e;
+    for (int v = 0; v < VPL; ++v) {  // this lane's best: larger key, then smaller index
+      const uint32_t cl = ~(uint32_t)(lane + 64 * v);
+      if (kh[v] > bh || (kh[v] == bh && kh[v] != 0u && cl > bl)) {
+        bh = kh[v];
+        bl = cl;
       }
     }
+    wave_max_u64_dpp(bh, bl);
+    const int bi = (int)~bl;
+    const float bv = f32_from_order_key(bh);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, kWave);
-      int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    for (int v = 0; v < VPL; ++v)
+      if (lane + 64 * v == bi) kh[v] = 0u;
     const float p = expf(bv - mx) / den;
     psum += p;
     if ((j & 63) == lane) {

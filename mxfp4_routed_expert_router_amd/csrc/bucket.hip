@@ -7,8 +7,8 @@
 // earlier waves of the chunk.  A chunk histogram plus a scan over chunks and buckets turns ranks
 // into global positions.  No atomics are used, so the permutation is the unique stable one and is
 // identical on every run.
-//   one chunk   : bucket_fused_kernel does rank + scan + scatter in one workgroup;
-//   many chunks : bucket_rank_kernel -> bucket_scan_kernel -> bucket_scatter_kernel.
+//   up to 4 chunks : bucket_fused_kernel does rank + scan + scatter in one workgroup;
+//   more chunks    : bucket_rank_kernel -> bucket_scan_kernel -> bucket_scatter_kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -90,38 +90,67 @@ __device__ int block_exclusive_scan(int* vals, int n, int* scratch /* kWaves + 1
   return total;
 }
 
+// Up to kFusedChunks chunks in one workgroup: the chunks are ranked one after another (ranks and
+// keys stay in registers, chunk histograms in LDS), then one scan and the scatter.  Saves the two
+// extra launches of the multi-kernel path for decode-sized calls.
+constexpr int kFusedChunks = 4;
+
 __global__ __launch_bounds__(kBucketChunk) void bucket_fused_kernel(const int32_t* __restrict__ ids, int n_slots,
                                                                      int n_buckets, int32_t* __restrict__ counts,
                                                                      int32_t* __restrict__ offsets,
                                                                      int32_t* __restrict__ sorted_slot,
                                                                      int32_t* __restrict__ slot_pos) {
   extern __shared__ int lds[];
-  int* wave_counts = lds;                                 // [kWaves][n_buckets+1]
-  int* base = lds + kWaves * (n_buckets + 1);             // [n_buckets]
-  int* scratch = base + n_buckets;                        // [kWaves+1]
+  const int stride = n_buckets + 1;
+  int* wave_counts = lds;                              // [kWaves][n_buckets+1]
+  int* table = wave_counts + kWaves * stride;          // [kFusedChunks][n_buckets]: counts, then bases
+  int* base = table + kFusedChunks * n_buckets;        // [n_buckets]
+  int* scratch = base + n_buckets;                     // [kWaves+1]
   const int tid = threadIdx.x;
-  SlotRank r = chunk_rank(ids, n_slots, n_buckets, 0, wave_counts);
+  const int n_chunks = (n_slots + kBucketChunk - 1) / kBucketChunk;  // 1 .. kFusedChunks
+  SlotRank r[kFusedChunks];
+#pragma unroll
+  for (int c = 0; c < kFusedChunks; ++c) {
+    r[c].key = -1;
+    r[c].rank = 0;
+    if (c < n_chunks) {  // uniform
+      r[c] = chunk_rank(ids, n_slots, n_buckets, c, wave_counts);
+      for (int b = tid; b < n_buckets; b += kBucketChunk) {
+        int v = 0;
+        for (int w = 0; w < kWaves; ++w) v += wave_counts[w * stride + b];
+        table[c * n_buckets + b] = v;
+      }
+      __syncthreads();  // the next chunk's ranking clears wave_counts
+    }
+  }
   for (int b = tid; b < n_buckets; b += kBucketChunk) {
-    int c = 0;
-    for (int w = 0; w < kWaves; ++w) c += wave_counts[w * (n_buckets + 1) + b];
-    base[b] = c;
-    counts[b] = c;
+    int run = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = table[c * n_buckets + b];
+      table[c * n_buckets + b] = run;
+      run += v;
+    }
+    base[b] = run;
+    counts[b] = run;
   }
   __syncthreads();
   const int total = block_exclusive_scan(base, n_buckets, scratch);
   for (int b = tid; b < n_buckets; b += kBucketChunk) offsets[b] = base[b];
   if (tid == 0) offsets[n_buckets] = total;
-  const int s = tid;
-  if (r.key >= 0) {
-    if (r.key < n_buckets) {
-      const int pos = base[r.key] + r.rank;
-      sorted_slot[pos] = s;
-      if (slot_pos) slot_pos[s] = pos;
-    } else if (slot_pos) {
-      slot_pos[s] = -1;
+#pragma unroll
+  for (int c = 0; c < kFusedChunks; ++c) {
+    const int s = c * kBucketChunk + tid;
+    if (r[c].key >= 0) {
+      if (r[c].key < n_buckets) {
+        const int pos = base[r[c].key] + table[c * n_buckets + r[c].key] + r[c].rank;
+        sorted_slot[pos] = s;
+        if (slot_pos) slot_pos[s] = pos;
+      } else if (slot_pos) {
+        slot_pos[s] = -1;
+      }
     }
+    if (s < n_slots && s >= total) sorted_slot[s] = -1;
   }
-  if (s < n_slots && s >= total) sorted_slot[s] = -1;
 }
 
 // ws layout: rank [n_slots] | chunk table [n_chunks][n_buckets] (counts, then bases in place)
@@ -189,8 +218,8 @@ hipError_t launch_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t
                          int32_t* sorted_slot, int32_t* slot_pos, int32_t* ws, hipStream_t stream) {
   const int n_chunks = (n_slots + kBucketChunk - 1) / kBucketChunk;
   const size_t rank_lds = sizeof(int) * (size_t)kWaves * (n_buckets + 1);
-  if (n_chunks <= 1) {
-    const size_t lds = rank_lds + sizeof(int) * ((size_t)n_buckets + kWaves + 1);
+  if (n_chunks <= kFusedChunks) {
+    const size_t lds = rank_lds + sizeof(int) * ((size_t)(kFusedChunks + 1) * n_buckets + kWaves + 1);
     bucket_fused_kernel<<<1, kBucketChunk, lds, stream>>>(ids, n_slots, n_buckets, counts, offsets, sorted_slot,
                                                           slot_pos);
     return hipGetLastError();

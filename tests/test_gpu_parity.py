@@ -122,6 +122,7 @@ def bucket_case_ids(kind):
         router, bias = synth.make_router(wl)
         return oracle.load().route(x, oracle.X_BF16, router, bias, wl.top_k, wl.n_shared)["ids"].reshape(-1), 257
     n, nb = {"one": (7, 1), "exact-chunk": (512, 128), "ragged": (513, 33), "sweep": (1408, 256),
+             "four-chunks": (2048, 257), "five-chunks": (2049, 300), "max-buckets-fused": (1500, 1024),
              "max-buckets": (3000, 1024), "skew": (5000, 64)}[kind]
     ids = rng.integers(0, nb, n).astype(np.int32)
     if kind == "skew":
@@ -129,7 +130,8 @@ def bucket_case_ids(kind):
     return ids, nb
 
 
-@pytest.mark.parametrize("kind", ["one", "exact-chunk", "ragged", "sweep", "max-buckets", "skew", "prefill"])
+@pytest.mark.parametrize("kind", ["one", "exact-chunk", "ragged", "sweep", "four-chunks", "five-chunks",
+                                  "max-buckets-fused", "max-buckets", "skew", "prefill"])
 def test_bucket(orc, kind):
     ids, nb = bucket_case_ids(kind)
     note(f"bucket {kind}: {ids.size} slots, {nb} buckets")

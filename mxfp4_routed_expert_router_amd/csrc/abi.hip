@@ -34,6 +34,12 @@ moe_status check_proj(const moe_proj& p, moe_w_format fmt, int n_experts, int N,
   return MOE_OK;
 }
 
+moe::ProjDev dev(const moe_proj& p);
+// The FFN's tile-size choice, derived from the weights description alone (see ffn_big_tiles).
+bool big_tiles(const moe_expert_weights* W, int T, int k_total) {
+  return moe::ffn_big_tiles(W->fmt, T, k_total, W->hidden, W->inter, dev(W->gate), dev(W->up), dev(W->down));
+}
+
 moe::ProjDev dev(const moe_proj& p) {
   moe::ProjDev d;
   d.w = (const uint8_t*)p.w;
@@ -121,7 +127,7 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weigh
   // h as a high plane and a low plane of 16-bit values, one row of `inter` per sorted slot,
   // then the tile table shared by the two phases
   const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
-  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts), 256);
+  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts, big_tiles(W, T, k_total)), 256);
 }
 
 }  // extern "C"
@@ -176,7 +182,8 @@ moe_status moe_expert_ffn_plan(moe_act_dtype x_dtype, int T, int k_total, const 
   moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, offsets, nullptr, false, false, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, offsets, table, (hipStream_t)stream));
+  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total), offsets, table,
+                                         (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, int k_total,
@@ -188,7 +195,8 @@ moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, in
   moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, nullptr, true, false, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->gate),
+  return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, big_tiles(W, T, k_total), W->hidden,
+                                           W->inter, dev(W->gate),
                                            dev(W->up), sorted_slot, h_hi, h_lo, table, (hipStream_t)stream));
 }
 
@@ -201,7 +209,8 @@ moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const 
   moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, false, true, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, W->hidden, W->inter, dev(W->down),
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, big_tiles(W, T, k_total), W->hidden,
+                                         W->inter, dev(W->down),
                                          sorted_slot, y_slots, h_hi, h_lo, table, (hipStream_t)stream));
 }
 
@@ -215,12 +224,13 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   const int H = W->hidden, I = W->inter;
-  hipError_t err = moe::launch_ffn_plan(T, k_total, W->n_experts, offsets, table, (hipStream_t)stream);
+  const bool big = big_tiles(W, T, k_total);
+  hipError_t err = moe::launch_ffn_plan(T, k_total, W->n_experts, big, offsets, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up), sorted_slot,
+  err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, big, H, I, dev(W->gate), dev(W->up), sorted_slot,
                                h_hi, h_lo, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, H, I, dev(W->down), sorted_slot, y_slots,
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, big, H, I, dev(W->down), sorted_slot, y_slots,
                                          h_hi, h_lo, table, (hipStream_t)stream));
 }
 

@@ -1217,7 +1217,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
 // expert that run together read each weight row from one L2.  Sub-tiles past the tile's rows are
 // computed on zero activations (branching around their MFMAs would split the scheduled loop).
 // ------------------------------------------------------------------------------------------------
-constexpr int kTileMT = 4;                     // 16-token sub-tiles per tile
+constexpr int kTileMT = 4;                     // 16-token sub-tiles per gate/up tile
+constexpr int kDnTileMT = 4;                   // 16-token sub-tiles per down work item (half a tile)
 constexpr int kTileRow = 128 * 2 + 16;         // LDS bytes per token row of one plane of a stage
 
 template <int NW>
@@ -1390,14 +1391,20 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     int n_nblk_pad, float* __restrict__ y_slots) {
-  constexpr int RT = 2, MT = kTileMT, NTOK = 16 * MT;
+  constexpr int RT = 2, MT = kDnTileMT, NTOK = 16 * MT;
+  constexpr int HALVES = kTileMT / kDnTileMT;     // work items per tile
   constexpr int kStage = 2 * NTOK * kTileRow;     // hi plane, then lo plane
   constexpr int LPT = 2 * NTOK * 16 / (64 * NW);  // 16-byte lane-loads of h per thread per chunk
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
+  const int item = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - item * n_nblk_pad;
   if (nblk >= n_nblk) return;
-  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, NTOK);
+  TileInfo ti = get_tile(tiles, item / HALVES, n_experts, n_slots, NTOK * HALVES);
+  {  // this item's part of the tile's rows
+    const int skip = (item % HALVES) * NTOK;
+    ti.r0 += skip;
+    ti.nr = min(ti.nr - skip, NTOK);
+  }
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, lq = lane >> 4;
@@ -1597,11 +1604,7 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
                      hipStream_t stream) {
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
   const int nb_rows = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
-  if (MT == kTileMT && streamable) {
-    const int nb = (I + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-    ffn_gateup_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * kTileMT * 16 * kTileRow, stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
-  } else if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
+  if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
     ffn_gateup_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, gateup_rows_lds(H), stream>>>(
         (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
@@ -1621,11 +1624,7 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const int n_slots = T * k_total;
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
   const int nb_rows = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
-  if (MT == kTileMT && streamable) {
-    const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-    ffn_down_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * 2 * kTileMT * 16 * kTileRow, stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, nbp, y_slots);
-  } else if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
+  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
     ffn_down_rows_kernel<kDnNW, kDnCPS><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I), stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
@@ -1635,6 +1634,25 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
     ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
   }
+  return hipGetLastError();
+}
+
+// The tile kernels (MXFP4 only; planned only when ffn_big_tiles() holds for the call).
+hipError_t gateup_tile(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+                       const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
+                       hipStream_t stream) {
+  const int nb = (I + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+  ffn_gateup_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * kTileMT * 16 * kTileRow, stream>>>(
+      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
+  return hipGetLastError();
+}
+hipError_t down_tile(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
+                     float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
+                     hipStream_t stream) {
+  const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+  ffn_down_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * (kTileMT / kDnTileMT) * nbp)), kNW * 64,
+                              2 * 2 * kDnTileMT * 16 * kTileRow, stream>>>(
+      h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, nbp, y_slots);
   return hipGetLastError();
 }
 
@@ -1662,45 +1680,60 @@ hipError_t down_fmt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev
 
 }  // namespace
 
-FfnPlan ffn_plan(int T, int k_total, int n_experts) {
+bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
+                   const ProjDev& down) {
+  return fmt == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && stream_ok(down, I, H) &&
+         (int64_t)T * H * 2 < INT32_MAX && (int64_t)T * k_total * I * 2 < INT32_MAX;
+}
+
+FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big) {
   // Tokens per tile from the mean rows per active expert (known on the host without a sync).
   const int64_t rows = (int64_t)T * k_total;
   const int64_t active = rows < n_experts ? rows : n_experts;
   const double mean = (double)rows / (double)(active > 0 ? active : 1);
   FfnPlan p;
   p.n_experts = n_experts;
-  p.mt = mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4);
+  p.tile = big && mean > 32.0;  // 16 * kTileMT-token tiles on the tile kernels
+  p.mt = p.tile ? kTileMT : (mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4));
   p.tiles = (max_tiles(rows, n_experts, 16 * p.mt) + kXcds - 1) / kXcds * kXcds;
   return p;
 }
 
-size_t ffn_table_bytes(int T, int k_total, int n_experts) {
-  return (size_t)ffn_plan(T, k_total, n_experts).tiles * sizeof(TileEntry);
+size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big) {
+  return (size_t)ffn_plan(T, k_total, n_experts, big).tiles * sizeof(TileEntry);
 }
 
-hipError_t launch_ffn_plan(int T, int k_total, int n_experts, const int32_t* offsets, void* table,
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,
                            hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
   ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, 16 * pl.mt, (int)pl.tiles,
                                            (TileEntry*)table);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
-                             ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, bool big, int H, int I,
+                             ProjDev gate, ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
                              const void* table, hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
   const TileEntry* tiles = (const TileEntry*)table;
+  if (pl.tile) {
+    if (fmt != MOE_W_MXFP4) return hipErrorInvalidValue;  // not planned for other formats
+    return gateup_tile(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+  }
   if (fmt == MOE_W_FP16)
     return gateup_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   return gateup_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
 }
 
-hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
+hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
   const TileEntry* tiles = (const TileEntry*)table;
+  if (pl.tile) {
+    if (fmt != MOE_W_MXFP4) return hipErrorInvalidValue;
+    return down_tile(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+  }
   if (fmt == MOE_W_FP16)
     return down_fmt<MOE_W_FP16>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   return down_fmt<MOE_W_MXFP4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);

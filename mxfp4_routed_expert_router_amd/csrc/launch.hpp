@@ -32,17 +32,23 @@ struct FfnPlan {
   int mt;  // 16*mt sorted rows (tokens) per tile
   int64_t tiles;
   int n_experts;
+  bool tile;  // the tile kernels (MXFP4, many rows per expert)
 };
-FfnPlan ffn_plan(int T, int k_total, int n_experts);
-size_t ffn_table_bytes(int T, int k_total, int n_experts);
+// Whether calls with many rows per expert may use the 128-token tile kernels (MXFP4, whole
+// 128-wide chunks, aligned scale rows, 32-bit offsets).  The three FFN entry points and the
+// workspace query must agree, so they all derive it from the same weights description.
+bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
+                   const ProjDev& down);
+FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big);
+size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big);
 // The plan builds the tile table in `table`; the gate/up phase reads it and writes h; the down
 // phase reads both.
-hipError_t launch_ffn_plan(int T, int k_total, int n_experts, const int32_t* offsets, void* table,
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,
                            hipStream_t stream);
-hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
-                             ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, bool big, int H, int I,
+                             ProjDev gate, ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
                              const void* table, hipStream_t stream);
-hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev down,
+hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream);
 

@@ -1217,18 +1217,20 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
 // expert that run together read each weight row from one L2.  Sub-tiles past the tile's rows are
 // computed on zero activations (branching around their MFMAs would split the scheduled loop).
 // ------------------------------------------------------------------------------------------------
-constexpr int kTileMT = 4;                     // 16-token sub-tiles per gate/up tile
+constexpr int kTileMT = 8;                     // 16-token sub-tiles per gate/up tile
+constexpr int kTileRT = 1;                     // 16-row tiles of each matrix per gate/up wave
 constexpr int kDnTileMT = 4;                   // 16-token sub-tiles per down work item (half a tile)
 constexpr int kTileRow = 128 * 2 + 16;         // LDS bytes per token row of one plane of a stage
 
-template <int NW>
+template <int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     int n_nblk_pad, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
-  constexpr int RT = 2, NM = 2, MT = kTileMT, NTOK = 16 * MT;
+  constexpr int NM = 2, NTOK = 16 * MT;
   constexpr int kStage = NTOK * kTileRow;
   constexpr int LPT = NTOK * 16 / (64 * NW);  // 16-byte lane-loads of x per thread per chunk
+  static_assert(LPT * 64 * NW == NTOK * 16, "a chunk of x over the workgroup");
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
@@ -1291,14 +1293,15 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
         d.sc[m][rt] = bld4(sr[m], soff[m][rt] + 4u * c);
       }
   };
-  u32x4 X[2][LPT];
-  auto fetch_x = [&](int c, u32x4 (&r)[LPT]) {
+  // x is fetched one chunk ahead (the next chunk's piece of this thread)
+  u32x4 Xr[LPT];
+  auto fetch_x = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) r[i] = bld16(xr, c < n_chunks ? xoff[i] + 256u * c : kOutOfRange);
+    for (int i = 0; i < LPT; ++i) Xr[i] = bld16(xr, c < n_chunks ? xoff[i] + 256u * c : kOutOfRange);
   };
-  auto put_x = [&](int c, const u32x4 (&r)[LPT]) {
+  auto put_x = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(lds + (c & 1) * kStage + xs_w[i]) = r[i];
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(lds + (c & 1) * kStage + xs_w[i]) = Xr[i];
   };
   auto compute = [&](int c, const Step& d) {
     const uint8_t* st = lds + (c & 1) * kStage + xs_r;
@@ -1309,54 +1312,53 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
       for (int rt = 0; rt < RT; ++rt) scl[m][rt] = e8m0_to_f32((d.sc[m][rt] >> (8 * lq)) & 255u);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      V xb[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xb[mt] = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
+      V ag[RT], au[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const V ag = decode8_bf16(d.q[0][rt][k], scl[0][rt]), au = decode8_bf16(d.q[1][rt][k], scl[1][rt]);
+        ag[rt] = decode8_bf16(d.q[0][rt][k], scl[0][rt]);
+        au[rt] = decode8_bf16(d.q[1][rt][k], scl[1][rt]);
+      }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          accg[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[mt], accg[rt][mt], 0, 0, 0);
-          accu[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[mt], accu[rt][mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        const V xb = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          accg[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[rt], xb, accg[rt][mt], 0, 0, 0);
+          accu[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[rt], xb, accu[rt][mt], 0, 0, 0);
         }
       }
     }
   };
-  auto step = [&](int c, Step& D, u32x4 (&Xn)[LPT]) {
+  auto step = [&](int c, Step& D) {
     __syncthreads();
-    put_x(c + 1, Xn);
+    put_x(c + 1);
+    fetch_x(c + 2);
+    __builtin_amdgcn_sched_barrier(0);
     compute(c, D);
     load(c + 2, D);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch_x(c + 3, Xn);
   };
   Step A, B;
-  fetch_x(0, X[0]);
-  __builtin_amdgcn_sched_barrier(0);
+  fetch_x(0);
   load(0, A);
-  __builtin_amdgcn_sched_barrier(0);
-  fetch_x(1, X[1]);
-  __builtin_amdgcn_sched_barrier(0);
   load(n_chunks > 1 ? 1 : 0, B);
-  __builtin_amdgcn_sched_barrier(0);
-  put_x(0, X[0]);
-  fetch_x(2, X[0]);
+  put_x(0);
+  fetch_x(1);
   __builtin_amdgcn_sched_barrier(0);
   int c = 0;
   for (; c + 3 < n_chunks; c += 2) {
-    step(c, A, X[1]);
+    step(c, A);
     __builtin_amdgcn_sched_barrier(0);
-    step(c + 1, B, X[0]);
+    step(c + 1, B);
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  if (c + 1 < n_chunks) put_x(c + 1, X[1]);
+  if (c + 1 < n_chunks) put_x(c + 1);
+  if (c + 2 < n_chunks) fetch_x(c + 2);
   compute(c, A);
   if (c + 2 < n_chunks) load(c + 2, A);
   if (c + 1 < n_chunks) {
     __syncthreads();
-    if (c + 2 < n_chunks) put_x(c + 2, X[0]);
+    if (c + 2 < n_chunks) put_x(c + 2);
     compute(c + 1, B);
   }
   if (c + 2 < n_chunks) {
@@ -1641,8 +1643,9 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
 hipError_t gateup_tile(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                        const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                        hipStream_t stream) {
-  const int nb = (I + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-  ffn_gateup_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64, 2 * kTileMT * 16 * kTileRow, stream>>>(
+  const int nb = (I + 16 * kTileRT * kNW - 1) / (16 * kTileRT * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+  ffn_gateup_tile_kernel<kNW, kTileRT, kTileMT><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64,
+                                                 2 * kTileMT * 16 * kTileRow, stream>>>(
       (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
   return hipGetLastError();
 }

@@ -24,6 +24,7 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 X_BF16, X_FP16 = 0, 1
 W_MXFP4, W_FP16 = 0, 1
+MX_FP8_E4M3, MX_FP4_E2M1, MX_FP6_E2M3 = 1, 2, 3
 
 _CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
 
@@ -118,6 +119,15 @@ class Oracle:
         lib.orc_weight.argtypes = [ctypes.POINTER(_Proj), i, i, i, i]
         lib.orc_mxfp4_decode_matrix.restype = None
         lib.orc_mxfp4_decode_matrix.argtypes = [vp, vp, i, i, vp]
+        lib.orc_mx_bits.restype = i; lib.orc_mx_bits.argtypes = [i]
+        lib.orc_mx_emax.restype = i; lib.orc_mx_emax.argtypes = [i]
+        lib.orc_mx_value.restype = d; lib.orc_mx_value.argtypes = [i, i]
+        lib.orc_mx_encode.restype = i; lib.orc_mx_encode.argtypes = [i, d]
+        lib.orc_mx_scale_code.restype = i; lib.orc_mx_scale_code.argtypes = [i, d]
+        lib.orc_mx_quantize.restype = None; lib.orc_mx_quantize.argtypes = [vp, i, i, i, vp, vp]
+        lib.orc_mx_dequantize.restype = None; lib.orc_mx_dequantize.argtypes = [vp, vp, i, i, i, vp]
+        lib.orc_expert_ffn_mx.restype = None
+        lib.orc_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(_Weights), i, vp, vp, vp, vp]
 
     # ---- formats ----
     def e2m1(self, c: int) -> float: return self.lib.orc_e2m1(c)
@@ -140,6 +150,40 @@ class Oracle:
         out = np.empty((n, k), np.float64)
         self.lib.orc_mxfp4_decode_matrix(_p(codes), _p(scales), n, k, _p(out))
         return out
+
+    # ---- MX activation formats ----
+    def mx_bits(self, fmt: int) -> int: return self.lib.orc_mx_bits(fmt)
+    def mx_emax(self, fmt: int) -> int: return self.lib.orc_mx_emax(fmt)
+    def mx_value(self, fmt: int, code: int) -> float: return self.lib.orc_mx_value(fmt, code)
+    def mx_encode(self, fmt: int, q: float) -> int: return self.lib.orc_mx_encode(fmt, q)
+    def mx_scale_code(self, fmt: int, amax: float) -> int: return self.lib.orc_mx_scale_code(fmt, amax)
+
+    def mx_quantize(self, v: np.ndarray, fmt: int):
+        """[n][K] float64 -> (codes [n][K] uint8, one code per byte; scales [n][K/32] uint8)."""
+        v = np.ascontiguousarray(v, np.float64)
+        n, K = v.shape
+        codes = np.empty((n, K), np.uint8); scales = np.empty((n, K // 32), np.uint8)
+        self.lib.orc_mx_quantize(_p(v), n, K, fmt, _p(codes), _p(scales))
+        return codes, scales
+
+    def mx_dequantize(self, codes: np.ndarray, scales: np.ndarray, fmt: int) -> np.ndarray:
+        codes = np.ascontiguousarray(codes, np.uint8); scales = np.ascontiguousarray(scales, np.uint8)
+        n, K = codes.shape
+        out = np.empty((n, K), np.float64)
+        self.lib.orc_mx_dequantize(_p(codes), _p(scales), n, K, fmt, _p(out))
+        return out
+
+    def expert_ffn_mx(self, x: np.ndarray, x_fmt: int, k_total: int, W: ExpertWeights, act_fmt: int,
+                      offsets: np.ndarray, sorted_slot: np.ndarray,
+                      slot_mask: Optional[np.ndarray] = None) -> np.ndarray:
+        x = np.ascontiguousarray(x, np.uint16)
+        T = x.shape[0]
+        offsets = np.ascontiguousarray(offsets, np.int32); sorted_slot = np.ascontiguousarray(sorted_slot, np.int32)
+        mask = None if slot_mask is None else np.ascontiguousarray(slot_mask, np.uint8)
+        y = np.full((T * k_total, W.hidden), np.nan)
+        self.lib.orc_expert_ffn_mx(_p(x), x_fmt, T, k_total, ctypes.byref(W.c), act_fmt, _p(offsets),
+                                   _p(sorted_slot), _p(mask), _p(y))
+        return y
 
     # ---- layer ----
     def route(self, x: np.ndarray, x_fmt: int, router: np.ndarray, bias: Optional[np.ndarray], top_k: int,

@@ -319,6 +319,157 @@ void orc_combine(const double *y_slots, const double *weights, int T, int k_tota
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* MX activation formats and the MX-mode expert FFN (readings stated in moe_oracle.h)          */
+/* ------------------------------------------------------------------------------------------ */
+
+int orc_mx_bits(int fmt) { return fmt == ORC_MX_FP8_E4M3 ? 8 : (fmt == ORC_MX_FP6_E2M3 ? 6 : 4); }
+int orc_mx_emax(int fmt) { return fmt == ORC_MX_FP8_E4M3 ? 8 : 2; }
+
+/* A code is sign | exponent field | fraction field.  Exponent field 0 gives the subnormal
+ * fr * 2^(1 - bias - m_bits); otherwise (2^m_bits + fr) * 2^(ex - bias - m_bits). */
+double orc_mx_value(int fmt, int code) {
+  int e_bits, m_bits, bias;
+  if (fmt == ORC_MX_FP8_E4M3) { e_bits = 4; m_bits = 3; bias = 7; }
+  else if (fmt == ORC_MX_FP6_E2M3) { e_bits = 2; m_bits = 3; bias = 1; }
+  else return orc_e2m1(code & 15);
+  int sign = (code >> (e_bits + m_bits)) & 1;
+  int ex = (code >> m_bits) & ((1 << e_bits) - 1), fr = code & ((1 << m_bits) - 1);
+  if (fmt == ORC_MX_FP8_E4M3 && ex == 15 && fr == 7) return NAN;
+  double v = ex == 0 ? ldexp((double)fr, 1 - bias - m_bits)
+                     : ldexp((double)((1 << m_bits) + fr), ex - bias - m_bits);
+  return sign ? -v : v;
+}
+
+/* Search over every non-negative code (their values ascend with the code): the nearest value to
+ * |q| wins, an exact tie goes to the even code.  Past the largest value the largest code is the
+ * nearest, which is the saturation.  The sign bit is the sign of q (so -0.0 and tiny negative
+ * values give the negative-zero code). */
+int orc_mx_encode(int fmt, double q) {
+  const int bits = orc_mx_bits(fmt);
+  const int n_pos = fmt == ORC_MX_FP8_E4M3 ? 127 : (1 << (bits - 1)); /* E4M3: 0x7F is NaN */
+  const double a = fabs(q);
+  int best = 0;
+  double best_d = a;
+  for (int c = 1; c < n_pos; ++c) {
+    double d = fabs(a - orc_mx_value(fmt, c));
+    if (d < best_d || (d == best_d && c % 2 == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return signbit(q) ? (best | (1 << (bits - 1))) : best;
+}
+
+/* X = 2^(floor(log2 amax) - emax), as the E8M0 code floor(log2 amax) - emax + 127 clamped to
+ * [0, 254]; a block of zeros takes code 0.  frexp gives amax = f 2^ex with f in [0.5, 1), so
+ * floor(log2 amax) = ex - 1 exactly. */
+int orc_mx_scale_code(int fmt, double amax) {
+  if (!(amax > 0.0)) return 0;
+  int ex;
+  frexp(amax, &ex);
+  int c = (ex - 1) - orc_mx_emax(fmt) + 127;
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+void orc_mx_quantize(const double *v, int n_rows, int K, int fmt, uint8_t *codes, uint8_t *scales) {
+  for (int r = 0; r < n_rows; ++r)
+    for (int b = 0; b < K / 32; ++b) {
+      const double *blk = v + (int64_t)r * K + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs(blk[i]) > amax) amax = fabs(blk[i]);
+      const int sc = orc_mx_scale_code(fmt, amax);
+      scales[(int64_t)r * (K / 32) + b] = (uint8_t)sc;
+      const double X = orc_e8m0(sc);
+      for (int i = 0; i < 32; ++i) codes[(int64_t)r * K + 32 * b + i] = (uint8_t)orc_mx_encode(fmt, blk[i] / X);
+    }
+}
+
+void orc_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int n_rows, int K, int fmt,
+                       double *out) {
+  for (int r = 0; r < n_rows; ++r)
+    for (int k = 0; k < K; ++k)
+      out[(int64_t)r * K + k] =
+          orc_mx_value(fmt, codes[(int64_t)r * K + k]) * orc_e8m0(scales[(int64_t)r * (K / 32) + k / 32]);
+}
+
+/* One vector through the MX round trip in place: v <- dequantize(quantize(v)). */
+static void mx_round_trip(double *v, int K, int fmt) {
+  uint8_t *c = (uint8_t *)malloc((size_t)K);
+  uint8_t *s = (uint8_t *)malloc((size_t)K / 32 + 1);
+  orc_mx_quantize(v, 1, K, fmt, c, s);
+  orc_mx_dequantize(c, s, 1, K, fmt, v);
+  free(c);
+  free(s);
+}
+
+void orc_expert_ffn_mx(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                       int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
+                       const uint8_t *slot_mask, double *y_slots) {
+  const int H = W->hidden, I = W->inter, E2 = W->n_experts;
+  const int64_t n_slots = (int64_t)T * k_total;
+  for (int e = 0; e < E2; ++e) {
+    int r0 = offsets[e], r1 = offsets[e + 1];
+    int n_rows = 0;
+    int *slot = (int *)malloc(sizeof(int) * (size_t)(r1 - r0 + 1));
+    for (int r = r0; r < r1; ++r) {
+      int s = sorted_slot[r];
+      if (s < 0 || s >= n_slots) continue;
+      if (slot_mask && !slot_mask[s]) continue;
+      slot[n_rows++] = s;
+    }
+    if (n_rows == 0) {
+      free(slot);
+      continue;
+    }
+    double *xs = (double *)malloc(sizeof(double) * (size_t)n_rows * H);
+    double *hs = (double *)malloc(sizeof(double) * (size_t)n_rows * I);
+    for (int i = 0; i < n_rows; ++i) {
+      int t = slot[i] / k_total;
+      for (int k = 0; k < H; ++k) xs[(int64_t)i * H + k] = act_value(x, x_fmt, (int64_t)t * H + k);
+      mx_round_trip(xs + (int64_t)i * H, H, act_fmt);
+    }
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < I; ++n) {
+      double *wg = (double *)malloc(sizeof(double) * (size_t)H);
+      double *wu = (double *)malloc(sizeof(double) * (size_t)H);
+      for (int k = 0; k < H; ++k) {
+        wg[k] = orc_weight(&W->gate, W->fmt, e, n, k);
+        wu[k] = orc_weight(&W->up, W->fmt, e, n, k);
+      }
+      for (int i = 0; i < n_rows; ++i) {
+        const double *xv = xs + (int64_t)i * H;
+        double g = 0.0, u = 0.0;
+        for (int k = 0; k < H; ++k) {
+          g += wg[k] * xv[k];
+          u += wu[k] * xv[k];
+        }
+        hs[(int64_t)i * I + n] = orc_silu(g) * u;
+      }
+      free(wg);
+      free(wu);
+    }
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < n_rows; ++i) mx_round_trip(hs + (int64_t)i * I, I, act_fmt);
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < H; ++m) {
+      double *wd = (double *)malloc(sizeof(double) * (size_t)I);
+      for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, m, n);
+      for (int i = 0; i < n_rows; ++i) {
+        const double *hv = hs + (int64_t)i * I;
+        double acc = 0.0;
+        for (int n = 0; n < I; ++n) acc += wd[n] * hv[n];
+        y_slots[(int64_t)slot[i] * H + m] = acc;
+      }
+      free(wd);
+    }
+    free(xs);
+    free(hs);
+    free(slot);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Cross-check forms                                                                          */
 /* ------------------------------------------------------------------------------------------ */
 

@@ -74,6 +74,30 @@ void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_
 void orc_combine(const double *y_slots, const double *weights, int T, int k_total, int H,
                  const uint8_t *token_mask, double *y);
 
+/* ---- MX activation formats (prefill MX mode) ----
+ * Not on the pages, which define only the E2M1 + E8M0 weight block [MX].  Reading: the activation
+ * blocks of the MX mode follow the OCP Microscaling (MX) v1.0 element formats -- E4M3 (bias 7, no
+ * infinities, S.1111.111 is NaN, max 448), E2M3 (bias 1, max 7.5) and E2M1 (the page's codes,
+ * max 6) -- with one E8M0 scale per 32 consecutive values along K and the scale rule
+ * X = 2^(floor(log2 amax) - emax) of that specification, emax being the exponent of the format's
+ * largest normal (8, 2, 2).  Elements are rounded to nearest, ties to the even code, saturating. */
+enum { ORC_MX_FP8_E4M3 = 1, ORC_MX_FP4_E2M1 = 2, ORC_MX_FP6_E2M3 = 3 };
+int orc_mx_bits(int fmt);                   /* bits per element code: 8, 4, 6 */
+int orc_mx_emax(int fmt);                   /* exponent of the largest normal: 8, 2, 2 */
+double orc_mx_value(int fmt, int code);     /* element value of a code (NaN for E4M3 NaN codes) */
+int orc_mx_encode(int fmt, double q);       /* nearest code to q, ties to even, saturating */
+int orc_mx_scale_code(int fmt, double amax);/* E8M0 code of a block with largest magnitude amax */
+/* codes [n_rows][K] one element code per byte; scales [n_rows][K/32] */
+void orc_mx_quantize(const double *v, int n_rows, int K, int fmt, uint8_t *codes, uint8_t *scales);
+void orc_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int n_rows, int K, int fmt,
+                       double *out);
+/* The grouped expert FFN of the MX mode: like orc_expert_ffn, with the token's x row and each
+ * slot's h row replaced by their MX round trip (quantize, then dequantize) before they enter a
+ * projection.  Weights stay the exact decoded MXFP4 values; all arithmetic is fp64. */
+void orc_expert_ffn_mx(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                       int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
+                       const uint8_t *slot_mask, double *y_slots);
+
 /* ---- cross-check forms ---- */
 void orc_layer_bruteforce(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
                           const int32_t *ids, const double *weights, double *y);

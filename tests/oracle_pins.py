@@ -429,6 +429,177 @@ def check_dense_slices(o):
     close(dense, np_expert(f(wg), f(wu), f(wd), np_act(L.x, X_FP16)), 1e-12, "dense vs numpy")
 
 
+# ------------------------------------------------------------------------------------------------
+# MX activation formats (MX mode).  The pages fix only E2M1 + E8M0; these pins hold the oracle to
+# the OCP MX element formats through independent decoders (minifloat, torch's float8_e4m3fn), to
+# the nearest/ties-to-even/saturation rule by exhaustive comparison, and to the scale rule through
+# exact binary fractions.
+# ------------------------------------------------------------------------------------------------
+MX_FORMATS = {o_fmt: spec for o_fmt, spec in [
+    (1, dict(bits=8, e_bits=4, m_bits=3, bias=7, emax=8, vmax=448.0)),
+    (2, dict(bits=4, e_bits=2, m_bits=1, bias=1, emax=2, vmax=6.0)),
+    (3, dict(bits=6, e_bits=2, m_bits=3, bias=1, emax=2, vmax=7.5)),
+]}
+
+
+def mx_table(o, fmt):
+    """Non-negative codes and values of a format (E4M3's NaN code 0x7F excluded)."""
+    n = 1 << (MX_FORMATS[fmt]["bits"] - 1)
+    codes = [c for c in range(n) if not (fmt == 1 and c == 0x7F)]
+    return np.array(codes), np.array([o.mx_value(fmt, c) for c in codes])
+
+
+def check_mx_tables(o):
+    """Every code of every MX element format decodes as the generic minifloat decoder says (sign,
+    exponent field with the format's bias, subnormals at field 0); E4M3 also against torch's
+    float8_e4m3fn on all 256 patterns, with NaN exactly at S.1111.111; largest values 448, 6, 7.5."""
+    import torch
+    for fmt, sp in MX_FORMATS.items():
+        for c in range(1 << sp["bits"]):
+            v = o.mx_value(fmt, c)
+            if fmt == 1 and (c & 0x7F) == 0x7F:
+                assert math.isnan(v), c
+                continue
+            assert v == minifloat(c, sp["e_bits"], sp["m_bits"], sp["bias"], False), (fmt, c, v)
+        _, vals = mx_table(o, fmt)
+        assert vals.max() == sp["vmax"] and np.all(np.diff(vals) > 0), fmt
+        assert o.mx_bits(fmt) == sp["bits"] and o.mx_emax(fmt) == sp["emax"]
+        assert sp["vmax"] >= 2.0 ** sp["emax"] > sp["vmax"] / 2
+    tv = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    ov = np.array([o.mx_value(1, c) for c in range(256)])
+    assert np.array_equal(np.isnan(tv), np.isnan(ov)) and np.array_equal(tv[~np.isnan(tv)], ov[~np.isnan(ov)])
+
+
+def check_mx_encode_nearest(o):
+    """Encoding picks the nearest value (exhaustive comparison with every code), an exact midpoint
+    goes to the even code, values past the largest saturate to it, and the sign is the input's
+    (including -0.0); E4M3 also equals torch's float8_e4m3fn conversion inside its range."""
+    import torch
+    rng = np.random.default_rng(11)
+    for fmt, sp in MX_FORMATS.items():
+        codes, vals = mx_table(o, fmt)
+        mids = (vals[1:] + vals[:-1]) / 2
+        q = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+                            rng.uniform(0, sp["vmax"] * 1.3, 3000), [sp["vmax"] * 4, 1e30]])
+        sign_bit = 1 << (sp["bits"] - 1)
+        for v in q:
+            c = o.mx_encode(fmt, float(v))
+            assert c < sign_bit, (fmt, v, c)
+            d = np.abs(vals - v)
+            best = d.min()
+            assert abs(o.mx_value(fmt, c) - v) == best, (fmt, v, c)
+            ties = codes[d == best]
+            if len(ties) > 1:
+                assert c % 2 == 0 and c in ties, (fmt, v, c, ties)
+            assert o.mx_encode(fmt, -float(v)) == c | sign_bit, (fmt, v)
+        assert o.mx_encode(fmt, sp["vmax"] * 10) == codes[-1]
+        assert o.mx_encode(fmt, -0.0) == sign_bit and o.mx_encode(fmt, 0.0) == 0
+        assert o.mx_encode(fmt, -1e-30) == sign_bit
+    q = rng.standard_normal(5000) * 60
+    q = np.concatenate([q, (vals_e4 := mx_table(o, 1)[1]), (vals_e4[1:] + vals_e4[:-1]) / 2])
+    q = q[np.abs(q) <= 448].astype(np.float32)
+    tc = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    oc = np.array([o.mx_encode(1, float(v)) for v in q])
+    assert np.array_equal(tc, oc)
+
+
+def check_mx_scale_rule(o):
+    """Scale code = floor(log2 amax) - emax + 127 for amax = (1 + j/8) 2^k (exact binary
+    fractions, so floor(log2) is k), clamped to [0, 254]; an all-zero block takes code 0."""
+    for fmt, sp in MX_FORMATS.items():
+        for k in range(-140, 140, 3):
+            for j in range(8):
+                amax = math.ldexp(1.0 + j / 8.0, k)
+                want = min(max(k - sp["emax"] + 127, 0), 254)
+                assert o.mx_scale_code(fmt, amax) == want, (fmt, k, j)
+        assert o.mx_scale_code(fmt, 0.0) == 0
+
+
+def check_mx_quantize_fp8_vs_torch(o):
+    """MXFP8 block quantisation against an independent torch formulation: per 32-block,
+    X = 2^(floor(log2 amax) - 8) from torch.frexp, codes = float8_e4m3fn(clamp(v / X, +-448))."""
+    import torch
+    rng = np.random.default_rng(12)
+    n, K = 6, 256
+    v = rng.standard_normal((n, K)) * np.exp(rng.uniform(-6, 6, (n, K // 32))).repeat(32, axis=1)
+    v[0, :32] = 0.0                                        # zero block
+    v[1, 32:64] = np.float32(1.99) * 2.0 ** np.arange(32)  # wide range, top values saturate
+    v[2, :32] = rng.choice([-3.0, -1.0, 0.5, 2.25, 448 / 256.0], 32)  # exact values and midpoints
+    v = v.astype(np.float32).astype(np.float64)            # binary32 inputs, as the kernels see
+    codes, scales = o.mx_quantize(v, 1)
+    t = torch.from_numpy(v).reshape(n, K // 32, 32)
+    amax = t.abs().amax(dim=2, keepdim=True)
+    _, ex = torch.frexp(amax)
+    sc = torch.where(amax > 0, (ex - 1 - 8 + 127).clamp(0, 254), torch.zeros_like(ex))
+    X = torch.ldexp(torch.ones_like(amax), (sc - 127).to(torch.float64))
+    tq = (t / X).clamp(-448, 448).float().to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, K).numpy()
+    assert np.array_equal(scales, sc.reshape(n, K // 32).numpy().astype(np.uint8))
+    # torch keeps +0 for -0.0 inputs in some paths; compare magnitudes there and signs elsewhere
+    assert np.array_equal(codes & 0x7F, tq & 0x7F)
+    nz = (codes & 0x7F) != 0
+    assert np.array_equal(codes[nz], tq[nz])
+
+
+def check_mx_quantize_blocks(o):
+    """For every format: values that are representable at the block's own scale come back exactly;
+    the block's largest element lands in the top binade [2^emax, vmax] (or saturates to vmax);
+    every element is within half a spacing of its value; blocks are independent."""
+    rng = np.random.default_rng(13)
+    for fmt, sp in MX_FORMATS.items():
+        codes_t, vals = mx_table(o, fmt)
+        top = vals[vals >= 2.0 ** sp["emax"]]
+        n, K = 4, 128
+        S = rng.integers(-20, 20, (n, K // 32))
+        pick = rng.choice(vals, (n, K)) * rng.choice([-1.0, 1.0], (n, K))
+        pick[:, ::32] = rng.choice(top, (n, K // 32))        # each block holds a top-binade element
+        v = pick * np.ldexp(1.0, S).repeat(32, axis=1)
+        c, s = o.mx_quantize(v, fmt)
+        assert np.array_equal(s.astype(int), S + 127), fmt
+        assert np.array_equal(o.mx_dequantize(c, s, fmt), v), fmt
+        w = rng.standard_normal((n, K)) * 3.0
+        c, s = o.mx_quantize(w, fmt)
+        d = o.mx_dequantize(c, s, fmt)
+        X = np.ldexp(1.0, s.astype(int) - 127).repeat(32, axis=1)
+        q = np.abs(w / X)
+        for r in range(n):
+            for b in range(K // 32):
+                blk = q[r, 32 * b:32 * b + 32]
+                m = np.argmax(blk)
+                assert 2.0 ** sp["emax"] <= blk[m] < 2.0 ** (sp["emax"] + 1)
+                assert abs(d[r, 32 * b + m]) / X[r, 32 * b] >= min(2.0 ** sp["emax"], sp["vmax"])
+        qc = np.minimum(q, sp["vmax"]).reshape(-1)
+        i_hi = np.searchsorted(vals, qc, side="left")          # first value >= q
+        hi = vals[i_hi]
+        lo = vals[np.maximum(np.searchsorted(vals, qc, side="right") - 1, 0)]  # last value <= q
+        err = np.abs(np.abs(d / X).reshape(-1) - qc)
+        assert np.all(err <= (hi - lo) / 2), fmt
+        w2 = w.copy(); w2[:, 32:64] *= 1e6
+        c2, s2 = o.mx_quantize(w2, fmt)
+        assert np.array_equal(c2[:, :32], c[:, :32]) and np.array_equal(c2[:, 64:], c[:, 64:])
+
+
+def check_expert_ffn_mx_vs_numpy(o):
+    """The MX-mode grouped FFN equals numpy on the same steps: x rows and h rows through the
+    (separately pinned) MX round trip, numpy matmuls over the numpy-decoded weights; non-square
+    shapes and two experts with several slots each."""
+    for fmt in (1, 2, 3):
+        L = small_layer(T=5, H=64, I=96, E=3, k=2)
+        W = ExpertWeights.from_layer(L)
+        r = o.route(L.x, X_BF16, L.router, L.bias, 2)
+        b = o.bucket(r["ids"], 3)
+        ys = o.expert_ffn_mx(L.x, X_BF16, 2, W, fmt, b["offsets"], b["sorted_slot"])
+        Wg, Wu, Wd = np_weights(L)
+        X = np_act(L.x, X_BF16)
+        rt = lambda a: o.mx_dequantize(*o.mx_quantize(a, fmt), fmt)
+        Xq = rt(X)
+        for s in range(10):
+            e, t = r["ids"].reshape(-1)[s], s // 2
+            h = np_silu(Xq[t:t + 1] @ Wg[e].T) * (Xq[t:t + 1] @ Wu[e].T)
+            close(ys[s], (rt(h) @ Wd[e].T)[0], 1e-10, f"mx ffn fmt={fmt} slot={s}")
+        ye = o.expert_ffn(L.x, X_BF16, 2, W, b["offsets"], b["sorted_slot"])
+        assert not np.allclose(ys, ye, rtol=0, atol=0)  # the round trips change the result
+
+
 ALL_CHECKS = [
     check_minifloat_reference, check_e2m1, check_e8m0, check_mxfp4_table, check_bf16_f16, check_storage,
     check_nibble_order, check_weight_access, check_silu, check_decode_matrix,
@@ -436,4 +607,6 @@ ALL_CHECKS = [
     check_router_shared, check_bucket, check_bucket_invalid,
     check_expert_apply_vs_numpy, check_layer_vs_numpy, check_layer_forms, check_single_expert_swiglu,
     check_combine, check_dense_slices,
+    check_mx_tables, check_mx_encode_nearest, check_mx_scale_rule, check_mx_quantize_fp8_vs_torch,
+    check_mx_quantize_blocks, check_expert_ffn_mx_vs_numpy,
 ]

@@ -38,6 +38,18 @@ MUTANTS = {
                                             "for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, (m + 1) % H, n);"),
     "fp16 exponent bias": ("v = ldexp(1024.0 + (double)fr, ex - 25);", "v = ldexp(1024.0 + (double)fr, ex - 24);"),
     "x row of the wrong token": ("int t = slot[i] / k_total;", "int t = slot[i] % T;"),
+    "E4M3 bias off by one": ("if (fmt == ORC_MX_FP8_E4M3) { e_bits = 4; m_bits = 3; bias = 7; }",
+                             "if (fmt == ORC_MX_FP8_E4M3) { e_bits = 4; m_bits = 3; bias = 6; }"),
+    "MX ties rounded up": ("if (d < best_d || (d == best_d && c % 2 == 0)) {", "if (d <= best_d) {"),
+    "MX scale emax off": ("int orc_mx_emax(int fmt) { return fmt == ORC_MX_FP8_E4M3 ? 8 : 2; }",
+                          "int orc_mx_emax(int fmt) { return fmt == ORC_MX_FP8_E4M3 ? 8 : 1; }"),
+    "MX scale from ceil(log2)": ("int c = (ex - 1) - orc_mx_emax(fmt) + 127;", "int c = ex - orc_mx_emax(fmt) + 127;"),
+    "MX sign dropped": ("return signbit(q) ? (best | (1 << (bits - 1))) : best;", "return best;"),
+    "MX x round trip skipped": ("      mx_round_trip(xs + (int64_t)i * H, H, act_fmt);\n", "\n"),
+    "MX h round trip skipped": ("for (int i = 0; i < n_rows; ++i) mx_round_trip(hs + (int64_t)i * I, I, act_fmt);",
+                                "for (int i = 0; i < n_rows; ++i) (void)0;"),
+    "MX block of 16": ("const double *blk = v + (int64_t)r * K + 32 * b;\n      double amax = 0.0;\n      for (int i = 0; i < 32; ++i)",
+                       "const double *blk = v + (int64_t)r * K + 32 * b;\n      double amax = 0.0;\n      for (int i = 0; i < 16; ++i)"),
     "probabilities mis-normalised by 1e-7": ("for (int e = 0; e < E; ++e) p[e] /= den;",
                                                "for (int e = 0; e < E; ++e) p[e] /= den * 1.0000001;"),
 }

@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--prefill", action="store_true",
                     help="measure the prefill layer instead (T=8192, 256 routed + 1 shared expert, top-8, "
                          "log-Zipf routing bias) and print its own JSON line with MFMA utilisation")
+    ap.add_argument("--mx", choices=["fp8", "fp6", "fp4"], default=None,
+                    help="with --prefill: the MX mode of the expert FFN (activations quantised to MXFP8 E4M3, "
+                         "MXFP6 E2M3 or MXFP4 E2M1 and multiplied with the FP4 weights on scaled MFMAs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain elementwise copy (torch.neg, fp32) of this many MiB three times, "
                          "for scaling memory counters, and exit")
@@ -56,10 +59,11 @@ def parse():
 class Runner:
     """Preallocated buffers for one T; step(set) enqueues the five library calls on the current stream."""
 
-    def __init__(self, moe, sets, T, top_k, n_shared, n_experts, H, I):
+    def __init__(self, moe, sets, T, top_k, n_shared, n_experts, H, I, mx=None):
         import torch
         dev = "cuda:0"
         self.moe, self.sets, self.T, self.top_k, self.n_shared = moe, sets, T, top_k, n_shared
+        self.mx = mx
         self.kt = top_k + n_shared
         self.n_experts = n_experts
         n = T * self.kt
@@ -71,7 +75,8 @@ class Runner:
                              torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
                              torch.empty(n, dtype=torch.int32, device=dev), None)
         self.bucket_ws = self._ws(moe.moe_bucket_workspace_bytes(n, n_experts))
-        self.ffn_ws = self._ws(moe.moe_expert_ffn_workspace_bytes(T, self.kt, W0))
+        self.ffn_ws = self._ws(moe.moe_expert_ffn_workspace_bytes(T, self.kt, W0) if mx is None
+                               else moe.moe_expert_ffn_mx_workspace_bytes(T, self.kt, W0, mx))
         self.y_slots = torch.empty((n, H), dtype=torch.float32, device=dev)
         self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
 
@@ -89,11 +94,19 @@ class Runner:
         rec(1)
         m.moe_bucket(self.ids, self.n_experts, out=self.b, workspace=self.bucket_ws)
         rec(2)
-        m.moe_expert_ffn_plan(self.T, s["W"], self.b.offsets, self.kt, self.ffn_ws)
-        rec(3)
-        m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws)
-        rec(4)
-        m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws, self.y_slots)
+        if self.mx is not None:  # MX mode: one call (x quantisation, plan, gate/up, down)
+            m.moe_expert_ffn_mx(s["x"][:self.T], s["W"], self.mx, self.b.offsets, self.b.sorted_slot, self.kt,
+                                out=self.y_slots, workspace=self.ffn_ws)
+            rec(3)
+            rec(4)
+        else:
+            m.moe_expert_ffn_plan(self.T, s["W"], self.b.offsets, self.kt, self.ffn_ws)
+            rec(3)
+            m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt,
+                                    self.ffn_ws)
+            rec(4)
+            m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws,
+                                  self.y_slots)
         rec(5)
         m.moe_combine(self.y_slots, self.w, out=self.y)
         rec(6)
@@ -300,7 +313,7 @@ def prefill_run(args):
     gen_s = time.time() - t0
     W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
     sets = [{"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t}]
-    runner = Runner(moe, sets, T, k, S, E + S, H, I)
+    runner = Runner(moe, sets, T, k, S, E + S, H, I, mx=args.mx)
     ms, per = time_steps(runner, args.steps, args.warmup)
     counts = runner.b.counts.cpu()
     A = int((counts > 0).sum().item())
@@ -308,23 +321,32 @@ def prefill_run(args):
     ffn_flops = 6.0 * H * I * T * kt
     router_flops = 2.0 * T * H * E
     bf16_peak = 2.5e15
-    gu_s, dn_s = per["ffn_gateup"] / 1e3, per["ffn_down"] / 1e3
+    ffn_s = (per["ffn_plan"] + per["ffn_gateup"] + per["ffn_down"]) / 1e3
+    mode = "exact mode" if args.mx is None else f"MX mode, {args.mx} activations"
     out = {
-        "metric": "prefill MoE-layer tokens/s and MFMA utilisation (exact mode)",
+        "metric": f"prefill MoE-layer tokens/s and MFMA utilisation ({mode})",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "ms_per_step": ms, "higher_is_better": True,
+        "dtype": "bf16" if args.mx is None else f"fp4 weights x {args.mx} activations", "data": "synthetic",
         "config": {"workload": f"moe_layer_prefill_H{H}_E{E}+{S}_top{k}_I{I}_mxfp4_T{T}", "tokens": T,
-                   "zipf_s": wl.zipf_s},
+                   "zipf_s": wl.zipf_s, "mode": "exact" if args.mx is None else f"mx_{args.mx}"},
         "active_experts": A, "max_rows_per_expert": int(counts.max().item()),
         "per_call_ms": {kk: round(v, 4) for kk, v in per.items()},
-        "ffn_tflops": ffn_flops / (gu_s + dn_s) / 1e12,
-        "gateup_tflops": 4.0 * H * I * T * kt / gu_s / 1e12,
-        "down_tflops": 2.0 * H * I * T * kt / dn_s / 1e12,
-        "frac_of_bf16_mfma_peak": ffn_flops / (gu_s + dn_s) / bf16_peak,
-        "frac_of_mxfp4_mfma_peak": ffn_flops / (gu_s + dn_s) / 10.1e15,
+        "ffn_ms": ffn_s * 1e3,
+        "ffn_tflops": ffn_flops / ffn_s / 1e12,
+        "frac_of_bf16_mfma_peak": ffn_flops / ffn_s / bf16_peak,
+        "frac_of_mxfp4_mfma_peak": ffn_flops / ffn_s / 10.1e15,
         "layer_flops": ffn_flops + router_flops,
         "input_generation_s": gen_s,
     }
+    if args.mx is None:
+        gu_s, dn_s = per["ffn_gateup"] / 1e3, per["ffn_down"] / 1e3
+        out["gateup_tflops"] = 4.0 * H * I * T * kt / gu_s / 1e12
+        out["down_tflops"] = 2.0 * H * I * T * kt / dn_s / 1e12
+    else:
+        out["per_call_ms"]["ffn_mx"] = out["per_call_ms"].pop("ffn_plan")
+        for kk in ("ffn_gateup", "ffn_down"):  # one call: its kernels are split by the profiler only
+            out["per_call_ms"].pop(kk)
     print(json.dumps(out), flush=True)
 
 

@@ -180,6 +180,61 @@ moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total,
                                size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * MX mode (prefill).  Not on the pages, which define only the MXFP4 weight block [MX]: the
+ * activations are quantised to an OCP Microscaling element format, one E8M0 scale per 32
+ * consecutive values along K, so that the expert FFN can run the FP4 weights on the matrix
+ * cores' scaled FP4 x FP8/FP6/FP4 instructions.  The result is NOT the exact layer: it differs
+ * from moe_expert_ffn by the quantisation of x and h (use moe_expert_ffn for exact results).
+ *
+ * Element formats (sign | exponent | fraction, subnormals at exponent field 0):
+ *   MOE_MX_FP8_E4M3  8-bit, bias 7, largest 448 (S.1111.111 is NaN and never produced)
+ *   MOE_MX_FP4_E2M1  4-bit, bias 1, largest 6 (the weights' E2M1 codes)
+ *   MOE_MX_FP6_E2M3  6-bit, bias 1, largest 7.5
+ * Quantisation of a block of 32 values v_i with amax = max |v_i|: scale code
+ * c = clamp(floor(log2 amax) - emax + 127, 0, 254) (emax = 8, 2, 2; c = 0 for an all-zero block),
+ * X = 2^(c - 127), and code_i = the element value nearest to v_i / X, ties to the even code,
+ * saturating at the largest value, with the sign of v_i (so -0 and tiny negative values give the
+ * negative-zero code).
+ * Packed codes: a block takes 4 * bits bytes -- FP8 one code per byte; FP4 two per byte, element
+ * 2j in the low nibble of byte j; FP6 element j in bits 6j .. 6j+5 of the block's little-endian
+ * 192-bit string.  A row of K values is K/32 consecutive blocks, rows are consecutive. */
+typedef enum { MOE_MX_FP8_E4M3 = 1, MOE_MX_FP4_E2M1 = 2, MOE_MX_FP6_E2M3 = 3 } moe_mx_format;
+
+/* Bytes of one packed row of K values (K/32 * 4 * bits); 0 for an unknown format or K % 32 != 0. */
+size_t moe_mx_row_bytes(moe_mx_format fmt, int K);
+
+/* moe_mx_quantize -- the activation quantiser of the MX mode on its own:
+ *   x [n_rows][K] bf16 or fp16 (contiguous, 16-byte aligned), codes [n_rows][row bytes] out
+ *   (16-byte aligned), scales [n_rows][K/32] E8M0 out.
+ * Errors: NULL, SHAPE (n_rows < 0, K < 1), BLOCK (K % 32), DTYPE (format or x dtype), ALIGN, HIP. */
+moe_status moe_mx_quantize(const void *x, moe_act_dtype x_dtype, int n_rows, int K, moe_mx_format fmt,
+                           uint8_t *codes, uint8_t *scales, void *stream);
+
+/* moe_expert_ffn_mx -- moe_expert_ffn with MX activations: for every sorted row r of expert e
+ * with slot s and token t = s / k_total,
+ *   xq = dequant(quant(x[t,:])),  g = W_gate[e] xq,  u = W_up[e] xq  (fp32 accumulation),
+ *   h = SiLU(g) * u (fp32),  hq = dequant(quant(h)),  y_slots[s,:] = W_down[e] hq  (fp32),
+ * quant/dequant being the block quantisation above along hidden (x) and inter (h).  Weights must
+ * be MXFP4 and x bf16.  hidden and inter must be multiples of 256; scale pointers and strides
+ * multiples of 4 bytes.  Arguments otherwise as for moe_expert_ffn, with the workspace from
+ * moe_expert_ffn_mx_workspace_bytes (it holds the x and h codes and the tile table).
+ * Errors: NULL, SHAPE (also hidden or inter not a multiple of 256, or buffers past 2^31 bytes),
+ * BLOCK, ALIGN, DTYPE (weights not MXFP4, x not bf16, unknown format), WORKSPACE, HIP. */
+size_t moe_expert_ffn_mx_workspace_bytes(int T, int k_total, const moe_expert_weights *W,
+                                         moe_mx_format fmt);
+moe_status moe_expert_ffn_mx(const void *x, moe_act_dtype x_dtype, int T, int k_total,
+                             const moe_expert_weights *W, moe_mx_format fmt, const int32_t *offsets,
+                             const int32_t *sorted_slot, float *y_slots, void *workspace,
+                             size_t workspace_bytes, void *stream);
+/* Where moe_expert_ffn_mx leaves its quantised activations in the workspace, for inspection:
+ * offsets[0] x codes ([T] packed rows of `hidden` values), offsets[1] x scales ([T][hidden/32]),
+ * offsets[2] h codes ([T*k_total] packed rows of `inter` values, row r belonging to sorted row r,
+ * i.e. slot sorted_slot[r]; rows of empty slots are unspecified), offsets[3] h scales
+ * ([T*k_total][inter/32]).  offsets is a host array of 4.  Errors: NULL, SHAPE, DTYPE. */
+moe_status moe_expert_ffn_mx_workspace_layout(int T, int k_total, const moe_expert_weights *W,
+                                              moe_mx_format fmt, size_t *offsets);
+
+/* ---------------------------------------------------------------------------------------------
  * moe_combine -- weighted reduction [C31] with FP32 output [C32]:
  *   y[t,:] = sum_{j = 0 .. k_total-1, in ascending j} weights[t,j] * y_slots[t*k_total+j,:]
  * Every output element has exactly one owner (no atomics).

@@ -27,6 +27,8 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 
 MOE_ACT_BF16, MOE_ACT_FP16 = 0, 1
 MOE_W_MXFP4, MOE_W_FP16 = 0, 1
+MOE_MX_FP8_E4M3, MOE_MX_FP4_E2M1, MOE_MX_FP6_E2M3 = 1, 2, 3
+MX_FORMATS = {"fp8": MOE_MX_FP8_E4M3, "fp4": MOE_MX_FP4_E2M1, "fp6": MOE_MX_FP6_E2M3}
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_BLOCK", 4: "MOE_ERR_ALIGN",
           5: "MOE_ERR_DTYPE", 6: "MOE_ERR_TOPK", 7: "MOE_ERR_WORKSPACE", 8: "MOE_ERR_HIP"}
@@ -83,6 +85,16 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [vp, vp, i, i, i, vp, vp]
         L.moe_mxfp4_dequant.restype = i
         L.moe_mxfp4_dequant.argtypes = [vp, vp, i, i, i64, i64, vp, vp]
+        L.moe_mx_row_bytes.restype = st; L.moe_mx_row_bytes.argtypes = [i, i]
+        L.moe_mx_quantize.restype = i
+        L.moe_mx_quantize.argtypes = [vp, i, i, i, i, vp, vp, vp]
+        L.moe_expert_ffn_mx_workspace_bytes.restype = st
+        L.moe_expert_ffn_mx_workspace_bytes.argtypes = [i, i, ctypes.POINTER(moe_expert_weights), i]
+        L.moe_expert_ffn_mx_workspace_layout.restype = i
+        L.moe_expert_ffn_mx_workspace_layout.argtypes = [i, i, ctypes.POINTER(moe_expert_weights), i,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_expert_ffn_mx.restype = i
+        L.moe_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), i, vp, vp, vp, vp, st, vp]
         _lib = L
     return _lib
 
@@ -274,14 +286,62 @@ def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor
     return out
 
 
+def _mx_fmt(fmt) -> int:
+    return MX_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def moe_mx_row_bytes(fmt, K: int) -> int:
+    return lib().moe_mx_row_bytes(_mx_fmt(fmt), K)
+
+
+def moe_mx_quantize(x: torch.Tensor, fmt) -> tuple:
+    """[n][K] bf16/fp16 -> (packed codes uint8 [n][row bytes], E8M0 scales uint8 [n][K/32])."""
+    n, K = x.shape
+    f = _mx_fmt(fmt)
+    codes = torch.empty((n, max(moe_mx_row_bytes(f, K), 1)), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, max(K // 32, 1)), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_mx_quantize(_ptr(x), _act_dtype(x), n, K, f, _ptr(codes), _ptr(scales), _stream(x.device)),
+           "moe_mx_quantize")
+    return codes, scales
+
+
+def moe_expert_ffn_mx_workspace_bytes(T: int, k_total: int, W: ExpertWeights, fmt) -> int:
+    return lib().moe_expert_ffn_mx_workspace_bytes(T, k_total, ctypes.byref(W.c), _mx_fmt(fmt))
+
+
+def moe_expert_ffn_mx_workspace_layout(T: int, k_total: int, W: ExpertWeights, fmt) -> dict:
+    """Byte offsets of the quantised x and h that moe_expert_ffn_mx leaves in its workspace."""
+    offs = (ctypes.c_size_t * 4)()
+    _check(lib().moe_expert_ffn_mx_workspace_layout(T, k_total, ctypes.byref(W.c), _mx_fmt(fmt), offs),
+           "moe_expert_ffn_mx_workspace_layout")
+    return dict(x_codes=offs[0], x_scales=offs[1], h_codes=offs[2], h_scales=offs[3])
+
+
+def moe_expert_ffn_mx(x: torch.Tensor, W: ExpertWeights, fmt, offsets: torch.Tensor, sorted_slot: torch.Tensor,
+                      k_total: int, out: Optional[torch.Tensor] = None, workspace=None) -> torch.Tensor:
+    """MX mode of moe_expert_ffn (x and h quantised to the MX format `fmt`): -> y_slots fp32."""
+    T = x.shape[0]
+    dev = x.device
+    f = _mx_fmt(fmt)
+    y = out if out is not None else torch.empty((T * k_total, W.hidden), dtype=torch.float32, device=dev)
+    need = moe_expert_ffn_mx_workspace_bytes(T, k_total, W, f)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_expert_ffn_mx(_ptr(x), _act_dtype(x), T, k_total, ctypes.byref(W.c), f, _ptr(offsets),
+                                   _ptr(sorted_slot), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(dev)), "moe_expert_ffn_mx")
+    return y
+
+
 # ----------------------------------------------------------------------------------------------------
 class MoELayer:
     """One routed-MoE layer with every intermediate buffer allocated once, so that forward() only
     enqueues the four library calls (capturable in a HIP graph)."""
 
     def __init__(self, W: ExpertWeights, T: int, top_k: int, n_shared: int = 0,
-                 w_router: Optional[torch.Tensor] = None, logit_bias: Optional[torch.Tensor] = None):
+                 w_router: Optional[torch.Tensor] = None, logit_bias: Optional[torch.Tensor] = None,
+                 mx=None):
         self.W, self.T, self.top_k, self.n_shared = W, T, top_k, n_shared
+        self.mx = None if mx is None else _mx_fmt(mx)  # MX mode: activation format of the FFN
         self.w_router, self.logit_bias = w_router, logit_bias
         dev = W.device
         kt = top_k + n_shared
@@ -304,7 +364,8 @@ class MoELayer:
                                torch.empty(n, dtype=torch.int32, device=dev))
         self.bucket_ws = _workspace(moe_bucket_workspace_bytes(n, W.n_experts), dev)
         self.y_slots = torch.empty((n, H), dtype=torch.float32, device=dev)
-        self.ffn_ws = _workspace(moe_expert_ffn_workspace_bytes(T, kt, W), dev)
+        self.ffn_ws = _workspace(moe_expert_ffn_workspace_bytes(T, kt, W) if self.mx is None
+                                 else moe_expert_ffn_mx_workspace_bytes(T, kt, W, self.mx), dev)
         self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
@@ -312,11 +373,17 @@ class MoELayer:
             moe_route(x, self.w_router, self.top_k, self.logit_bias, self.n_shared,
                       out=(self.ids, self.weights, None), workspace=self.route_ws)
         moe_bucket(self.ids, self.W.n_experts, out=self.buckets, workspace=self.bucket_ws)
-        moe_expert_ffn(x, self.W, self.buckets.offsets, self.buckets.sorted_slot, self.k_total, out=self.y_slots,
-                       workspace=self.ffn_ws)
+        if self.mx is None:
+            moe_expert_ffn(x, self.W, self.buckets.offsets, self.buckets.sorted_slot, self.k_total, out=self.y_slots,
+                           workspace=self.ffn_ws)
+        else:
+            moe_expert_ffn_mx(x, self.W, self.mx, self.buckets.offsets, self.buckets.sorted_slot, self.k_total,
+                              out=self.y_slots, workspace=self.ffn_ws)
         return moe_combine(self.y_slots, self.weights, out=self.y)
 
 
-__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_plan", "moe_expert_ffn_gateup", "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant",
+__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
+           "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
+           "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",
            "ExpertWeights", "Buckets", "MoELayer", "MoEError", "lib"]

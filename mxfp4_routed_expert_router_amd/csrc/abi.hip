@@ -235,6 +235,128 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
 }
 
 // ---------------------------------------------------------------------------------------------
+// MX mode
+size_t moe_mx_row_bytes(moe_mx_format fmt, int K) {
+  const int bits = moe::mx_bits(fmt);
+  if (bits == 0 || K < 1 || K % 32 != 0) return 0;
+  return (size_t)(K / 32) * 4 * (size_t)bits;
+}
+
+moe_status moe_mx_quantize(const void* x, moe_act_dtype x_dtype, int n_rows, int K, moe_mx_format fmt,
+                           uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n_rows == 0) return MOE_OK;
+  if (n_rows < 0 || K < 1) return MOE_ERR_SHAPE;
+  if (K % 32 != 0) return MOE_ERR_BLOCK;
+  if (moe::mx_bits(fmt) == 0 || (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16)) return MOE_ERR_DTYPE;
+  if (!x || !codes || !scales) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(codes)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_mx_quantize(x, x_dtype == MOE_ACT_FP16, n_rows, K, fmt, codes, scales,
+                                            (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of an MX call: x codes, x scales, h codes, h scales, tile table (each 256-aligned).
+struct MxWs {
+  size_t xq, xs, hq, hs, table, total;
+};
+MxWs mx_ws(int T, int k_total, const moe_expert_weights* W, moe_mx_format fmt) {
+  MxWs w{};
+  const size_t n_slots = (size_t)T * (size_t)k_total;
+  w.xq = 0;
+  w.xs = w.xq + round_up((size_t)T * moe_mx_row_bytes(fmt, W->hidden), 256);
+  w.hq = w.xs + round_up((size_t)T * (size_t)(W->hidden / 32), 256);
+  w.hs = w.hq + round_up(n_slots * moe_mx_row_bytes(fmt, W->inter), 256);
+  w.table = w.hs + round_up(n_slots * (size_t)(W->inter / 32), 256);
+  w.total = w.table + round_up((size_t)moe::mx_tiles(T, k_total, W->n_experts) * 16, 256);
+  return w;
+}
+
+// The MX kernels address weight rows, scale rows and activation rows with 32-bit buffer offsets.
+bool mx_offsets_ok(const moe_proj& p, int N) {
+  return (int64_t)N * p.w_row_stride < INT32_MAX && (int64_t)N * p.s_row_stride < INT32_MAX;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_ffn_mx_workspace_bytes(int T, int k_total, const moe_expert_weights* W, moe_mx_format fmt) {
+  if (!W || T <= 0 || k_total <= 0 || W->hidden <= 0 || W->inter <= 0 || W->n_experts <= 0 ||
+      moe::mx_bits(fmt) == 0 || W->hidden % 32 != 0 || W->inter % 32 != 0)
+    return 0;
+  return mx_ws(T, k_total, W, fmt).total;
+}
+
+moe_status moe_expert_ffn_mx_workspace_layout(int T, int k_total, const moe_expert_weights* W, moe_mx_format fmt,
+                                              size_t* offsets) {
+  if (!W || !offsets) return MOE_ERR_NULL;
+  if (moe::mx_bits(fmt) == 0) return MOE_ERR_DTYPE;
+  if (T <= 0 || k_total <= 0 || W->hidden <= 0 || W->inter <= 0 || W->n_experts <= 0 || W->hidden % 32 != 0 ||
+      W->inter % 32 != 0)
+    return MOE_ERR_SHAPE;
+  const MxWs w = mx_ws(T, k_total, W, fmt);
+  offsets[0] = w.xq;
+  offsets[1] = w.xs;
+  offsets[2] = w.hq;
+  offsets[3] = w.hs;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn_mx(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                             moe_mx_format fmt, const int32_t* offsets, const int32_t* sorted_slot, float* y_slots,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (!W) return MOE_ERR_NULL;
+  if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_SHAPE;
+  if (W->fmt != MOE_W_MXFP4 || x_dtype != MOE_ACT_BF16 || moe::mx_bits(fmt) == 0) return MOE_ERR_DTYPE;
+  if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
+  if (!x || !offsets || !sorted_slot || !y_slots) return MOE_ERR_NULL;
+  const int H = W->hidden, I = W->inter;
+  moe_status st;
+  if ((st = check_proj(W->gate, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->up, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->down, W->fmt, W->n_experts, H, I)) != MOE_OK) return st;
+  if (H % 256 != 0 || I % 256 != 0) return MOE_ERR_SHAPE;
+  const moe_proj* ps[3] = {&W->gate, &W->up, &W->down};
+  for (const moe_proj* p : ps)
+    if (!al4(p->scales) || p->s_row_stride % 4 != 0 || p->s_expert_stride % 4 != 0) return MOE_ERR_ALIGN;
+  if (!mx_offsets_ok(W->gate, I) || !mx_offsets_ok(W->up, I) || !mx_offsets_ok(W->down, H)) return MOE_ERR_SHAPE;
+  const int64_t n_slots = (int64_t)T * k_total;
+  if ((int64_t)T * (int64_t)moe_mx_row_bytes(fmt, H) >= INT32_MAX ||
+      n_slots * (int64_t)moe_mx_row_bytes(fmt, I) >= INT32_MAX)
+    return MOE_ERR_SHAPE;
+  if (!al16(x) || !al16(y_slots) || !al4(offsets) || !al4(sorted_slot)) return MOE_ERR_ALIGN;
+  const MxWs w = mx_ws(T, k_total, W, fmt);
+  if (!workspace || workspace_bytes < w.total) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  uint8_t* ws = (uint8_t*)workspace;
+  moe::MxFfnArgs a;
+  a.fmt = fmt;
+  a.x = x;
+  a.T = T;
+  a.k_total = k_total;
+  a.n_experts = W->n_experts;
+  a.H = H;
+  a.I = I;
+  a.gate = dev(W->gate);
+  a.up = dev(W->up);
+  a.down = dev(W->down);
+  a.offsets = offsets;
+  a.sorted_slot = sorted_slot;
+  a.y_slots = y_slots;
+  a.xq = ws + w.xq;
+  a.xs = ws + w.xs;
+  a.hq = ws + w.hq;
+  a.hs = ws + w.hs;
+  a.table = ws + w.table;
+  return hip_status(moe::launch_ffn_mx(a, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------------------------
 moe_status moe_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,
                        void* stream) {
   if (T == 0) return MOE_OK;

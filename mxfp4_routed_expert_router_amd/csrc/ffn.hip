@@ -25,25 +25,14 @@
 // bits.  FP16 weights use the f16 MFMA with fp16 activations and an fp16 high/low pair for h.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kTileMaxExperts = 1024;  // == MOE_MAX_EXPERTS
-
-struct TileInfo {
-  int e, r0, nr;  // expert, first sorted row, rows in this tile (0 => no tile)
-};
-
-// Tile table, built once per expert-FFN call by ffn_tiles_kernel: entry t = (expert, first sorted
-// row, rows) of tile t, tiles numbered expert by expert (an expert with n rows owns
-// ceil(n / rows_per_tile) consecutive tiles); entries from the tile count up to the grid's bound
-// hold rows = 0.  The gate/up and down phases read the same table.
-struct TileEntry {
-  int e, r0, nr, pad;
-};
-
+// Builds the tile table (TileEntry, tiles.hpp) from the bucket offsets: one thread per expert
+// (MOE_MAX_EXPERTS <= 1024), a block-wide scan of the tile counts, then each expert's entries.
 __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restrict__ offsets, int n_experts,
                                                          int n_rows_max, int rows_per_tile, int n_entries,
                                                          TileEntry* __restrict__ table) {
@@ -81,32 +70,6 @@ __global__ __launch_bounds__(1024) void ffn_tiles_kernel(const int32_t* __restri
   }
   const int total = s_total;
   for (int t = total + tid; t < n_entries; t += blockDim.x) table[t] = TileEntry{0, 0, 0, 0};
-}
-
-// Entry `tile`, checked against the launch: an entry naming an expert outside [0, n_experts), more
-// than max_rows rows or rows outside [0, n_rows) (a table not built for this call) reads as empty,
-// so the kernels never index outside their buffers.
-__device__ __forceinline__ TileInfo get_tile(const TileEntry* __restrict__ table, int tile, int n_experts, int n_rows,
-                                             int max_rows) {
-  const TileEntry t = table[tile];
-  TileInfo r;
-  r.e = __builtin_amdgcn_readfirstlane(t.e);
-  r.r0 = __builtin_amdgcn_readfirstlane(t.r0);
-  r.nr = __builtin_amdgcn_readfirstlane(t.nr);
-  if (r.e < 0 || r.e >= n_experts || r.r0 < 0 || r.nr > max_rows || r.r0 > n_rows - r.nr) r.nr = 0;
-  return r;
-}
-
-// Work item of workgroup b.  Workgroups are dispatched round-robin over the 8 XCDs (b % 8), and
-// each XCD has its own L2.  Tile t runs all of its n-blocks on XCD t % 8, consecutively, so the
-// activation rows of an expert (and, in the down phase, its h rows written by the gate/up phase
-// with the same mapping) are fetched into one L2 instead of eight.  The grid holds
-// 8 * ceil(tiles / 8) * n_nblk workgroups.
-constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_work(int b, int n_nblk, int& tile, int& nblk) {
-  const int xcd = b % kXcds, slot = b / kXcds;
-  tile = (slot / n_nblk) * kXcds + xcd;
-  nblk = slot % n_nblk;
 }
 
 template <int FMT>
@@ -474,18 +437,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
 // share for the workgroup's 64 (matrix, row) pairs in a private LDS table filled once per work
 // item with row-contiguous dword loads, instead of one scale load per row and chunk.
 // ------------------------------------------------------------------------------------------------
-constexpr int kBufferFlags = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
-}
-__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
 // Two chunks in flight over the chunks [c0, c1) of a wave: register set A holds chunk c, B chunk
 // c+1, and A is refilled with c+2 right after chunk c is consumed.  The steady-state loop issues
 // its loads unconditionally (a load skipped on some path would make the compiler's vmcnt
@@ -518,8 +469,6 @@ __device__ __forceinline__ void run_pipeline_impl(int c0, int c1, Load& load, Co
 }
 
 constexpr int kMaxChunksPerWave = 64;  // K share of one wave <= 8192
-// A buffer offset past every descriptor range (ranges are < 2^31; offsets added to it stay < 2^32).
-constexpr uint32_t kOutOfRange = 0x80000000u;
 // Scale table of one wave: [pairs][cpw dwords]
 __host__ __device__ constexpr int stab_bytes(int pairs, int cpw) { return pairs * cpw * 4; }
 
@@ -1548,12 +1497,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
   }
 }
 
-// Upper bound of the number of tiles: A active experts hold at least one row each, so
-// sum_e ceil(n_e / R) <= A + (rows - A) / R with A <= min(n_experts, rows).
-int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {
-  const int64_t a = rows < n_experts ? rows : n_experts;
-  return a + (rows - a) / rows_per_tile;
-}
 
 constexpr int kNW = 4, kRT1 = 2, kRT2 = 4;
 
@@ -1704,6 +1647,13 @@ FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big) {
 
 size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big) {
   return (size_t)ffn_plan(T, k_total, n_experts, big).tiles * sizeof(TileEntry);
+}
+
+hipError_t launch_ffn_tiles(const int32_t* offsets, int n_experts, int n_rows, int rows_per_tile, int64_t n_entries,
+                            void* table, hipStream_t stream) {
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, n_rows, rows_per_tile, (int)n_entries,
+                                           (TileEntry*)table);
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,

@@ -41,6 +41,9 @@ bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gat
                    const ProjDev& down);
 FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big);
 size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big);
+// The tile table of `rows_per_tile`-row tiles for the bucket offsets (entries up to n_entries).
+hipError_t launch_ffn_tiles(const int32_t* offsets, int n_experts, int n_rows, int rows_per_tile, int64_t n_entries,
+                            void* table, hipStream_t stream);
 // The plan builds the tile table in `table`; the gate/up phase reads it and writes h; the down
 // phase reads both.
 hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,
@@ -51,6 +54,27 @@ hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_e
 hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream);
+
+// ---- expert FFN, MX mode (MXFP4 weights x MX-quantised activations on scaled MFMAs) ----
+int mx_bits(int fmt);                                  // 8, 6 or 4 bits per code; 0 for an unknown format
+int64_t mx_tiles(int T, int k_total, int n_experts);   // tile-table entries of an MX call
+struct MxFfnArgs {
+  int fmt;                                   // moe_mx_format
+  const void* x;                             // [T][H] bf16
+  int T, k_total, n_experts, H, I;
+  ProjDev gate, up, down;
+  const int32_t* offsets;
+  const int32_t* sorted_slot;
+  float* y_slots;
+  uint8_t *xq, *xs;                          // x codes [T][H/32 blocks], scales [T][H/32]
+  uint8_t *hq, *hs;                          // h codes [T*k_total][I/32 blocks], scales
+  void* table;                               // tile table
+};
+// Quantises a contiguous [n_rows][K] bf16/fp16 matrix into packed codes + E8M0 scales.
+hipError_t launch_mx_quantize(const void* x, bool x_fp16, int64_t n_rows, int K, int fmt, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
+// x quantisation, tile table, gate/up (writes h codes), down (writes y_slots).
+hipError_t launch_ffn_mx(const MxFfnArgs& a, hipStream_t stream);
 
 // ---- combine ----
 hipError_t launch_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,

@@ -1,0 +1,69 @@
+// Tile schedule shared by the expert-FFN kernels, and the buffer-load helpers they use.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+struct TileInfo {
+  int e, r0, nr;  // expert, first sorted row, rows in this tile (0 => no tile)
+};
+
+// Tile table, built once per expert-FFN call by ffn_tiles_kernel: entry t = (expert, first sorted
+// row, rows) of tile t, tiles numbered expert by expert (an expert with n rows owns
+// ceil(n / rows_per_tile) consecutive tiles); entries from the tile count up to the grid's bound
+// hold rows = 0.  The gate/up and down phases read the same table.
+struct TileEntry {
+  int e, r0, nr, pad;
+};
+
+// Entry `tile`, checked against the launch: an entry naming an expert outside [0, n_experts), more
+// than max_rows rows or rows outside [0, n_rows) (a table not built for this call) reads as empty,
+// so the kernels never index outside their buffers.
+__device__ __forceinline__ TileInfo get_tile(const TileEntry* __restrict__ table, int tile, int n_experts, int n_rows,
+                                             int max_rows) {
+  const TileEntry t = table[tile];
+  TileInfo r;
+  r.e = __builtin_amdgcn_readfirstlane(t.e);
+  r.r0 = __builtin_amdgcn_readfirstlane(t.r0);
+  r.nr = __builtin_amdgcn_readfirstlane(t.nr);
+  if (r.e < 0 || r.e >= n_experts || r.r0 < 0 || r.nr > max_rows || r.r0 > n_rows - r.nr) r.nr = 0;
+  return r;
+}
+
+// Work item of workgroup b.  Workgroups are dispatched round-robin over the 8 XCDs (b % 8), and
+// each XCD has its own L2.  Tile t runs all of its n-blocks on XCD t % 8, consecutively, so the
+// activation rows of an expert (and, in the down phase, its h rows written by the gate/up phase
+// with the same mapping) are fetched into one L2 instead of eight.  The grid holds
+// 8 * ceil(tiles / 8) * n_nblk workgroups.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_work(int b, int n_nblk, int& tile, int& nblk) {
+  const int xcd = b % kXcds, slot = b / kXcds;
+  tile = (slot / n_nblk) * kXcds + xcd;
+  nblk = slot % n_nblk;
+}
+
+// Upper bound of the number of tiles: A active experts hold at least one row each, so
+// sum_e ceil(n_e / R) <= A + (rows - A) / R with A <= min(n_experts, rows).
+inline int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {
+  const int64_t a = rows < n_experts ? rows : n_experts;
+  return a + (rows - a) / rows_per_tile;
+}
+
+// MUBUF buffer loads: a descriptor bounds every access, and a load past its range returns zeros
+// without touching memory.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// A buffer offset past every descriptor range (ranges are < 2^31; offsets added to it stay < 2^32).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+}  // namespace moe

@@ -127,7 +127,7 @@ class Oracle:
         lib.orc_mx_quantize.restype = None; lib.orc_mx_quantize.argtypes = [vp, i, i, i, vp, vp]
         lib.orc_mx_dequantize.restype = None; lib.orc_mx_dequantize.argtypes = [vp, vp, i, i, i, vp]
         lib.orc_expert_ffn_mx.restype = None
-        lib.orc_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(_Weights), i, vp, vp, vp, vp]
+        lib.orc_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(_Weights), i, vp, vp, vp, vp, vp]
 
     # ---- formats ----
     def e2m1(self, c: int) -> float: return self.lib.orc_e2m1(c)
@@ -175,15 +175,18 @@ class Oracle:
 
     def expert_ffn_mx(self, x: np.ndarray, x_fmt: int, k_total: int, W: ExpertWeights, act_fmt: int,
                       offsets: np.ndarray, sorted_slot: np.ndarray,
-                      slot_mask: Optional[np.ndarray] = None) -> np.ndarray:
+                      slot_mask: Optional[np.ndarray] = None, want_h: bool = False):
+        """-> y_slots [T*k_total][H]; with want_h also the fp64 h before quantisation per sorted row
+        [T*k_total][I] (NaN for rows not computed)."""
         x = np.ascontiguousarray(x, np.uint16)
         T = x.shape[0]
         offsets = np.ascontiguousarray(offsets, np.int32); sorted_slot = np.ascontiguousarray(sorted_slot, np.int32)
         mask = None if slot_mask is None else np.ascontiguousarray(slot_mask, np.uint8)
         y = np.full((T * k_total, W.hidden), np.nan)
+        h = np.full((T * k_total, W.inter), np.nan) if want_h else None
         self.lib.orc_expert_ffn_mx(_p(x), x_fmt, T, k_total, ctypes.byref(W.c), act_fmt, _p(offsets),
-                                   _p(sorted_slot), _p(mask), _p(y))
-        return y
+                                   _p(sorted_slot), _p(mask), _p(y), _p(h))
+        return (y, h) if want_h else y
 
     # ---- layer ----
     def route(self, x: np.ndarray, x_fmt: int, router: np.ndarray, bias: Optional[np.ndarray], top_k: int,

@@ -239,23 +239,30 @@ void orc_expert_apply(const orc_weights *W, int e, const double *xv, double *out
  * applied to all of its bucket's rows -- the same sums as orc_expert_apply, in the same k order.
  * slot_mask (optional): only slots with slot_mask[s] != 0 are computed; other rows of y_slots are
  * left untouched. */
-void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
-                    const int32_t *offsets, const int32_t *sorted_slot, const uint8_t *slot_mask,
-                    double *y_slots) {
+static void mx_round_trip(double *v, int K, int fmt);
+
+/* act_fmt = 0: the exact FFN.  act_fmt = an ORC_MX_* format: the MX mode, where the token's x row
+ * and each slot's h row go through the MX round trip before entering a projection. */
+static void grouped_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                        int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
+                        const uint8_t *slot_mask, double *y_slots, double *h_pre) {
   const int H = W->hidden, I = W->inter, E2 = W->n_experts;
   const int64_t n_slots = (int64_t)T * k_total;
   for (int e = 0; e < E2; ++e) {
     int r0 = offsets[e], r1 = offsets[e + 1];
     int n_rows = 0;
     int *slot = (int *)malloc(sizeof(int) * (size_t)(r1 - r0 + 1));
+    int *srow = (int *)malloc(sizeof(int) * (size_t)(r1 - r0 + 1));
     for (int r = r0; r < r1; ++r) {
       int s = sorted_slot[r];
       if (s < 0 || s >= n_slots) continue;
       if (slot_mask && !slot_mask[s]) continue;
+      srow[n_rows] = r;
       slot[n_rows++] = s;
     }
     if (n_rows == 0) {
       free(slot);
+      free(srow);
       continue;
     }
     double *xs = (double *)malloc(sizeof(double) * (size_t)n_rows * H);
@@ -263,6 +270,7 @@ void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_
     for (int i = 0; i < n_rows; ++i) {
       int t = slot[i] / k_total;
       for (int k = 0; k < H; ++k) xs[(int64_t)i * H + k] = act_value(x, x_fmt, (int64_t)t * H + k);
+      if (act_fmt) mx_round_trip(xs + (int64_t)i * H, H, act_fmt);
     }
 #pragma omp parallel for schedule(static)
     for (int n = 0; n < I; ++n) {
@@ -284,6 +292,12 @@ void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_
       free(wg);
       free(wu);
     }
+    if (h_pre)
+      for (int i = 0; i < n_rows; ++i) memcpy(h_pre + (int64_t)srow[i] * I, hs + (int64_t)i * I, sizeof(double) * (size_t)I);
+    if (act_fmt) {
+#pragma omp parallel for schedule(static)
+      for (int i = 0; i < n_rows; ++i) mx_round_trip(hs + (int64_t)i * I, I, act_fmt);
+    }
 #pragma omp parallel for schedule(static)
     for (int m = 0; m < H; ++m) {
       double *wd = (double *)malloc(sizeof(double) * (size_t)I);
@@ -299,7 +313,14 @@ void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_
     free(xs);
     free(hs);
     free(slot);
+    free(srow);
   }
+}
+
+void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                    const int32_t *offsets, const int32_t *sorted_slot, const uint8_t *slot_mask,
+                    double *y_slots) {
+  grouped_ffn(x, x_fmt, T, k_total, W, 0, offsets, sorted_slot, slot_mask, y_slots, NULL);
 }
 
 /* Weighted reduction [C31]: y[t,:] = sum_{j = 0..k_total-1, ascending} w[t,j] * y_slots[t*k_total+j,:].
@@ -405,68 +426,8 @@ static void mx_round_trip(double *v, int K, int fmt) {
 
 void orc_expert_ffn_mx(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
                        int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
-                       const uint8_t *slot_mask, double *y_slots) {
-  const int H = W->hidden, I = W->inter, E2 = W->n_experts;
-  const int64_t n_slots = (int64_t)T * k_total;
-  for (int e = 0; e < E2; ++e) {
-    int r0 = offsets[e], r1 = offsets[e + 1];
-    int n_rows = 0;
-    int *slot = (int *)malloc(sizeof(int) * (size_t)(r1 - r0 + 1));
-    for (int r = r0; r < r1; ++r) {
-      int s = sorted_slot[r];
-      if (s < 0 || s >= n_slots) continue;
-      if (slot_mask && !slot_mask[s]) continue;
-      slot[n_rows++] = s;
-    }
-    if (n_rows == 0) {
-      free(slot);
-      continue;
-    }
-    double *xs = (double *)malloc(sizeof(double) * (size_t)n_rows * H);
-    double *hs = (double *)malloc(sizeof(double) * (size_t)n_rows * I);
-    for (int i = 0; i < n_rows; ++i) {
-      int t = slot[i] / k_total;
-      for (int k = 0; k < H; ++k) xs[(int64_t)i * H + k] = act_value(x, x_fmt, (int64_t)t * H + k);
-      mx_round_trip(xs + (int64_t)i * H, H, act_fmt);
-    }
-#pragma omp parallel for schedule(static)
-    for (int n = 0; n < I; ++n) {
-      double *wg = (double *)malloc(sizeof(double) * (size_t)H);
-      double *wu = (double *)malloc(sizeof(double) * (size_t)H);
-      for (int k = 0; k < H; ++k) {
-        wg[k] = orc_weight(&W->gate, W->fmt, e, n, k);
-        wu[k] = orc_weight(&W->up, W->fmt, e, n, k);
-      }
-      for (int i = 0; i < n_rows; ++i) {
-        const double *xv = xs + (int64_t)i * H;
-        double g = 0.0, u = 0.0;
-        for (int k = 0; k < H; ++k) {
-          g += wg[k] * xv[k];
-          u += wu[k] * xv[k];
-        }
-        hs[(int64_t)i * I + n] = orc_silu(g) * u;
-      }
-      free(wg);
-      free(wu);
-    }
-#pragma omp parallel for schedule(static)
-    for (int i = 0; i < n_rows; ++i) mx_round_trip(hs + (int64_t)i * I, I, act_fmt);
-#pragma omp parallel for schedule(static)
-    for (int m = 0; m < H; ++m) {
-      double *wd = (double *)malloc(sizeof(double) * (size_t)I);
-      for (int n = 0; n < I; ++n) wd[n] = orc_weight(&W->down, W->fmt, e, m, n);
-      for (int i = 0; i < n_rows; ++i) {
-        const double *hv = hs + (int64_t)i * I;
-        double acc = 0.0;
-        for (int n = 0; n < I; ++n) acc += wd[n] * hv[n];
-        y_slots[(int64_t)slot[i] * H + m] = acc;
-      }
-      free(wd);
-    }
-    free(xs);
-    free(hs);
-    free(slot);
-  }
+                       const uint8_t *slot_mask, double *y_slots, double *h_pre) {
+  grouped_ffn(x, x_fmt, T, k_total, W, act_fmt, offsets, sorted_slot, slot_mask, y_slots, h_pre);
 }
 
 /* ------------------------------------------------------------------------------------------ */

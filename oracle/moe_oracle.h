@@ -93,10 +93,12 @@ void orc_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int n_rows, 
                        double *out);
 /* The grouped expert FFN of the MX mode: like orc_expert_ffn, with the token's x row and each
  * slot's h row replaced by their MX round trip (quantize, then dequantize) before they enter a
- * projection.  Weights stay the exact decoded MXFP4 values; all arithmetic is fp64. */
+ * projection.  Weights stay the exact decoded MXFP4 values; all arithmetic is fp64.
+ * h_pre (optional, [n_slots][I] indexed by sorted row): the fp64 h of every computed row before
+ * its quantisation. */
 void orc_expert_ffn_mx(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
                        int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
-                       const uint8_t *slot_mask, double *y_slots);
+                       const uint8_t *slot_mask, double *y_slots, double *h_pre);
 
 /* ---- cross-check forms ---- */
 void orc_layer_bruteforce(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,

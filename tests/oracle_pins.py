@@ -587,7 +587,7 @@ def check_expert_ffn_mx_vs_numpy(o):
         W = ExpertWeights.from_layer(L)
         r = o.route(L.x, X_BF16, L.router, L.bias, 2)
         b = o.bucket(r["ids"], 3)
-        ys = o.expert_ffn_mx(L.x, X_BF16, 2, W, fmt, b["offsets"], b["sorted_slot"])
+        ys, hp = o.expert_ffn_mx(L.x, X_BF16, 2, W, fmt, b["offsets"], b["sorted_slot"], want_h=True)
         Wg, Wu, Wd = np_weights(L)
         X = np_act(L.x, X_BF16)
         rt = lambda a: o.mx_dequantize(*o.mx_quantize(a, fmt), fmt)
@@ -596,6 +596,7 @@ def check_expert_ffn_mx_vs_numpy(o):
             e, t = r["ids"].reshape(-1)[s], s // 2
             h = np_silu(Xq[t:t + 1] @ Wg[e].T) * (Xq[t:t + 1] @ Wu[e].T)
             close(ys[s], (rt(h) @ Wd[e].T)[0], 1e-10, f"mx ffn fmt={fmt} slot={s}")
+            close(hp[b["slot_pos"][s]], h[0], 1e-12, f"mx ffn h before quantisation fmt={fmt} slot={s}")
         ye = o.expert_ffn(L.x, X_BF16, 2, W, b["offsets"], b["sorted_slot"])
         assert not np.allclose(ys, ye, rtol=0, atol=0)  # the round trips change the result
 

@@ -162,6 +162,51 @@ def test_expert_ffn_plan_validation():
     assert plan(W, kt=0) == SHAPE
 
 
+def test_mx_validation():
+    L = m.lib()
+    FP8, FP4, FP6 = m.MOE_MX_FP8_E4M3, m.MOE_MX_FP4_E2M1, m.MOE_MX_FP6_E2M3
+    assert [L.moe_mx_row_bytes(f, 256) for f in (FP8, FP4, FP6)] == [256, 128, 192]
+    assert L.moe_mx_row_bytes(FP8, 48) == 0 and L.moe_mx_row_bytes(9, 256) == 0
+    q = lambda **k: L.moe_mx_quantize(k.get("x", fake()), k.get("xdt", 0), k.get("n", 4), k.get("K", 256),
+                                      k.get("f", FP8), k.get("c", fake(0x1000)), k.get("s", fake(0x2000)), None)
+    assert L.moe_mx_quantize(None, 0, 0, 256, FP8, None, None, None) == OK
+    assert q(n=-1) == SHAPE
+    assert q(K=0) == SHAPE
+    assert q(K=48) == BLOCK
+    assert q(f=0) == DTYPE and q(f=4) == DTYPE and q(xdt=3) == DTYPE
+    assert q(x=None) == NULL and q(c=None) == NULL and q(s=None) == NULL
+    assert q(x=fake(8)) == ALIGN and q(c=fake(0x1008)) == ALIGN
+
+    def mx(W, T=4, kt=2, f=FP6, xdt=0, ws=fake(0x4000), wsb=None, x=fake()):
+        need = L.moe_expert_ffn_mx_workspace_bytes(T, kt, ctypes.byref(W), f)
+        return L.moe_expert_ffn_mx(x, xdt, T, kt, ctypes.byref(W), f, fake(0x100), fake(0x200), fake(0x300),
+                                   ws, need if wsb is None else wsb, None)
+
+    W = weights(H=256, I=512, hidden=256, inter=512)
+    for name, (N, K) in (("gate", (512, 256)), ("up", (512, 256)), ("down", (256, 512))):
+        p = getattr(W, name)
+        p.w_row_stride, p.w_expert_stride = K // 2, N * K // 2
+        p.s_row_stride, p.s_expert_stride = K // 32, N * K // 32
+    need = L.moe_expert_ffn_mx_workspace_bytes(4, 2, ctypes.byref(W), FP6)
+    # x codes + x scales + h codes + h scales + tile table
+    assert need >= 4 * 192 + 4 * 8 + 8 * 384 + 8 * 16
+    assert L.moe_expert_ffn_mx(None, 0, 0, 2, None, FP6, None, None, None, None, 0, None) == OK
+    assert mx(W, f=0) == DTYPE
+    assert mx(W, xdt=1) == DTYPE
+    assert mx(weights(fmt=m.MOE_W_FP16, hidden=256, inter=512), xdt=0) == DTYPE
+    assert mx(W, wsb=need - 1) == WORKSPACE
+    assert mx(W, ws=fake(0x4008)) == ALIGN
+    assert mx(W, x=None) == NULL
+    assert mx(weights(hidden=96, inter=512)) == SHAPE      # hidden not a multiple of 256
+    assert mx(weights(hidden=256, inter=96)) == SHAPE      # inter not a multiple of 256
+    W2 = weights(H=256, I=512, hidden=256, inter=512)
+    W2.gate.s_row_stride = 10
+    assert mx(W2) == ALIGN                                  # scale rows must be 4-byte aligned
+    W3 = weights(H=256, I=512, hidden=256, inter=512)
+    W3.up.scales = P + 0x20002
+    assert mx(W3) == ALIGN
+
+
 def test_combine_and_dequant_validation():
     L = m.lib()
     assert L.moe_combine(None, None, 0, 2, 64, None, None) == OK

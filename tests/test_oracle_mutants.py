@@ -45,7 +45,7 @@ MUTANTS = {
                           "int orc_mx_emax(int fmt) { return fmt == ORC_MX_FP8_E4M3 ? 8 : 1; }"),
     "MX scale from ceil(log2)": ("int c = (ex - 1) - orc_mx_emax(fmt) + 127;", "int c = ex - orc_mx_emax(fmt) + 127;"),
     "MX sign dropped": ("return signbit(q) ? (best | (1 << (bits - 1))) : best;", "return best;"),
-    "MX x round trip skipped": ("      mx_round_trip(xs + (int64_t)i * H, H, act_fmt);\n", "\n"),
+    "MX x round trip skipped": ("if (act_fmt) mx_round_trip(xs + (int64_t)i * H, H, act_fmt);", ";"),
     "MX h round trip skipped": ("for (int i = 0; i < n_rows; ++i) mx_round_trip(hs + (int64_t)i * I, I, act_fmt);",
                                 "for (int i = 0; i < n_rows; ++i) (void)0;"),
     "MX block of 16": ("const double *blk = v + (int64_t)r * K + 32 * b;\n      double amax = 0.0;\n      for (int i = 0; i < 32; ++i)",

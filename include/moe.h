@@ -216,7 +216,7 @@ moe_status moe_mx_quantize(const void *x, moe_act_dtype x_dtype, int n_rows, int
  *   h = SiLU(g) * u (fp32),  hq = dequant(quant(h)),  y_slots[s,:] = W_down[e] hq  (fp32),
  * quant/dequant being the block quantisation above along hidden (x) and inter (h).  Weights must
  * be MXFP4 and x bf16.  hidden and inter must be multiples of 256; scale pointers and strides
- * multiples of 4 bytes.  Arguments otherwise as for moe_expert_ffn, with the workspace from
+ * multiples of 8 bytes.  Arguments otherwise as for moe_expert_ffn, with the workspace from
  * moe_expert_ffn_mx_workspace_bytes (it holds the x and h codes and the tile table).
  * Errors: NULL, SHAPE (also hidden or inter not a multiple of 256, or buffers past 2^31 bytes),
  * BLOCK, ALIGN, DTYPE (weights not MXFP4, x not bf16, unknown format), WORKSPACE, HIP. */

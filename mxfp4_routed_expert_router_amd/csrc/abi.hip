@@ -323,7 +323,8 @@ moe_status moe_expert_ffn_mx(const void* x, moe_act_dtype x_dtype, int T, int k_
   if (H % 256 != 0 || I % 256 != 0) return MOE_ERR_SHAPE;
   const moe_proj* ps[3] = {&W->gate, &W->up, &W->down};
   for (const moe_proj* p : ps)
-    if (!al4(p->scales) || p->s_row_stride % 4 != 0 || p->s_expert_stride % 4 != 0) return MOE_ERR_ALIGN;
+    if (((uintptr_t)p->scales & 7u) != 0 || p->s_row_stride % 8 != 0 || p->s_expert_stride % 8 != 0)
+      return MOE_ERR_ALIGN;
   if (!mx_offsets_ok(W->gate, I) || !mx_offsets_ok(W->up, I) || !mx_offsets_ok(W->down, H)) return MOE_ERR_SHAPE;
   const int64_t n_slots = (int64_t)T * k_total;
   if ((int64_t)T * (int64_t)moe_mx_row_bytes(fmt, H) >= INT32_MAX ||

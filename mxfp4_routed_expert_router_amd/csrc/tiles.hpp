@@ -62,6 +62,16 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+__device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// With a wave-uniform offset part in an SGPR (added to the per-lane offset).
+__device__ __forceinline__ u32x4 bld16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ uint32_t bld4s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
 
 // A buffer offset past every descriptor range (ranges are < 2^31; offsets added to it stay < 2^32).
 constexpr uint32_t kOutOfRange = 0x80000000u;

@@ -203,7 +203,7 @@ def test_mx_validation():
     W2.gate.s_row_stride = 10
     assert mx(W2) == ALIGN                                  # scale rows must be 4-byte aligned
     W3 = weights(H=256, I=512, hidden=256, inter=512)
-    W3.up.scales = P + 0x20002
+    W3.up.scales = P + 0x20004
     assert mx(W3) == ALIGN
 
 

@@ -172,9 +172,10 @@ template <int F>
 struct MxTile {
   static constexpr int kBB = 4 * Mx<F>::kBits;             // bytes per 32-value block
   static constexpr int kRowStep = 8 * kBB;                 // code bytes of one token per step
-  // LDS row stride: FP6 rows are read as 8-byte pieces by 16 lanes of consecutive rows, so their
-  // stride is 2 (mod 4) dwords... (200 bytes: the 16 rows hit 16 distinct bank pairs); FP8 and
-  // FP4 rows are read as 16-byte pieces by 8 lanes, so 16 bytes of padding spread them.
+  // LDS row stride.  FP6 fragments are read as 8-byte pieces, 16 lanes (16 consecutive rows) at a
+  // time: a 200-byte stride (50 dwords, 18 mod 32 banks) puts the 16 rows on 16 distinct bank
+  // pairs.  FP8 and FP4 fragments are read as 16-byte pieces, 8 lanes at a time: 16 bytes of
+  // padding (a stride of 4 mod 32 banks) spreads 8 rows over all 32 banks.
   static constexpr int kRS = kRowStep + (Mx<F>::kBits == 6 ? 8 : 16);
   static constexpr int kCodes = kMxTok * kRS;              // code bytes of a stage
   static constexpr int kScales = kCodes;                   // 8 scale bytes per token
@@ -193,7 +194,6 @@ template <int GU>
 struct WRows {
   static constexpr int kPerWave = GU ? 64 : 128;  // rows of I (of each of gate, up) or of H
 };
-
 
 // Codes of 16 consecutive values (half a block) packed as in the block layout: 2 * bits bytes.
 template <int F>
@@ -357,11 +357,11 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
         load_a(s_next2);
       }
       if (!active) continue;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      // B fragment (column tile b, position p) and its scale byte; the next tile's fragment is
+      // read before the current tile's MFMAs, so LDS latency overlaps the matrix work
+      auto load_bf = [&](int b, v8i& bf, int& sb) {
         const uint8_t* row = base + (16 * b + l16) * P::kRS;
         const uint32_t bsc = *reinterpret_cast<const uint32_t*>(base + P::kCodes + (16 * b + l16) * 8 + 4 * p);
-        v8i bf;
         if constexpr (Mx<F>::kBits == 8) {
           const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 128 * p + 16 * q);
           const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 128 * p + 64 + 16 * q);
@@ -376,14 +376,21 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
           const u32x4 x0 = *reinterpret_cast<const u32x4*>(row + 16 * (4 * p + q));
           bf = v8i{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], 0, 0, 0, 0};
         }
-        const int sb = (int)((bsc >> (8 * q)) & 0xFFu);
+        sb = (int)((bsc >> (8 * q)) & 0xFFu);
+      };
+      v8i bf[2];
+      int sb[2];
+      load_bf(0, bf[0], sb[0]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b + 1 < NB) load_bf(b + 1, bf[(b + 1) & 1], sb[(b + 1) & 1]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const u32x4 c = af4[t];
           const v8i af = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
           const int sa = (int)((was[t] >> (8 * q)) & 0xFFu);
-          acc[t][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[t][b], kWFmtFp4, Mx<F>::kMfma,
-                                                                       0, sa, 0, sb);
+          acc[t][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[b & 1], acc[t][b], kWFmtFp4,
+                                                                       Mx<F>::kMfma, 0, sa, 0, sb[b & 1]);
         }
       }
     }

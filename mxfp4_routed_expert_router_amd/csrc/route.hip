@@ -35,22 +35,30 @@ __device__ __forceinline__ bf16x8 to_bf16x8_rne(const float (&v)[8]) {
 // full memory latency per k-step).
 constexpr int kU = 4;
 
-template <int XF16, int VEC>
+// MT: 16-token tiles per wave (more than one when T is large: each router-weight fragment, and its
+// three-way split, then serves MT token tiles, which cuts the weight re-reads through L2).
+template <int XF16, int VEC, int MT>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ w, int E, int ks_per_split,
                                                           float* __restrict__ partial) {
   const int lane = threadIdx.x, l16 = lane & 15, lq = lane >> 4;
   const int e = blockIdx.x * 16 + l16;
-  const int t = blockIdx.y * 16 + l16;
   const int split = blockIdx.z;
   const int nks = (H + 31) / 32;
   const int ks0 = split * ks_per_split, ks1 = min(ks0 + ks_per_split, nks);
   const float* wrow = w + (int64_t)(e < E ? e : 0) * H;
-  const uint16_t* xrow = x + (int64_t)(t < T ? t : 0) * H;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = (blockIdx.y * MT + mt) * 16 + l16;
+    xrow[mt] = x + (int64_t)(t < T ? t : 0) * H;
+  }
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int ks = ks0; ks < ks1; ks += kU) {
     float wv[kU][8];
-    uint16_t xv[kU][8];
+    uint16_t xv[kU][MT][8];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       // k-steps past the slice reload the slice's last step and are skipped below
@@ -58,18 +66,22 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
       if (VEC && k + 8 <= H) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(wrow + k);
         const f32x4 b = *reinterpret_cast<const f32x4*>(wrow + k + 4);
-        const u32x4 q = ld16(xrow + k);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           wv[u][j] = a[j];
           wv[u][4 + j] = b[j];
         }
-        __builtin_memcpy(xv[u], &q, 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x4 q = ld16(xrow[mt] + k);
+          __builtin_memcpy(xv[u][mt], &q, 16);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           wv[u][j] = (k + j < H) ? wrow[k + j] : 0.f;
-          xv[u][j] = (k + j < H) ? xrow[k + j] : 0;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xv[u][mt][j] = (k + j < H) ? xrow[mt][k + j] : 0;
         }
       }
     }
@@ -81,10 +93,12 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 #pragma unroll
         for (int j = 0; j < 8; ++j) wv[u][j] = 0.f;
       }
-      if (t >= T) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xv[u][j] = 0;
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        if ((blockIdx.y * MT + mt) * 16 + l16 >= T) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[u][mt][j] = 0;
+        }
       const bf16x8 hi = to_bf16x8_rne(wv[u]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) r[j] = wv[u][j] - (float)hi[j];
@@ -92,37 +106,44 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 #pragma unroll
       for (int j = 0; j < 8; ++j) r[j] -= (float)mid[j];
       const bf16x8 lo = to_bf16x8_rne(r);
-      if (XF16) {
-        // fp16 -> fp32 exactly, then two bf16 terms (8 + 8 >= 11 significant bits)
-        float xf[8], xr2[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xf[j] = (float)bitcast<_Float16>(xv[u][j]);
-        const bf16x8 xh = to_bf16x8_rne(xf);
+      for (int mt = 0; mt < MT; ++mt) {
+        if (XF16) {
+          // fp16 -> fp32 exactly, then two bf16 terms (8 + 8 >= 11 significant bits)
+          float xf[8], xr2[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xr2[j] = xf[j] - (float)xh[j];
-        const bf16x8 xl = to_bf16x8_rne(xr2);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xl, acc, 0, 0, 0);
-      } else {
-        bf16x8 b;
-        __builtin_memcpy(&b, xv[u], 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);
+          for (int j = 0; j < 8; ++j) xf[j] = (float)bitcast<_Float16>(xv[u][mt][j]);
+          const bf16x8 xh = to_bf16x8_rne(xf);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xr2[j] = xf[j] - (float)xh[j];
+          const bf16x8 xl = to_bf16x8_rne(xr2);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xh, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xh, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xh, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xl, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xl, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xl, acc[mt], 0, 0, 0);
+        } else {
+          bf16x8 b;
+          __builtin_memcpy(&b, xv[u][mt], 16);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[mt], 0, 0, 0);
+        }
       }
     }
   }
-  // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16
-  if (t < T) {
-    float* out = partial + ((int64_t)split * T + t) * E;
+  // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16 of each token tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ee = blockIdx.x * 16 + 4 * lq + i;
-      if (ee < E) out[ee] = acc[i];
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = (blockIdx.y * MT + mt) * 16 + l16;
+    if (t < T) {
+      float* out = partial + ((int64_t)split * T + t) * E;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ee = blockIdx.x * 16 + 4 * lq + i;
+        if (ee < E) out[ee] = acc[mt][i];
+      }
     }
   }
 }
@@ -232,8 +253,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 // Each wave computes one 16-expert x 16-token tile over a K slice.  The logits are latency-bound,
 // so many small waves (about 2048) beat fewer waves that reuse each router-weight fragment for
 // more tokens (measured).
+// Token tiles per wave: more than one once there are many more 16 x 16 tiles than waves needed.
+int route_mt(int T, int E) {
+  const int64_t g1 = (int64_t)((E + 15) / 16) * ((T + 15) / 16);
+  return g1 >= 4 * 2048 ? 4 : (g1 >= 2 * 2048 ? 2 : 1);
+}
+
 int route_splits(int T, int H, int E) {
-  const int64_t groups = (int64_t)((E + 15) / 16) * ((T + 15) / 16);
+  const int mt = route_mt(T, E);
+  const int64_t groups = (int64_t)((E + 15) / 16) * ((T + 16 * mt - 1) / (16 * mt));
   const int nks = (H + 31) / 32;
   int s = (int)((2048 + groups - 1) / groups);
   const int cap = nks / 4 < 1 ? 1 : nks / 4;  // at least 4 k-steps of 32 per slice
@@ -247,9 +275,12 @@ template <int XF16, int VEC>
 void launch_logits(const void* x, int T, int H, const float* w, int E, int splits, float* partial, hipStream_t st) {
   const int nks = (H + 31) / 32;
   const int per = (nks + splits - 1) / splits;
-  const dim3 g((E + 15) / 16, (T + 15) / 16, splits);
+  const int mt = route_mt(T, E);
+  const dim3 g((E + 15) / 16, (T + 16 * mt - 1) / (16 * mt), splits);
   const uint16_t* xx = (const uint16_t*)x;
-  route_logits_kernel<XF16, VEC><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  if (mt == 4) route_logits_kernel<XF16, VEC, 4><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else if (mt == 2) route_logits_kernel<XF16, VEC, 2><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
 }
 
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,

@@ -205,6 +205,12 @@ def test_mx_validation():
     W3 = weights(H=256, I=512, hidden=256, inter=512)
     W3.up.scales = P + 0x20004
     assert mx(W3) == ALIGN
+    offs = (ctypes.c_size_t * 4)()
+    assert L.moe_expert_ffn_mx_workspace_layout(4, 2, ctypes.byref(W), FP6, offs) == OK
+    assert 0 == offs[0] < offs[1] < offs[2] < offs[3] < need and all(o % 256 == 0 for o in offs)
+    assert L.moe_expert_ffn_mx_workspace_layout(4, 2, ctypes.byref(W), 7, offs) == DTYPE
+    assert L.moe_expert_ffn_mx_workspace_layout(0, 2, ctypes.byref(W), FP6, offs) == SHAPE
+    assert L.moe_expert_ffn_mx_workspace_layout(4, 2, None, FP6, offs) == NULL
 
 
 def test_combine_and_dequant_validation():

@@ -323,3 +323,38 @@ def test_mx_deterministic():
     a = sync_np(layer.forward(t["x"])).copy()
     b = sync_np(layer.forward(t["x"]))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_mx_zero_tokens():
+    L = host_layer("tiny", 16)
+    t = synth.to_torch(L, DEV)
+    W = expert_weights(t)
+    x0 = t["x"][:0]
+    off = torch.zeros(9, dtype=torch.int32, device=DEV)
+    y = moe.moe_expert_ffn_mx(x0, W, "fp6", off, torch.zeros(0, dtype=torch.int32, device=DEV), 2)
+    assert y.shape == (0, 256)
+    c, s = moe.moe_mx_quantize(x0, "fp8")
+    torch.cuda.synchronize()
+
+
+def test_mx_dropped_slots(orc):
+    """Out-of-range ids: bucketing drops them, the MX FFN leaves their rows untouched and the
+    valid rows still match the MX oracle exactly (MXFP6)."""
+    L = host_layer("tiny", 16)
+    r = orc.route(L.x, oracle.X_BF16, L.router, None, 2)
+    ids = r["ids"].copy()
+    ids[3, 1] = 8
+    ids[7, 0] = -1
+    t = synth.to_torch(L, DEV)
+    b = moe.moe_bucket(torch.from_numpy(ids).to(DEV), 8)
+    sentinel = torch.full((16 * 2, 256), 12345.0, dtype=torch.float32, device=DEV)
+    y = moe.moe_expert_ffn_mx(t["x"], expert_weights(t), "fp6", b.offsets, b.sorted_slot, 2, out=sentinel)
+    got = sync_np(y)
+    ob = orc.bucket(ids, 8)
+    W = oracle.ExpertWeights.from_layer(L)
+    ref = orc.expert_ffn_mx(L.x, oracle.X_BF16, 2, W, oracle.MX_FP6_E2M3, ob["offsets"], ob["sorted_slot"])
+    dropped = [3 * 2 + 1, 7 * 2 + 0]
+    assert np.all(got[dropped] == 12345.0)
+    keep = np.setdiff1d(np.arange(32), dropped)
+    assert np.array_equal(got[keep], ref[keep].astype(np.float32))
+

@@ -164,9 +164,18 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __rest
 }
 
 // ---- the scaled-MFMA FFN kernels ----
-constexpr int kMxNW = 4;       // waves per workgroup
+constexpr int kMxNW = 8;       // waves per workgroup (two per SIMD)
 constexpr int kMxTok = 128;    // sorted rows (tokens) per tile
 constexpr int kMxStepK = 256;  // K per step: 8 blocks of 32 (two MFMA K positions of 128)
+
+// Weight rows of a wave: 32 rows of I of each of gate and up (gate/up), or 64 rows of H (down), as
+// four 16-row MFMA tiles: two of gate then two of up, or four of down.
+template <bool GU>
+struct WRows {
+  static constexpr int kPerMatrix = GU ? 32 : 64;  // rows per wave of each matrix
+  static constexpr int kTiles = kPerMatrix / 16;   // MFMA tiles per matrix
+};
+constexpr int kMxRows = 64;  // weight rows per wave (both phases)
 
 template <int F>
 struct MxTile {
@@ -180,28 +189,24 @@ struct MxTile {
   static constexpr int kCodes = kMxTok * kRS;              // code bytes of a stage
   static constexpr int kScales = kCodes;                   // 8 scale bytes per token
   static constexpr int kStage = kScales + kMxTok * 8;      // one stage of the shared activation ring
-  // After the two stages: per wave, a private copy of its 128 weight rows for one step (128 bytes
+  // After the two stages: per wave, a private copy of its 64 weight rows for one step (128 bytes
   // per row, 16-byte pieces XOR-swizzled by row) and their 8 scale bytes.
   static constexpr int kPrivA = 2 * kStage;
-  static constexpr int kPrivS = kPrivA + kMxNW * 128 * 128;
-  static constexpr int kLds = kPrivS + kMxNW * 128 * 8;
+  static constexpr int kPrivS = kPrivA + kMxNW * kMxRows * 128;
+  static constexpr int kLds = kPrivS + kMxNW * kMxRows * 8;
   static constexpr int kPieces = kRowStep / 16;            // 16-byte pieces per token per step
   static constexpr int kLPT = kMxTok * kPieces / (64 * kMxNW);  // fill loads per thread per step
   static_assert(kLPT * 64 * kMxNW == kMxTok * kPieces, "a step of codes over the workgroup");
 };
 
-template <int GU>
-struct WRows {
-  static constexpr int kPerWave = GU ? 64 : 128;  // rows of I (of each of gate, up) or of H
-};
-
-// Codes of 16 consecutive values (half a block) packed as in the block layout: 2 * bits bytes.
+// Codes of 8 consecutive values (a quarter block) packed as in the block layout: bits bytes, in
+// dw[0] and (FP6, FP8) dw[1].
 template <int F>
-__device__ __forceinline__ void mx_pack_half(const float (&v)[16], float inv, uint32_t (&dw)[4]) {
+__device__ __forceinline__ void mx_pack_quarter(const float (&v)[8], float inv, uint32_t (&dw)[2]) {
+  dw[0] = 0;
+  dw[1] = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dw[i] = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const uint32_t c = mx_encode<F>(v[j] * inv);
     constexpr int B = Mx<F>::kBits;
     const int bit = B * j, w = bit >> 5, o = bit & 31;
@@ -215,8 +220,13 @@ __device__ __forceinline__ void mx_pack_half(const float (&v)[16], float inv, ui
 //   FP8 operand: values 16(q%2)..+15 of K-blocks q/2 and 2 + q/2;
 //   E8M0 scale of a lane: K-block q of its row or column;
 //   D: lane l holds column l%16, rows 4q + i in accumulator i.
-// A 256-wide step holds positions p = 0, 1 over its K-blocks 4p .. 4p+3 in memory order, so the
-// four lanes of a weight row read one contiguous 64-byte piece per position.
+// A 256-wide step holds positions p = 0, 1 over its K-blocks 4p .. 4p+3 in memory order.
+//
+// Weight rows are assigned to tile rows so that a lane quarter's accumulators cover consecutive
+// rows: row 4q + i of the wave's tile t of a matrix is the matrix row n0 + (R/4) q + 4t + i (R =
+// the wave's rows of that matrix).  Lane quarter q then holds rows n0 + (R/4) q .. + R/4 - 1 of
+// its column (token): a quarter of h's 32-value block in the gate/up epilogue, 64 contiguous
+// bytes of y in the down epilogue.
 template <int F, bool GU, int NB>
 __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8_t* __restrict__ act,
                                         const uint8_t* __restrict__ act_s, int n_act_rows, int k_total, int K,
@@ -228,14 +238,14 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, q = lane >> 4;
-  constexpr int RPW = WRows<GU>::kPerWave;
-  const int n0 = (nblk * kMxNW + wave) * RPW;
-  const bool active = n0 < N;  // N % RPW == 0, so a wave's rows are all in or all out
+  constexpr int R = WRows<GU>::kPerMatrix, TM = WRows<GU>::kTiles, TA = 4;
+  const int n0 = (nblk * kMxNW + wave) * R;
+  const bool active = n0 < N;  // N % R == 0, so a wave's rows are all in or all out
   const int e = ti.e;
   const int n_steps = K / kMxStepK;
   const int RB = (K / 32) * P::kBB, KB = K / 32;
 
-  // ---- LDS fill addressing: piece i of a thread -> token (threadIdx.x + 256 i) / kPieces
+  // ---- LDS fill addressing: piece i of a thread -> token (threadIdx.x + 512 i) / kPieces
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(act, (int64_t)n_act_rows * RB);
   const __amdgpu_buffer_rsrc_t asr = make_rsrc(act_s, (int64_t)n_act_rows * KB);
   auto act_row = [&](int tok) -> int {
@@ -247,28 +257,32 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
       return ti.r0 + tok;
     }
   };
-  uint32_t aoff[P::kLPT], aw[P::kLPT];
+  uint32_t aoff[P::kLPT];
 #pragma unroll
   for (int i = 0; i < P::kLPT; ++i) {
     const int qq = threadIdx.x + 64 * kMxNW * i, tok = qq / P::kPieces, col = qq % P::kPieces;
     const int row = act_row(tok);
     aoff[i] = row >= 0 ? (uint32_t)row * (uint32_t)RB + 16u * col : kOutOfRange;
-    aw[i] = (uint32_t)(tok * P::kRS + 16 * col);
   }
+  auto aw = [&](int i) -> uint32_t {  // LDS offset of fill piece i (recomputed, no register held)
+    const int qq = threadIdx.x + 64 * kMxNW * i, tok = qq / P::kPieces, col = qq % P::kPieces;
+    return (uint32_t)(tok * P::kRS + 16 * col);
+  };
+  // The tile's 128 x 8 scale bytes of a step: one dword per thread of the first four waves.
+  const bool sfill = threadIdx.x < 2 * kMxTok;
   uint32_t asoff, asw;
   {
-    const int tok = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int tok = (threadIdx.x >> 1) & (kMxTok - 1), half = threadIdx.x & 1;
     const int row = act_row(tok);
     asoff = row >= 0 ? (uint32_t)row * (uint32_t)KB + 4u * half : kOutOfRange;
     asw = (uint32_t)(P::kCodes + tok * 8 + 4 * half);
   }
 
-  // ---- weights: wave row r (0..127) is row r % 16 of tile t = r / 16, i.e. row n0 + 16*(t % 4) +
-  //      r % 16 of gate (t < 4) / up (t >= 4) for gate/up, row n0 + r of down.  A step's 128 bytes
-  //      of the wave's rows are loaded as whole 128-byte lines (8 lanes per row, 8 rows per
-  //      instruction), written to the wave's private LDS copy with piece c of row r in slot
-  //      c ^ (r & 7), and read back in MFMA layout (conflict-free both ways).  Loads run two steps
-  //      ahead of the MFMAs: staged in registers one step, in LDS the next.
+  // ---- weights: wave row r (0..63) is row r of gate (r < 32) / up for gate/up, row n0 + r of
+  //      down.  A step's 128 bytes of the wave's rows are loaded as whole 128-byte lines (8 lanes
+  //      per row, 8 rows per instruction), written to the wave's private LDS copy with piece c of
+  //      row r in slot c ^ (r & 7), and read back in MFMA layout (conflict-free both ways).  Loads
+  //      run two steps ahead of the MFMAs: staged in registers one step, in LDS the next.
   const int64_t wrows = (int64_t)N - 1;
   const __amdgpu_buffer_rsrc_t wr0 = make_rsrc(w0.w + (int64_t)e * w0.we, wrows * w0.wr + K / 2);
   const __amdgpu_buffer_rsrc_t wr1 = make_rsrc(w1.w + (int64_t)e * w1.we, wrows * w1.wr + K / 2);
@@ -277,83 +291,94 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   const int lr = lane >> 3, lc = lane & 7;  // line loads: row lr of 8, 16-byte piece lc
   const uint32_t lv0 = active ? (uint32_t)((n0 + lr) * w0.wr) + 16u * lc : kOutOfRange;
   const uint32_t lv1 = active ? (uint32_t)((n0 + lr) * w1.wr) + 16u * lc : kOutOfRange;
-  const uint32_t wt0 = (uint32_t)(16 * w0.wr), wt1 = (uint32_t)(16 * w1.wr);  // per 16-row tile
-  // scale rows of lane l: wave rows l and 64 + l
-  const uint32_t sv0 = active ? (uint32_t)((n0 + lane) * w0.sr) : kOutOfRange;
-  const uint32_t sv1 = active ? (GU ? (uint32_t)((n0 + lane) * w1.sr) : (uint32_t)((n0 + 64 + lane) * w0.sr)) : kOutOfRange;
-  u32x4 ast[16];
-  u32x2 sst[2];
+  // scale row of lane l: wave row l (gate/up: gate row l for l < 32, up row l - 32)
+  const bool sup = GU && lane >= 32;
+  const uint32_t sv = active ? (uint32_t)((n0 + (GU ? (lane & 31) : lane)) * (sup ? w1.sr : w0.sr)) : kOutOfRange;
+  u32x4 ast[8];
+  u32x2 sst;
   auto load_a = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = i >> 1;
-      const bool second = GU && t >= 4;
-      const uint32_t tt = GU ? (uint32_t)(t & 3) : (uint32_t)t;
-      const uint32_t wt = second ? wt1 : wt0;
-      ast[i] = bld16s(second ? wr1 : wr0, second ? lv1 : lv0, wt * tt + (wt >> 1) * (uint32_t)(i & 1) + (uint32_t)(s * 128));
+    for (int i = 0; i < 8; ++i) {  // rows 8i .. 8i+7 of the wave
+      const bool second = GU && i >= 4;
+      const uint32_t ii = (uint32_t)(second ? i - 4 : i);
+      const uint32_t wrs = (uint32_t)(second ? w1.wr : w0.wr);
+      ast[i] = bld16s(second ? wr1 : wr0, second ? lv1 : lv0, 8u * wrs * ii + (uint32_t)(s * 128));
     }
-    sst[0] = bld8(sr0, sv0 + (uint32_t)(s * 8));
-    sst[1] = bld8(GU ? sr1 : sr0, sv1 + (uint32_t)(s * 8));
+    sst = sup ? bld8(sr1, sv + (uint32_t)(s * 8)) : bld8(sr0, sv + (uint32_t)(s * 8));
   };
-  uint8_t* const privA = lds + P::kPrivA + wave * (128 * 128);
-  uint8_t* const privS = lds + P::kPrivS + wave * (128 * 8);
+  uint8_t* const privA = lds + P::kPrivA + wave * (kMxRows * 128);
+  uint8_t* const privS = lds + P::kPrivS + wave * (kMxRows * 8);
   const uint32_t wslot = (uint32_t)(lr * 128 + 16 * (lc ^ lr));  // + 1024 per instruction
   auto store_a = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(privA + 1024 * i + wslot) = ast[i];
-    *reinterpret_cast<u32x2*>(privS + 8 * lane) = sst[0];
-    *reinterpret_cast<u32x2*>(privS + 8 * (64 + lane)) = sst[1];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(privA + 1024 * i + wslot) = ast[i];
+    *reinterpret_cast<u32x2*>(privS + 8 * lane) = sst;
   };
-  // MFMA-layout reads: tile t, position p -> row 16t + l16, piece 4p + q in slot (4p + q) ^ (l16 & 7)
-  const uint32_t rslot0 = (uint32_t)(l16 * 128 + 16 * ((0 + q) ^ (l16 & 7)));
-  const uint32_t rslot1 = (uint32_t)(l16 * 128 + 16 * ((4 + q) ^ (l16 & 7)));
+  // MFMA-layout reads: tile t (tile tt = t % TM of matrix m = t / TM for gate/up), lane row l16 ->
+  // wave row r = 32 m + (R/4)(l16 / 4) + 4 tt + l16 % 4, piece 4p + q in slot (4p + q) ^ (r & 7).
+  // As r & 7 = 4 (tt & 1) + l16 % 4, the slot is 4 (p ^ (tt & 1)) + (q ^ (l16 % 4)): every read is
+  // one per-lane base plus a constant.
+  const int rbase = (R / 4) * (l16 >> 2) + (l16 & 3);
+  const uint8_t* const abase = privA + 128 * rbase + 16 * (q ^ (l16 & 3));
+  const uint8_t* const sbase = privS + 8 * rbase;
 
-  u32x4 fill[P::kLPT];
+  // A step's fill goes in two parts (pieces [0, H0), then [H0, kLPT) and the scales) through the
+  // same staging registers, so the two parts' lifetimes (load to LDS store) must not overlap; the
+  // pipeline below loads part 1 after storing part 0 and part 0 after storing part 1.
+  constexpr int H0 = (P::kLPT + 1) / 2;
+  u32x4 fill[H0];
   uint32_t fills;
-  auto load_b = [&](int s) {
+  auto load_b = [&](int s, int part) {
 #pragma unroll
-    for (int i = 0; i < P::kLPT; ++i) fill[i] = bld16(ar, aoff[i] + (uint32_t)(s * P::kRowStep));
-    fills = bld4(asr, asoff + (uint32_t)(s * 8));
+    for (int i = part ? H0 : 0; i < (part ? P::kLPT : H0); ++i)
+      fill[i - (part ? H0 : 0)] = bld16(ar, aoff[i] + (uint32_t)(s * P::kRowStep));
+    if (part && sfill) fills = bld4(asr, asoff + (uint32_t)(s * 8));
   };
-  auto store_b = [&](int stage) {
+  auto store_b = [&](int stage, int part) {
     uint8_t* base = lds + stage * P::kStage;
 #pragma unroll
-    for (int i = 0; i < P::kLPT; ++i) {
+    for (int i = part ? H0 : 0; i < (part ? P::kLPT : H0); ++i) {
+      const u32x4 f = fill[i - (part ? H0 : 0)];
       if constexpr (Mx<F>::kBits == 6) {  // 8-byte aligned rows
-        *reinterpret_cast<u32x2*>(base + aw[i]) = u32x2{fill[i][0], fill[i][1]};
-        *reinterpret_cast<u32x2*>(base + aw[i] + 8) = u32x2{fill[i][2], fill[i][3]};
+        *reinterpret_cast<u32x2*>(base + aw(i)) = u32x2{f[0], f[1]};
+        *reinterpret_cast<u32x2*>(base + aw(i) + 8) = u32x2{f[2], f[3]};
       } else {
-        *reinterpret_cast<u32x4*>(base + aw[i]) = fill[i];
+        *reinterpret_cast<u32x4*>(base + aw(i)) = f;
       }
     }
-    *reinterpret_cast<uint32_t*>(base + asw) = fills;
+    if (part && sfill) *reinterpret_cast<uint32_t*>(base + asw) = fills;
   };
 
-  f32x4 acc[8][NB];
+  f32x4 acc[TA][NB];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < TA; ++t)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One step of MFMAs over the stage's activations and the wave's private weight copy, position
-  // by position (so only one position's weight operands are in registers).  After the last reads
-  // of the private copy, the next step's weights (staged in registers) are written in their place
-  // and the loads of the step after that are started.
-  auto step = [&](int stage, int s_next2) {
+  // by position.  After the last reads of the private copy, the next step's weights (staged in
+  // registers) are written in their place and the loads of the step after that are started.
+  auto step = [&](int stage, int s_next1, int s_next2) {
     const uint8_t* base = lds + stage * P::kStage;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      u32x4 af4[8];
-      uint32_t was[8];
-      if (active) {
+      // activation fill of step s+1 into the other stage: part p stored, then the next part loaded
+      // (part 1 of step s+1 at p = 0, part 0 of step s+2 at p = 1)
+      store_b(stage ^ 1, p);
+      load_b(p ? s_next2 : s_next1, p ^ 1);
+      // A wave past the last row (ragged N) reads and writes its private copy like the others
+      // (its loads are out of range and return zeros) and skips only the MFMAs and the epilogue:
+      // the same loads stay pending on every path, so the wait counts are exact.
+      u32x4 af4[TA];
+      uint32_t was[TA];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          af4[t] = *reinterpret_cast<const u32x4*>(privA + 2048 * t + (p ? rslot1 : rslot0));
-          was[t] = *reinterpret_cast<const uint32_t*>(privS + 8 * (16 * t + l16) + 4 * p);
-        }
+      for (int t = 0; t < TA; ++t) {
+        const int m = GU ? (t / TM) : 0, tt = GU ? (t % TM) : t;
+        af4[t] = *reinterpret_cast<const u32x4*>(abase + 128 * (32 * m + 4 * tt) + 64 * (p ^ (tt & 1)));
+        was[t] = *reinterpret_cast<const uint32_t*>(sbase + 8 * (32 * m + 4 * tt) + 4 * p);
       }
       if (p == 1) {
-        if (active) store_a();  // LDS accesses of a wave stay in order: the reads above come first
+        store_a();  // LDS accesses of a wave stay in order: the reads above come first
         load_a(s_next2);
       }
       if (!active) continue;
@@ -385,7 +410,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
       for (int b = 0; b < NB; ++b) {
         if (b + 1 < NB) load_bf(b + 1, bf[(b + 1) & 1], sb[(b + 1) & 1]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < TA; ++t) {
           const u32x4 c = af4[t];
           const v8i af = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
           const int sa = (int)((was[t] >> (8 * q)) & 0xFFu);
@@ -396,97 +421,104 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
     }
   };
 
-  // ---- pipeline.  Step s: write step s+1's activations (loaded during step s-1) into the other
-  //      ring stage and start loading step s+2's; MFMAs of step s (its weights were written to the
-  //      private copy during step s-1), replacing them with step s+1's and starting the loads of
-  //      step s+2's weights; barrier.  Loads are issued unconditionally (a step past the end
-  //      re-reads the last one), so every iteration has the same outstanding loads.
+  // ---- pipeline.  Step s: at each position, a part of step s+1's activations goes into the other
+  //      ring stage and the next part's loads start; the MFMAs of step s (its weights were written
+  //      to the private copy during step s-1), replacing them with step s+1's and starting the
+  //      loads of step s+2's weights; barrier.  Loads are issued unconditionally (a step past the
+  //      end re-reads the last one), and in the same order before the loop as inside it, so the
+  //      wait counts at the loop head hold for both of its entries.
+  const int last = n_steps - 1;
   load_a(0);
-  load_b(0);
-  if (active) store_a();
-  store_b(0);
-  load_a(min(1, n_steps - 1));
-  load_b(min(1, n_steps - 1));
+  load_b(0, 0);
+  store_a();
+  store_b(0, 0);
+  load_b(0, 1);
+  store_b(0, 1);
+  load_b(min(1, last), 0);
+  load_a(min(1, last));
   __syncthreads();
   for (int s = 0; s < n_steps; ++s) {
-    store_b((s + 1) & 1);
-    load_b(min(s + 2, n_steps - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    step(s & 1, min(s + 2, n_steps - 1));
+    step(s & 1, min(s + 1, last), min(s + 2, last));
     __syncthreads();
   }
   if (!active) return;
 
   // ---- epilogue ----
+  // Down: the slots of the lane's tokens, all loaded before the first store (a load between stores
+  // would wait for every store before it).
+  int yslot[GU ? 1 : NB];
+  if constexpr (!GU) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yslot[b] = sorted_slot[ti.r0 + min(16 * b + l16, ti.nr - 1)];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int sl = yslot[b];
+      yslot[b] = (16 * b + l16 < ti.nr && sl >= 0 && sl < n_slots) ? sl : -1;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int tok = 16 * b + l16;
     const bool ok = tok < ti.nr;
     if constexpr (GU) {
-      // h of the wave's 64 rows for this token: lane quarter q' holds rows 16t + 4q' + i (t = 0..3).
-      // A 4 x 4 exchange over the quarters leaves quarter q with rows 16q .. 16q+15, i.e. half
-      // q % 2 of block q / 2 of the wave.
-      float h[4][4];
+      // rows n0 + 8q + j (j = 4t + i) of this token: a quarter of h's block n0 / 32
+      float v[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < TM; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float g = acc[t][b][i], u = acc[4 + t][b][i];
-          h[t][i] = (g / (1.0f + expf(-g))) * u;
+          // SiLU(g) * u with the hardware exp2 and reciprocal (about 2 ulp; -0 or 0 for g << 0)
+          const float g = acc[t][b][i], u = acc[TM + t][b][i];
+          const float ex = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+          v[4 * t + i] = g * u * __builtin_amdgcn_rcpf(1.0f + ex);
         }
-      float v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // round r: send the rows of tile q ^ r (the tile of the receiving quarter q ^ r), receive
-        // the rows 4 (q ^ r) + i of tile q from quarter q ^ r
-        const int ts = q ^ r;
-        float got[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float snd = ts == 0 ? h[0][i] : (ts == 1 ? h[1][i] : (ts == 2 ? h[2][i] : h[3][i]));
-          got[i] = r == 0 ? snd : __shfl_xor(snd, 16 * r, kWave);
-        }
-        // source quarter j = q ^ r: place at v[4j + i] with a select over j
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * j + i] = (j == (q ^ r)) ? got[i] : v[4 * j + i];
-      }
       float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));  // the block's other half: quarter q ^ 1
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
       const uint32_t sc = mx_scale_code<F>(amax);
-      uint32_t dw[4];
-      mx_pack_half<F>(v, mx_inv_scale(sc), dw);
-      if (ok) {
-        const int row = ti.r0 + tok, kb = n0 / 32 + (q >> 1);
-        uint8_t* dst = h_codes + (int64_t)row * ((N / 32) * P::kBB) + kb * P::kBB + (q & 1) * (P::kBB / 2);
-        if constexpr (Mx<F>::kBits == 8) {
-          st16(dst, u32x4{dw[0], dw[1], dw[2], dw[3]});
-        } else if constexpr (Mx<F>::kBits == 6) {
-#pragma unroll
-          for (int i = 0; i < 3; ++i) *reinterpret_cast<uint32_t*>(dst + 4 * i) = dw[i];
-        } else {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{dw[0], dw[1]};
+      uint32_t dw[2];
+      mx_pack_quarter<F>(v, mx_inv_scale(sc), dw);
+      const int kb = n0 / 32;
+      uint8_t* const blk = h_codes + (int64_t)(ti.r0 + tok) * ((N / 32) * P::kBB) + kb * P::kBB;
+      if constexpr (Mx<F>::kBits == 6) {
+        // 6 bytes per quarter: quarter pairs join into 12 bytes (4-byte aligned)
+        const uint32_t o0 = (uint32_t)__shfl_xor((int)dw[0], 16, kWave);
+        const uint32_t o1 = (uint32_t)__shfl_xor((int)dw[1], 16, kWave);
+        if (ok && (q & 1) == 0) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(blk + 12 * (q >> 1));
+          dst[0] = dw[0];
+          dst[1] = (dw[1] & 0xFFFFu) | (o0 << 16);
+          dst[2] = (o0 >> 16) | (o1 << 16);
         }
-        if ((q & 1) == 0) h_scales[(int64_t)row * (N / 32) + kb] = (uint8_t)sc;
+      } else if constexpr (Mx<F>::kBits == 8) {
+        if (ok) *reinterpret_cast<u32x2*>(blk + 8 * q) = u32x2{dw[0], dw[1]};
+      } else {
+        if (ok) *reinterpret_cast<uint32_t*>(blk + 4 * q) = dw[0];
       }
+      if (ok && q == 0) h_scales[(int64_t)(ti.r0 + tok) * (N / 32) + kb] = (uint8_t)sc;
     } else {
-      const int sl = ok ? sorted_slot[ti.r0 + tok] : -1;
-      if (sl >= 0 && sl < n_slots) {
-        float* dst = y_slots + (int64_t)sl * N + n0 + 4 * q;
+      // The 16 tokens x 64 rows of column tile b go through the wave's private LDS copy (free
+      // after the last step): lane (token, q) writes rows 16q .. 16q+15 of its token, then each
+      // store instruction writes 4 whole token rows (256 contiguous bytes each) of y.
+      constexpr int kYS = 272;  // LDS bytes per token row (256 + 16: the 16 tokens on distinct banks)
+      uint8_t* const ybuf = privA;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = acc[t][b];
+      for (int t = 0; t < TA; ++t) *reinterpret_cast<f32x4*>(ybuf + l16 * kYS + 64 * q + 16 * t) = acc[t][b];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tk = 4 * j + (lane >> 4), piece = lane & 15;  // token of the tile, 16-byte piece
+        const int sl = __shfl(yslot[b], tk, kWave);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ybuf + tk * kYS + 16 * piece);
+        if (sl >= 0) *reinterpret_cast<f32x4*>(y_slots + (int64_t)sl * N + n0 + 4 * piece) = v;
       }
     }
   }
 }
 
 template <int F, bool GU>
-__global__ __launch_bounds__(kMxNW * 64, 1) void ffn_mx_kernel(
+__global__ __launch_bounds__(kMxNW * 64, 2) void ffn_mx_kernel(
     const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_s, int n_act_rows, int k_total, int K, int N,
     ProjDev w0, ProjDev w1, const TileEntry* __restrict__ tiles, int n_experts,
     const int32_t* __restrict__ sorted_slot, int n_slots, int n_nblk, int n_nblk_pad, uint8_t* __restrict__ h_codes,
@@ -537,14 +569,14 @@ hipError_t ffn_mx_fmt(const MxFfnArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const size_t lds = (size_t)MxTile<F>::kLds;
   {
-    const int nb = (a.I + kMxNW * 64 - 1) / (kMxNW * 64), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+    const int nb = (a.I + kMxNW * 32 - 1) / (kMxNW * 32), nbp = (nb + kXcds - 1) / kXcds * kXcds;
     ffn_mx_kernel<F, true><<<dim3((unsigned)(tiles * nbp)), kMxNW * 64, lds, stream>>>(
         a.xq, a.xs, a.T, a.k_total, a.H, a.I, a.gate, a.up, (const TileEntry*)a.table, a.n_experts,
         a.sorted_slot, n_slots, nb, nbp, a.hq, a.hs, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   {
-    const int nb = (a.H + kMxNW * 128 - 1) / (kMxNW * 128), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+    const int nb = (a.H + kMxNW * 64 - 1) / (kMxNW * 64), nbp = (nb + kXcds - 1) / kXcds * kXcds;
     ffn_mx_kernel<F, false><<<dim3((unsigned)(tiles * nbp)), kMxNW * 64, lds, stream>>>(
         a.hq, a.hs, n_slots, a.k_total, a.I, a.H, a.down, a.down, (const TileEntry*)a.table, a.n_experts,
         a.sorted_slot, n_slots, nb, nbp, nullptr, nullptr, a.y_slots);

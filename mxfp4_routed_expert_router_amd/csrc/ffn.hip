@@ -787,50 +787,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
   }
 
-  // Scale table [pair][n_chunks] dwords (a dword: the four block scales of one row in one chunk),
-  // pair = m * 16 * RT + row offset.  Filled per matrix, 8 loads in flight per lane, in 16-byte
-  // units when rows allow it.
-  {
-    const int rows = 16 * RT;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const ProjDev& p = m ? up : gate;
-      const bool vec = (n_chunks & 3) == 0 && (p.sr & 15) == 0 && ((uintptr_t)(p.s + (int64_t)e * p.se) & 15) == 0;
-      uint32_t* tm = stab + m * rows * n_chunks;
-      if (vec) {
-        const int upr = n_chunks >> 2, total = rows * upr;
-        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
-          u32x4 v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
-            v[i] = bld16(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 16u * u : kOutOfRange);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int f = f0 + 64 * i + lane;
-            if (f < total) *reinterpret_cast<u32x4*>(tm + 4 * f) = v[i];
-          }
-        }
-      } else {
-        const int total = rows * n_chunks;
-        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
-          uint32_t v[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
-            v[i] = bld4(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 4u * j : kOutOfRange);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int f = f0 + 64 * i + lane;
-            if (f < total) tm[f] = v[i];
-          }
-        }
-      }
-    }
-  }
-
   f32x4 accg[RT], accu[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -904,6 +860,51 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   __builtin_amdgcn_sched_barrier(0);
   load(n_steps > 1 ? 1 : 0, B);
   __builtin_amdgcn_sched_barrier(0);
+  // The scale table is filled while the first steps' loads are in flight: one memory round trip
+  // before the first MFMA instead of two.
+  // Scale table [pair][n_chunks] dwords (a dword: the four block scales of one row in one chunk),
+  // pair = m * 16 * RT + row offset.  Filled per matrix, 8 loads in flight per lane, in 16-byte
+  // units when rows allow it.
+  {
+    const int rows = 16 * RT;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const ProjDev& p = m ? up : gate;
+      const bool vec = (n_chunks & 3) == 0 && (p.sr & 15) == 0 && ((uintptr_t)(p.s + (int64_t)e * p.se) & 15) == 0;
+      uint32_t* tm = stab + m * rows * n_chunks;
+      if (vec) {
+        const int upr = n_chunks >> 2, total = rows * upr;
+        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+          u32x4 v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
+            v[i] = bld16(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 16u * u : kOutOfRange);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane;
+            if (f < total) *reinterpret_cast<u32x4*>(tm + 4 * f) = v[i];
+          }
+        }
+      } else {
+        const int total = rows * n_chunks;
+        for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+          uint32_t v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
+            v[i] = bld4(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * p.sr) + 4u * j : kOutOfRange);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int f = f0 + 64 * i + lane;
+            if (f < total) tm[f] = v[i];
+          }
+        }
+      }
+    }
+  }
   put_x(0, X[0]);
   fetch_x(2, X[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -1008,42 +1009,6 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   uint32_t coff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) coff[rt] = (uint32_t)(min(n0 + rt * 16 + l16, H - 1) * down.wr) + 16u * lq;
-  {  // scale table [row][n_chunks] dwords, 8 loads in flight per lane, 16-byte units when possible
-    const bool vec = (n_chunks & 3) == 0 && (down.sr & 15) == 0 &&
-                     ((uintptr_t)(down.s + (int64_t)ex * down.se) & 15) == 0;
-    if (vec) {
-      const int upr = n_chunks >> 2, total = NP * upr;
-      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
-        u32x4 v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
-          v[i] = bld16(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 16u * u : kOutOfRange);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = f0 + 64 * i + lane;
-          if (f < total) *reinterpret_cast<u32x4*>(stab + 4 * f) = v[i];
-        }
-      }
-    } else {
-      const int total = NP * n_chunks;
-      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
-        uint32_t v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
-          v[i] = bld4(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 4u * j : kOutOfRange);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = f0 + 64 * i + lane;
-          if (f < total) stab[f] = v[i];
-        }
-      }
-    }
-  }
-
   f32x4 acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1112,6 +1077,42 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   __builtin_amdgcn_sched_barrier(0);
   load(n_steps > 1 ? 1 : 0, B);
   __builtin_amdgcn_sched_barrier(0);
+  // scale table [row][n_chunks] dwords, filled while the first steps' loads are in flight
+  {  // 8 loads in flight per lane, 16-byte units when possible
+    const bool vec = (n_chunks & 3) == 0 && (down.sr & 15) == 0 &&
+                     ((uintptr_t)(down.s + (int64_t)ex * down.se) & 15) == 0;
+    if (vec) {
+      const int upr = n_chunks >> 2, total = NP * upr;
+      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane, r = f / upr, u = f - r * upr;
+          v[i] = bld16(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 16u * u : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane;
+          if (f < total) *reinterpret_cast<u32x4*>(stab + 4 * f) = v[i];
+        }
+      }
+    } else {
+      const int total = NP * n_chunks;
+      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane, r = f / n_chunks, j = f - r * n_chunks;
+          v[i] = bld4(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 4u * j : kOutOfRange);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = f0 + 64 * i + lane;
+          if (f < total) stab[f] = v[i];
+        }
+      }
+    }
+  }
   put_h(0, Hc[0]);
   fetch_h(2, Hc[0]);
   __builtin_amdgcn_sched_barrier(0);

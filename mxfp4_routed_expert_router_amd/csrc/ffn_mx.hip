@@ -190,10 +190,10 @@ struct MxTile {
   static constexpr int kScales = kCodes;                   // 8 scale bytes per token
   static constexpr int kStage = kScales + kMxTok * 8;      // one stage of the shared activation ring
   // After the two stages: per wave, a private copy of its 64 weight rows for one step (128 bytes
-  // per row, 16-byte pieces XOR-swizzled by row) and their 8 scale bytes.
+  // per row, 16-byte pieces XOR-swizzled by row) and their scale bytes of two steps (16 per row).
   static constexpr int kPrivA = 2 * kStage;
   static constexpr int kPrivS = kPrivA + kMxNW * kMxRows * 128;
-  static constexpr int kLds = kPrivS + kMxNW * kMxRows * 8;
+  static constexpr int kLds = kPrivS + kMxNW * kMxRows * 16;
   static constexpr int kPieces = kRowStep / 16;            // 16-byte pieces per token per step
   static constexpr int kLPT = kMxTok * kPieces / (64 * kMxNW);  // fill loads per thread per step
   static_assert(kLPT * 64 * kMxNW == kMxTok * kPieces, "a step of codes over the workgroup");
@@ -294,8 +294,14 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   // scale row of lane l: wave row l (gate/up: gate row l for l < 32, up row l - 32)
   const bool sup = GU && lane >= 32;
   const uint32_t sv = active ? (uint32_t)((n0 + (GU ? (lane & 31) : lane)) * (sup ? w1.sr : w0.sr)) : kOutOfRange;
+  // Scales: with an even step count (and 16-byte aligned scale rows), the 16 scale bytes of steps
+  // (s, s+1) of a row come in one load at even s and the load at odd s reads nothing (out of
+  // range): half the scale requests.  Otherwise 8 bytes every step.  Either way one load per step, so the wait counts
+  // do not depend on the step.
+  const bool spair = (n_steps & 1) == 0 && ((w0.sr | w1.sr) & 15) == 0 &&
+                     ((((uintptr_t)(w0.s + (int64_t)e * w0.se)) | ((uintptr_t)(w1.s + (int64_t)e * w1.se))) & 15) == 0;
   u32x4 ast[8];
-  u32x2 sst;
+  u32x4 sst;
   auto load_a = [&](int s) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {  // rows 8i .. 8i+7 of the wave
@@ -304,15 +310,25 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
       const uint32_t wrs = (uint32_t)(second ? w1.wr : w0.wr);
       ast[i] = bld16s(second ? wr1 : wr0, second ? lv1 : lv0, 8u * wrs * ii + (uint32_t)(s * 128));
     }
-    sst = sup ? bld8(sr1, sv + (uint32_t)(s * 8)) : bld8(sr0, sv + (uint32_t)(s * 8));
+    const __amdgpu_buffer_rsrc_t srr = sup ? sr1 : sr0;
+    if (spair) {
+      sst = bld16(srr, (s & 1) ? kOutOfRange : sv + (uint32_t)(s * 8));
+    } else {
+      const u32x2 v = bld8(srr, sv + (uint32_t)(s * 8));
+      sst = u32x4{v[0], v[1], 0u, 0u};
+    }
   };
   uint8_t* const privA = lds + P::kPrivA + wave * (kMxRows * 128);
-  uint8_t* const privS = lds + P::kPrivS + wave * (kMxRows * 8);
+  uint8_t* const privS = lds + P::kPrivS + wave * (kMxRows * 16);
   const uint32_t wslot = (uint32_t)(lr * 128 + 16 * (lc ^ lr));  // + 1024 per instruction
-  auto store_a = [&]() {
+  auto store_a = [&](int s) {  // s: the step the staged registers were loaded for
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(privA + 1024 * i + wslot) = ast[i];
-    *reinterpret_cast<u32x2*>(privS + 8 * lane) = sst;
+    if (spair) {
+      if ((s & 1) == 0) *reinterpret_cast<u32x4*>(privS + 16 * lane) = sst;
+    } else {
+      *reinterpret_cast<u32x2*>(privS + 16 * lane + 8 * (s & 1)) = u32x2{sst[0], sst[1]};
+    }
   };
   // MFMA-layout reads: tile t (tile tt = t % TM of matrix m = t / TM for gate/up), lane row l16 ->
   // wave row r = 32 m + (R/4)(l16 / 4) + 4 tt + l16 % 4, piece 4p + q in slot (4p + q) ^ (r & 7).
@@ -320,7 +336,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   // one per-lane base plus a constant.
   const int rbase = (R / 4) * (l16 >> 2) + (l16 & 3);
   const uint8_t* const abase = privA + 128 * rbase + 16 * (q ^ (l16 & 3));
-  const uint8_t* const sbase = privS + 8 * rbase;
+  const uint8_t* const sbase = privS + 16 * rbase;
 
   // A step's fill goes in two parts (pieces [0, H0), then [H0, kLPT) and the scales) through the
   // same staging registers, so the two parts' lifetimes (load to LDS store) must not overlap; the
@@ -358,7 +374,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   // One step of MFMAs over the stage's activations and the wave's private weight copy, position
   // by position.  After the last reads of the private copy, the next step's weights (staged in
   // registers) are written in their place and the loads of the step after that are started.
-  auto step = [&](int stage, int s_next1, int s_next2) {
+  auto step = [&](int stage, int s_cur, int s_next1, int s_next2) {
     const uint8_t* base = lds + stage * P::kStage;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -375,10 +391,10 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
       for (int t = 0; t < TA; ++t) {
         const int m = GU ? (t / TM) : 0, tt = GU ? (t % TM) : t;
         af4[t] = *reinterpret_cast<const u32x4*>(abase + 128 * (32 * m + 4 * tt) + 64 * (p ^ (tt & 1)));
-        was[t] = *reinterpret_cast<const uint32_t*>(sbase + 8 * (32 * m + 4 * tt) + 4 * p);
+        was[t] = *reinterpret_cast<const uint32_t*>(sbase + 16 * (32 * m + 4 * tt) + 8 * (s_cur & 1) + 4 * p);
       }
       if (p == 1) {
-        store_a();  // LDS accesses of a wave stay in order: the reads above come first
+        store_a(s_next1);  // LDS accesses of a wave stay in order: the reads above come first
         load_a(s_next2);
       }
       if (!active) continue;
@@ -430,7 +446,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   const int last = n_steps - 1;
   load_a(0);
   load_b(0, 0);
-  store_a();
+  store_a(0);
   store_b(0, 0);
   load_b(0, 1);
   store_b(0, 1);
@@ -438,7 +454,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   load_a(min(1, last));
   __syncthreads();
   for (int s = 0; s < n_steps; ++s) {
-    step(s & 1, min(s + 1, last), min(s + 2, last));
+    step(s & 1, s, min(s + 1, last), min(s + 2, last));
     __syncthreads();
   }
   if (!active) return;

@@ -320,10 +320,19 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
   };
   uint8_t* const privA = lds + P::kPrivA + wave * (kMxRows * 128);
   uint8_t* const privS = lds + P::kPrivS + wave * (kMxRows * 16);
-  const uint32_t wslot = (uint32_t)(lr * 128 + 16 * (lc ^ lr));  // + 1024 per instruction
+  // Private copy layout: piece c of wave row r in 16-byte slot c ^ sw(r), sw(r) = 2 ((r >> S) & 3)
+  // + ((r >> 1) & 1), S = log2(R/4).  Writes: the 16 lanes of a bank pass hold 2 rows x 8 pieces,
+  // conflict-free for any sw.  Reads (MFMA layout): the 16 lanes l16 of a bank pass read rows
+  // (R/4)(l16 / 4) + l16 % 4 + c, for which (r & 1, sw(r)) takes 16 distinct values: no conflicts.
+  constexpr int S = GU ? 3 : 4;
+  const uint32_t wrow = (uint32_t)(lr * 128);                   // + 1024 per instruction
+  const uint32_t wlc = (uint32_t)(lc ^ ((lr >> 1) & 1));         // ^ 2 ((row >> S) & 3)
   auto store_a = [&](int s) {  // s: the step the staged registers were loaded for
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(privA + 1024 * i + wslot) = ast[i];
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t hi = (uint32_t)(((8 * i) >> S) & 3) << 1;  // rows 8i + lr: (r >> S) & 3
+      *reinterpret_cast<u32x4*>(privA + 1024 * i + wrow + 16 * (wlc ^ hi)) = ast[i];
+    }
     if (spair) {
       if ((s & 1) == 0) *reinterpret_cast<u32x4*>(privS + 16 * lane) = sst;
     } else {
@@ -331,11 +340,13 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
     }
   };
   // MFMA-layout reads: tile t (tile tt = t % TM of matrix m = t / TM for gate/up), lane row l16 ->
-  // wave row r = 32 m + (R/4)(l16 / 4) + 4 tt + l16 % 4, piece 4p + q in slot (4p + q) ^ (r & 7).
-  // As r & 7 = 4 (tt & 1) + l16 % 4, the slot is 4 (p ^ (tt & 1)) + (q ^ (l16 % 4)): every read is
-  // one per-lane base plus a constant.
+  // wave row r = 32 m + (R/4)(l16 / 4) + 4 tt + l16 % 4, piece 4p + q.  For these rows sw(r) =
+  // g = 2 (l16 / 4) + ((l16 / 2) & 1) whatever m and tt, so the slot (4p + q) ^ g is
+  // 4 (p ^ (g >> 2)) + ((q ^ g) & 3): every read is one of two per-lane bases plus a constant.
   const int rbase = (R / 4) * (l16 >> 2) + (l16 & 3);
-  const uint8_t* const abase = privA + 128 * rbase + 16 * (q ^ (l16 & 3));
+  const int g = 2 * (l16 >> 2) + ((l16 >> 1) & 1);
+  const uint8_t* const abase0 = privA + 128 * rbase + 16 * ((q ^ g) & 3) + 64 * (g >> 2);
+  const uint8_t* const abase1 = privA + 128 * rbase + 16 * ((q ^ g) & 3) + 64 * ((g >> 2) ^ 1);
   const uint8_t* const sbase = privS + 16 * rbase;
 
   // A step's fill goes in two parts (pieces [0, H0), then [H0, kLPT) and the scales) through the
@@ -390,7 +401,7 @@ __device__ __forceinline__ void mx_tile(const TileInfo ti, int nblk, const uint8
 #pragma unroll
       for (int t = 0; t < TA; ++t) {
         const int m = GU ? (t / TM) : 0, tt = GU ? (t % TM) : t;
-        af4[t] = *reinterpret_cast<const u32x4*>(abase + 128 * (32 * m + 4 * tt) + 64 * (p ^ (tt & 1)));
+        af4[t] = *reinterpret_cast<const u32x4*>((p ? abase1 : abase0) + 128 * (32 * m + 4 * tt));
         was[t] = *reinterpret_cast<const uint32_t*>(sbase + 16 * (32 * m + 4 * tt) + 8 * (s_cur & 1) + 4 * p);
       }
       if (p == 1) {

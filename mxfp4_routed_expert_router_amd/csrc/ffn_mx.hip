@@ -14,19 +14,20 @@
 // little-endian 128-bit string, FP6 element j in bits 6j..6j+5 of its 192-bit string, FP8 one
 // byte per element.  The MFMA operand layout is stated next to mx_tile.
 //
-// Work split.  A workgroup (4 waves) takes one 128-token tile of an expert (the tile table of the
-// exact path, built with 128 rows per tile) and 4 * 64 rows of I (gate/up: 64 rows of each matrix
-// per wave) or 4 * 128 rows of H (down: 128 rows per wave).  Each wave streams its FP4 weight rows
-// straight from memory into registers, one step ahead, every instruction reading whole 64-byte
-// pieces of 16 rows; the tile's activation codes and scales go through a two-stage LDS ring
-// shared by the four waves, written one step ahead, with one barrier per step.  Workgroups are
+// Work split.  A workgroup (8 waves, two per SIMD) takes one 128-token tile of an expert (the tile
+// table of the exact path, built with 128 rows per tile) and 8 * 32 rows of I (gate/up: 32 rows
+// of each matrix per wave) or 8 * 64 rows of H (down).  Each wave loads its FP4 weight rows as
+// whole 128-byte lines two steps ahead, stages them in registers, and transposes them through a
+// private LDS copy into MFMA layout; the tile's activation codes and scales go through a
+// two-stage LDS ring shared by the eight waves, with one barrier per step.  Workgroups are
 // numbered tile-major with the row blocks padded to a multiple of 8, so row block j of every tile
 // runs on XCD j % 8 and the tiles of a hot expert read each weight row from one L2.  Only the
 // 16-token column tiles that hold rows of the tile (rounded up to 32 tokens) are computed.
 //
-// The gate/up epilogue forms h = SiLU(g) * u in fp32, exchanges values between the four lane
-// quarters so that each lane holds 16 consecutive values of h for its token (half a K-block), and
-// writes their codes and the block's E8M0 scale -- the layout the down phase reads.
+// The gate/up epilogue forms h = SiLU(g) * u in fp32; each lane holds 8 consecutive values of h
+// for its token (a quarter of a K-block) and writes their codes, one lane per token the block's
+// E8M0 scale -- the layout the down phase reads.  The down epilogue writes fp32 y_slots through
+// the wave's private LDS copy, whole token rows per store.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"

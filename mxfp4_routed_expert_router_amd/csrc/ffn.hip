@@ -1538,10 +1538,14 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
 size_t gateup_rows_lds(int H) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, H / 128); }
-constexpr int kDnNW = 8;   // waves per down workgroup: 8 share each h stage
+// Waves per down workgroup (they share each h stage): 8, or 4 when 8-wave row blocks would give
+// fewer than kDnSmallBlocks workgroups -- then smaller workgroups fill the chip better (measured on
+// the sweep workload: T = 8 101 -> 94 us, T = 15 156 -> 149 us; from T = 64 on, 8 waves are faster).
+constexpr int kDnNW = 8, kDnNWSmall = 4;
+constexpr int64_t kDnSmallBlocks = 2048;
 constexpr int kDnCPS = 1;  // chunks per down step
-size_t down_rows_lds(int I) {
-  return 2 * (size_t)DnStage<kDnCPS>::kBytes + kDnNW * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
+size_t down_rows_lds(int I, int nw) {
+  return 2 * (size_t)DnStage<kDnCPS>::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
 }
 
 template <int FMT, int MT>
@@ -1569,10 +1573,18 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
                    hipStream_t stream) {
   const int n_slots = T * k_total;
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
-  const int nb_rows = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
-  if (MT == 1 && streamable && down_rows_lds(I) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
-    ffn_down_rows_kernel<kDnNW, kDnCPS><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I), stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
+  const int nb8 = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
+  const bool small = pl.tiles * nb8 < kDnSmallBlocks;
+  const int nw = small ? kDnNWSmall : kDnNW;
+  const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
+  if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
+    const dim3 grid((unsigned)(pl.tiles * nb_rows));
+    if (small)
+      ffn_down_rows_kernel<kDnNWSmall, kDnCPS><<<grid, kDnNWSmall * 64, down_rows_lds(I, nw), stream>>>(
+          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
+    else
+      ffn_down_rows_kernel<kDnNW, kDnCPS><<<grid, kDnNW * 64, down_rows_lds(I, nw), stream>>>(
+          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
     launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {

@@ -739,12 +739,12 @@ struct XStage {
 constexpr int kGuXRow = 2 * 256 + 16;     // one token's two chunks of x + padding
 constexpr int kGuXStage = 16 * kGuXRow;  // bytes of one stage
 
-template <int NW>
+template <int NW, int RT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
-  constexpr int RT = kRowsRT1, NM = 2, NP = NM * RT * 16;
+  constexpr int NM = 2, NP = NM * RT * 16;
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
@@ -1537,7 +1537,11 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 // streams; below that the K-split kernels spread each expert over more workgroups.
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
-size_t gateup_rows_lds(int H) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * kRowsRT1, H / 128); }
+size_t gateup_rows_lds(int H, int rt) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * rt, H / 128); }
+// Gate/up row tiles per wave: 2 (32 rows of each matrix), or 1 when 2-tile row blocks would give
+// fewer than kGuSmallBlocks workgroups (measured on the sweep workload: T = 8 167 -> 152 us,
+// T = 32 448 -> 430 us, T = 88 653 -> 640 us; from T = 128 on, 2 tiles are as fast or faster).
+constexpr int64_t kGuSmallBlocks = 4608;
 // Waves per down workgroup (they share each h stage): 8, or 4 when 8-wave row blocks would give
 // fewer than kDnSmallBlocks workgroups -- then smaller workgroups fill the chip better (measured on
 // the sweep workload: T = 8 101 -> 94 us, T = 15 156 -> 149 us; from T = 64 on, 8 waves are faster).
@@ -1553,10 +1557,17 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
                      const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
-  const int nb_rows = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
-  if (MT == 1 && streamable && gateup_rows_lds(H) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks) {
-    ffn_gateup_rows_kernel<kNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kNW * 64, gateup_rows_lds(H), stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
+  const int nb2 = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
+  const int rt = pl.tiles * nb2 < kGuSmallBlocks ? 1 : kRowsRT1;
+  const int nb_rows = (I + 16 * rt * kNW - 1) / (16 * rt * kNW);
+  if (MT == 1 && streamable && gateup_rows_lds(H, rt) <= kMaxLds && pl.tiles * nb2 >= kRowsMinBlocks) {
+    const dim3 grid((unsigned)(pl.tiles * nb_rows));
+    if (rt == 1)
+      ffn_gateup_rows_kernel<kNW, 1><<<grid, kNW * 64, gateup_rows_lds(H, 1), stream>>>(
+          (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
+    else
+      ffn_gateup_rows_kernel<kNW, kRowsRT1><<<grid, kNW * 64, gateup_rows_lds(H, kRowsRT1), stream>>>(
+          (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
     launch_gateup_stream<MT, kRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {

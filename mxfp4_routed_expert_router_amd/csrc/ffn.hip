@@ -1500,6 +1500,10 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
 
 
 constexpr int kNW = 4, kRT1 = 2, kRT2 = 4;
+// Row tiles per wave of the K-split streaming kernels (few tiles, e.g. T = 1): one per matrix for
+// gate/up, two for down -- twice the workgroups of kRT1 / kRT2 (measured at T = 1 / 4 on the sweep
+// workload: gate/up 26.1 -> 25.2 / 108 -> 104 us, down 20.5 -> 18.6 us at T = 1).
+constexpr int kStRT1 = 1, kStRT2 = 2;
 
 inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 // The streaming kernels need whole 128-wide chunks, dword-aligned scale rows, a K share per wave
@@ -1569,7 +1573,7 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
       ffn_gateup_rows_kernel<kNW, kRowsRT1><<<grid, kNW * 64, gateup_rows_lds(H, kRowsRT1), stream>>>(
           (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
-    launch_gateup_stream<MT, kRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+    launch_gateup_stream<MT, kStRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
     ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
@@ -1597,7 +1601,7 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
       ffn_down_rows_kernel<kDnNW, kDnCPS><<<grid, kDnNW * 64, down_rows_lds(I, nw), stream>>>(
           h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
-    launch_down_stream<MT, kRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+    launch_down_stream<MT, kStRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
     ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(

@@ -99,24 +99,17 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 #undef MOE_DPP_ADD
   return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
 }
-// Maximum of a 64-bit key (hi, lo) over the wave, compared as unsigned; returns it uniform.
-__device__ __forceinline__ void wave_max_u64_dpp(uint32_t& hi, uint32_t& lo) {
-#define MOE_DPP_MAX64(C, R)                                                \
-  {                                                                        \
-    const uint32_t th = dpp_u32<C, R>(hi, hi), tl = dpp_u32<C, R>(lo, lo); \
-    const bool gt = th > hi || (th == hi && tl > lo);                      \
-    hi = gt ? th : hi;                                                     \
-    lo = gt ? tl : lo;                                                     \
-  }
-  MOE_DPP_MAX64(kDppRowShr1, 0xF);
-  MOE_DPP_MAX64(kDppRowShr2, 0xF);
-  MOE_DPP_MAX64(kDppRowShr4, 0xF);
-  MOE_DPP_MAX64(kDppRowShr8, 0xF);
-  MOE_DPP_MAX64(kDppRowBcast15, 0xA);
-  MOE_DPP_MAX64(kDppRowBcast31, 0xC);
-#undef MOE_DPP_MAX64
-  hi = __builtin_amdgcn_readlane(hi, 63);
-  lo = __builtin_amdgcn_readlane(lo, 63);
+// Maximum of an unsigned 32-bit value over the wave, returned uniform.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t u) {
+#define MOE_DPP_MAXU(C, R) u = max(u, dpp_u32<C, R>(u, u))
+  MOE_DPP_MAXU(kDppRowShr1, 0xF);
+  MOE_DPP_MAXU(kDppRowShr2, 0xF);
+  MOE_DPP_MAXU(kDppRowShr4, 0xF);
+  MOE_DPP_MAXU(kDppRowShr8, 0xF);
+  MOE_DPP_MAXU(kDppRowBcast15, 0xA);
+  MOE_DPP_MAXU(kDppRowBcast31, 0xC);
+#undef MOE_DPP_MAXU
+  return __builtin_amdgcn_readlane(u, 63);
 }
 // Order-preserving map of a float (finite or infinite) onto uint32, and back.
 __device__ __forceinline__ uint32_t f32_order_key(float f) {

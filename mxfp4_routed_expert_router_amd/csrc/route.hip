@@ -149,7 +149,10 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
   }
 }
 
-template <int VPL>
+// Lane l holds experts VPL l .. VPL l + VPL - 1 (contiguous, so with E % VPL == 0 -- VEC -- a
+// lane reads each slice's VPL partial logits with one vector load, and writes its probabilities
+// together).
+template <int VPL, bool VEC>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ partial, int splits, int T,
                                                            int E, const float* __restrict__ bias, int top_k,
                                                            int n_shared, int32_t* __restrict__ ids,
@@ -157,16 +160,28 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier follows
+  const int e0 = VPL * lane;
   float L[VPL];
-  // Sum the hidden-dimension slices in slice order (all loads issued together).
+  // Sum the hidden-dimension slices in slice order (all loads issued together).  A lane past E
+  // reads the last valid lane's values and discards them.
   float part[kMaxSplits][VPL];
 #pragma unroll
-  for (int q = 0; q < kMaxSplits; ++q)
+  for (int q = 0; q < kMaxSplits; ++q) {
+    if (VEC) {
+      const float* src = partial + ((int64_t)min(q, splits - 1) * T + t) * E + min(e0, E - VPL);
+      typedef float fv __attribute__((ext_vector_type(VPL)));
+      fv val;
+      __builtin_memcpy(&val, __builtin_assume_aligned(src, VPL >= 4 ? 16 : 4 * VPL), 4 * VPL);  // workspace: 16-byte aligned
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + 64 * v;
-      part[q][v] = (q < splits && e < E) ? partial[((int64_t)q * T + t) * E + e] : 0.0f;
+      for (int v = 0; v < VPL; ++v) part[q][v] = (q < splits && e0 < E) ? val[v] : 0.0f;
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = e0 + v;
+        part[q][v] = (q < splits && e < E) ? partial[((int64_t)q * T + t) * E + e] : 0.0f;
+      }
     }
+  }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     L[v] = 0.0f;
@@ -175,7 +190,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
-    const int e = lane + 64 * v;
+    const int e = e0 + v;
     L[v] = (e < E) ? L[v] + (bias ? bias[e] : 0.0f) : -INFINITY;
   }
   float mx = -INFINITY;
@@ -184,41 +199,41 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   mx = wave_max_dpp(mx);
   float esum = 0.0f;
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) esum += (lane + 64 * v < E) ? expf(L[v] - mx) : 0.0f;
+  for (int v = 0; v < VPL; ++v) esum += (e0 + v < E) ? expf(L[v] - mx) : 0.0f;
   const float den = wave_sum_dpp(esum);
   if (probs) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      int e = lane + 64 * v;
+      const int e = e0 + v;
       if (e < E) probs[(int64_t)t * E + e] = expf(L[v] - mx) / den;
     }
   }
-  // k rounds of wave argmax over (logit desc, index asc), each one maximum of a 64-bit key
-  // (order key of the logit, then the complement of the index).  Taken and padded experts carry
-  // key 0, below every logit's key.  The winner of round j is kept by lane j % 64 in register
-  // q = j / 64 (k_total <= MOE_MAX_SLOTS_PER_TOKEN = 4 * 64).
+  // k rounds of wave argmax over (logit desc, index asc): the largest order key of the logits
+  // (one 32-bit DPP maximum), then the lowest index holding it -- expert e = VPL lane + v, so per
+  // v the lowest lane with a match (a ballot), then the smallest of those VPL indices.  Taken and
+  // padded experts carry key 0, below every logit's key.  The winner of round j is kept by lane
+  // j % 64 in register q = j / 64 (k_total <= MOE_MAX_SLOTS_PER_TOKEN = 4 * 64).
   uint32_t kh[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) kh[v] = (lane + 64 * v < E) ? f32_order_key(L[v]) : 0u;
+  for (int v = 0; v < VPL; ++v) kh[v] = (e0 + v < E) ? f32_order_key(L[v]) : 0u;
   float psum = 0.0f;
   int my_id[4] = {0, 0, 0, 0};
   float my_p[4] = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < top_k; ++j) {
-    uint32_t bh = 0u, bl = 0u;
+    uint32_t m = kh[0];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {  // this lane's best: larger key, then smaller index
-      const uint32_t cl = ~(uint32_t)(lane + 64 * v);
-      if (kh[v] > bh || (kh[v] == bh && kh[v] != 0u && cl > bl)) {
-        bh = kh[v];
-        bl = cl;
-      }
+    for (int v = 1; v < VPL; ++v) m = max(m, kh[v]);
+    m = wave_max_u32_dpp(m);
+    int bi = INT_MAX;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const uint64_t b = __ballot(kh[v] == m);
+      if (b) bi = min(bi, VPL * (__builtin_ffsll((long long)b) - 1) + v);
     }
-    wave_max_u64_dpp(bh, bl);
-    const int bi = (int)~bl;
-    const float bv = f32_from_order_key(bh);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-      if (lane + 64 * v == bi) kh[v] = 0u;
+      if (e0 + v == bi) kh[v] = 0u;
+    const float bv = f32_from_order_key(m);
     const float p = expf(bv - mx) / den;
     psum += p;
     if ((j & 63) == lane) {
@@ -300,12 +315,20 @@ hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_
   if (err != hipSuccess) return err;
   dim3 g2((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-#define MOE_SEL(V) route_select_kernel<V><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared, ids, weights, probs)
-  if (vpl <= 1) MOE_SEL(1);
-  else if (vpl <= 2) MOE_SEL(2);
-  else if (vpl <= 4) MOE_SEL(4);
-  else if (vpl <= 8) MOE_SEL(8);
-  else MOE_SEL(16);
+#define MOE_SEL(V)                                                                                           \
+  {                                                                                                          \
+    if (E % V == 0)                                                                                          \
+      route_select_kernel<V, true><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared, ids, \
+                                                           weights, probs);                                  \
+    else                                                                                                     \
+      route_select_kernel<V, false><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared,    \
+                                                            ids, weights, probs);                            \
+  }
+  if (vpl <= 1) MOE_SEL(1)
+  else if (vpl <= 2) MOE_SEL(2)
+  else if (vpl <= 4) MOE_SEL(4)
+  else if (vpl <= 8) MOE_SEL(8)
+  else MOE_SEL(16)
 #undef MOE_SEL
   return hipGetLastError();
 }

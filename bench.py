@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--mx", choices=["fp8", "fp6", "fp4"], default=None,
                     help="with --prefill: the MX mode of the expert FFN (activations quantised to MXFP8 E4M3, "
                          "MXFP6 E2M3 or MXFP4 E2M1 and multiplied with the FP4 weights on scaled MFMAs)")
+    ap.add_argument("--workload", choices=["decode", "dense"], default=None,
+                    help="measure another layer workload instead and print its own JSON line: the decode "
+                         "layer (hidden 4096, 128 experts, top-8, I 1536, MXFP4; T = 1, 8, 32, 64) or the "
+                         "dense FFN as 8 all-active FP16 slices (hidden 4096, I 16384; T = 1, 16, 128)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain elementwise copy (torch.neg, fp32) of this many MiB three times, "
                          "for scaling memory counters, and exit")
@@ -59,18 +63,22 @@ def parse():
 class Runner:
     """Preallocated buffers for one T; step(set) enqueues the five library calls on the current stream."""
 
-    def __init__(self, moe, sets, T, top_k, n_shared, n_experts, H, I, mx=None):
+    def __init__(self, moe, sets, T, top_k, n_shared, n_experts, H, I, mx=None, fixed_routing=False):
         import torch
         dev = "cuda:0"
         self.moe, self.sets, self.T, self.top_k, self.n_shared = moe, sets, T, top_k, n_shared
         self.mx = mx
+        self.fixed = fixed_routing  # dense slices: ids [t][j] = j, weights 1, no router call
         self.kt = top_k + n_shared
         self.n_experts = n_experts
         n = T * self.kt
         W0 = sets[0]["W"]
         self.ids = torch.empty((T, self.kt), dtype=torch.int32, device=dev)
         self.w = torch.empty((T, self.kt), dtype=torch.float32, device=dev)
-        self.route_ws = self._ws(moe.moe_route_workspace_bytes(T, H, n_experts - n_shared))
+        if fixed_routing:
+            self.ids.copy_(torch.arange(self.kt, dtype=torch.int32, device=dev).expand(T, self.kt))
+            self.w.fill_(1.0)
+        self.route_ws = None if fixed_routing else self._ws(moe.moe_route_workspace_bytes(T, H, n_experts - n_shared))
         self.b = moe.Buckets(torch.empty(n_experts, dtype=torch.int32, device=dev),
                              torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
                              torch.empty(n, dtype=torch.int32, device=dev), None)
@@ -89,8 +97,9 @@ class Runner:
         m, s = self.moe, self.sets[i % len(self.sets)]
         rec = (lambda k: events[k].record()) if events is not None else (lambda k: None)
         rec(0)
-        m.moe_route(s["x"][:self.T], s["router"], self.top_k, s["bias"], self.n_shared,
-                    out=(self.ids, self.w, None), workspace=self.route_ws)
+        if not self.fixed:
+            m.moe_route(s["x"][:self.T], s["router"], self.top_k, s["bias"], self.n_shared,
+                        out=(self.ids, self.w, None), workspace=self.route_ws)
         rec(1)
         m.moe_bucket(self.ids, self.n_experts, out=self.b, workspace=self.bucket_ws)
         rec(2)
@@ -198,6 +207,8 @@ def main():
         return copy_calibration(args.copy_calibration_mib)
     if args.prefill:
         return prefill_run(args)
+    if args.workload:
+        return side_run(args)
     import synth
     import mxfp4_routed_expert_router_amd as moe
 
@@ -293,6 +304,64 @@ def main():
         out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def side_run(args):
+    """The decode or dense-slices workload at each of its token counts (its own JSON line; weight
+    sets rotated past the Infinity Cache as in the sweep)."""
+    import torch
+    import synth
+    import mxfp4_routed_expert_router_amd as moe
+    moe.lib()
+    name = "decode" if args.workload == "decode" else "dense_slices"
+    wl = synth.WORKLOADS[name]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_routed, wl.top_k
+    dense = wl.dense_slices
+    Ts = list(wl.tokens)
+    t0 = time.time()
+    L = synth.make_layer(wl, max(Ts))
+    base = synth.to_torch(L, "cuda:0")
+    gen_s = time.time() - t0
+    expert_bytes = 3 * H * I * (2.0 if dense else MXFP4_BYTES_PER_WEIGHT)
+
+    def make_sets(T):
+        a = E if dense else E * (1.0 - (1.0 - k / E) ** T)
+        r = max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes))))
+        sets = []
+        for j in range(r):
+            t = base if j == 0 else {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base.items()}
+            if dense and j > 0:  # keep the slice views over the copied dense matrices
+                E2 = wl.n_experts
+                t["gate"], t["up"] = t["dense_gate"].view(E2, I, H), t["dense_up"].view(E2, I, H)
+                t["down"] = t["dense_down"].as_strided((E2, H, I), (I, E2 * I, 1))
+            W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+            sets.append({"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t})
+        return sets
+
+    lines = []
+    for T in Ts:
+        print(f"bench {name}: T={T}", file=sys.stderr, flush=True)
+        sets = make_sets(T)
+        runner = Runner(moe, sets, T, k, 0, E, H, I, fixed_routing=dense)
+        eager_ms, per = time_steps(runner, args.sweep_steps, min(args.warmup, 5))
+        ms = time_graph(runner, args.sweep_steps, min(args.warmup, 5))
+        A = E if dense else active_experts(runner)
+        wb = A * expert_bytes
+        lines.append({"T": T, "us_per_layer": ms * 1e3, "eager_us_per_layer": eager_ms * 1e3,
+                      "tokens_per_s": T / (ms / 1e3), "active_experts": A, "weight_GBps": wb / (ms / 1e3) / 1e9,
+                      "weight_frac_of_hbm_peak": wb / (ms / 1e3) / HBM_PEAK,
+                      "per_call_us": {kk: round(v * 1e3, 2) for kk, v in per.items()},
+                      "rotation_sets": len(sets)})
+        del runner, sets
+        torch.cuda.empty_cache()
+    wdesc = "fp16 (8 all-active slices of one dense FFN)" if dense else "mxfp4 (E2M1 + E8M0/32)"
+    out = {"metric": f"{name} MoE-layer tokens/s and HBM GB/s on expert weights (side measurement)",
+           "n_gpus": 1, "data": "synthetic", "higher_is_better": True,
+           "config": {"workload": f"moe_layer_{name}_H{H}_E{E}_top{k}_I{I}", "hidden": H, "experts": E,
+                      "top_k": k, "inter": I, "weights": wdesc, "activations": wl.act_dtype, "output": "fp32",
+                      "timing": "HIP graph replay of whole layer calls"},
+           "sweep": lines, "input_generation_s": gen_s}
     print(json.dumps(out), flush=True)
 
 

@@ -712,24 +712,16 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
-// Row-split streaming variants (many active experts).  The four waves of a workgroup own
+// Row-split streaming variants (many active experts).  The waves of a workgroup (4 or 8) own
 // different weight rows, each over the whole reduction dimension, so no cross-wave reduction is
 // needed; the activation (or h) chunk of the tile's tokens is shared: each wave loads a part of
 // it into registers, writes it to an LDS stage, and every wave reads its MFMA operands from LDS.
-// This cuts the L1 requests spent on activations 4x (the L1 request rate, more than HBM, bounds
+// This cuts the L1 requests spent on activations 4-8x (the L1 request rate, more than HBM, bounds
 // these kernels).  Each wave keeps the block scales of its rows over the whole reduction in an
 // LDS table filled once: refilling a smaller table in windows re-fetches the partial 128-byte
 // lines that straddle the windows (scale rows are 224 bytes for a 7168-wide matrix).
 // ------------------------------------------------------------------------------------------------
-constexpr int kRowsRT1 = 2, kRowsRT2 = 4;  // 16-row tiles per wave: gate/up (of each matrix), down
-
-// One LDS stage holds a 16-token x 128-K chunk of 16-bit operands in PL planes (x: one plane;
-// h: hi and lo planes).  Rows are padded by 16 bytes so the MFMA operand reads spread over banks.
-template <int PL>
-struct XStage {
-  static constexpr int kRow = 128 * 2 + 16;
-  static constexpr int kBytes = PL * 16 * kRow;
-};
+constexpr int kRowsRT2 = 4;  // 16-row tiles per down wave (gate/up: one tile of each matrix)
 
 // Gate/up: a step covers two 128-K chunks, i.e. a whole 128-byte line of every weight row, so the
 // two halves of a line are requested together (one step apart, a line's second half was often
@@ -740,11 +732,13 @@ constexpr int kGuXRow = 2 * 256 + 16;     // one token's two chunks of x + paddi
 constexpr int kGuXStage = 16 * kGuXRow;  // bytes of one stage
 
 template <int NW, int RT>
-__global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   constexpr int NM = 2, NP = NM * RT * 16;
+  constexpr int XPT = 512 / (64 * NW);  // 16-byte lane-loads of x per thread per step
+  static_assert(XPT * 64 * NW == 512 && (XPT == 1 || XPT == 2), "a step's x: 16 tokens x 2 chunks x 256 bytes");
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
@@ -761,18 +755,20 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   uint8_t* xs = lds;  // [2][kGuXStage]
   uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kGuXStage + wave * stab_bytes(NP, n_chunks));
 
-  // Activations: thread q = 64*wave + lane moves token q/16, 16-byte column q%16 of both chunks of
-  // a step.  Padded tokens get an out-of-range offset (reads zeros, no memory access).
+  // Activations: thread q = 64*wave + lane moves 16-byte column q%16 of token q/16, both chunks of
+  // a step (4 waves), or of token q/32, chunk (q/16)%2 (8 waves).  Padded tokens get an
+  // out-of-range offset (reads zeros, no memory access).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
-  const int q_tok = (64 * wave + lane) >> 4, q_col = lane & 15;
+  const int q = 64 * wave + lane;
+  const int q_tok = XPT == 2 ? q >> 4 : q >> 5, q_col = q & 15, q_j = XPT == 2 ? 0 : (q >> 4) & 1;
   uint32_t xoff;
   {
     bool ok = q_tok < ti.nr;
     const int sl = ok ? sorted_slot[ti.r0 + q_tok] : -1;
     ok = ok && sl >= 0 && sl < n_slots;
-    xoff = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 16u * q_col : kOutOfRange;
+    xoff = ok ? (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 256u * q_j + 16u * q_col : kOutOfRange;
   }
-  const uint32_t xs_w = (uint32_t)(q_tok * kGuXRow + 16 * q_col);  // + 256 * chunk of the step
+  const uint32_t xs_w = (uint32_t)(q_tok * kGuXRow + 256 * q_j + 16 * q_col);  // + 256 * lane-load
   const uint32_t xs_r = (uint32_t)(l16 * kGuXRow + 64 * lq);        // + 256 * chunk + 16 * s
 
   const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
@@ -810,14 +806,15 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   };
   // Activations are fetched two steps ahead, like the weights: X[s % 2] holds step s's chunks
   // until they are written to their stage, then is refilled with step s + 2's.
-  u32x4 X[2][2];
-  auto fetch_x = [&](int s, u32x4 (&r)[2]) {
+  u32x4 X[2][XPT];
+  auto fetch_x = [&](int s, u32x4 (&r)[XPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) r[j] = bld16(xr, 2 * s + j < n_chunks ? xoff + 512u * s + 256u * j : kOutOfRange);
+    for (int j = 0; j < XPT; ++j)
+      r[j] = bld16(xr, 2 * s + q_j + j < n_chunks ? xoff + 512u * s + 256u * j : kOutOfRange);
   };
-  auto put_x = [&](int s, const u32x4 (&r)[2]) {
+  auto put_x = [&](int s, const u32x4 (&r)[XPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(xs + (s & 1) * kGuXStage + xs_w + 256 * j) = r[j];
+    for (int j = 0; j < XPT; ++j) *reinterpret_cast<u32x4*>(xs + (s & 1) * kGuXStage + xs_w + 256 * j) = r[j];
   };
   auto compute_chunk = [&](int s, int j, const Step& d) {
     const int c = 2 * s + j;
@@ -840,9 +837,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   };
   // Step s: sync, publish step s+1's activations (held in Xn), compute step s from register set D,
   // refill D with step s+2's weights and Xn with step s+3's activations.  Every step issues its
-  // loads in one order (8 weights, then 2 activations) and the prologue issues the same sequence,
+  // loads in one order (the weights, then the activations) and the prologue issues the same sequence,
   // so the wait counts the compiler derives at the loop head are the steady ones.
-  auto step = [&](int s, Step& D, u32x4 (&Xn)[2]) {
+  auto step = [&](int s, Step& D, u32x4 (&Xn)[XPT]) {
     __syncthreads();
     put_x(s + 1, Xn);
     compute_chunk(s, 0, D);
@@ -954,25 +951,29 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_rows_kernel(
   }
 }
 
-// Down: the same step structure as gate/up (CPS 128-K chunks per step, 2-stage ring written after
-// the step's barrier, scale table over the whole K).  A stage holds the hi and lo planes of h.
-template <int CPS>
+// Down: whole lines per step.  A step covers two 128-K chunks -- one whole 128-byte line of every
+// weight row -- for half of the wave's row tiles, and the next step the same two chunks for the
+// other half, so both halves of a line are requested by one pair of loads.  (With one chunk of all
+// the row tiles per step, the half-read lines of a workgroup's rows stayed open for a whole step,
+// more of them than an XCD's L2 holds, and about 9% of the lines were fetched twice.)  A step's
+// weights are four 16-byte loads per lane.  The h ring (two stages, written after the barrier as
+// in gate/up) advances every two steps: a stage holds the hi and lo planes of both chunks of a
+// pair of steps, with one barrier per pair.  The scale table covers the whole K.
 struct DnStage {
-  static constexpr int kRow = CPS * 256 + 16;     // one token's chunks of one h plane + padding
-  static constexpr int kBytes = 2 * 16 * kRow;    // hi plane, then lo plane
+  static constexpr int kRow = 2 * 256 + 16;    // one token's two chunks of one h plane + padding
+  static constexpr int kBytes = 2 * 16 * kRow;  // hi plane, then lo plane
 };
 
-template <int NW, int CPS>
-__global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
-  constexpr int RT = kRowsRT2, NP = RT * 16;
-  constexpr int LPT = CPS * 512 / (64 * NW);  // 16-byte lane-loads of h per thread per step
-  static_assert(LPT * 64 * NW == CPS * 512, "a step's h (2 planes x 16 tokens x CPS x 256 bytes)");
-  static_assert(CPS == 1 || CPS == 2, "one or two chunks per step");
-  constexpr int JB = CPS == 2 ? 1 : 0;  // bits of the chunk index within a step
-  constexpr int kDnXRow = DnStage<CPS>::kRow, kDnXStage = DnStage<CPS>::kBytes;
+  constexpr int RT = kRowsRT2, HT = RT / 2, NP = RT * 16;
+  constexpr int LPT = 1024 / (64 * NW);  // 16-byte lane-loads of h per thread per pair
+  static_assert(LPT * 64 * NW == 1024, "a pair's h: 2 planes x 16 tokens x 2 chunks x 256 bytes");
+  static_assert(RT % 2 == 0, "two halves of the row tiles");
+  constexpr int kRow = DnStage::kRow, kStage = DnStage::kBytes;
   typedef bf16x8 V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int tile, nblk;
@@ -983,26 +984,26 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = (nblk * NW + wave) * 16 * RT;
   const int ex = __builtin_amdgcn_readfirstlane(ti.e);
-  const int n_chunks = I >> 7, n_steps = (n_chunks + CPS - 1) / CPS;
+  const int n_chunks = I >> 7, n_pairs = (n_chunks + 1) >> 1;
 
-  uint8_t* xs = lds;  // [2][kDnXStage]
-  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kDnXStage + wave * stab_bytes(NP, n_chunks));
+  uint8_t* xs = lds;  // [2][kStage]
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kStage + wave * stab_bytes(NP, n_chunks));
 
-  // Lane-load i of a thread: q = 64 * (NW * i + wave) + lane covers 16-byte column q % 16, chunk
-  // (q / 16) % CPS of the step, then token, then plane.  The plane is uniform over a wave's load,
-  // so each load uses one buffer descriptor.
+  // h lane-load i: q = 64 * (NW * i + wave) + lane covers 16-byte column q % 16 of chunk (q / 16) % 2
+  // of the pair, token (q / 32) % 16 and plane q / 512 (uniform over a wave's load).
   const __amdgpu_buffer_rsrc_t hr[2] = {make_rsrc(h_hi, (int64_t)n_slots * I * 2), make_rsrc(h_lo, (int64_t)n_slots * I * 2)};
   uint32_t hoff[LPT], hs_w[LPT];
   int hplane[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int q = 64 * (NW * i + wave) + lane;
-    const int plane = q >> (8 + JB), tok = (q >> (4 + JB)) & 15, j = (q >> 4) & (CPS - 1), col = q & 15;
+    const int plane = q >> 9, tok = (q >> 5) & 15, j = (q >> 4) & 1, col = q & 15;
     hplane[i] = __builtin_amdgcn_readfirstlane(plane);
     hoff[i] = tok < ti.nr ? (uint32_t)(ti.r0 + tok) * (uint32_t)I * 2u + 256u * j + 16u * col : kOutOfRange;
-    hs_w[i] = (uint32_t)(plane * 16 * kDnXRow + tok * kDnXRow + 256 * j + 16 * col);
+    hs_w[i] = (uint32_t)(plane * 16 * kRow + tok * kRow + 256 * j + 16 * col);
   }
-  const uint32_t hs_r = (uint32_t)(l16 * kDnXRow + 64 * lq);  // + 256 * chunk + 16 * k (+ lo plane)
+  const int hj = (lane >> 4) & 1;  // the chunk of the pair that this lane's h loads cover
+  const uint32_t hs_r = (uint32_t)(l16 * kRow + 64 * lq);  // + 256 * chunk + 16 * k (+ lo plane)
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
@@ -1013,71 +1014,74 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  struct Step {
-    u32x4 q[RT][CPS];  // [row tile][chunk of the step]
+  struct Half {
+    u32x4 q[HT][2];  // [row tile of the half][chunk of the pair]
   };
-  auto load = [&](int s, Step& d) {
+  // pair p, half th: row tiles HT * th .. HT * th + HT - 1, chunks 2p and 2p + 1
+  auto load = [&](int p, int th, Half& d) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int r = 0; r < HT; ++r)
 #pragma unroll
-      for (int j = 0; j < CPS; ++j)
-        d.q[rt][j] = bld16(wr, CPS * s + j < n_chunks ? coff[rt] + 64u * (CPS * s + j) : kOutOfRange);
+      for (int j = 0; j < 2; ++j)
+        d.q[r][j] = bld16(wr, 2 * p + j < n_chunks ? coff[HT * th + r] + 64u * (2 * p + j) : kOutOfRange);
   };
-  u32x4 Hc[2][LPT];  // [step parity][lane-load]: fetched two steps ahead
-  auto fetch_h = [&](int s, u32x4 (&r)[LPT]) {
+  auto fetch_h = [&](int p, u32x4 (&r)[LPT]) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int j = ((64 * (NW * i + wave) + lane) >> 4) & (CPS - 1);
-      r[i] = bld16(hr[hplane[i]], CPS * s + j < n_chunks ? hoff[i] + 256u * CPS * s : kOutOfRange);
-    }
+    for (int i = 0; i < LPT; ++i) r[i] = bld16(hr[hplane[i]], 2 * p + hj < n_chunks ? hoff[i] + 512u * p : kOutOfRange);
   };
-  auto put_h = [&](int s, const u32x4 (&r)[LPT]) {
+  auto put_h = [&](int p, const u32x4 (&r)[LPT]) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(xs + (s & 1) * kDnXStage + hs_w[i]) = r[i];
+    for (int i = 0; i < LPT; ++i) *reinterpret_cast<u32x4*>(xs + (p & 1) * kStage + hs_w[i]) = r[i];
   };
-  auto compute_chunk = [&](int s, int j, const Step& d) {
-    const int c = CPS * s + j;
-    const uint8_t* st = xs + (s & 1) * kDnXStage + hs_r + 256 * j;
-    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
-    float scale[RT];
+  // tail: the pair may be the last one, whose second chunk is missing for an odd chunk count
+  auto compute = [&](int p, int th, const Half& d, bool tail) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) scale[rt] = e8m0_to_f32(sc[4 * n_chunks * (rt * 16 + l16)]);
+    for (int j = 0; j < 2; ++j) {
+      if (j == 1 && tail && 2 * p + 1 >= n_chunks) break;
+      const int c = 2 * p + j;
+      const uint8_t* st = xs + (p & 1) * kStage + hs_r + 256 * j;
+      const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
+      float scale[HT];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const V bh = *reinterpret_cast<const V*>(st + 16 * k);
-      const V bl = *reinterpret_cast<const V*>(st + 16 * kDnXRow + 16 * k);
+      for (int r = 0; r < HT; ++r) scale[r] = e8m0_to_f32(sc[4 * n_chunks * ((HT * th + r) * 16 + l16)]);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const V a = decode8_bf16(d.q[rt][j][k], scale[rt]);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[rt], 0, 0, 0);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[rt], 0, 0, 0);
+      for (int k = 0; k < 4; ++k) {
+        const V bh = *reinterpret_cast<const V*>(st + 16 * k);
+        const V bl = *reinterpret_cast<const V*>(st + 16 * kRow + 16 * k);
+#pragma unroll
+        for (int r = 0; r < HT; ++r) {
+          const V a = decode8_bf16(d.q[r][j][k], scale[r]);
+          acc[HT * th + r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[HT * th + r], 0, 0, 0);
+          acc[HT * th + r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[HT * th + r], 0, 0, 0);
+        }
       }
     }
   };
-  auto compute_step = [&](int s, const Step& d) {
-#pragma unroll
-    for (int j = 0; j < CPS; ++j)
-      if (j == 0 || CPS * s + j < n_chunks) compute_chunk(s, j, d);
-  };
-  auto step = [&](int s, Step& D, u32x4 (&Hn)[LPT]) {  // as in gate/up
+  // Pair p: sync, publish pair p+1's h (held in Hn), compute both halves of pair p, each followed by
+  // the load of the same half of pair p+1 into its registers, then fetch pair p+3's h into Hn.  The
+  // prologue issues its loads in the same order.
+  auto pair = [&](int p, Half& A, Half& B, u32x4 (&Hn)[LPT]) {
     __syncthreads();
-    put_h(s + 1, Hn);
-#pragma unroll
-    for (int j = 0; j < CPS; ++j) compute_chunk(s, j, D);
-    load(s + 2, D);
+    put_h(p + 1, Hn);
+    compute(p, 0, A, false);
+    load(p + 1, 0, A);
     __builtin_amdgcn_sched_barrier(0);
-    fetch_h(s + 3, Hn);
+    compute(p, 1, B, false);
+    load(p + 1, 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_h(p + 3, Hn);
   };
-  Step A, B;
+  Half A, B;
+  u32x4 Hc[2][LPT];
   fetch_h(0, Hc[0]);
   __builtin_amdgcn_sched_barrier(0);
-  load(0, A);
+  load(0, 0, A);
   __builtin_amdgcn_sched_barrier(0);
   fetch_h(1, Hc[1]);
   __builtin_amdgcn_sched_barrier(0);
-  load(n_steps > 1 ? 1 : 0, B);
+  load(0, 1, B);
   __builtin_amdgcn_sched_barrier(0);
-  // scale table [row][n_chunks] dwords, filled while the first steps' loads are in flight
+  // scale table [row][n_chunks] dwords, filled while the first pair's loads are in flight
   {  // 8 loads in flight per lane, 16-byte units when possible
     const bool vec = (n_chunks & 3) == 0 && (down.sr & 15) == 0 &&
                      ((uintptr_t)(down.s + (int64_t)ex * down.se) & 15) == 0;
@@ -1116,25 +1120,32 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_rows_kernel(
   put_h(0, Hc[0]);
   fetch_h(2, Hc[0]);
   __builtin_amdgcn_sched_barrier(0);
-  int s = 0;
-  for (; s + 3 < n_steps; s += 2) {
-    step(s, A, Hc[1]);
+  int p = 0;  // even: Hc[1] holds pair p+1's h, Hc[0] pair p+2's
+  for (; p + 3 < n_pairs; p += 2) {
+    pair(p, A, B, Hc[1]);
     __builtin_amdgcn_sched_barrier(0);
-    step(s + 1, B, Hc[0]);
+    pair(p + 1, A, B, Hc[0]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // last 1-3 pairs: no loads past the end
   __syncthreads();
-  if (s + 1 < n_steps) put_h(s + 1, Hc[1]);
-  compute_step(s, A);
-  if (s + 2 < n_steps) load(s + 2, A);
-  if (s + 1 < n_steps) {
+  if (p + 1 < n_pairs) put_h(p + 1, Hc[1]);
+  compute(p, 0, A, true);
+  if (p + 1 < n_pairs) load(p + 1, 0, A);
+  compute(p, 1, B, true);
+  if (p + 1 < n_pairs) {
+    load(p + 1, 1, B);
     __syncthreads();
-    if (s + 2 < n_steps) put_h(s + 2, Hc[0]);
-    compute_step(s + 1, B);
+    if (p + 2 < n_pairs) put_h(p + 2, Hc[0]);
+    compute(p + 1, 0, A, true);
+    if (p + 2 < n_pairs) load(p + 2, 0, A);
+    compute(p + 1, 1, B, true);
+    if (p + 2 < n_pairs) load(p + 2, 1, B);
   }
-  if (s + 2 < n_steps) {
+  if (p + 2 < n_pairs) {
     __syncthreads();
-    compute_step(s + 2, A);
+    compute(p + 2, 0, A, true);
+    compute(p + 2, 1, B, true);
   }
 
   const int m = l16;
@@ -1541,19 +1552,20 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 // streams; below that the K-split kernels spread each expert over more workgroups.
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
-size_t gateup_rows_lds(int H, int rt) { return 2 * (size_t)kGuXStage + kNW * (size_t)stab_bytes(2 * 16 * rt, H / 128); }
-// Gate/up row tiles per wave: 2 (32 rows of each matrix), or 1 when 2-tile row blocks would give
-// fewer than kGuSmallBlocks workgroups (measured on the sweep workload: T = 8 167 -> 152 us,
-// T = 32 448 -> 430 us, T = 88 653 -> 640 us; from T = 128 on, 2 tiles are as fast or faster).
-constexpr int64_t kGuSmallBlocks = 4608;
+size_t gateup_rows_lds(int H, int rt, int nw) { return 2 * (size_t)kGuXStage + nw * (size_t)stab_bytes(2 * 16 * rt, H / 128); }
+// Gate/up row-split workgroups: one 16-row tile of each matrix per wave and 8 waves sharing each
+// x stage, or 4 waves when 8-wave row blocks would give fewer than kGuSmallBlocks workgroups
+// (measured on the sweep workload, 8 waves: T = 176 685 -> 667 us, T = 128 673 -> 657 us,
+// T = 64 600 -> 595 us, T = 8 153 -> 159 us; two tiles per wave were slower at every T).
+constexpr int64_t kGuSmallBlocks = 4096;
+constexpr int kGuNW = 8, kGuNWSmall = 4;
 // Waves per down workgroup (they share each h stage): 8, or 4 when 8-wave row blocks would give
 // fewer than kDnSmallBlocks workgroups -- then smaller workgroups fill the chip better (measured on
 // the sweep workload: T = 8 101 -> 94 us, T = 15 156 -> 149 us; from T = 64 on, 8 waves are faster).
 constexpr int kDnNW = 8, kDnNWSmall = 4;
 constexpr int64_t kDnSmallBlocks = 2048;
-constexpr int kDnCPS = 1;  // chunks per down step
 size_t down_rows_lds(int I, int nw) {
-  return 2 * (size_t)DnStage<kDnCPS>::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
+  return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
 }
 
 template <int FMT, int MT>
@@ -1561,16 +1573,17 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
                      const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
-  const int nb2 = (I + 16 * kRowsRT1 * kNW - 1) / (16 * kRowsRT1 * kNW);
-  const int rt = pl.tiles * nb2 < kGuSmallBlocks ? 1 : kRowsRT1;
-  const int nb_rows = (I + 16 * rt * kNW - 1) / (16 * rt * kNW);
-  if (MT == 1 && streamable && gateup_rows_lds(H, rt) <= kMaxLds && pl.tiles * nb2 >= kRowsMinBlocks) {
+  const int nb8 = (I + 16 * kGuNW - 1) / (16 * kGuNW);
+  const bool small = pl.tiles * nb8 < kGuSmallBlocks;
+  const int nw = small ? kGuNWSmall : kGuNW;
+  const int nb_rows = (I + 16 * nw - 1) / (16 * nw);
+  if (MT == 1 && streamable && gateup_rows_lds(H, 1, nw) <= kMaxLds && pl.tiles * nb8 >= kRowsMinBlocks) {
     const dim3 grid((unsigned)(pl.tiles * nb_rows));
-    if (rt == 1)
-      ffn_gateup_rows_kernel<kNW, 1><<<grid, kNW * 64, gateup_rows_lds(H, 1), stream>>>(
+    if (small)
+      ffn_gateup_rows_kernel<kGuNWSmall, 1><<<grid, kGuNWSmall * 64, gateup_rows_lds(H, 1, nw), stream>>>(
           (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
     else
-      ffn_gateup_rows_kernel<kNW, kRowsRT1><<<grid, kNW * 64, gateup_rows_lds(H, kRowsRT1), stream>>>(
+      ffn_gateup_rows_kernel<kGuNW, 1><<<grid, kGuNW * 64, gateup_rows_lds(H, 1, nw), stream>>>(
           (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
   } else if (streamable) {
     launch_gateup_stream<MT, kStRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
@@ -1595,10 +1608,10 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
     const dim3 grid((unsigned)(pl.tiles * nb_rows));
     if (small)
-      ffn_down_rows_kernel<kDnNWSmall, kDnCPS><<<grid, kDnNWSmall * 64, down_rows_lds(I, nw), stream>>>(
+      ffn_down_lines_kernel<kDnNWSmall><<<grid, kDnNWSmall * 64, down_rows_lds(I, nw), stream>>>(
           h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
     else
-      ffn_down_rows_kernel<kDnNW, kDnCPS><<<grid, kDnNW * 64, down_rows_lds(I, nw), stream>>>(
+      ffn_down_lines_kernel<kDnNW><<<grid, kDnNW * 64, down_rows_lds(I, nw), stream>>>(
           h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
     launch_down_stream<MT, kStRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);

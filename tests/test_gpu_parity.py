@@ -239,6 +239,26 @@ def test_expert_ffn_edges(orc, case):
     assert err <= LAYER_TOL
 
 
+# Wide matrices with about 16 rows per expert: enough row blocks for the 8-wave row-split kernels.
+# Down at 5 and 7 chunks of 128 (pairs of steps whose second chunk is missing; the 7-chunk case
+# also runs the steady loop); gate/up at 5 chunks (a last step with one chunk).  Sampled tokens
+# keep the oracle to a few seconds.
+FFN_WIDE = [(128, 16384, 640, 32, 4), (128, 16384, 896, 32, 4), (128, 640, 8192, 32, 4)]
+
+
+@pytest.mark.parametrize("case", FFN_WIDE, ids=[f"T{c[0]}-H{c[1]}-I{c[2]}-E{c[3]}-k{c[4]}" for c in FFN_WIDE])
+def test_expert_ffn_wide(orc, case):
+    T, H, I, E, k = case
+    note(f"expert ffn wide {case}")
+    wl = synth.custom(hidden=H, n_routed=E, top_k=k, inter=I, weight_format="mxfp4", act_dtype="bf16",
+                      router_std=0.3, weight_std=0.05)
+    L = synth.make_layer(wl, T, seed=22)
+    ids = orc.route(L.x, x_fmt(wl), L.router, L.bias, k)["ids"]
+    err = ffn_vs_oracle(orc, L, ids, sample_tokens=[0, 1, 2, 40, 63, 64, 100, 126, 127])
+    note(f"  max-abs / rms = {err:.3e}")
+    assert err <= LAYER_TOL
+
+
 @pytest.mark.parametrize("T,kt,H", [(1, 8, 4096), (37, 3, 96), (176, 8, 7168)])
 def test_combine(orc, T, kt, H):
     rng = np.random.default_rng(T)

@@ -1169,11 +1169,12 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
 }
 
 // ------------------------------------------------------------------------------------------------
-// Tile kernels for calls with many rows per expert (prefill): 64-token tiles.  Each wave decodes
-// its 32 weight rows once per chunk and applies them to all four 16-token sub-tiles, so the work is
-// MFMA-bound rather than decode- or HBM-bound.  The tile's activations (or h) go through a
-// two-stage LDS ring, written right after each step's barrier.  Block scales are loaded with the
-// weights (one dword per row and chunk).  Workgroups are numbered tile-major with the row blocks
+// Tile kernels for calls with many rows per expert (prefill, or FP16 slices with many tokens):
+// 128-token tiles.  A gate/up wave decodes its 16 rows of each matrix once per chunk and applies
+// them to all eight 16-token sub-tiles (a down wave: 32 rows, a 64-token half of a tile), so the
+// work is MFMA-bound rather than decode- or HBM-bound.  The tile's activations (or h) go through a
+// two-stage LDS ring, written right after each step's barrier.  MXFP4 block scales are loaded with
+// the weights (one dword per row and chunk); FP16 weights are four 16-byte loads per row and chunk.  Workgroups are numbered tile-major with the row blocks
 // padded to a multiple of 8, so row block j of every tile runs on XCD j % 8: the tiles of a hot
 // expert that run together read each weight row from one L2.  Sub-tiles past the tile's rows are
 // computed on zero activations (branching around their MFMAs would split the scheduled loop).
@@ -1183,7 +1184,56 @@ constexpr int kTileRT = 1;                     // 16-row tiles of each matrix pe
 constexpr int kDnTileMT = 4;                   // 16-token sub-tiles per down work item (half a tile)
 constexpr int kTileRow = 128 * 2 + 16;         // LDS bytes per token row of one plane of a stage
 
-template <int NW, int RT, int MT>
+// Weights of one lane for one 16-row tile in one 128-K chunk, as the tile kernels load them: the
+// 16-byte MXFP4 block plus the row's four block scales of the chunk (byte lq is the lane's), or
+// 4 x 16 bytes of fp16 (the lane's 32 consecutive K values).
+template <int FMT>
+struct TileW;
+template <>
+struct TileW<MOE_W_MXFP4> {
+  u32x4 q;
+  uint32_t sc;
+  static constexpr uint32_t kLaneBytes = 16;  // per lane-quarter of a row, per chunk
+};
+template <>
+struct TileW<MOE_W_FP16> {
+  u32x4 q[4];
+  static constexpr uint32_t kLaneBytes = 64;
+};
+template <int FMT>
+__device__ __forceinline__ void tile_load(TileW<FMT>& d, __amdgpu_buffer_rsrc_t w, __amdgpu_buffer_rsrc_t s,
+                                          uint32_t coff, uint32_t soff, int c) {
+  if constexpr (FMT == MOE_W_MXFP4) {
+    d.q = bld16(w, coff + 64u * c);
+    d.sc = bld4(s, soff + 4u * c);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d.q[k] = bld16(w, coff + 256u * c + 16u * k);
+  }
+}
+// k-th MFMA operand (K values 32*lq + 8k .. +7 of the chunk); scale = the lane's block scale
+template <int FMT>
+__device__ __forceinline__ typename Op<FMT>::V tile_operand(const TileW<FMT>& d, int k, float scale) {
+  if constexpr (FMT == MOE_W_MXFP4) return decode8_bf16(d.q[k], scale);
+  else return bitcast<f16x8>(d.q[k]);
+}
+template <int FMT>
+__device__ __forceinline__ float tile_scale(const TileW<FMT>& d, int lq) {
+  if constexpr (FMT == MOE_W_MXFP4) return e8m0_to_f32((d.sc >> (8 * lq)) & 255u);
+  else return 1.0f;
+}
+// Buffer descriptors of one expert's weight matrix (rows x K) and its scale grid (MXFP4 only).
+template <int FMT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_wrsrc(const ProjDev& p, int e, int rows, int K) {
+  return make_rsrc(p.w + (int64_t)e * p.we, (int64_t)(rows - 1) * p.wr + (FMT == MOE_W_MXFP4 ? K / 2 : 2 * K));
+}
+template <int FMT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_srsrc(const ProjDev& p, int e, int rows, int K) {
+  return FMT == MOE_W_MXFP4 ? make_rsrc(p.s + (int64_t)e * p.se, (int64_t)(rows - 1) * p.sr + K / 32)
+                            : make_rsrc(p.w, 0);
+}
+
+template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
@@ -1192,7 +1242,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
   constexpr int kStage = NTOK * kTileRow;
   constexpr int LPT = NTOK * 16 / (64 * NW);  // 16-byte lane-loads of x per thread per chunk
   static_assert(LPT * 64 * NW == NTOK * 16, "a chunk of x over the workgroup");
-  typedef bf16x8 V;
+  typedef typename Op<FMT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
   const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
@@ -1218,16 +1268,14 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
   }
   const uint32_t xs_r = (uint32_t)(l16 * kTileRow + 64 * lq);
 
-  const __amdgpu_buffer_rsrc_t wr[NM] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
-                                         make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
-  const __amdgpu_buffer_rsrc_t sr[NM] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
-                                         make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
+  const __amdgpu_buffer_rsrc_t wr[NM] = {tile_wrsrc<FMT>(gate, e, I, H), tile_wrsrc<FMT>(up, e, I, H)};
+  const __amdgpu_buffer_rsrc_t sr[NM] = {tile_srsrc<FMT>(gate, e, I, H), tile_srsrc<FMT>(up, e, I, H)};
   uint32_t coff[NM][RT], soff[NM][RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int n = min(n0 + rt * 16 + l16, I - 1);
-    coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
-    coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
+    coff[0][rt] = (uint32_t)(n * gate.wr) + TileW<FMT>::kLaneBytes * lq;
+    coff[1][rt] = (uint32_t)(n * up.wr) + TileW<FMT>::kLaneBytes * lq;
     soff[0][rt] = (uint32_t)(n * gate.sr);
     soff[1][rt] = (uint32_t)(n * up.sr);
   }
@@ -1242,17 +1290,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
     }
 
   struct Step {
-    u32x4 q[NM][RT];
-    uint32_t sc[NM][RT];  // the four block scales of the row in this chunk; byte lq is this lane's
+    TileW<FMT> w[NM][RT];
   };
   auto load = [&](int c, Step& d) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        d.q[m][rt] = bld16(wr[m], coff[m][rt] + 64u * c);
-        d.sc[m][rt] = bld4(sr[m], soff[m][rt] + 4u * c);
-      }
+      for (int rt = 0; rt < RT; ++rt) tile_load<FMT>(d.w[m][rt], wr[m], sr[m], coff[m][rt], soff[m][rt], c);
   };
   // x is fetched one chunk ahead (the next chunk's piece of this thread)
   u32x4 Xr[LPT];
@@ -1270,22 +1314,22 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) scl[m][rt] = e8m0_to_f32((d.sc[m][rt] >> (8 * lq)) & 255u);
+      for (int rt = 0; rt < RT; ++rt) scl[m][rt] = tile_scale<FMT>(d.w[m][rt], lq);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       V ag[RT], au[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        ag[rt] = decode8_bf16(d.q[0][rt][k], scl[0][rt]);
-        au[rt] = decode8_bf16(d.q[1][rt][k], scl[1][rt]);
+        ag[rt] = tile_operand<FMT>(d.w[0][rt], k, scl[0][rt]);
+        au[rt] = tile_operand<FMT>(d.w[1][rt], k, scl[1][rt]);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const V xb = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          accg[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[rt], xb, accg[rt][mt], 0, 0, 0);
-          accu[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[rt], xb, accu[rt][mt], 0, 0, 0);
+          accg[rt][mt] = Op<FMT>::mfma(ag[rt], xb, accg[rt][mt]);
+          accu[rt][mt] = Op<FMT>::mfma(au[rt], xb, accu[rt][mt]);
         }
       }
     }
@@ -1341,7 +1385,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
           const float g = accg[rt][mt][i], u = accu[rt][mt][i];
           const float h = (g / (1.0f + expf(-g))) * u;
           uint16_t hi, lo;
-          Op<MOE_W_MXFP4>::split(h, hi, lo);
+          Op<FMT>::split(h, hi, lo);
           h_hi[base + n] = hi;
           h_lo[base + n] = lo;
         }
@@ -1349,7 +1393,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
   }
 }
 
-template <int NW>
+template <int FMT, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
@@ -1358,7 +1402,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
   constexpr int HALVES = kTileMT / kDnTileMT;     // work items per tile
   constexpr int kStage = 2 * NTOK * kTileRow;     // hi plane, then lo plane
   constexpr int LPT = 2 * NTOK * 16 / (64 * NW);  // 16-byte lane-loads of h per thread per chunk
-  typedef bf16x8 V;
+  typedef typename Op<FMT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int item = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - item * n_nblk_pad;
   if (nblk >= n_nblk) return;
@@ -1389,13 +1433,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
   }
   const uint32_t hs_r = (uint32_t)(l16 * kTileRow + 64 * lq);
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
+  const __amdgpu_buffer_rsrc_t wr = tile_wrsrc<FMT>(down, ex, H, I);
+  const __amdgpu_buffer_rsrc_t sr = tile_srsrc<FMT>(down, ex, H, I);
   uint32_t coff[RT], soff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int n = min(n0 + rt * 16 + l16, H - 1);
-    coff[rt] = (uint32_t)(n * down.wr) + 16u * lq;
+    coff[rt] = (uint32_t)(n * down.wr) + TileW<FMT>::kLaneBytes * lq;
     soff[rt] = (uint32_t)(n * down.sr);
   }
 
@@ -1406,15 +1450,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
     for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   struct Step {
-    u32x4 q[RT];
-    uint32_t sc[RT];
+    TileW<FMT> w[RT];
   };
   auto load = [&](int c, Step& d) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      d.q[rt] = bld16(wr, coff[rt] + 64u * c);
-      d.sc[rt] = bld4(sr, soff[rt] + 4u * c);
-    }
+    for (int rt = 0; rt < RT; ++rt) tile_load<FMT>(d.w[rt], wr, sr, coff[rt], soff[rt], c);
   };
   // h is fetched one chunk ahead (its rows are shared by every row block of the tile and mostly
   // come from L2)
@@ -1431,7 +1471,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
     const uint8_t* st = lds + (c & 1) * kStage + hs_r;
     float scl[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) scl[rt] = e8m0_to_f32((d.sc[rt] >> (8 * lq)) & 255u);
+    for (int rt = 0; rt < RT; ++rt) scl[rt] = tile_scale<FMT>(d.w[rt], lq);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       V bh[MT], bl[MT];
@@ -1442,11 +1482,11 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const V a = decode8_bf16(d.q[rt][k], scl[rt]);
+        const V a = tile_operand<FMT>(d.w[rt], k, scl[rt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[mt], acc[rt][mt], 0, 0, 0);
-          acc[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[mt], acc[rt][mt], 0, 0, 0);
+          acc[rt][mt] = Op<FMT>::mfma(a, bh[mt], acc[rt][mt]);
+          acc[rt][mt] = Op<FMT>::mfma(a, bl[mt], acc[rt][mt]);
         }
       }
     }
@@ -1623,21 +1663,23 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   return hipGetLastError();
 }
 
-// The tile kernels (MXFP4 only; planned only when ffn_big_tiles() holds for the call).
+// The tile kernels (planned only when ffn_big_tiles() holds for the call).
+template <int FMT>
 hipError_t gateup_tile(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                        const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                        hipStream_t stream) {
   const int nb = (I + 16 * kTileRT * kNW - 1) / (16 * kTileRT * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-  ffn_gateup_tile_kernel<kNW, kTileRT, kTileMT><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64,
+  ffn_gateup_tile_kernel<FMT, kNW, kTileRT, kTileMT><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64,
                                                  2 * kTileMT * 16 * kTileRow, stream>>>(
       (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
   return hipGetLastError();
 }
+template <int FMT>
 hipError_t down_tile(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
                      float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
   const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-  ffn_down_tile_kernel<kNW><<<dim3((unsigned)(pl.tiles * (kTileMT / kDnTileMT) * nbp)), kNW * 64,
+  ffn_down_tile_kernel<FMT, kNW><<<dim3((unsigned)(pl.tiles * (kTileMT / kDnTileMT) * nbp)), kNW * 64,
                               2 * 2 * kDnTileMT * 16 * kTileRow, stream>>>(
       h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, nbp, y_slots);
   return hipGetLastError();
@@ -1669,7 +1711,7 @@ hipError_t down_fmt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev
 
 bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
                    const ProjDev& down) {
-  return fmt == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && stream_ok(down, I, H) &&
+  return (fmt == MOE_W_MXFP4 || fmt == MOE_W_FP16) && stream_ok(gate, H, I) && stream_ok(up, H, I) && stream_ok(down, I, H) &&
          (int64_t)T * H * 2 < INT32_MAX && (int64_t)T * k_total * I * 2 < INT32_MAX;
 }
 
@@ -1711,8 +1753,9 @@ hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_e
   const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
   const TileEntry* tiles = (const TileEntry*)table;
   if (pl.tile) {
-    if (fmt != MOE_W_MXFP4) return hipErrorInvalidValue;  // not planned for other formats
-    return gateup_tile(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+    if (fmt == MOE_W_FP16)
+      return gateup_tile<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+    return gateup_tile<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   }
   if (fmt == MOE_W_FP16)
     return gateup_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
@@ -1725,8 +1768,9 @@ hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big,
   const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
   const TileEntry* tiles = (const TileEntry*)table;
   if (pl.tile) {
-    if (fmt != MOE_W_MXFP4) return hipErrorInvalidValue;
-    return down_tile(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+    if (fmt == MOE_W_FP16)
+      return down_tile<MOE_W_FP16>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+    return down_tile<MOE_W_MXFP4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   }
   if (fmt == MOE_W_FP16)
     return down_fmt<MOE_W_FP16>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);

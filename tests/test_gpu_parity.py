@@ -218,6 +218,9 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     (300, 384, 256, 3, 2, "mxfp4", "routed"),
     (200, 128, 256, 4, 1, "mxfp4", "one-expert"),
     (70, 256, 128, 3, 2, "mxfp4", "two-experts"),
+    # the same tile kernels on FP16 weights: ragged tiles, 3 and 5 chunks of 128
+    (300, 384, 640, 3, 2, "fp16", "routed"),
+    (200, 128, 256, 4, 1, "fp16", "one-expert"),
 ]
 
 

@@ -5,10 +5,14 @@
 //
 // Work unit.  A "tile" is up to 16*MT consecutive sorted rows (tokens) of one expert; tiles are
 // numbered expert by expert, so an expert with n rows owns ceil(n / (16*MT)) tiles.  A workgroup
-// takes one tile and one block of 16*RT weight rows and covers the full reduction dimension K:
-// each of its NW waves reduces a contiguous share of K's 128-wide chunks, then the partial sums
-// meet in LDS.  Weights are therefore read from HBM once per tile -- once per active expert when
-// an expert has at most 16*MT tokens, which is the decode regime.
+// takes one tile and one block of weight rows and covers the full reduction dimension K, so the
+// weights are read from HBM once per tile -- once per active expert when an expert has at most
+// 16*MT tokens, which is the decode regime.  Four kernel families split that work differently:
+//   K-split (general and streaming kernels): the NW waves reduce contiguous shares of K's
+//     128-wide chunks for the same 16*RT rows, and the partial sums meet in LDS (few tiles);
+//   row-split streaming kernels: the waves own different rows over the whole K and share the
+//     tile's activations (or h) through LDS (many small tiles: the decode sweep);
+//   tile kernels: 128-token tiles for experts with many rows (prefill).
 //
 // MFMA mapping (v_mfma_f32_16x16x32_{bf16,f16}).  A = 16 weight rows x 32 k, B = 32 k x 16 tokens,
 // D = 16 rows x 16 tokens.  Lane l holds A row l%16 and B column l%16 with k slots
@@ -1578,9 +1582,9 @@ inline bool stream_ok(const ProjDev& p, int K, int64_t rows) {
          rows * p.wr < INT32_MAX;
 }
 
-// Streaming kernels: RT 16-row tiles per workgroup (2 for gate/up -- 32 rows of each matrix --
-// and 4 for down).  Wider blocks amortise each activation chunk over more weight rows but cost
-// occupancy; measured on the sweep workload, these were the best.
+// K-split streaming kernels: RT 16-row tiles per workgroup (kStRT1 of each matrix for gate/up,
+// kStRT2 for down).  Wider blocks amortise each activation chunk over more weight rows but cost
+// occupancy and workgroups.
 template <int MT, int RT>
 void launch_gateup_stream(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate,
                           ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,

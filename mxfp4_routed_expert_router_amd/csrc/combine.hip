@@ -1,12 +1,17 @@
 // Weighted combine (Cascadia, Sec. 3.1 "weighted reduction"; FP32 output as in Cascadia Fig. 2):
 //   y[t, :] = sum_{j ascending} weights[t, j] * y_slots[t*k + j, :]
 // One thread owns four consecutive outputs of one token (16-byte loads and stores); no atomics.
+// The slots are read in batches of kBatch with all of a batch's loads issued before the first
+// multiply-add (a load-then-use loop waits one memory latency per slot); indices past the last
+// slot re-read the last one (a cache hit) and their products are dropped.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
+constexpr int kBatch = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_slots,
                                                       const float* __restrict__ weights, int T, int k_total,
                                                       int H, float* __restrict__ y) {
@@ -16,13 +21,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(i / h4), c = (int)(i % h4) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const float* src = y_slots + (int64_t)t * k_total * H + c;
-  for (int j = 0; j < k_total; ++j) {
-    const float w = weights[(int64_t)t * k_total + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (int64_t)j * H);
-    acc[0] += w * v[0];
-    acc[1] += w * v[1];
-    acc[2] += w * v[2];
-    acc[3] += w * v[3];
+  const float* wt = weights + (int64_t)t * k_total;
+  for (int j0 = 0; j0 < k_total; j0 += kBatch) {
+    float w[kBatch];
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = min(j0 + u, k_total - 1);
+      w[u] = wt[j];
+      v[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)j * H);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // selects, not a branch: the loads stay ahead of the adds
+      const bool ok = j0 + u < k_total;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float s = acc[e] + w[u] * v[u][e];
+        acc[e] = ok ? s : acc[e];
+      }
+    }
   }
   *reinterpret_cast<f32x4*>(y + (int64_t)t * H + c) = acc;
 }

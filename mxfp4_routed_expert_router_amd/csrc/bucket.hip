@@ -22,10 +22,17 @@ struct SlotRank {
   int rank;  // number of earlier slots in the chunk with the same key
 };
 
-// Rank of this thread's slot within its chunk.  wave_counts: LDS [kWaves][n_buckets + 1].
-// Leaves wave_counts filled (per-wave counts of every key) and ends with a barrier.
-__device__ SlotRank chunk_rank(const int32_t* __restrict__ ids, int n_slots, int n_buckets, int chunk,
-                               int* wave_counts) {
+// This thread's id in chunk `chunk` (read before ranking, so that a workgroup ranking several
+// chunks issues all of their reads together), or -1 past the end.
+__device__ __forceinline__ int chunk_id(const int32_t* __restrict__ ids, int n_slots, int chunk) {
+  const int s = chunk * kBucketChunk + threadIdx.x;
+  return s < n_slots ? ids[s] : -1;
+}
+
+// Rank of this thread's slot within its chunk, given its id from chunk_id.  wave_counts: LDS
+// [kWaves][n_buckets + 1].  Leaves wave_counts filled (per-wave counts of every key) and ends with
+// a barrier.
+__device__ SlotRank chunk_rank(int id, int n_slots, int n_buckets, int chunk, int* wave_counts) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int stride = n_buckets + 1;
   for (int i = tid; i < kWaves * stride; i += kBucketChunk) wave_counts[i] = 0;
@@ -33,7 +40,7 @@ __device__ SlotRank chunk_rank(const int32_t* __restrict__ ids, int n_slots, int
   const bool in = s < n_slots;
   int key = -1;
   if (in) {
-    key = ids[s];
+    key = id;
     if (key < 0 || key >= n_buckets) key = n_buckets;
   }
   uint64_t same = __ballot(in);
@@ -108,13 +115,16 @@ __global__ __launch_bounds__(kBucketChunk) void bucket_fused_kernel(const int32_
   int* scratch = base + n_buckets;                     // [kWaves+1]
   const int tid = threadIdx.x;
   const int n_chunks = (n_slots + kBucketChunk - 1) / kBucketChunk;  // 1 .. kFusedChunks
+  int id[kFusedChunks];
+#pragma unroll
+  for (int c = 0; c < kFusedChunks; ++c) id[c] = chunk_id(ids, n_slots, c);
   SlotRank r[kFusedChunks];
 #pragma unroll
   for (int c = 0; c < kFusedChunks; ++c) {
     r[c].key = -1;
     r[c].rank = 0;
     if (c < n_chunks) {  // uniform
-      r[c] = chunk_rank(ids, n_slots, n_buckets, c, wave_counts);
+      r[c] = chunk_rank(id[c], n_slots, n_buckets, c, wave_counts);
       for (int b = tid; b < n_buckets; b += kBucketChunk) {
         int v = 0;
         for (int w = 0; w < kWaves; ++w) v += wave_counts[w * stride + b];
@@ -159,7 +169,7 @@ __global__ __launch_bounds__(kBucketChunk) void bucket_rank_kernel(const int32_t
                                                                     int32_t* __restrict__ table) {
   extern __shared__ int lds[];
   const int chunk = blockIdx.x;
-  SlotRank r = chunk_rank(ids, n_slots, n_buckets, chunk, lds);
+  SlotRank r = chunk_rank(chunk_id(ids, n_slots, chunk), n_slots, n_buckets, chunk, lds);
   const int s = chunk * kBucketChunk + threadIdx.x;
   if (s < n_slots) rank[s] = r.rank;
   for (int b = threadIdx.x; b < n_buckets; b += kBucketChunk) {

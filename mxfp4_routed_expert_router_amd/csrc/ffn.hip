@@ -1252,7 +1252,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_srsrc(const ProjDev& p, i
 }
 
 template <int FMT, int NW, int RT, int MT>
-__global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
+__global__ __launch_bounds__(NW * 64, FMT == MOE_W_MXFP4 ? 2 : 1) void ffn_gateup_tile_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     int n_nblk_pad, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
@@ -1352,42 +1352,47 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_tile_kernel(
       }
     }
   };
-  auto step = [&](int c, Step& D) {
+  // Weights three chunks deep (register sets A, B, C; two waves per SIMD for MXFP4 needs the
+  // register cap in the launch bounds), activations one chunk ahead.  Measured on the prefill
+  // layer: 6.0 -> 5.66 ms; the same for the down kernel gave nothing and cost FP16 occupancy.
+  auto step = [&](int c, Step& D) {  // D holds chunk c; refilled with chunk c + 3
     __syncthreads();
     put_x(c + 1);
     fetch_x(c + 2);
     __builtin_amdgcn_sched_barrier(0);
     compute(c, D);
-    load(c + 2, D);
+    load(c + 3, D);
   };
-  Step A, B;
+  // the last 1-5 chunks: no loads past the end
+  auto tail_step = [&](int c, Step& D) {
+    __syncthreads();
+    if (c + 1 < n_chunks) put_x(c + 1);
+    if (c + 2 < n_chunks) fetch_x(c + 2);
+    compute(c, D);
+    if (c + 3 < n_chunks) load(c + 3, D);
+  };
+  Step A, B, C;
   fetch_x(0);
   load(0, A);
-  load(n_chunks > 1 ? 1 : 0, B);
+  load(min(1, n_chunks - 1), B);
+  load(min(2, n_chunks - 1), C);
   put_x(0);
   fetch_x(1);
   __builtin_amdgcn_sched_barrier(0);
   int c = 0;
-  for (; c + 3 < n_chunks; c += 2) {
+  for (; c + 5 < n_chunks; c += 3) {
     step(c, A);
     __builtin_amdgcn_sched_barrier(0);
     step(c + 1, B);
     __builtin_amdgcn_sched_barrier(0);
+    step(c + 2, C);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();
-  if (c + 1 < n_chunks) put_x(c + 1);
-  if (c + 2 < n_chunks) fetch_x(c + 2);
-  compute(c, A);
-  if (c + 2 < n_chunks) load(c + 2, A);
-  if (c + 1 < n_chunks) {
-    __syncthreads();
-    if (c + 2 < n_chunks) put_x(c + 2);
-    compute(c + 1, B);
-  }
-  if (c + 2 < n_chunks) {
-    __syncthreads();
-    compute(c + 2, A);
-  }
+  tail_step(c, A);
+  if (c + 1 < n_chunks) tail_step(c + 1, B);
+  if (c + 2 < n_chunks) tail_step(c + 2, C);
+  if (c + 3 < n_chunks) tail_step(c + 3, A);
+  if (c + 4 < n_chunks) tail_step(c + 4, B);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {

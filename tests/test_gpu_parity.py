@@ -262,7 +262,7 @@ def test_expert_ffn_wide(orc, case):
     assert err <= LAYER_TOL
 
 
-@pytest.mark.parametrize("T,kt,H", [(1, 8, 4096), (37, 3, 96), (176, 8, 7168)])
+@pytest.mark.parametrize("T,kt,H", [(1, 8, 4096), (37, 3, 96), (176, 8, 7168), (5, 11, 256), (3, 16, 64)])
 def test_combine(orc, T, kt, H):
     rng = np.random.default_rng(T)
     ys = rng.standard_normal((T * kt, H)).astype(np.float32) * 1e3

@@ -1175,7 +1175,9 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
       for (int rt = 0; rt < RT; ++rt) {
         const int n = n0 + rt * 16 + 4 * lq;
         if ((H & 3) == 0 && n + 3 < H) {
-          *reinterpret_cast<f32x4*>(dst + n) = acc[rt];
+          // streaming stores: y_slots is read by the next call, not by this kernel, and keeping it
+          // out of L2 shortens the end-of-kernel write-back (T = 176: 378 -> 374 us)
+          __builtin_nontemporal_store(acc[rt], reinterpret_cast<f32x4*>(dst + n));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)

@@ -1626,9 +1626,10 @@ constexpr int64_t kGuSmallBlocks = 4096;
 constexpr int kGuNW = 8, kGuNWSmall = 4;
 // Waves per down workgroup (they share each h stage): 8, or 4 when 8-wave row blocks would give
 // fewer than kDnSmallBlocks workgroups -- then smaller workgroups fill the chip better (measured on
-// the sweep workload: T = 8 101 -> 94 us, T = 15 156 -> 149 us; from T = 64 on, 8 waves are faster).
+// the sweep workload with the whole-line kernel, 4 waves: T = 8 91 -> 84 us, T = 32 236 -> 229 us,
+// T = 64 321 -> 318 us; from T = 128 on, 8 waves are as fast or faster: T = 176 372 against 383 us).
 constexpr int kDnNW = 8, kDnNWSmall = 4;
-constexpr int64_t kDnSmallBlocks = 2048;
+constexpr int64_t kDnSmallBlocks = 4096;
 size_t down_rows_lds(int I, int nw) {
   return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
 }

@@ -965,18 +965,31 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
     const int64_t base = (int64_t)(ti.r0 + m) * I;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
+    {  // four consecutive h values of one token: one 8-byte store per plane
+      const int nb = n0 + rt * 16 + 4 * lq;
+      uint32_t ph[2], pl[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = n0 + rt * 16 + 4 * lq + i;
-        if (n < I) {
-          const float g = accg[rt][i], u = accu[rt][i];
-          const float h = (g / (1.0f + expf(-g))) * u;
-          uint16_t hi, lo;
-          Op<MOE_W_MXFP4>::split(h, hi, lo);
-          h_hi[base + n] = hi;
-          h_lo[base + n] = lo;
-        }
+        const float g = accg[rt][i], u = accu[rt][i];
+        const float h = (g / (1.0f + expf(-g))) * u;
+        uint16_t hi, lo;
+        Op<MOE_W_MXFP4>::split(h, hi, lo);
+        if (i & 1) { ph[i >> 1] |= (uint32_t)hi << 16; pl[i >> 1] |= (uint32_t)lo << 16; }
+        else { ph[i >> 1] = hi; pl[i >> 1] = lo; }
       }
+      if ((I & 3) == 0 && nb + 3 < I) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(h_hi + base + nb) = u32x2{ph[0], ph[1]};
+        *reinterpret_cast<u32x2*>(h_lo + base + nb) = u32x2{pl[0], pl[1]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nb + i < I) {
+            h_hi[base + nb + i] = (uint16_t)(ph[i >> 1] >> (16 * (i & 1)));
+            h_lo[base + nb + i] = (uint16_t)(pl[i >> 1] >> (16 * (i & 1)));
+          }
+      }
+    }
   }
 }
 

@@ -218,6 +218,10 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     (300, 384, 256, 3, 2, "mxfp4", "routed"),
     (200, 128, 256, 4, 1, "mxfp4", "one-expert"),
     (70, 256, 128, 3, 2, "mxfp4", "two-experts"),
+    # 7 and 9 chunks of 128 in gate/up: the three-deep weight ring ends with 4 and 3 chunks left
+    # (5 on the prefill and dense workloads, 1 and 2 above)
+    (200, 896, 256, 4, 1, "mxfp4", "one-expert"),
+    (160, 1152, 128, 3, 2, "mxfp4", "routed"),
     # the same tile kernels on FP16 weights: ragged tiles, 3 and 5 chunks of 128
     (300, 384, 640, 3, 2, "fp16", "routed"),
     (200, 128, 256, 4, 1, "fp16", "one-expert"),

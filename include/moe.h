@@ -9,10 +9,11 @@
  *        decode inside the reduction with FP32 accumulation, row-major banks read with no repack.
  *  [BP]  same post, section "Why it would not run": a partition that cuts an FP4 32-value block
  *        is rejected instead of producing garbage; weights and scale grids are sliced together.
- *  [C31] "Cascadia: Resident 975B MoE Inference on Eleven AI PCs", Sec. 3.1: expert-major banks;
- *        gate/up projections, SwiGLU, down projection and weighted reduction over the selected
- *        experts; routing yields expert ids and routing weights; shared experts are always-included
- *        selections after the routed ones.
+ *  [C31] "Cascadia: Resident 975B MoE Inference on Eleven AI PCs", Sec. 3.1: expert weights are
+ *        stored expert by expert; each selected expert is a SwiGLU block (two input projections,
+ *        the gated activation, one output projection) whose outputs are summed with the routing
+ *        coefficients; the router hands the expert path ids plus coefficients, and shared experts
+ *        are selections every row carries after its routed ones.
  *  [C32] Cascadia Sec. 3.2: a layer call supplies rows, expert ids and routing weights; the
  *        expert path returns FP32 output (Fig. 2).
  *  [C34] Cascadia Sec. 3.4, Eq. 2: a dense FFN is the sum of its all-active, unit-weight slices,
@@ -49,8 +50,8 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,      /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,     /* a size is negative, zero where it must not be, or beyond a limit */
-  MOE_ERR_BLOCK = 3,     /* an MXFP4 dimension, slice or stride cuts a 32-value block [BP] */
-  MOE_ERR_ALIGN = 4,     /* a pointer or byte stride is not 16-byte aligned */
+  MOE_ERR_BLOCK = 3,     /* an MXFP4 dimension, slice base or stride cuts a 32-value block [BP] */
+  MOE_ERR_ALIGN = 4,     /* a pointer or byte stride is not aligned (activations, outputs, FP16) */
   MOE_ERR_DTYPE = 5,     /* an unknown enum value, or an activation dtype the format cannot take */
   MOE_ERR_TOPK = 6,      /* top_k < 1 or top_k > E */
   MOE_ERR_WORKSPACE = 7, /* workspace NULL or smaller than the size query returns */
@@ -64,15 +65,17 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP16 = 1 } moe_w_format;
  *  MXFP4: `w` holds two E2M1 codes per byte, element k of a row in byte k/2 with even k in the
  *         low nibble (bits 3..0) and odd k in the high nibble; bit 3 of a code is its sign.
  *         `scales` holds one E8M0 byte per 32 elements: scale of element k at byte k/32 of the
- *         row.  Decoded weight = v(code) * 2^(scale - 127) [MX].  Scale codes 0..254 are
- *         supported; 255 is outside the contract.
+ *         row.  Decoded weight = v(code) * 2^(scale - 127) [MX].  Scale codes 0..252 are
+ *         supported (every decoded value is then finite in fp32 and bf16); at 253 and 254 the
+ *         largest magnitudes overflow bf16, and 255 is outside the contract.
  *  FP16:  `w` holds IEEE binary16 values; `scales` must be NULL.
  *  Strides are in bytes between consecutive experts / rows, so a projection may be a slice of a
  *  larger matrix [C34] -- e.g. columns [j*I, (j+1)*I) of a dense [H][8*I] down projection have
  *  w = base + j*I*(bytes per element), w_expert_stride = I*(bytes per element),
  *  w_row_stride = 8*I*(bytes per element).  w, w_expert_stride and w_row_stride must be
- *  multiples of 16 bytes (for MXFP4 that is exactly one 32-code block, so an aligned slice never
- *  cuts a block [BP]); scale pointers and strides have no alignment rule. */
+ *  multiples of 16 bytes: for MXFP4 that is exactly one 32-code block, so a base or stride off
+ *  that grid would start inside a block and is refused with MOE_ERR_BLOCK [BP]; for FP16 it is
+ *  the 128-bit load alignment (MOE_ERR_ALIGN).  Scale pointers and strides have no alignment rule. */
 typedef struct {
   const void *w;
   const uint8_t *scales;
@@ -147,8 +150,8 @@ moe_status moe_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *c
  *   workspace moe_expert_ffn_workspace_bytes(T, k_total, W) bytes, 16-byte aligned
  * Sorted rows whose slot lies outside [0, T*k_total) are skipped, so corrupt device-side indices
  * cannot cause out-of-bounds accesses.
- * Errors: NULL, SHAPE, BLOCK (MXFP4 hidden or inter not a multiple of 32), ALIGN, DTYPE,
- * WORKSPACE, HIP. */
+ * Errors: NULL, SHAPE, BLOCK (MXFP4 hidden or inter not a multiple of 32, or a weight base or
+ * stride that cuts a 32-value block), ALIGN, DTYPE, WORKSPACE, HIP. */
 size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weights *W);
 moe_status moe_expert_ffn(const void *x, moe_act_dtype x_dtype, int T, int k_total,
                           const moe_expert_weights *W, const int32_t *offsets,
@@ -250,7 +253,8 @@ moe_status moe_combine(const float *y_slots, const float *weights, int T, int k_
  * exact in bf16 whenever it is finite (all scale codes 0..252; larger codes can overflow).
  *   codes [n_rows] rows of K/2 bytes at code_row_stride; scales [n_rows] rows of K/32 bytes at
  *   scale_row_stride; out [n_rows][K] bf16 (uint16 bits), 16-byte aligned.
- * Errors: NULL, SHAPE, BLOCK (K % 32), ALIGN, HIP. */
+ * Errors: NULL, SHAPE, BLOCK (K % 32, or codes / code_row_stride off the 16-byte block grid),
+ * ALIGN (out), HIP. */
 moe_status moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int n_rows, int K,
                              int64_t code_row_stride, int64_t scale_row_stride, uint16_t *out,
                              void *stream);

@@ -28,7 +28,11 @@ moe_status check_proj(const moe_proj& p, moe_w_format fmt, int n_experts, int N,
     if (K % 32 != 0) return MOE_ERR_SHAPE;
     if (p.w_row_stride < 2 * (int64_t)K || p.w_expert_stride < 0) return MOE_ERR_SHAPE;
   }
-  if (!al16(p.w) || p.w_row_stride % 16 != 0 || p.w_expert_stride % 16 != 0) return MOE_ERR_ALIGN;
+  // A 16-byte step of packed MXFP4 codes is exactly one 32-value block, so a base or stride off that
+  // grid starts a slice inside a block (FreeToken DeepSeek-V4-Flash post, "Why it would not run":
+  // such partitions are refused).  For FP16 weights the same rule is only the 128-bit load alignment.
+  if (!al16(p.w) || p.w_row_stride % 16 != 0 || p.w_expert_stride % 16 != 0)
+    return fmt == MOE_W_MXFP4 ? MOE_ERR_BLOCK : MOE_ERR_ALIGN;
   (void)n_experts;
   (void)N;
   return MOE_OK;
@@ -375,7 +379,8 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int n_
   if (K % 32 != 0) return MOE_ERR_BLOCK;
   if (!codes || !scales || !out) return MOE_ERR_NULL;
   if (code_row_stride < K / 2 || scale_row_stride < K / 32) return MOE_ERR_SHAPE;
-  if (!al16(codes) || code_row_stride % 16 != 0 || !al16(out)) return MOE_ERR_ALIGN;
+  if (!al16(codes) || code_row_stride % 16 != 0) return MOE_ERR_BLOCK;  // a row would start mid-block
+  if (!al16(out)) return MOE_ERR_ALIGN;
   return hip_status(moe::launch_dequant(codes, scales, n_rows, K, code_row_stride, scale_row_stride, out,
                                         (hipStream_t)stream));
 }

@@ -1,7 +1,7 @@
-// Grouped SwiGLU expert FFN over the buckets (Cascadia, Sec. 3.1: gate/up projections, SwiGLU and
-// down projection of the selected experts), with MXFP4 decode inside the reduction and FP32
-// accumulation (FreeToken DeepSeek-V4-Flash post, "MXFP4 is not NVFP4": scales load once per
-// 32-weight block and broadcast; no BF16 copy of an expert is ever materialised).
+// Grouped SwiGLU expert FFN over the buckets (Cascadia, Sec. 3.1), with the MXFP4 weights decoded
+// in registers as part of each dot product and summed in FP32 (FreeToken DeepSeek-V4-Flash post,
+// "MXFP4 is not NVFP4"): every lane fetches a block's scale byte together with its 16 code bytes,
+// and the decoded weights exist only as MFMA operands, never as a bf16 matrix in memory.
 //
 // Work unit.  A "tile" is up to 16*MT consecutive sorted rows (tokens) of one expert; tiles are
 // numbered expert by expert, so an expert with n rows owns ceil(n / (16*MT)) tiles.  A workgroup

@@ -130,9 +130,13 @@ def test_expert_ffn_validation():
     assert ffn(weights(), T=-3) == SHAPE
     assert ffn(weights(gate__w=None)) == NULL
     assert ffn(weights(down__scales=None)) == NULL
-    assert ffn(weights(up__w=P + 8)) == ALIGN
-    assert ffn(weights(gate__w_row_stride=40)) == ALIGN   # >= K/2 = 32 but not a multiple of 16
-    assert ffn(weights(down__w_expert_stride=100 * 16 + 8)) == ALIGN
+    # MXFP4: a base or byte stride off the 16-byte grid starts inside a 32-value block
+    assert ffn(weights(up__w=P + 8)) == BLOCK
+    assert ffn(weights(gate__w_row_stride=40)) == BLOCK   # >= K/2 = 32 but not a multiple of 16
+    assert ffn(weights(down__w_expert_stride=100 * 16 + 8)) == BLOCK
+    # FP16 weights: the same offsets only break the 128-bit load alignment
+    assert ffn(weights(fmt=m.MOE_W_FP16, up__w=P + 8), xdt=1) == ALIGN
+    assert ffn(weights(fmt=m.MOE_W_FP16, down__w_expert_stride=100 * 16 + 8), xdt=1) == ALIGN
     assert ffn(weights(gate__w_row_stride=16)) == SHAPE   # rows would overlap
     assert ffn(weights(), x=fake(4)) == ALIGN
     assert ffn(weights(), ws=fake(0x4008)) == ALIGN
@@ -141,7 +145,7 @@ def test_expert_ffn_validation():
     assert need >= 4 * 4 * 2 * 96
     assert ffn(W, wsb=need - 1) == WORKSPACE
     # a slice of a larger MXFP4 projection that starts mid-block (8 bytes = 16 codes) is refused
-    assert ffn(weights(down__w=P + 0x10000 + 8)) == ALIGN
+    assert ffn(weights(down__w=P + 0x10000 + 8)) == BLOCK
 
 
 def test_expert_ffn_plan_validation():
@@ -222,7 +226,9 @@ def test_combine_and_dequant_validation():
     assert L.moe_combine(fake(4), fake(0x100), 4, 2, 64, fake(0x200), None) == ALIGN
     assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 48, 24, 2, fake(0x200), None) == BLOCK
     assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 64, 16, 2, fake(0x200), None) == SHAPE
-    assert L.moe_mxfp4_dequant(fake(8), fake(0x100), 3, 64, 32, 2, fake(0x200), None) == ALIGN
+    assert L.moe_mxfp4_dequant(fake(8), fake(0x100), 3, 64, 32, 2, fake(0x200), None) == BLOCK
+    assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 64, 40, 2, fake(0x200), None) == BLOCK
+    assert L.moe_mxfp4_dequant(fake(), fake(0x100), 3, 64, 32, 2, fake(0x208), None) == ALIGN
     assert L.moe_mxfp4_dequant(None, fake(0x100), 3, 64, 32, 2, fake(0x200), None) == NULL
 
 

@@ -269,11 +269,12 @@ def test_mx_expert_ffn(orc, name, T, sample, fmt):
     assert mx_ffn_case(orc, L, ids, fmt, sample) <= LAYER_TOL
 
 
-@pytest.mark.parametrize("fmt", ["fp6", "fp8"])
+@pytest.mark.parametrize("fmt", ["fp6", "fp8", "fp4"])
 def test_mx_layer_prefill(orc, fmt):
     """The whole prefill layer (T=8192, 256 routed + 1 shared expert, skewed routing) in MX mode,
-    as the benchmark runs it; the oracle checks tokens of the hottest and coldest experts, with the
-    same h check as the FFN tests (tokens with an h value on a rounding point get the looser bound)."""
+    as the benchmark runs it; the oracle checks tokens of the hottest expert (its first and last
+    128-row tiles) and of the coldest one, with the same h check as the FFN tests (tokens with an h
+    value on a rounding point get the looser bound)."""
     f_lib, f_orc, bits = FORMATS[fmt]
     L = host_layer("prefill", 8192)
     wl = L.wl
@@ -290,7 +291,10 @@ def test_mx_layer_prefill(orc, fmt):
     counts = np.bincount(r["ids"][:, :wl.top_k].reshape(-1), minlength=wl.n_routed)
     hot, cold = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
     has = lambda e: np.nonzero((r["ids"][:, :wl.top_k] == e).any(axis=1))[0]
-    sample = sorted(set(has(hot)[:3].tolist() + has(cold)[:3].tolist() + [0, T - 1]))
+    h = has(hot)
+    last = (len(h) - 1) // 128 * 128  # first token of the hot expert's last 128-row tile
+    sample = sorted(set(h[:3].tolist() + h[last:last + 2].tolist() + h[-2:].tolist() + has(cold)[:3].tolist()
+                        + [0, T - 1]))
     sample = np.array([s for s in sample if r["near_tie"][s] == 0])
     note(f"  sampled tokens {sample.tolist()} (hot expert {hot}: {counts[hot]} tokens, cold {cold}: {counts[cold]})")
     b = orc.bucket(r["ids"], wl.n_experts)

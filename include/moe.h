@@ -158,6 +158,22 @@ moe_status moe_expert_ffn(const void *x, moe_act_dtype x_dtype, int T, int k_tot
                           const int32_t *sorted_slot, float *y_slots, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* moe_expert_ffn_static -- moe_expert_ffn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels
+ * and the same results, bit for bit, with the workspace taken from a fixed array of
+ * MOE_FFN_STATIC_SCRATCH_BYTES bytes inside the library's device code (one per GPU, held until the
+ * process ends) instead of a caller buffer.  The call allocates nothing.  Limit: calls whose
+ * moe_expert_ffn_workspace_bytes(T, k_total, W) exceeds MOE_FFN_STATIC_SCRATCH_BYTES are refused
+ * with MOE_ERR_WORKSPACE (with inter 2048 and top-8 that is T = 256 and above).  Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU (different streams, or
+ * several host threads) race and give wrong results; calls ordered on one stream are safe.
+ * Arguments and other errors as for moe_expert_ffn; HIP also when the array's device address
+ * cannot be looked up. */
+#define MOE_FFN_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_expert_ffn_static(const void *x, moe_act_dtype x_dtype, int T, int k_total,
+                                 const moe_expert_weights *W, const int32_t *offsets,
+                                 const int32_t *sorted_slot, float *y_slots, void *stream);
+
 /* The three steps of moe_expert_ffn as separate calls, for callers that time or overlap them.
  * moe_expert_ffn_plan writes the tile schedule (which expert and sorted rows each 16-row tile
  * covers, from offsets) into the workspace; moe_expert_ffn_gateup computes

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_workspace_bytes.argtypes = [i, i, ctypes.POINTER(moe_expert_weights)]
         L.moe_expert_ffn.restype = i
         L.moe_expert_ffn.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp, st, vp]
+        L.moe_expert_ffn_static.restype = i
+        L.moe_expert_ffn_static.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp]
         L.moe_expert_ffn_plan.restype = i
         L.moe_expert_ffn_plan.argtypes = [i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, st, vp]
         L.moe_expert_ffn_gateup.restype = i
@@ -239,6 +241,22 @@ def moe_expert_ffn(x: torch.Tensor, W: ExpertWeights, offsets: torch.Tensor, sor
     return y
 
 
+MOE_FFN_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_expert_ffn_static(x: torch.Tensor, W: ExpertWeights, offsets: torch.Tensor, sorted_slot: torch.Tensor,
+                          k_total: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_expert_ffn with the library's fixed device scratch array as its workspace (no workspace
+    argument; calls needing more than MOE_FFN_STATIC_SCRATCH_BYTES are refused).  Only `out` may be
+    allocated here, and only when the caller passes none."""
+    T = x.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((T * k_total, W.hidden), dtype=torch.float32, device=dev)
+    _check(lib().moe_expert_ffn_static(_ptr(x), _act_dtype(x), T, k_total, ctypes.byref(W.c), _ptr(offsets),
+                                       _ptr(sorted_slot), _ptr(y), _stream(dev)), "moe_expert_ffn_static")
+    return y
+
+
 def moe_expert_ffn_plan(T: int, W: ExpertWeights, offsets: torch.Tensor, k_total: int,
                         workspace: torch.Tensor) -> None:
     """Step 1 of moe_expert_ffn: the tile schedule (from offsets) into `workspace`
@@ -382,7 +400,7 @@ class MoELayer:
         return moe_combine(self.y_slots, self.weights, out=self.y)
 
 
-__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
+__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
            "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
            "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",

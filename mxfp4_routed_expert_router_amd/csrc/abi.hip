@@ -3,6 +3,9 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/moe.h"
@@ -236,6 +239,60 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
   if (err != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, big, H, I, dev(W->down), sorted_slot, y_slots,
                                          h_hi, h_lo, table, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// moe_expert_ffn_static: moe_expert_ffn with its workspace (h planes and tile table) in a fixed
+// device array instead of a caller buffer.  In host code `scratch` only names a host-side stand-in;
+// the array's device address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_FFN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn_static(const void* x, moe_act_dtype x_dtype, int T, int k_total,
+                                 const moe_expert_weights* W, const int32_t* offsets, const int32_t* sorted_slot,
+                                 float* y_slots, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (!W) return MOE_ERR_NULL;
+  if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN || (int64_t)T * k_total > INT_MAX)
+    return MOE_ERR_SHAPE;
+  const size_t need = moe_expert_ffn_workspace_bytes(T, k_total, W);
+  if (need > MOE_FFN_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const moe_status st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  // Every byte the kernels read from the workspace is written earlier in the same call (the plan
+  // writes all tile-table entries, gate/up every h row that down reads), so nothing is cleared.
+  return moe_expert_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, ws, MOE_FFN_STATIC_SCRATCH_BYTES,
+                        stream);
 }
 
 // ---------------------------------------------------------------------------------------------

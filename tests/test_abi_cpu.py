@@ -239,3 +239,16 @@ def test_workspace_queries_are_host_only():
     W = weights(H=7168, I=2048, E=257)
     # two 16-bit h planes plus the tile table (16 bytes per tile of the bound)
     assert L.moe_expert_ffn_workspace_bytes(8192, 9, ctypes.byref(W)) >= 4 * 8192 * 9 * 2048 + 16 * 257
+
+
+def test_expert_ffn_static_validation():
+    """The no-allocation FFN: checks that come before the scratch array is looked up."""
+    L = m.lib()
+    assert L.moe_expert_ffn_static(None, 0, 0, 2, None, None, None, None, None) == OK     # T = 0
+    assert L.moe_expert_ffn_static(fake(), 0, 4, 2, None, fake(), fake(), fake(), None) == NULL
+    assert L.moe_expert_ffn_static(fake(), 0, -1, 2, ctypes.byref(weights()), fake(), fake(), fake(), None) == SHAPE
+    W = weights(E=256, H=7168, I=2048)
+    need = L.moe_expert_ffn_workspace_bytes(300, 8, ctypes.byref(W))
+    assert need > m.MOE_FFN_STATIC_SCRATCH_BYTES
+    assert L.moe_expert_ffn_static(fake(), 0, 300, 8, ctypes.byref(W), fake(0x100), fake(0x200), fake(0x300),
+                                   None) == WORKSPACE

@@ -126,6 +126,11 @@ class Oracle:
         lib.orc_mx_scale_code.restype = i; lib.orc_mx_scale_code.argtypes = [i, d]
         lib.orc_mx_quantize.restype = None; lib.orc_mx_quantize.argtypes = [vp, i, i, i, vp, vp]
         lib.orc_mx_dequantize.restype = None; lib.orc_mx_dequantize.argtypes = [vp, vp, i, i, i, vp]
+        lib.orc_expert_ffn_attenuated.restype = None
+        lib.orc_expert_ffn_attenuated.argtypes = [vp, i, i, i, ctypes.POINTER(_Weights), i, vp, vp, vp, vp]
+        lib.orc_row_factor.restype = d; lib.orc_row_factor.argtypes = [vp, i]
+        lib.orc_combine_restore.restype = None
+        lib.orc_combine_restore.argtypes = [vp, vp, i, i, i, i, vp, vp]
         lib.orc_expert_ffn_mx.restype = None
         lib.orc_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(_Weights), i, vp, vp, vp, vp, vp]
 
@@ -227,6 +232,35 @@ class Oracle:
         y = np.full((T * k_total, W.hidden), np.nan)
         self.lib.orc_expert_ffn(_p(x), x_fmt, T, k_total, ctypes.byref(W.c), _p(offsets), _p(sorted_slot),
                                 _p(mask), _p(y))
+        return y
+
+    # ---- FP16 range management (Cascadia Sec. 3.3, Eq. 1) ----
+    def expert_ffn_attenuated(self, x: np.ndarray, x_fmt: int, k_total: int, W: ExpertWeights, att_log2: int,
+                              offsets: np.ndarray, sorted_slot: np.ndarray,
+                              slot_mask: Optional[np.ndarray] = None) -> np.ndarray:
+        """-> E(x) / 2^att_log2 per slot, [T*k_total][H] (NaN for rows not computed)."""
+        x = np.ascontiguousarray(x, np.uint16)
+        T = x.shape[0]
+        offsets = np.ascontiguousarray(offsets, np.int32); sorted_slot = np.ascontiguousarray(sorted_slot, np.int32)
+        mask = None if slot_mask is None else np.ascontiguousarray(slot_mask, np.uint8)
+        y = np.full((T * k_total, W.hidden), np.nan)
+        self.lib.orc_expert_ffn_attenuated(_p(x), x_fmt, T, k_total, ctypes.byref(W.c), att_log2, _p(offsets),
+                                           _p(sorted_slot), _p(mask), _p(y))
+        return y
+
+    def row_factor(self, w: np.ndarray) -> float:
+        w = np.ascontiguousarray(w, np.float64).reshape(-1)
+        return self.lib.orc_row_factor(_p(w), w.size)
+
+    def combine_restore(self, y_slots_att: np.ndarray, weights: np.ndarray, att_log2: int,
+                        token_mask: Optional[np.ndarray] = None) -> np.ndarray:
+        weights = np.ascontiguousarray(weights, np.float64)
+        T, kt = weights.shape
+        y_slots_att = np.ascontiguousarray(y_slots_att, np.float64).reshape(T * kt, -1)
+        H = y_slots_att.shape[1]
+        mask = None if token_mask is None else np.ascontiguousarray(token_mask, np.uint8)
+        y = np.full((T, H), np.nan)
+        self.lib.orc_combine_restore(_p(y_slots_att), _p(weights), T, kt, H, att_log2, _p(mask), _p(y))
         return y
 
     def combine(self, y_slots: np.ndarray, weights: np.ndarray, token_mask: Optional[np.ndarray] = None):

@@ -244,8 +244,9 @@ static void mx_round_trip(double *v, int K, int fmt);
 /* act_fmt = 0: the exact FFN.  act_fmt = an ORC_MX_* format: the MX mode, where the token's x row
  * and each slot's h row go through the MX round trip before entering a projection. */
 static void grouped_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
-                        int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
-                        const uint8_t *slot_mask, double *y_slots, double *h_pre) {
+                        int act_fmt, double up_scale, const int32_t *offsets,
+                        const int32_t *sorted_slot, const uint8_t *slot_mask, double *y_slots,
+                        double *h_pre) {
   const int H = W->hidden, I = W->inter, E2 = W->n_experts;
   const int64_t n_slots = (int64_t)T * k_total;
   for (int e = 0; e < E2; ++e) {
@@ -287,7 +288,7 @@ static void grouped_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const 
           g += wg[k] * xv[k];
           u += wu[k] * xv[k];
         }
-        hs[(int64_t)i * I + n] = orc_silu(g) * u;
+        hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);
       }
       free(wg);
       free(wu);
@@ -320,7 +321,48 @@ static void grouped_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const 
 void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
                     const int32_t *offsets, const int32_t *sorted_slot, const uint8_t *slot_mask,
                     double *y_slots) {
-  grouped_ffn(x, x_fmt, T, k_total, W, 0, offsets, sorted_slot, slot_mask, y_slots, NULL);
+  grouped_ffn(x, x_fmt, T, k_total, W, 0, 1.0, offsets, sorted_slot, slot_mask, y_slots, NULL);
+}
+
+/* Cascadia Sec. 3.3, Eq. 1, expert side: the layer's up projection is attenuated by
+ * A = 2^att_log2, so h~ = SiLU(g) (u / A) and the expert output becomes E(x) / A (the up branch
+ * enters SwiGLU as a factor, so the attenuation carries straight through the down projection). */
+void orc_expert_ffn_attenuated(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                               int att_log2, const int32_t *offsets, const int32_t *sorted_slot,
+                               const uint8_t *slot_mask, double *y_slots) {
+  grouped_ffn(x, x_fmt, T, k_total, W, 0, ldexp(1.0, -att_log2), offsets, sorted_slot, slot_mask, y_slots,
+              NULL);
+}
+
+/* Cascadia Sec. 3.3, Eq. 1, row factor: F = 2^ceil(log2 max(1, sum_j |w_j|)) over the row's
+ * selections.  frexp gives m = f 2^ex with f in [0.5, 1): m is a power of two exactly when
+ * f == 0.5, and then ceil(log2 m) = ex - 1; otherwise it is ex. */
+double orc_row_factor(const double *w, int k_total) {
+  double sum = 0.0;
+  for (int j = 0; j < k_total; ++j) sum += fabs(w[j]);
+  double m = sum > 1.0 ? sum : 1.0;
+  int ex;
+  double f = frexp(m, &ex);
+  return ldexp(1.0, f == 0.5 ? ex - 1 : ex);
+}
+
+/* Cascadia Sec. 3.3, Eq. 1, combination and restoration: per row i with factor F_i,
+ * y~_i = sum_j (w_ij / F_i) y_slots~[i,j] (ascending j), then y_i = A F_i y~_i, where y_slots~
+ * holds the attenuated expert outputs E / A.  In real arithmetic y equals the unscaled combine. */
+void orc_combine_restore(const double *y_slots_att, const double *weights, int T, int k_total, int H,
+                         int att_log2, const uint8_t *token_mask, double *y) {
+  const double A = ldexp(1.0, att_log2);
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    if (token_mask && !token_mask[t]) continue;
+    const double *w = weights + (int64_t)t * k_total;
+    const double F = orc_row_factor(w, k_total);
+    for (int m = 0; m < H; ++m) {
+      double acc = 0.0;
+      for (int j = 0; j < k_total; ++j) acc += (w[j] / F) * y_slots_att[((int64_t)t * k_total + j) * H + m];
+      y[(int64_t)t * H + m] = (A * F) * acc;
+    }
+  }
 }
 
 /* Weighted reduction [C31]: y[t,:] = sum_{j = 0..k_total-1, ascending} w[t,j] * y_slots[t*k_total+j,:].
@@ -427,7 +469,7 @@ static void mx_round_trip(double *v, int K, int fmt) {
 void orc_expert_ffn_mx(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
                        int act_fmt, const int32_t *offsets, const int32_t *sorted_slot,
                        const uint8_t *slot_mask, double *y_slots, double *h_pre) {
-  grouped_ffn(x, x_fmt, T, k_total, W, act_fmt, offsets, sorted_slot, slot_mask, y_slots, h_pre);
+  grouped_ffn(x, x_fmt, T, k_total, W, act_fmt, 1.0, offsets, sorted_slot, slot_mask, y_slots, h_pre);
 }
 
 /* ------------------------------------------------------------------------------------------ */

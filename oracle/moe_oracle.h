@@ -15,6 +15,9 @@
  *        gate/up projections, SwiGLU, down projection, weighted reduction; routing yields expert
  *        ids and routing weights; shared experts are always-included selections.
  *  [C32] Cascadia Sec. 3.2: a call supplies rows, expert ids and weights; FP32 output.
+ *  [C33] Cascadia Sec. 3.3, Eq. 1: a layer attenuation A = 2^n on the up projection and a row
+ *        factor F_i on the routing weights keep the FP16 expert path in range; both are restored
+ *        in FP32 afterwards.
  *  [C34] Cascadia Sec. 3.4, Eq. 2: a dense FFN equals the sum of its all-active slices.
  *
  * Where the pages leave a step open the reading used here is stated next to the function.
@@ -73,6 +76,18 @@ void orc_expert_ffn(const uint16_t *x, int x_fmt, int T, int k_total, const orc_
                     double *y_slots);
 void orc_combine(const double *y_slots, const double *weights, int T, int k_total, int H,
                  const uint8_t *token_mask, double *y);
+
+/* ---- FP16 range management (Cascadia Sec. 3.3, Eq. 1) ----
+ * A = 2^att_log2 attenuates the layer's up projection, so each expert returns E(x) / A; each row i
+ * takes F_i = 2^ceil(log2 max(1, sum_j |w_ij|)), combines y~_i = sum_j (w_ij / F_i) E_ij / A and is
+ * restored as y_i = A F_i y~_i.  All in fp64: with powers of two and no overflow or underflow the
+ * result is the plain layer's, bit for bit. */
+void orc_expert_ffn_attenuated(const uint16_t *x, int x_fmt, int T, int k_total, const orc_weights *W,
+                               int att_log2, const int32_t *offsets, const int32_t *sorted_slot,
+                               const uint8_t *slot_mask, double *y_slots);
+double orc_row_factor(const double *w, int k_total);
+void orc_combine_restore(const double *y_slots_att, const double *weights, int T, int k_total, int H,
+                         int att_log2, const uint8_t *token_mask, double *y);
 
 /* ---- MX activation formats (prefill MX mode) ----
  * Not on the pages, which define only the E2M1 + E8M0 weight block [MX].  Reading: the activation

@@ -430,6 +430,61 @@ def check_dense_slices(o):
 
 
 # ------------------------------------------------------------------------------------------------
+# FP16 range management (Cascadia Sec. 3.3, Eq. 1)
+# ------------------------------------------------------------------------------------------------
+def check_eq1_row_factor(o):
+    """F = 2^ceil(log2 max(1, sum |w|)): the fixture's hand-worked rows, and on random rows the
+    defining property -- F is a power of two with F/2 < max(1, sum |w|) <= F -- checked with exact
+    binary arithmetic (frexp) rather than log2."""
+    g = golden("cascadia_range.json")
+    for case in g["row_factor_cases"]:
+        assert o.row_factor(np.array(case["weights"], np.float64)) == case["F"], case
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        w = rng.standard_normal(rng.integers(1, 12)) * np.exp2(rng.integers(-4, 5))
+        F = o.row_factor(w)
+        m = max(1.0, float(np.sum(np.abs(w))))
+        mant, ex = math.frexp(F)
+        assert mant == 0.5 and F >= 1.0, F
+        assert F / 2 < m <= F, (m, F)
+
+
+def check_eq1_restores_plain_layer(o):
+    """Eq. 1 preserves the function, and with powers of two and no overflow it does so exactly:
+    the attenuated experts are the plain experts divided by A (printed example A_8 = 16) bit for
+    bit, and the restored combine equals the plain combine bit for bit -- on rows whose weights
+    sum to 1 (F = 1), 2 (one shared expert, F = 2) and 3 (two shared experts, F = 4)."""
+    g = golden("cascadia_range.json")
+    n = g["att_log2"]
+    assert 2 ** n == g["A"]
+    for S in (0, 1, 2):
+        L = small_layer(T=6, H=64, E=5, k=2, S=S, I=96)
+        W = ExpertWeights.from_layer(L)
+        r = o.route(L.x, X_BF16, L.router, L.bias, 2, S)
+        b = o.bucket(r["ids"], 5 + S)
+        ys = o.expert_ffn(L.x, X_BF16, 2 + S, W, b["offsets"], b["sorted_slot"])
+        ya = o.expert_ffn_attenuated(L.x, X_BF16, 2 + S, W, n, b["offsets"], b["sorted_slot"])
+        assert np.array_equal(ya, ys / g["A"]), S
+        F = np.array([o.row_factor(w) for w in r["weights"]])
+        assert np.all(F == {0: 1.0, 1: 2.0, 2: 4.0}[S]), (S, F)
+        y = o.combine(ys, r["weights"])
+        yr = o.combine_restore(ya, r["weights"], n)
+        assert np.array_equal(yr, y), S
+        # the same steps in numpy, in the equation's order
+        yt = np.einsum("tj,tjh->th", r["weights"] / F[:, None], ya.reshape(6, 2 + S, -1))
+        close(yr, g["A"] * F[:, None] * yt, 1e-13, "eq1 numpy")
+    # an FP16-weight layer (the arithmetic the equation is written for) and a larger exponent
+    L = small_layer(T=4, H=64, E=3, k=2, S=1, I=64, fmt="fp16")
+    W = ExpertWeights.from_layer(L)
+    r = o.route(L.x, X_FP16, L.router, L.bias, 2, 1)
+    b = o.bucket(r["ids"], 4)
+    ys = o.expert_ffn(L.x, X_FP16, 3, W, b["offsets"], b["sorted_slot"])
+    ya = o.expert_ffn_attenuated(L.x, X_FP16, 3, W, 9, b["offsets"], b["sorted_slot"])
+    assert np.array_equal(ya * 512.0, ys)
+    assert np.array_equal(o.combine_restore(ya, r["weights"], 9), o.combine(ys, r["weights"]))
+
+
+# ------------------------------------------------------------------------------------------------
 # MX activation formats (MX mode).  The pages fix only E2M1 + E8M0; these pins hold the oracle to
 # the OCP MX element formats through independent decoders (minifloat, torch's float8_e4m3fn), to
 # the nearest/ties-to-even/saturation rule by exhaustive comparison, and to the scale rule through
@@ -607,7 +662,7 @@ ALL_CHECKS = [
     check_router_vs_numpy, check_router_tiebreak, check_router_k_equals_E, check_router_shift_invariance,
     check_router_shared, check_bucket, check_bucket_invalid,
     check_expert_apply_vs_numpy, check_layer_vs_numpy, check_layer_forms, check_single_expert_swiglu,
-    check_combine, check_dense_slices,
+    check_combine, check_dense_slices, check_eq1_row_factor, check_eq1_restores_plain_layer,
     check_mx_tables, check_mx_encode_nearest, check_mx_scale_rule, check_mx_quantize_fp8_vs_torch,
     check_mx_quantize_blocks, check_expert_ffn_mx_vs_numpy,
 ]

@@ -20,7 +20,15 @@ MUTANTS = {
     "sign bit dropped": ("return (code & 8) ? -mag : mag;", "return mag;"),
     "magnitudes 3 and 4 swapped": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 4.0, 3.0, 6.0}"),
     "wrong scale block": ("return orc_mxfp4(code, srow[k / 32]);", "return orc_mxfp4(code, srow[k / 64]);"),
-    "gate and up swapped in SwiGLU": ("hs[(int64_t)i * I + n] = orc_silu(g) * u;", "hs[(int64_t)i * I + n] = orc_silu(u) * g;"),
+    "gate and up swapped in SwiGLU": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
+                                      "hs[(int64_t)i * I + n] = orc_silu(u * up_scale) * g;"),
+    "attenuation not applied": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
+                                "hs[(int64_t)i * I + n] = orc_silu(g) * u;"),
+    "attenuation applied to the gate": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
+                                        "hs[(int64_t)i * I + n] = orc_silu(g * up_scale) * u;"),
+    "row factor not restored": ("y[(int64_t)t * H + m] = (A * F) * acc;", "y[(int64_t)t * H + m] = A * acc;"),
+    "row factor rounded down": ("return ldexp(1.0, f == 0.5 ? ex - 1 : ex);", "return ldexp(1.0, ex - 1);"),
+    "row factor without the floor of 1": ("double m = sum > 1.0 ? sum : 1.0;", "double m = sum > 0.0 ? sum : 1.0;"),
     "SiLU sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "routing weights not renormalised": ("weights[(int64_t)t * k_total + j] = p[order[j]] / sel;",
                                          "weights[(int64_t)t * k_total + j] = p[order[j]];"),

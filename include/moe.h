@@ -16,6 +16,9 @@
  *        are selections every row carries after its routed ones.
  *  [C32] Cascadia Sec. 3.2: a layer call supplies rows, expert ids and routing weights; the
  *        expert path returns FP32 output (Fig. 2).
+ *  [C33] Cascadia Sec. 3.3, Eq. 1: range management across the FP16/FP32 boundary -- a per-layer
+ *        power-of-two attenuation of the up projection and a per-row power-of-two factor on the
+ *        routing weights, both undone in FP32.
  *  [C34] Cascadia Sec. 3.4, Eq. 2: a dense FFN is the sum of its all-active, unit-weight slices,
  *        cut at quantisation-group boundaries.
  *
@@ -140,8 +143,12 @@ moe_status moe_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *c
  * For every expert e and sorted row r in [offsets[e], offsets[e+1]) with slot s = sorted_slot[r]
  * and token t = s / k_total:
  *   g = W_gate[e] x_t,  u = W_up[e] x_t  (fp32 accumulation of exact products),
- *   h = SiLU(g) * u     (fp32; fed to the down projection as a bf16 (fp16 for FP16 weights)
- *                        high + low pair, i.e. about 16 significant bits),
+ *   h = SiLU(g) * u     (fp32; fed to the down projection as a high + low pair: bf16 for MXFP4
+ *                        weights, about 16 significant bits over the whole fp32 range; binary16
+ *                        for FP16 weights, which holds only |h| <= 65504 -- larger h overflows
+ *                        to infinity, see moe_expert_ffn_f16 [C33] -- and keeps about 22 bits
+ *                        for |h| >= 2^-3, below which the low part is subnormal and the pair's
+ *                        error stays under 2^-25 absolute),
  *   y_slots[s,:] = W_down[e] h   (fp32).
  *   x        [T][hidden] activations; MXFP4 weights need MOE_ACT_BF16, FP16 weights MOE_ACT_FP16
  *   W        host pointer to the weight description (device pointers inside)
@@ -197,6 +204,40 @@ moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total,
                                const moe_expert_weights *W, const int32_t *offsets,
                                const int32_t *sorted_slot, float *y_slots, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Range-managed FP16 path [C33] (Cascadia Sec. 3.3, Eq. 1).  For a layer with attenuation
+ * A = 2^attenuation_log2 applied to its up projection, the expert path works on E(x) / A and
+ * crosses the FP16 boundary in binary16; every row i is combined with its weights divided by
+ * F_i = 2^ceil(log2 max(1, sum_j |w_ij|)) and restored as y_i = A F_i y~_i in FP32.  In real
+ * arithmetic the result is the plain layer's; the attenuation keeps h, the expert outputs and
+ * the combination inside the binary16 range (the configuration recorded for layer 8 uses A = 16),
+ * and the factors, being powers of two, are applied and removed exactly.
+ *
+ * moe_expert_ffn_f16: for every sorted row as in moe_expert_ffn,
+ *   u~ = (W_up[e] x_t) / A,  h~ = binary16(SiLU(W_gate[e] x_t) * u~)   (fp32, then rounded),
+ *   y_slots[s,:] = binary16(W_down[e] h~)                              (fp32 accumulation)
+ * i.e. binary16 expert outputs E(x) / A (IEEE half bits; values past 65504 become infinite, which
+ * is what the attenuation is for).  Weights MXFP4 (bf16 x) or FP16 (fp16 x), as for
+ * moe_expert_ffn; runs the K-split kernels.  y_slots [T*k_total][hidden] binary16, 2-byte aligned;
+ * dropped slots' rows are left unwritten.  workspace: moe_expert_ffn_f16_workspace_bytes bytes,
+ * 16-byte aligned.  Errors as for moe_expert_ffn, plus SHAPE for attenuation_log2 outside
+ * [0, MOE_MAX_ATTENUATION_LOG2]. */
+#define MOE_MAX_ATTENUATION_LOG2 30
+size_t moe_expert_ffn_f16_workspace_bytes(int T, int k_total, const moe_expert_weights *W);
+moe_status moe_expert_ffn_f16(const void *x, moe_act_dtype x_dtype, int T, int k_total,
+                              const moe_expert_weights *W, int attenuation_log2,
+                              const int32_t *offsets, const int32_t *sorted_slot, uint16_t *y_slots,
+                              void *workspace, size_t workspace_bytes, void *stream);
+/* moe_combine_restore: per token t with F_t = 2^ceil(log2 max(1, sum_j |weights[t,j]|)) (fp32 sum
+ * in ascending j),
+ *   y~[t,:] = binary16(sum_{j ascending} (weights[t,j] / F_t) * y_slots[t*k_total+j,:])  (fp32 sum)
+ *   y[t,:]  = A * F_t * y~[t,:]                                                      (fp32, exact)
+ * y_slots [T*k_total][H] binary16 (8-byte aligned), weights [T][k_total] fp32, y [T][H] fp32 out
+ * (16-byte aligned), H % 4 == 0.  Errors: NULL, SHAPE (also attenuation_log2 out of range), ALIGN,
+ * HIP. */
+moe_status moe_combine_restore(const uint16_t *y_slots, const float *weights, int T, int k_total, int H,
+                               int attenuation_log2, float *y, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * MX mode (prefill).  Not on the pages, which define only the MXFP4 weight block [MX]: the

@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp, st, vp]
         L.moe_expert_ffn_static.restype = i
         L.moe_expert_ffn_static.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, vp, vp]
+        L.moe_expert_ffn_f16_workspace_bytes.restype = st
+        L.moe_expert_ffn_f16_workspace_bytes.argtypes = [i, i, ctypes.POINTER(moe_expert_weights)]
+        L.moe_expert_ffn_f16.restype = i
+        L.moe_expert_ffn_f16.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), i, vp, vp, vp, vp, st, vp]
+        L.moe_combine_restore.restype = i
+        L.moe_combine_restore.argtypes = [vp, vp, i, i, i, i, vp, vp]
         L.moe_expert_ffn_plan.restype = i
         L.moe_expert_ffn_plan.argtypes = [i, i, i, ctypes.POINTER(moe_expert_weights), vp, vp, st, vp]
         L.moe_expert_ffn_gateup.restype = i
@@ -286,6 +292,37 @@ def moe_expert_ffn_down(T: int, W: ExpertWeights, offsets: torch.Tensor, sorted_
     return out
 
 
+def moe_expert_ffn_f16_workspace_bytes(T: int, k_total: int, W: ExpertWeights) -> int:
+    return lib().moe_expert_ffn_f16_workspace_bytes(T, k_total, ctypes.byref(W.c))
+
+
+def moe_expert_ffn_f16(x: torch.Tensor, W: ExpertWeights, attenuation_log2: int, offsets: torch.Tensor,
+                       sorted_slot: torch.Tensor, k_total: int, out: Optional[torch.Tensor] = None,
+                       workspace=None) -> torch.Tensor:
+    """Range-managed expert FFN (Cascadia Eq. 1): -> binary16 y_slots [T*k_total][hidden] holding
+    E(x) / 2^attenuation_log2 (float16 tensor)."""
+    T = x.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((T * k_total, W.hidden), dtype=torch.float16, device=dev)
+    need = moe_expert_ffn_f16_workspace_bytes(T, k_total, W)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_expert_ffn_f16(_ptr(x), _act_dtype(x), T, k_total, ctypes.byref(W.c), attenuation_log2,
+                                    _ptr(offsets), _ptr(sorted_slot), _ptr(y), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)), "moe_expert_ffn_f16")
+    return y
+
+
+def moe_combine_restore(y_slots: torch.Tensor, weights: torch.Tensor, attenuation_log2: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Eq. 1 combination of binary16 attenuated slots with row factors, restored to fp32 y [T][H]."""
+    T, kt = weights.shape
+    H = y_slots.shape[-1]
+    y = out if out is not None else torch.empty((T, H), dtype=torch.float32, device=y_slots.device)
+    _check(lib().moe_combine_restore(_ptr(y_slots), _ptr(weights), T, kt, H, attenuation_log2, _ptr(y),
+                                     _stream(y_slots.device)), "moe_combine_restore")
+    return y
+
+
 def moe_combine(y_slots: torch.Tensor, weights: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     T, kt = weights.shape
     H = y_slots.shape[-1]
@@ -400,7 +437,8 @@ class MoELayer:
         return moe_combine(self.y_slots, self.weights, out=self.y)
 
 
-__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
+__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
+           "moe_expert_ffn_f16_workspace_bytes", "moe_combine_restore", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
            "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
            "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",

@@ -241,6 +241,53 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
                                          h_hi, h_lo, table, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------------------------
+// Range-managed FP16 path (Cascadia Sec. 3.3, Eq. 1)
+size_t moe_expert_ffn_f16_workspace_bytes(int T, int k_total, const moe_expert_weights* W) {
+  if (!W || T <= 0 || k_total <= 0 || W->inter <= 0 || W->n_experts <= 0) return 0;
+  const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
+  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts, false), 256);
+}
+
+moe_status moe_expert_ffn_f16(const void* x, moe_act_dtype x_dtype, int T, int k_total, const moe_expert_weights* W,
+                              int attenuation_log2, const int32_t* offsets, const int32_t* sorted_slot,
+                              uint16_t* y_slots, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (!W) return MOE_ERR_NULL;
+  if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN || (int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
+  if (attenuation_log2 < 0 || attenuation_log2 > MOE_MAX_ATTENUATION_LOG2) return MOE_ERR_SHAPE;
+  if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
+  if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
+  if ((W->fmt == MOE_W_MXFP4) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
+  if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
+  if (!x || !offsets || !sorted_slot || !y_slots) return MOE_ERR_NULL;
+  const int H = W->hidden, I = W->inter;
+  moe_status st;
+  if ((st = check_proj(W->gate, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->up, W->fmt, W->n_experts, I, H)) != MOE_OK) return st;
+  if ((st = check_proj(W->down, W->fmt, W->n_experts, H, I)) != MOE_OK) return st;
+  if (!al16(x) || !al4(offsets) || !al4(sorted_slot) || ((uintptr_t)y_slots & 1u)) return MOE_ERR_ALIGN;
+  const size_t need = moe_expert_ffn_f16_workspace_bytes(T, k_total, W);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)I, 256);
+  uint8_t* ws = (uint8_t*)workspace;
+  return hip_status(moe::launch_ffn_range(x, T, k_total, W->fmt, W->n_experts, H, I, dev(W->gate), dev(W->up),
+                                          dev(W->down), offsets, sorted_slot, (uint16_t*)ws, (uint16_t*)(ws + plane),
+                                          ws + 2 * plane, attenuation_log2, y_slots, (hipStream_t)stream));
+}
+
+moe_status moe_combine_restore(const uint16_t* y_slots, const float* weights, int T, int k_total, int H,
+                               int attenuation_log2, float* y, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (T < 0 || k_total < 1 || H < 1 || H % 4 != 0) return MOE_ERR_SHAPE;
+  if (attenuation_log2 < 0 || attenuation_log2 > MOE_MAX_ATTENUATION_LOG2) return MOE_ERR_SHAPE;
+  if (!y_slots || !weights || !y) return MOE_ERR_NULL;
+  if (((uintptr_t)y_slots & 7u) || !al16(y) || !al4(weights)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine_restore(y_slots, weights, T, k_total, H, attenuation_log2, y,
+                                                (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------------

@@ -151,11 +151,15 @@ __device__ __forceinline__ typename Op<FMT>::V decode_step(const RawW<FMT>& r, i
 // ------------------------------------------------------------------------------------------------
 // gate/up + SwiGLU:  h[r, n] = SiLU(sum_k Wg[e,n,k] x[t,k]) * (sum_k Wu[e,n,k] x[t,k])
 // ------------------------------------------------------------------------------------------------
+// u_scale and h_f16 serve the range-managed path (Cascadia Sec. 3.3, Eq. 1): u is multiplied by
+// the layer's attenuation 1/A = u_scale (a power of two, so exact), and h is rounded to binary16
+// before it is split, as the FP16 intermediate of that path.  u_scale = 1, h_f16 = 0 is the plain
+// FFN.
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float u_scale, int h_f16) {
   typedef typename Op<FMT>::V V;
   __shared__ float s_red[NW][RT][2][256];
   const int n_slots = T * k_total;
@@ -292,7 +296,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
       }
       const int n = n0 + rt * 16 + row, m = mt * 16 + tok;
       if (n < I && m < ti.nr) {
-        const float h = (g / (1.0f + expf(-g))) * u;
+        float h = (g / (1.0f + expf(-g))) * (u * u_scale);
+        if (h_f16) h = (float)(_Float16)h;
         uint16_t hi, lo;
         Op<FMT>::split(h, hi, lo);
         const int64_t idx = (int64_t)(ti.r0 + m) * I + n;
@@ -306,11 +311,13 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
 // ------------------------------------------------------------------------------------------------
 // down:  y_slots[s, n] = sum_k Wd[e,n,k] (h_hi[r,k] + h_lo[r,k])
 // ------------------------------------------------------------------------------------------------
+// y16 (the range-managed path): when non-null, each output is rounded to binary16 and stored
+// there instead of y_slots.
 template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
-    float* __restrict__ y_slots) {
+    float* __restrict__ y_slots, uint16_t* __restrict__ y16) {
   typedef typename Op<FMT>::V V;
   __shared__ float s_red[NW][RT][256];
   int tile, nblk;
@@ -427,7 +434,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
       const int n = n0 + rt * 16 + row, m = mt * 16 + tok;
       if (n < H && m < ti.nr) {
         const int s = sorted_slot[ti.r0 + m];
-        if (s >= 0 && s < n_slots) y_slots[(int64_t)s * H + n] = v;
+        if (s >= 0 && s < n_slots) {
+          if (y16)
+            y16[(int64_t)s * H + n] = bitcast<uint16_t>((_Float16)v);
+          else
+            y_slots[(int64_t)s * H + n] = v;
+        }
       }
     }
   }
@@ -1669,7 +1681,7 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
   } else {
     const int nb = (I + 16 * kRT1 - 1) / (16 * kRT1);
     ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
-        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo, 1.0f, 0);
   }
   return hipGetLastError();
 }
@@ -1697,9 +1709,36 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   } else {
     const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
     ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots, nullptr);
   }
   return hipGetLastError();
+}
+
+// The range-managed FFN (Cascadia Sec. 3.3, Eq. 1) on the general kernels: u attenuated by
+// u_scale, h rounded to binary16, outputs stored as binary16 in y16.
+template <int FMT, int MT>
+hipError_t ffn_range_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+                        ProjDev down, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+                        const TileEntry* tiles, float u_scale, uint16_t* y16, hipStream_t stream) {
+  const int nb1 = (I + 16 * kRT1 - 1) / (16 * kRT1);
+  ffn_gateup_kernel<FMT, kNW, kRT1, MT><<<dim3((unsigned)(pl.tiles * nb1)), kNW * 64, 0, stream>>>(
+      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb1, h_hi, h_lo, u_scale, 1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nb2 = (H + 16 * kRT2 - 1) / (16 * kRT2);
+  ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb2)), kNW * 64, 0, stream>>>(
+      h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb2, nullptr, y16);
+  return hipGetLastError();
+}
+template <int FMT>
+hipError_t ffn_range_fmt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate,
+                         ProjDev up, ProjDev down, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
+                         const TileEntry* tiles, float u_scale, uint16_t* y16, hipStream_t stream) {
+  switch (pl.mt) {
+    case 1: return ffn_range_mt<FMT, 1>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale, y16, stream);
+    case 2: return ffn_range_mt<FMT, 2>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale, y16, stream);
+    default: return ffn_range_mt<FMT, 4>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale, y16, stream);
+  }
 }
 
 // The tile kernels (planned only when ffn_big_tiles() holds for the call).
@@ -1747,6 +1786,22 @@ hipError_t down_fmt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev
 }
 
 }  // namespace
+
+hipError_t launch_ffn_range(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
+                            ProjDev up, ProjDev down, const int32_t* offsets, const int32_t* sorted_slot,
+                            uint16_t* h_hi, uint16_t* h_lo, void* table, int att_log2, uint16_t* y16,
+                            hipStream_t stream) {
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, false);
+  hipError_t err = launch_ffn_plan(T, k_total, n_experts, false, offsets, table, stream);
+  if (err != hipSuccess) return err;
+  const float u_scale = ldexpf(1.0f, -att_log2);
+  const TileEntry* tiles = (const TileEntry*)table;
+  if (fmt == MOE_W_FP16)
+    return ffn_range_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale,
+                                     y16, stream);
+  return ffn_range_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale,
+                                    y16, stream);
+}
 
 bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
                    const ProjDev& down) {

@@ -55,6 +55,14 @@ hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream);
 
+// The range-managed FFN (Cascadia Sec. 3.3, Eq. 1): builds its own tile table (non-tile plan) in
+// `table`, runs the general kernels with u attenuated by 2^-att_log2 and h rounded to binary16,
+// and writes binary16 outputs to y16.
+hipError_t launch_ffn_range(const void* x, int T, int k_total, int fmt, int n_experts, int H, int I, ProjDev gate,
+                            ProjDev up, ProjDev down, const int32_t* offsets, const int32_t* sorted_slot,
+                            uint16_t* h_hi, uint16_t* h_lo, void* table, int att_log2, uint16_t* y16,
+                            hipStream_t stream);
+
 // ---- expert FFN, MX mode (MXFP4 weights x MX-quantised activations on scaled MFMAs) ----
 int mx_bits(int fmt);                                  // 8, 6 or 4 bits per code; 0 for an unknown format
 int64_t mx_tiles(int T, int k_total, int n_experts);   // tile-table entries of an MX call
@@ -79,6 +87,8 @@ hipError_t launch_ffn_mx(const MxFfnArgs& a, hipStream_t stream);
 // ---- combine ----
 hipError_t launch_combine(const float* y_slots, const float* weights, int T, int k_total, int H, float* y,
                           hipStream_t stream);
+hipError_t launch_combine_restore(const uint16_t* y16, const float* weights, int T, int k_total, int H, int att_log2,
+                                  float* y, hipStream_t stream);
 
 // ---- decode primitive ----
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n_rows, int K, int64_t code_stride,

@@ -252,3 +252,29 @@ def test_expert_ffn_static_validation():
     assert need > m.MOE_FFN_STATIC_SCRATCH_BYTES
     assert L.moe_expert_ffn_static(fake(), 0, 300, 8, ctypes.byref(W), fake(0x100), fake(0x200), fake(0x300),
                                    None) == WORKSPACE
+
+
+def test_range_path_validation():
+    """moe_expert_ffn_f16 and moe_combine_restore (Cascadia Eq. 1) reject bad arguments on the host."""
+    L = m.lib()
+    W = weights()
+    need = L.moe_expert_ffn_f16_workspace_bytes(4, 2, ctypes.byref(W))
+    assert need >= 2 * 4 * 2 * 96 * 2
+
+    def f16(W, n=4, T=4, kt=2, xdt=0, y=fake(0x300), ws=fake(0x4000), wsb=need):
+        return L.moe_expert_ffn_f16(fake(), xdt, T, kt, ctypes.byref(W), n, fake(0x100), fake(0x200), y, ws, wsb,
+                                    None)
+
+    assert L.moe_expert_ffn_f16(None, 0, 0, 2, None, 4, None, None, None, None, 0, None) == OK
+    assert f16(W, n=-1) == SHAPE and f16(W, n=31) == SHAPE
+    assert f16(W, xdt=1) == DTYPE
+    assert f16(W, y=None) == NULL
+    assert f16(W, y=fake(0x301)) == ALIGN
+    assert f16(W, wsb=need - 1) == WORKSPACE
+    assert f16(weights(up__w=P + 8)) == BLOCK
+    cr = lambda **k: L.moe_combine_restore(k.get("ys", fake()), k.get("w", fake(0x100)), k.get("T", 4), 2,
+                                           k.get("H", 64), k.get("n", 4), k.get("y", fake(0x200)), None)
+    assert L.moe_combine_restore(None, None, 0, 2, 64, 4, None, None) == OK
+    assert cr(n=-2) == SHAPE and cr(n=31) == SHAPE and cr(H=66) == SHAPE
+    assert cr(ys=None) == NULL
+    assert cr(ys=fake(4)) == ALIGN and cr(y=fake(0x208)) == ALIGN

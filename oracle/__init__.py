@@ -101,6 +101,8 @@ class Oracle:
         lib.orc_num_threads.restype = i; lib.orc_num_threads.argtypes = []
         lib.orc_route.restype = None
         lib.orc_route.argtypes = [vp, i, i, i, vp, vp, i, i, i, d, vp, vp, vp, vp, vp]
+        lib.orc_route_sigmoid.restype = None
+        lib.orc_route_sigmoid.argtypes = [vp, i, i, i, vp, vp, i, i, i, d, d, d, vp, vp, vp, vp]
         lib.orc_bucket.restype = i
         lib.orc_bucket.argtypes = [vp, i, i, vp, vp, vp, vp]
         lib.orc_expert_apply.restype = None
@@ -206,6 +208,22 @@ class Oracle:
         self.lib.orc_route(_p(x), x_fmt, T, H, _p(router), _p(bias), E, top_k, n_shared, tie_eps,
                            _p(out["logits"]), _p(out["probs"]), _p(out["ids"]), _p(out["weights"]),
                            _p(out["near_tie"]))
+        return out
+
+    def route_sigmoid(self, x: np.ndarray, x_fmt: int, router: np.ndarray, sel_bias: Optional[np.ndarray],
+                      top_k: int, n_shared: int = 0, routed_scale: float = 1.0, shared_weight: float = 1.0,
+                      tie_eps: float = 1e-6) -> dict:
+        """Sigmoid router (Cascadia Sec. 3.1) -> dict(scores, ids, weights, near_tie)."""
+        x = np.ascontiguousarray(x, np.uint16); router = np.ascontiguousarray(router, np.float32)
+        sel_bias = None if sel_bias is None else np.ascontiguousarray(sel_bias, np.float32)
+        T, H = x.shape
+        E = router.shape[0]
+        kt = top_k + n_shared
+        out = dict(scores=np.empty((T, E)), ids=np.empty((T, kt), np.int32), weights=np.empty((T, kt)),
+                   near_tie=np.zeros(T, np.uint8))
+        self.lib.orc_route_sigmoid(_p(x), x_fmt, T, H, _p(router), _p(sel_bias), E, top_k, n_shared, routed_scale,
+                                   shared_weight, tie_eps, _p(out["scores"]), _p(out["ids"]), _p(out["weights"]),
+                                   _p(out["near_tie"]))
         return out
 
     def bucket(self, ids: np.ndarray, n_buckets: int) -> dict:

@@ -172,6 +172,68 @@ void orc_route(const uint16_t *x, int x_fmt, int T, int H, const float *w_router
   }
 }
 
+/* Sigmoid router of Cascadia Sec. 3.1 (Inkling's gate): per token t
+ *   L[t,e] = sum_h x[t,h] W_r[e,h]                 (no bias inside the score)
+ *   s[t,e] = 1 / (1 + e^-L[t,e])                   (sigmoid scores)
+ *   the k experts with the largest s[t,e] + b[e], ordered by (that key desc, index asc)
+ *       (bias-adjusted selection: b moves the choice only)
+ *   w_j    = gamma * s_j / sum_{j'<k} s_j'         (selected scores normalised to 1, times the
+ *                                                   model's scale factor gamma)
+ *   slots k .. k+S-1: shared experts E .. E+S-1 with weight shared_weight.
+ * Readings: the page names the steps (sigmoid scores, bias-adjusted top-k, selected/shared
+ * normalisation, model-specific scale factors) without their formulas; the normalisation over the
+ * selected scores, gamma as one multiplier of the routed weights and a fixed shared weight are the
+ * plainest forms of those steps.  near_tie as in orc_route, on the selection keys. */
+void orc_route_sigmoid(const uint16_t *x, int x_fmt, int T, int H, const float *w_router,
+                       const float *sel_bias, int E, int top_k, int n_shared, double routed_scale,
+                       double shared_weight, double tie_eps, double *scores, int32_t *ids,
+                       double *weights, uint8_t *near_tie) {
+  const int k_total = top_k + n_shared;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; ++t) {
+    double *sc = (double *)malloc(sizeof(double) * (size_t)E);
+    double *key = (double *)malloc(sizeof(double) * (size_t)E);
+    int *order = (int *)malloc(sizeof(int) * (size_t)E);
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];
+      sc[e] = 1.0 / (1.0 + exp(-acc));
+      key[e] = sc[e] + (sel_bias ? (double)sel_bias[e] : 0.0);
+    }
+    for (int e = 0; e < E; ++e) order[e] = e;
+    int n_sort = top_k + 1 < E ? top_k + 1 : E;
+    for (int j = 0; j < n_sort; ++j) {
+      int best = j;
+      for (int i = j + 1; i < E; ++i) {
+        int a = order[i], b = order[best];
+        if (key[a] > key[b] || (key[a] == key[b] && a < b)) best = i;
+      }
+      int tmp = order[j];
+      order[j] = order[best];
+      order[best] = tmp;
+    }
+    double sel = 0.0;
+    for (int j = 0; j < top_k; ++j) sel += sc[order[j]];
+    for (int j = 0; j < top_k; ++j) {
+      ids[(int64_t)t * k_total + j] = order[j];
+      weights[(int64_t)t * k_total + j] = routed_scale * (sc[order[j]] / sel);
+    }
+    for (int s = 0; s < n_shared; ++s) {
+      ids[(int64_t)t * k_total + top_k + s] = E + s;
+      weights[(int64_t)t * k_total + top_k + s] = shared_weight;
+    }
+    uint8_t tie = 0;
+    for (int j = 0; j + 1 < n_sort; ++j)
+      if (key[order[j]] - key[order[j + 1]] <= tie_eps) tie = 1;
+    if (near_tie) near_tie[t] = tie;
+    if (scores) memcpy(scores + (int64_t)t * E, sc, sizeof(double) * (size_t)E);
+    free(sc);
+    free(key);
+    free(order);
+  }
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Bucketing: group slots by expert                                                           */
 /* ------------------------------------------------------------------------------------------ */

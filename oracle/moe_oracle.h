@@ -68,6 +68,13 @@ int64_t orc_mxfp4_bytes(int64_t n_rows, int64_t k);  /* codes + scales of an [n_
 void orc_route(const uint16_t *x, int x_fmt, int T, int H, const float *w_router, const float *bias,
                int E, int top_k, int n_shared, double tie_eps,
                double *logits, double *probs, int32_t *ids, double *weights, uint8_t *near_tie);
+/* Sigmoid router (Cascadia Sec. 3.1): sigmoid scores, top-k by score + sel_bias (bias moves the
+ * selection only), selected scores normalised to 1 and multiplied by routed_scale, shared slots
+ * with shared_weight.  scores [T][E] (optional) are the sigmoid scores. */
+void orc_route_sigmoid(const uint16_t *x, int x_fmt, int T, int H, const float *w_router,
+                       const float *sel_bias, int E, int top_k, int n_shared, double routed_scale,
+                       double shared_weight, double tie_eps, double *scores, int32_t *ids,
+                       double *weights, uint8_t *near_tie);
 int orc_bucket(const int32_t *ids, int n_slots, int n_buckets, int32_t *counts, int32_t *offsets,
                int32_t *sorted_slot, int32_t *slot_pos);
 void orc_expert_apply(const orc_weights *W, int e, const double *xv, double *out);

@@ -429,6 +429,60 @@ def check_dense_slices(o):
     close(dense, np_expert(f(wg), f(wu), f(wd), np_act(L.x, X_FP16)), 1e-12, "dense vs numpy")
 
 
+def np_route_sigmoid(x, fmt, router, bias, k, gamma):
+    X = np_act(x, fmt)
+    sc = scipy.special.expit(X @ router.astype(np.float64).T)
+    key = sc + (0.0 if bias is None else bias.astype(np.float64))
+    T, E = sc.shape
+    order = np.stack([np.lexsort((np.arange(E), -key[t])) for t in range(T)])
+    sel = order[:, :k]
+    s_sel = np.take_along_axis(sc, sel, axis=1)
+    return sc, sel, gamma * s_sel / s_sel.sum(axis=1, keepdims=True)
+
+
+def check_router_sigmoid_vs_numpy(o):
+    """Sigmoid router (Cascadia Sec. 3.1): scores against scipy's expit of numpy logits, selection
+    against a lexsort of score + bias, weights against gamma * s / sum s over the selection, and the
+    Cascadia row of six routed plus two shared selections (ids 256 and 257) from the fixture."""
+    g = golden("cascadia_routing.json")
+    for (T, H, E, k, S, gamma, sw, bias_std) in [(9, 64, 20, 3, 0, 1.0, 1.0, 0.0), (7, 96, 33, 5, 2, 2.5, 1.0, 0.3),
+                                                 (4, 32, g["routed_experts"], g["top_k"], len(g["shared_ids"]),
+                                                  1.5, 0.75, 0.1)]:
+        wl = synth.custom(hidden=H, n_routed=E, top_k=k, n_shared=S, router_std=0.4)
+        x = synth.make_x(wl, T, seed=3)
+        router, _ = synth.make_router(wl, seed=3)
+        rng = np.random.default_rng(E)
+        bias = (rng.standard_normal(E) * bias_std).astype(np.float32) if bias_std else None
+        r = o.route_sigmoid(x, X_BF16, router, bias, k, S, gamma, sw)
+        sc, sel, w = np_route_sigmoid(x, X_BF16, router, bias, k, gamma)
+        close(r["scores"], sc, 1e-12, "sigmoid scores")
+        keep = r["near_tie"] == 0
+        assert np.array_equal(r["ids"][keep, :k], sel[keep])
+        close(r["weights"][keep, :k], w[keep], 1e-12, "sigmoid weights")
+        close(r["weights"][:, :k].sum(axis=1), np.full(T, gamma), 1e-12, "routed weights sum to gamma")
+        assert np.all(r["ids"][:, k:] == np.arange(E, E + S)) and np.all(r["weights"][:, k:] == sw)
+        if E == g["routed_experts"]:
+            assert r["ids"].shape[1] == g["selections_per_row"]
+            assert r["ids"][:, k:].tolist() == [g["shared_ids"]] * T
+
+
+def check_router_sigmoid_bias_selects_only(o):
+    """The bias moves the selection, never the weights: a large bias on one expert puts it in every
+    row, with the weight its unbiased score earns; without bias the selection is the softmax
+    router's (both scores are increasing in the logit)."""
+    L = small_layer(T=10, H=64, E=16, k=4, router_std=0.4)
+    bias = np.zeros(16, np.float32); bias[11] = 10.0
+    r = o.route_sigmoid(L.x, X_BF16, L.router, bias, 4)
+    sc = scipy.special.expit(np_act(L.x, X_BF16) @ L.router.astype(np.float64).T)
+    assert np.all(r["ids"][:, 0] == 11)
+    close(r["weights"][:, 0], sc[:, 11] / np.take_along_axis(sc, r["ids"][:, :4], axis=1).sum(axis=1), 1e-12,
+          "forced expert weight")
+    r0 = o.route_sigmoid(L.x, X_BF16, L.router, None, 4)
+    rs = o.route(L.x, X_BF16, L.router, None, 4)
+    keep = (r0["near_tie"] == 0) & (rs["near_tie"] == 0)
+    assert np.array_equal(r0["ids"][keep], rs["ids"][keep])
+
+
 # ------------------------------------------------------------------------------------------------
 # FP16 range management (Cascadia Sec. 3.3, Eq. 1)
 # ------------------------------------------------------------------------------------------------
@@ -660,7 +714,8 @@ ALL_CHECKS = [
     check_minifloat_reference, check_e2m1, check_e8m0, check_mxfp4_table, check_bf16_f16, check_storage,
     check_nibble_order, check_weight_access, check_silu, check_decode_matrix,
     check_router_vs_numpy, check_router_tiebreak, check_router_k_equals_E, check_router_shift_invariance,
-    check_router_shared, check_bucket, check_bucket_invalid,
+    check_router_shared, check_router_sigmoid_vs_numpy, check_router_sigmoid_bias_selects_only,
+    check_bucket, check_bucket_invalid,
     check_expert_apply_vs_numpy, check_layer_vs_numpy, check_layer_forms, check_single_expert_swiglu,
     check_combine, check_dense_slices, check_eq1_row_factor, check_eq1_restores_plain_layer,
     check_mx_tables, check_mx_encode_nearest, check_mx_scale_rule, check_mx_quantize_fp8_vs_torch,

@@ -22,6 +22,14 @@ MUTANTS = {
     "wrong scale block": ("return orc_mxfp4(code, srow[k / 32]);", "return orc_mxfp4(code, srow[k / 64]);"),
     "gate and up swapped in SwiGLU": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
                                       "hs[(int64_t)i * I + n] = orc_silu(u * up_scale) * g;"),
+    "sigmoid weights from the biased keys": ("weights[(int64_t)t * k_total + j] = routed_scale * (sc[order[j]] / sel);",
+                                             "weights[(int64_t)t * k_total + j] = routed_scale * (key[order[j]] / sel);"),
+    "sigmoid selection ignores the bias": ("key[e] = sc[e] + (sel_bias ? (double)sel_bias[e] : 0.0);", "key[e] = sc[e];"),
+    "sigmoid scale factor dropped": ("weights[(int64_t)t * k_total + j] = routed_scale * (sc[order[j]] / sel);",
+                                     "weights[(int64_t)t * k_total + j] = sc[order[j]] / sel;"),
+    "sigmoid of the negated logit": ("sc[e] = 1.0 / (1.0 + exp(-acc));", "sc[e] = 1.0 / (1.0 + exp(acc));"),
+    "shared weight fixed at 1": ("weights[(int64_t)t * k_total + top_k + s] = shared_weight;",
+                                 "weights[(int64_t)t * k_total + top_k + s] = 1.0;"),
     "attenuation not applied": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
                                 "hs[(int64_t)i * I + n] = orc_silu(g) * u;"),
     "attenuation applied to the gate": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
@@ -34,10 +42,16 @@ MUTANTS = {
                                          "weights[(int64_t)t * k_total + j] = p[order[j]];"),
     "router bias dropped": ("L[e] = acc + (bias ? (double)bias[e] : 0.0);", "L[e] = acc;"),
     "tie-break to the highest index": ("(p[a] == p[b] && a < b)", "(p[a] == p[b] && a > b)"),
-    "last hidden term dropped in router": ("for (int h = 0; h < H; ++h)\n        acc += act_value",
-                                           "for (int h = 0; h < H - 1; ++h)\n        acc += act_value"),
-    "shared expert id off": ("ids[(int64_t)t * k_total + top_k + s] = E + s;",
-                             "ids[(int64_t)t * k_total + top_k + s] = E - 1 - s;"),
+    "last hidden term dropped in router": (
+        "for (int h = 0; h < H; ++h)\n        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];\n      L[e]",
+        "for (int h = 0; h < H - 1; ++h)\n        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];\n      L[e]"),
+    "last hidden term dropped in sigmoid router": (
+        "for (int h = 0; h < H; ++h)\n        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];\n      sc[e]",
+        "for (int h = 0; h < H - 1; ++h)\n        acc += act_value(x, x_fmt, (int64_t)t * H + h) * (double)w_router[(int64_t)e * H + h];\n      sc[e]"),
+    "shared expert id off": ("ids[(int64_t)t * k_total + top_k + s] = E + s;\n      weights[(int64_t)t * k_total + top_k + s] = 1.0;",
+                             "ids[(int64_t)t * k_total + top_k + s] = E - 1 - s;\n      weights[(int64_t)t * k_total + top_k + s] = 1.0;"),
+    "sigmoid shared expert id off": ("ids[(int64_t)t * k_total + top_k + s] = E + s;\n      weights[(int64_t)t * k_total + top_k + s] = shared_weight;",
+                                     "ids[(int64_t)t * k_total + top_k + s] = E + 1 + s;\n      weights[(int64_t)t * k_total + top_k + s] = shared_weight;"),
     "bucket order not stable": ("int pos = offsets[b] + fill[b]++;",
                                 "int pos = offsets[b + 1] - 1 - fill[b]++;"),
     "combine uses reversed weights": ("acc += weights[(int64_t)t * k_total + j] * y_slots",

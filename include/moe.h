@@ -120,6 +120,45 @@ moe_status moe_route(const void *x, moe_act_dtype x_dtype, int T, int H, const f
                      float *weights, float *probs, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* moe_route_sigmoid -- the sigmoid router of [C31] (Cascadia Sec. 3.1: sigmoid scores, a
+ * bias-adjusted top-k selection, normalisation of the selected weights and a model scale factor;
+ * the page names these steps without formulas, and the plainest forms are taken):
+ *   L[t,e] = sum_h x[t,h] * w_router[e,h] (fp32 accumulation), s[t,e] = 1 / (1 + e^-L[t,e]);
+ *   the top_k experts by (s[t,e] + selection_bias[e] descending, index ascending) fill slots
+ *   j = 0..top_k-1 in that order with weights[t,j] = routed_scale * s_j / sum_{j'<top_k} s_j'
+ *   (the bias moves the selection only, never a weight); slots top_k .. top_k+n_shared-1 hold
+ *   the shared experts E .. E+n_shared-1 with weight shared_weight (Cascadia's rows carry six
+ *   routed and two shared selections, ids 256 and 257).
+ *   scores [T][E] fp32 out (the sigmoid scores s), or NULL; other arguments as for moe_route,
+ *   with the same workspace size.
+ * Errors: as moe_route, and SHAPE for a non-finite routed_scale or shared_weight. */
+moe_status moe_route_sigmoid(const void *x, moe_act_dtype x_dtype, int T, int H, const float *w_router,
+                             const float *selection_bias, int E, int top_k, int n_shared,
+                             float routed_scale, float shared_weight, int32_t *ids, float *weights,
+                             float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Fixed row shapes [C32] (Cascadia Sec. 3.2: a call's rows are run at one of the row shapes the
+ * compiled layer supports, the extra rows padded with zero routing weights, and only the real
+ * rows are handed back).  Here a row shape is a T for which the caller has buffers (and, say, a
+ * captured HIP graph of the layer's calls); the real row count n lives in device memory, so one
+ * graph serves every n up to its shape:
+ *   moe_route(..., T_shape, ...) -> moe_pad_rows(n_rows, T_shape, ...) -> moe_bucket ->
+ *   moe_expert_ffn -> moe_combine, then read rows [0, n) of y.
+ *
+ * moe_row_shape (host): the smallest entry of shapes[0 .. n_shapes) that is >= T (entries <= 0
+ * are ignored; the array need not be sorted); -1 when none is, or for T < 0, shapes NULL or
+ * n_shapes < 1. */
+int moe_row_shape(int T, const int *shapes, int n_shapes);
+/* moe_pad_rows: with n = *n_rows (a device int32, clamped to [0, T_shape]), every slot of rows
+ * t >= n gets weights[t,j] = 0 and ids[t,j] = -1 -- the invalid id makes moe_bucket drop it, so no
+ * expert runs on padding.  Rows < n are untouched.  Padding changes no real row's result: every
+ * kernel computes each token from its own x row and weights only (the rows past n of y_slots and
+ * y are left unspecified).  ids, weights [T_shape][k_total] in/out.
+ * Errors: NULL, SHAPE (T_shape < 0, k_total outside [1, MOE_MAX_SLOTS_PER_TOKEN]), ALIGN, HIP. */
+moe_status moe_pad_rows(const int32_t *n_rows, int T_shape, int k_total, int32_t *ids, float *weights,
+                        void *stream);
+
 /* ---------------------------------------------------------------------------------------------
  * moe_bucket -- group slots by expert (the fused path runs only the selected experts' work
  * [C31]).  Slot s = t*k_total + j.

@@ -68,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_bytes.restype = st; L.moe_route_workspace_bytes.argtypes = [i, i, i]
         L.moe_route.restype = i
         L.moe_route.argtypes = [vp, i, i, i, vp, vp, i, i, i, vp, vp, vp, vp, st, vp]
+        L.moe_route_sigmoid.restype = i
+        L.moe_route_sigmoid.argtypes = [vp, i, i, i, vp, vp, i, i, i, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                                        vp, st, vp]
+        L.moe_row_shape.restype = i; L.moe_row_shape.argtypes = [i, ctypes.POINTER(ctypes.c_int), i]
+        L.moe_pad_rows.restype = i; L.moe_pad_rows.argtypes = [vp, i, i, vp, vp, vp]
         L.moe_bucket_workspace_bytes.restype = st; L.moe_bucket_workspace_bytes.argtypes = [i, i]
         L.moe_bucket.restype = i
         L.moe_bucket.argtypes = [vp, i, i, vp, vp, vp, vp, vp, st, vp]
@@ -199,6 +204,40 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, top_k: int, logit_bias: O
                            _ptr(ids), _ptr(w), _ptr(probs), _ptr(ws), 0 if ws is None else ws.numel(),
                            _stream(dev)), "moe_route")
     return ids, w, probs
+
+
+def moe_route_sigmoid(x: torch.Tensor, w_router: torch.Tensor, top_k: int,
+                      selection_bias: Optional[torch.Tensor] = None, n_shared: int = 0, routed_scale: float = 1.0,
+                      shared_weight: float = 1.0, want_scores: bool = False, out=None, workspace=None):
+    """Cascadia's sigmoid router -> (ids int32 [T][k'], weights fp32 [T][k'], scores fp32 [T][E] or None)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    kt = top_k + n_shared
+    dev = x.device
+    if out is None:
+        ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
+        w = torch.empty((T, kt), dtype=torch.float32, device=dev)
+        scores = torch.empty((T, E), dtype=torch.float32, device=dev) if want_scores else None
+    else:
+        ids, w, scores = out
+    need = moe_route_workspace_bytes(T, H, E)
+    ws = workspace if workspace is not None else _workspace(need, dev)
+    _check(lib().moe_route_sigmoid(_ptr(x), _act_dtype(x), T, H, _ptr(w_router), _ptr(selection_bias), E, top_k,
+                                   n_shared, routed_scale, shared_weight, _ptr(ids), _ptr(w), _ptr(scores), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(dev)), "moe_route_sigmoid")
+    return ids, w, scores
+
+
+def moe_row_shape(T: int, shapes) -> int:
+    """Smallest supported row shape >= T (-1 if none)."""
+    arr = (ctypes.c_int * len(shapes))(*shapes)
+    return lib().moe_row_shape(T, arr, len(shapes))
+
+
+def moe_pad_rows(n_rows: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor) -> None:
+    """Rows >= n_rows[0] (a device int32 scalar) get zero weights and id -1, in place."""
+    T, kt = ids.shape
+    _check(lib().moe_pad_rows(_ptr(n_rows), T, kt, _ptr(ids), _ptr(weights), _stream(ids.device)), "moe_pad_rows")
 
 
 @dataclass
@@ -437,9 +476,89 @@ class MoELayer:
         return moe_combine(self.y_slots, self.weights, out=self.y)
 
 
-__all__ = ["moe_route", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
+class FixedShapeLayer:
+    """A routed-MoE layer run at fixed row shapes (Cascadia Sec. 3.2): for each supported shape S
+    the five calls (route, pad, bucket, expert FFN, combine) on S rows are captured once in a HIP
+    graph; a call with T rows copies them into the shape's input buffer, writes T to the device
+    row count, replays the graph of the smallest S >= T and returns the first T rows of y.  The
+    padding rows carry zero routing weights and invalid ids, so they cost no expert work and
+    change no real row.  Buffers are allocated once here; forward() allocates nothing."""
+
+    def __init__(self, W: ExpertWeights, shapes, top_k: int, w_router: torch.Tensor,
+                 logit_bias: Optional[torch.Tensor] = None, n_shared: int = 0):
+        self.shapes = sorted(set(int(s) for s in shapes))
+        self.W, self.top_k, self.n_shared = W, top_k, n_shared
+        self.w_router, self.logit_bias = w_router, logit_bias
+        dev = W.device
+        S = self.shapes[-1]
+        kt = top_k + n_shared
+        self.k_total = kt
+        H = W.hidden
+        E = W.n_experts - n_shared
+        self.x = torch.zeros((S, H), dtype=torch.bfloat16 if W.fmt == MOE_W_MXFP4 else torch.float16, device=dev)
+        self.n_rows = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ids = torch.empty((S, kt), dtype=torch.int32, device=dev)
+        self.weights = torch.empty((S, kt), dtype=torch.float32, device=dev)
+        self.route_ws = _workspace(max(moe_route_workspace_bytes(s, H, E) for s in self.shapes), dev)
+        self.buckets = Buckets(torch.empty(W.n_experts, dtype=torch.int32, device=dev),
+                               torch.empty(W.n_experts + 1, dtype=torch.int32, device=dev),
+                               torch.empty(S * kt, dtype=torch.int32, device=dev), None)
+        self.bucket_ws = _workspace(max(moe_bucket_workspace_bytes(s * kt, W.n_experts) for s in self.shapes), dev)
+        self.ffn_ws = _workspace(max(moe_expert_ffn_workspace_bytes(s, kt, W) for s in self.shapes), dev)
+        self.y_slots = torch.empty((S * kt, H), dtype=torch.float32, device=dev)
+        self.y = torch.empty((S, H), dtype=torch.float32, device=dev)
+        self.graphs = {}
+
+    def run_shape(self, S: int) -> None:
+        """Enqueue the five calls for row shape S (eager; also what each graph holds)."""
+        kt = self.k_total
+        ids, w = self.ids[:S], self.weights[:S]
+        moe_route(self.x[:S], self.w_router, self.top_k, self.logit_bias, self.n_shared, out=(ids, w, None),
+                  workspace=self.route_ws)
+        moe_pad_rows(self.n_rows, ids, w)
+        b = Buckets(self.buckets.counts, self.buckets.offsets, self.buckets.sorted_slot[:S * kt], None)
+        moe_bucket(ids, self.W.n_experts, out=b, workspace=self.bucket_ws)
+        moe_expert_ffn(self.x[:S], self.W, b.offsets, b.sorted_slot, kt, out=self.y_slots[:S * kt],
+                       workspace=self.ffn_ws)
+        moe_combine(self.y_slots[:S * kt], w, out=self.y[:S])
+
+    def capture(self) -> None:
+        """Capture one graph per shape (after one eager pass of each on a side stream)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for S in self.shapes:
+                self.run_shape(S)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for S in self.shapes:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.run_shape(S)
+            self.graphs[S] = g
+        torch.cuda.synchronize()
+
+    def forward(self, x: torch.Tensor, use_graph: bool = True) -> torch.Tensor:
+        """y[:T] for the T rows of x (a view into the layer's output buffer, valid until the next call)."""
+        T = x.shape[0]
+        S = moe_row_shape(T, self.shapes)
+        if S < 0:
+            raise ValueError(f"{T} rows exceed the largest supported row shape {self.shapes[-1]}")
+        self.x[:T].copy_(x)
+        self.n_rows.fill_(T)
+        if use_graph:
+            if not self.graphs:
+                self.capture()
+            self.graphs[S].replay()
+        else:
+            self.run_shape(S)
+        return self.y[:T]
+
+
+__all__ = ["moe_route", "moe_route_sigmoid", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
            "moe_expert_ffn_f16_workspace_bytes", "moe_combine_restore", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
            "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
            "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",
-           "ExpertWeights", "Buckets", "MoELayer", "MoEError", "lib"]
+           "moe_row_shape", "moe_pad_rows", "ExpertWeights", "Buckets", "MoELayer", "FixedShapeLayer", "MoEError",
+           "lib"]

@@ -106,6 +106,48 @@ moe_status moe_route(const void* x, moe_act_dtype x_dtype, int T, int H, const f
                                       (hipStream_t)stream));
 }
 
+moe_status moe_route_sigmoid(const void* x, moe_act_dtype x_dtype, int T, int H, const float* w_router,
+                             const float* selection_bias, int E, int top_k, int n_shared, float routed_scale,
+                             float shared_weight, int32_t* ids, float* weights, float* scores, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (T < 0 || H < 1 || E < 1 || E > MOE_MAX_EXPERTS || n_shared < 0) return MOE_ERR_SHAPE;
+  if (!(routed_scale - routed_scale == 0.0f) || !(shared_weight - shared_weight == 0.0f)) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
+  if (top_k < 1 || top_k > E || top_k + n_shared > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_TOPK;
+  if (!x || !w_router || !ids || !weights) return MOE_ERR_NULL;
+  if ((int64_t)T * (top_k + n_shared) > INT_MAX || (int64_t)T * E > INT_MAX) return MOE_ERR_SHAPE;
+  if (!al16(x) || !al4(w_router) || !al4(ids) || !al4(weights) || (scores && !al4(scores)) ||
+      (selection_bias && !al4(selection_bias)))
+    return MOE_ERR_ALIGN;
+  const size_t need = moe_route_workspace_bytes(T, H, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, selection_bias, E, top_k,
+                                      n_shared, ids, weights, scores, (float*)workspace,
+                                      moe::route_splits(T, H, E), (hipStream_t)stream, true, routed_scale,
+                                      shared_weight));
+}
+
+// ---------------------------------------------------------------------------------------------
+int moe_row_shape(int T, const int* shapes, int n_shapes) {
+  if (T < 0 || !shapes || n_shapes < 1) return -1;
+  int best = -1;
+  for (int i = 0; i < n_shapes; ++i)
+    if (shapes[i] >= T && shapes[i] > 0 && (best < 0 || shapes[i] < best)) best = shapes[i];
+  return best;
+}
+
+moe_status moe_pad_rows(const int32_t* n_rows, int T_shape, int k_total, int32_t* ids, float* weights,
+                        void* stream) {
+  if (T_shape == 0) return MOE_OK;
+  if (T_shape < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN || (int64_t)T_shape * k_total > INT_MAX)
+    return MOE_ERR_SHAPE;
+  if (!n_rows || !ids || !weights) return MOE_ERR_NULL;
+  if (!al4(n_rows) || !al4(ids) || !al4(weights)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_pad_rows(n_rows, T_shape, k_total, ids, weights, (hipStream_t)stream));
+}
+
 // ---------------------------------------------------------------------------------------------
 size_t moe_bucket_workspace_bytes(int n_slots, int n_buckets) {
   if (n_slots <= moe::kBucketChunk || n_buckets <= 0) return 0;

@@ -11,9 +11,16 @@ namespace moe {
 
 // ---- router ----
 int route_splits(int T, int H, int E);
+// sigmoid: Cascadia's sigmoid router (bias on the selection only, weights routed_scale * s / sum s,
+// shared slots shared_weight) instead of softmax -> top-k -> renormalise.
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias,
                         int E, int top_k, int n_shared, int32_t* ids, float* weights, float* probs,
-                        float* partial, int splits, hipStream_t stream);
+                        float* partial, int splits, hipStream_t stream, bool sigmoid = false,
+                        float routed_scale = 1.0f, float shared_weight = 1.0f);
+
+// ---- fixed row shapes: zero routing weights and invalid ids on rows past the device row count ----
+hipError_t launch_pad_rows(const int32_t* n_rows, int T_shape, int k_total, int32_t* ids, float* weights,
+                           hipStream_t stream);
 
 // ---- bucketing ----
 constexpr int kBucketChunk = 512;

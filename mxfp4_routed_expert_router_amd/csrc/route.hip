@@ -155,11 +155,16 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
 // Lane l holds experts VPL l .. VPL l + VPL - 1 (contiguous, so with E % VPL == 0 -- VEC -- a
 // lane reads each slice's VPL partial logits with one vector load, and writes its probabilities
 // together).
-template <int VPL, bool VEC>
+//
+// SIG selects the sigmoid router of Cascadia Sec. 3.1 instead of the softmax one: scores
+// s = 1 / (1 + e^-L), selection by s + bias (the bias moves the choice only), weights
+// routed_scale * s / (sum of the selected s), shared slots shared_weight; `probs` receives s.
+template <int VPL, bool VEC, bool SIG>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ partial, int splits, int T,
                                                            int E, const float* __restrict__ bias, int top_k,
                                                            int n_shared, int32_t* __restrict__ ids,
-                                                           float* __restrict__ weights, float* __restrict__ probs) {
+                                                           float* __restrict__ weights, float* __restrict__ probs,
+                                                           float routed_scale, float shared_weight) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // whole wave leaves together; no block-wide barrier follows
@@ -190,6 +195,62 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     L[v] = 0.0f;
 #pragma unroll
     for (int q = 0; q < kMaxSplits; ++q) L[v] += part[q][v];
+  }
+  if constexpr (SIG) {
+    // scores, and the selection keys score + bias; the winner of a round reads its score from the
+    // lane that holds it
+    float sv[VPL];
+    uint32_t kh[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = e0 + v;
+      sv[v] = (e < E) ? 1.0f / (1.0f + expf(-L[v])) : 0.0f;
+      kh[v] = (e < E) ? f32_order_key(sv[v] + (bias ? bias[e] : 0.0f)) : 0u;
+      if (probs && e < E) probs[(int64_t)t * E + e] = sv[v];
+    }
+    float psum = 0.0f;
+    int my_id[4] = {0, 0, 0, 0};
+    float my_p[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < top_k; ++j) {
+      uint32_t m = kh[0];
+#pragma unroll
+      for (int v = 1; v < VPL; ++v) m = max(m, kh[v]);
+      m = wave_max_u32_dpp(m);
+      int bi = INT_MAX;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const uint64_t b = __ballot(kh[v] == m);
+        if (b) bi = min(bi, VPL * (__builtin_ffsll((long long)b) - 1) + v);
+      }
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (e0 + v == bi) kh[v] = 0u;
+      const int bv = bi % VPL;  // uniform: every lane offers its score of that register
+      float cand = sv[0];
+#pragma unroll
+      for (int v = 1; v < VPL; ++v) cand = (v == bv) ? sv[v] : cand;
+      const float p = __shfl(cand, bi / VPL, kWave);
+      psum += p;
+      if ((j & 63) == lane) {
+        const int q = j >> 6;
+#pragma unroll
+        for (int z = 0; z < 4; ++z)
+          if (z == q) {
+            my_id[z] = bi;
+            my_p[z] = p;
+          }
+      }
+    }
+    const int k_total = top_k + n_shared;
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const int j = lane + 64 * z;
+      if (j >= k_total) break;
+      const bool routed = j < top_k;
+      ids[(int64_t)t * k_total + j] = routed ? my_id[z] : E + (j - top_k);
+      weights[(int64_t)t * k_total + j] = routed ? routed_scale * (my_p[z] / psum) : shared_weight;
+    }
+    return;
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
@@ -305,7 +366,7 @@ void launch_logits(const void* x, int T, int H, const float* w, int E, int split
 
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,
                         int top_k, int n_shared, int32_t* ids, float* weights, float* probs, float* partial,
-                        int splits, hipStream_t stream) {
+                        int splits, hipStream_t stream, bool sigmoid, float routed_scale, float shared_weight) {
   const bool vec = ((uintptr_t)w_router % 16 == 0) && (H % 8 == 0);
   if (x_fp16) {
     if (vec) launch_logits<1, 1>(x, T, H, w_router, E, splits, partial, stream);
@@ -318,14 +379,23 @@ hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_
   if (err != hipSuccess) return err;
   dim3 g2((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-#define MOE_SEL(V)                                                                                           \
+#define MOE_SEL2(V, SG)                                                                                       \
   {                                                                                                          \
     if (E % V == 0)                                                                                          \
-      route_select_kernel<V, true><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared, ids, \
-                                                           weights, probs);                                  \
+      route_select_kernel<V, true, SG><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared,  \
+                                                               ids, weights, probs, routed_scale,            \
+                                                               shared_weight);                               \
     else                                                                                                     \
-      route_select_kernel<V, false><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared,    \
-                                                            ids, weights, probs);                            \
+      route_select_kernel<V, false, SG><<<g2, 256, 0, stream>>>(partial, splits, T, E, bias, top_k, n_shared, \
+                                                                ids, weights, probs, routed_scale,           \
+                                                                shared_weight);                              \
+  }
+#define MOE_SEL(V)          \
+  {                         \
+    if (sigmoid)            \
+      MOE_SEL2(V, true)     \
+    else                    \
+      MOE_SEL2(V, false)    \
   }
   if (vpl <= 1) MOE_SEL(1)
   else if (vpl <= 2) MOE_SEL(2)
@@ -333,6 +403,7 @@ hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_
   else if (vpl <= 8) MOE_SEL(8)
   else MOE_SEL(16)
 #undef MOE_SEL
+#undef MOE_SEL2
   return hipGetLastError();
 }
 

@@ -278,3 +278,33 @@ def test_range_path_validation():
     assert cr(n=-2) == SHAPE and cr(n=31) == SHAPE and cr(H=66) == SHAPE
     assert cr(ys=None) == NULL
     assert cr(ys=fake(4)) == ALIGN and cr(y=fake(0x208)) == ALIGN
+
+
+def test_row_shape_and_padding_validation():
+    """moe_row_shape (host) picks the smallest supported shape that holds T; moe_pad_rows checks."""
+    L = m.lib()
+    assert m.moe_row_shape(5, [1, 2, 4, 8, 16]) == 8
+    assert m.moe_row_shape(8, [16, 8, 1]) == 8
+    assert m.moe_row_shape(0, [4, 2]) == 2
+    assert m.moe_row_shape(17, [1, 16]) == -1
+    assert m.moe_row_shape(3, [0, -2, 3]) == 3
+    assert m.moe_row_shape(-1, [4]) == -1
+    assert L.moe_row_shape(4, None, 3) == -1
+    assert L.moe_pad_rows(None, 0, 2, None, None, None) == OK
+    assert L.moe_pad_rows(fake(), -1, 2, fake(0x100), fake(0x200), None) == SHAPE
+    assert L.moe_pad_rows(fake(), 8, 0, fake(0x100), fake(0x200), None) == SHAPE
+    assert L.moe_pad_rows(None, 8, 2, fake(0x100), fake(0x200), None) == NULL
+    assert L.moe_pad_rows(fake(), 8, 2, fake(0x102), fake(0x200), None) == ALIGN
+
+
+def test_sigmoid_route_validation():
+    L = m.lib()
+    r = lambda **k: L.moe_route_sigmoid(k.get("x", fake()), 0, k.get("T", 4), 64, fake(0x100), None, k.get("E", 8),
+                                        k.get("k", 2), k.get("S", 0), k.get("g", 1.0), k.get("sw", 1.0),
+                                        fake(0x200), fake(0x300), None, fake(0x1000), 1 << 20, None)
+    assert L.moe_route_sigmoid(None, 0, 0, 64, None, None, 8, 2, 0, 1.0, 1.0, None, None, None, None, 0, None) == OK
+    assert r(k=0) == TOPK and r(k=9) == TOPK
+    assert r(E=0) == SHAPE
+    assert r(g=float("nan")) == SHAPE and r(sw=float("inf")) == SHAPE
+    assert r(x=None) == NULL
+    assert r(x=fake(8)) == ALIGN

@@ -23,7 +23,8 @@ SOURCE = os.path.join(HERE, "moe_oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 X_BF16, X_FP16 = 0, 1
-W_MXFP4, W_FP16 = 0, 1
+W_MXFP4, W_FP16, W_INT4_G32, W_NVFP4 = 0, 1, 2, 3
+W_FORMATS = {"mxfp4": W_MXFP4, "fp16": W_FP16, "int4g32": W_INT4_G32, "nvfp4": W_NVFP4}
 MX_FP8_E4M3, MX_FP4_E2M1, MX_FP6_E2M3 = 1, 2, 3
 
 _CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
@@ -40,7 +41,9 @@ def build(source: str = SOURCE, out: str = LIBRARY) -> str:
 class _Proj(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("w_expert_stride", ctypes.c_int64), ("w_row_stride", ctypes.c_int64),
-                ("s_expert_stride", ctypes.c_int64), ("s_row_stride", ctypes.c_int64)]
+                ("s_expert_stride", ctypes.c_int64), ("s_row_stride", ctypes.c_int64),
+                ("zeros", ctypes.c_void_p), ("z_expert_stride", ctypes.c_int64), ("z_row_stride", ctypes.c_int64),
+                ("tensor_scale", ctypes.c_void_p)]
 
 
 class _Weights(ctypes.Structure):
@@ -51,32 +54,45 @@ class _Weights(ctypes.Structure):
 class ExpertWeights:
     """Holds the numpy arrays (kept alive) and the C struct describing them.
 
-    codes: [E'][N][K/2] uint8 (MXFP4) or [E'][N][K] uint16 (FP16), possibly a strided view whose
-    innermost dimension is contiguous; scales: [E'][N][K/32] uint8 or None."""
+    codes: [E'][N][K/2] uint8 (MXFP4, INT4_G32, NVFP4) or [E'][N][K] uint16 (FP16), possibly a
+    strided view whose innermost dimension is contiguous; scales: [E'][N][K/32] uint8 (MXFP4),
+    [E'][N][K/32] binary16 bits as uint16 (INT4_G32), [E'][N][K/16] uint8 E4M3 (NVFP4) or None;
+    extras (per projection, INT4_G32: zero points [E'][N][K/64] uint8; NVFP4: tensor scales [E']
+    float32)."""
 
-    def __init__(self, fmt, gate, gate_s, up, up_s, down, down_s):
-        self.keep = [gate, gate_s, up, up_s, down, down_s]
+    def __init__(self, fmt, gate, gate_s, up, up_s, down, down_s, extras=None):
+        extras = dict(extras or {})
+        if fmt == W_NVFP4:
+            extras = {k: np.ascontiguousarray(v, np.float32) for k, v in extras.items()}
+        self.keep = [gate, gate_s, up, up_s, down, down_s, extras]
         E2, I = gate.shape[0], gate.shape[1]
         H = down.shape[1]
         self.n_experts, self.hidden, self.inter, self.fmt = E2, H, I, fmt
 
-        def proj(c, s):
+        def proj(c, s, ex):
             assert c.strides[-1] == c.itemsize
             p = _Proj()
             p.w = c.ctypes.data
             p.w_expert_stride, p.w_row_stride = c.strides[0], c.strides[1]
             if s is not None:
-                assert s.strides[-1] == 1
+                assert s.strides[-1] == s.itemsize
                 p.scales = s.ctypes.data
                 p.s_expert_stride, p.s_row_stride = s.strides[0], s.strides[1]
+            if ex is not None and fmt == W_INT4_G32:
+                p.zeros = ex.ctypes.data
+                p.z_expert_stride, p.z_row_stride = ex.strides[0], ex.strides[1]
+            if ex is not None and fmt == W_NVFP4:
+                p.tensor_scale = ex.ctypes.data
             return p
 
-        self.c = _Weights(fmt, E2, H, I, proj(gate, gate_s), proj(up, up_s), proj(down, down_s))
+        self.c = _Weights(fmt, E2, H, I, proj(gate, gate_s, extras.get("gate")), proj(up, up_s, extras.get("up")),
+                          proj(down, down_s, extras.get("down")))
 
     @classmethod
     def from_layer(cls, L) -> "ExpertWeights":
-        fmt = W_MXFP4 if L.wl.weight_format == "mxfp4" else W_FP16
-        return cls(fmt, L.gate_codes, L.gate_scales, L.up_codes, L.up_scales, L.down_codes, L.down_scales)
+        fmt = W_FORMATS[L.wl.weight_format]
+        return cls(fmt, L.gate_codes, L.gate_scales, L.up_codes, L.up_scales, L.down_codes, L.down_scales,
+                   getattr(L, "extras", None))
 
 
 def _p(a):
@@ -96,6 +112,8 @@ class Oracle:
         lib.orc_f16.restype = d; lib.orc_f16.argtypes = [ctypes.c_uint16]
         lib.orc_silu.restype = d; lib.orc_silu.argtypes = [d]
         lib.orc_mxfp4_bits_per_weight.restype = d; lib.orc_mxfp4_bits_per_weight.argtypes = []
+        lib.orc_int4g32_bits_per_weight.restype = d; lib.orc_int4g32_bits_per_weight.argtypes = []
+        lib.orc_nvfp4_bits_per_weight.restype = d; lib.orc_nvfp4_bits_per_weight.argtypes = []
         lib.orc_mxfp4_bytes.restype = ctypes.c_int64
         lib.orc_mxfp4_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
         lib.orc_num_threads.restype = i; lib.orc_num_threads.argtypes = []
@@ -144,6 +162,8 @@ class Oracle:
     def f16(self, b: int) -> float: return self.lib.orc_f16(b)
     def silu(self, z: float) -> float: return self.lib.orc_silu(z)
     def bits_per_weight(self) -> float: return self.lib.orc_mxfp4_bits_per_weight()
+    def int4g32_bits_per_weight(self) -> float: return self.lib.orc_int4g32_bits_per_weight()
+    def nvfp4_bits_per_weight(self) -> float: return self.lib.orc_nvfp4_bits_per_weight()
     def mxfp4_bytes(self, n_rows: int, k: int) -> int: return self.lib.orc_mxfp4_bytes(n_rows, k)
     def num_threads(self) -> int: return self.lib.orc_num_threads()
 

@@ -39,6 +39,14 @@ double orc_mxfp4(int code, int e) { return orc_e2m1(code) * orc_e8m0(e); }
 /* [MX]: a 32-weight block stores 32 four-bit codes and one 8-bit scale: 4 + 8/32 bits per weight. */
 double orc_mxfp4_bits_per_weight(void) { return (32.0 * 4.0 + 8.0) / 32.0; }
 
+/* Cascadia Sec. 3.1 and 3.5: a group of 32 four-bit codes carries a binary16 scale and (reading)
+ * a four-bit zero point: 4 + 16/32 + 4/32 bits per weight. */
+double orc_int4g32_bits_per_weight(void) { return (32.0 * 4.0 + 16.0 + 4.0) / 32.0; }
+
+/* FreeToken post, "MXFP4 is not NVFP4": E2M1 codes with one E4M3 scale per 16 values, 4 + 8/16
+ * bits per weight before the tensor scale. */
+double orc_nvfp4_bits_per_weight(void) { return (16.0 * 4.0 + 8.0) / 16.0; }
+
 int64_t orc_mxfp4_bytes(int64_t n_rows, int64_t k) {
   return n_rows * (k / 2) + n_rows * (k / 32);
 }
@@ -70,18 +78,32 @@ static double act_value(const uint16_t *x, int x_fmt, int64_t i) {
 
 /* Element (n, k) of expert e of one projection.  [MX]: element k of a packed row lives in byte
  * k/2 (reading: even k in the low nibble) and uses the scale of block floor(k/32); rows are
- * row-major with K contiguous, read in place with no repack. */
+ * row-major with K contiguous, read in place with no repack.  The other formats as described in
+ * moe_oracle.h. */
 double orc_weight(const orc_proj *p, int fmt, int e, int n, int k) {
+  const uint8_t *row = (const uint8_t *)p->w + (int64_t)e * p->w_expert_stride + (int64_t)n * p->w_row_stride;
   if (fmt == ORC_W_FP16) {
-    const uint8_t *row = (const uint8_t *)p->w + (int64_t)e * p->w_expert_stride + (int64_t)n * p->w_row_stride;
     uint16_t bits;
     memcpy(&bits, row + 2 * (int64_t)k, 2);
     return orc_f16(bits);
   }
-  const uint8_t *row = (const uint8_t *)p->w + (int64_t)e * p->w_expert_stride + (int64_t)n * p->w_row_stride;
   const uint8_t *srow = p->scales + (int64_t)e * p->s_expert_stride + (int64_t)n * p->s_row_stride;
   uint8_t byte = row[k / 2];
   int code = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+  if (fmt == ORC_W_INT4_G32) {
+    /* Cascadia Sec. 3.1: group-32 unsigned INT4 codes with a binary16 scale; zero point (reading:
+     * four bits, low nibble first) */
+    const int g = k / 32;
+    const uint16_t sbits = (uint16_t)(srow[2 * g] | (srow[2 * g + 1] << 8));
+    const uint8_t *zrow = p->zeros + (int64_t)e * p->z_expert_stride + (int64_t)n * p->z_row_stride;
+    const int zero = (g % 2 == 0) ? (zrow[g / 2] & 0x0F) : (zrow[g / 2] >> 4);
+    return (double)(code - zero) * orc_f16(sbits);
+  }
+  if (fmt == ORC_W_NVFP4) {
+    /* FreeToken post: E2M1 value times the E4M3 scale of its 16-value block times the tensor
+     * scale */
+    return orc_e2m1(code) * orc_mx_value(ORC_MX_FP8_E4M3, srow[k / 16]) * (double)p->tensor_scale[e];
+  }
   return orc_mxfp4(code, srow[k / 32]);
 }
 

@@ -31,17 +31,27 @@
 extern "C" {
 #endif
 
-enum { ORC_W_MXFP4 = 0, ORC_W_FP16 = 1 };
+enum { ORC_W_MXFP4 = 0, ORC_W_FP16 = 1, ORC_W_INT4_G32 = 2, ORC_W_NVFP4 = 3 };
 enum { ORC_X_BF16 = 0, ORC_X_FP16 = 1 };
 
 /* One projection of every expert, logical [n_experts][N][K] with K contiguous.
  * MXFP4: w holds bytes, element k of a row in byte k/2, even k in the low nibble; scales hold one
  *        E8M0 byte per 32 elements along K.  FP16: w holds binary16 words, scales unused.
+ * INT4_G32 (Cascadia Sec. 3.1 and 3.5): w holds unsigned 4-bit codes packed as for MXFP4; group
+ *        g = k/32 has a binary16 scale (little-endian bytes 2g, 2g+1 of the scale row) and an
+ *        unsigned 4-bit zero point (nibble g%2 of byte g/2 of the zero row, low nibble first);
+ *        weight = (code - zero) * scale.
+ * NVFP4 (FreeToken post, "MXFP4 is not NVFP4"): w holds E2M1 codes packed as for MXFP4; block
+ *        b = k/16 has an E4M3 scale byte (byte b of the scale row); each expert has one fp32
+ *        tensor scale; weight = v(code) * e4m3(scale) * tensor_scale[e].
  * Strides are in bytes, so slices of a larger matrix can be described. */
 typedef struct {
   const void *w;
   const uint8_t *scales;
   int64_t w_expert_stride, w_row_stride, s_expert_stride, s_row_stride;
+  const uint8_t *zeros;          /* INT4_G32 zero points */
+  int64_t z_expert_stride, z_row_stride;
+  const float *tensor_scale;     /* NVFP4: [n_experts] */
 } orc_proj;
 
 typedef struct {
@@ -62,6 +72,8 @@ double orc_bf16(uint16_t bits);
 double orc_f16(uint16_t bits);
 double orc_weight(const orc_proj *p, int fmt, int e, int n, int k);
 double orc_mxfp4_bits_per_weight(void);     /* storage cost of one block, per weight */
+double orc_int4g32_bits_per_weight(void);   /* 32 codes + binary16 scale + 4-bit zero point */
+double orc_nvfp4_bits_per_weight(void);     /* 16 codes + E4M3 scale (tensor scale not counted) */
 int64_t orc_mxfp4_bytes(int64_t n_rows, int64_t k);  /* codes + scales of an [n_rows][k] matrix */
 
 /* ---- the layer ---- */

@@ -14,7 +14,9 @@ weights can be regenerated on its own and in any order.  Normals use the
 Box-Muller transform on pairs of 53-bit uniforms (both branches).
 
 Stream ids: x 0, router weight 1, gate codes 2, gate scales 3, up codes 4,
-up scales 5, down codes 6, down scales 7 (FP16 weights use 2, 4, 6).
+up scales 5, down codes 6, down scales 7 (FP16 weights use 2, 4, 6); INT4
+group-32 zero points 8, 9, 10 and NVFP4 tensor scales 11, 12, 13 (gate, up,
+down).
 """
 from __future__ import annotations
 
@@ -34,6 +36,8 @@ STREAM_UP = 4
 STREAM_UP_SCALE = 5
 STREAM_DOWN = 6
 STREAM_DOWN_SCALE = 7
+STREAM_ZERO = {"gate": 8, "up": 9, "down": 10}
+STREAM_TENSOR_SCALE = {"gate": 11, "up": 12, "down": 13}
 
 _M64 = (1 << 64) - 1
 
@@ -60,6 +64,13 @@ def uniform_uint(seed: int, stream: int, n: int, lo: int, hi: int, sub: int = 0)
     r = g.bit_generator.random_raw(int(n)).astype(np.uint64) >> np.uint64(32)
     span = np.uint64(hi - lo + 1)
     return (lo + ((r * span) >> np.uint64(32))).astype(np.int64)
+
+
+def uniform(seed: int, stream: int, n: int, lo: float, hi: float, sub: int = 0) -> np.ndarray:
+    """n independent float64 values uniform in [lo, hi) (53-bit uniforms)."""
+    g = _gen(seed, stream, sub)
+    u = (g.bit_generator.random_raw(int(n)) >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
+    return lo + (hi - lo) * u
 
 
 def normal(seed: int, stream: int, n: int, std: float = 1.0, sub: int = 0) -> np.ndarray:
@@ -107,7 +118,7 @@ class Workload:
     top_k: int             # k
     n_shared: int          # S (always-on experts appended after the k routed slots)
     inter: int             # I, per-expert SwiGLU intermediate size
-    weight_format: str     # "mxfp4" or "fp16"
+    weight_format: str     # "mxfp4", "fp16", "int4g32" or "nvfp4"
     act_dtype: str         # "bf16" or "fp16"
     router_std: float      # standard deviation of router weight entries
     zipf_s: float = 0.0    # >0: logit bias b_e = -s * ln(e + 1)
@@ -152,6 +163,10 @@ class LayerInputs:
     x: uint16 [T][H] (bf16 or fp16 bits).  router: float32 [E][H].  bias: float32 [E] or None.
     MXFP4: *_codes uint8 [E'][N][K/2] (two codes per byte), *_scales uint8 [E'][N][K/32].
     FP16:  *_codes uint16 [E'][N][K] (binary16 bits), *_scales None.
+    INT4_G32: *_codes uint8 [E'][N][K/2] (unsigned codes), *_scales uint16 [E'][N][K/32] (binary16
+           bits), extras[m] uint8 [E'][N][ceil(K/64)] zero points (group 2j in the low nibble).
+    NVFP4: *_codes uint8 [E'][N][K/2] (E2M1), *_scales uint8 [E'][N][K/16] (E4M3 bits),
+           extras[m] float32 [E'] tensor scales.
     gate/up have N = I, K = H; down has N = H, K = I.
     """
     wl: Workload
@@ -165,6 +180,7 @@ class LayerInputs:
     up_scales: Optional[np.ndarray]
     down_codes: np.ndarray
     down_scales: Optional[np.ndarray]
+    extras: Optional[dict] = None
 
 
 def make_x(wl: Workload, T: int, seed: int = 0) -> np.ndarray:
@@ -192,8 +208,42 @@ def make_expert_matrix(wl: Workload, which: str, expert: int, seed: int = 0):
         codes = random_bytes(seed, stream, N * K // 2, sub=expert).reshape(N, K // 2)
         sc = uniform_uint(seed, stream + 1, N * K // 32, wl.scale_lo, wl.scale_hi, sub=expert)
         return codes, sc.astype(np.uint8).reshape(N, K // 32)
+    if wl.weight_format == "int4g32":
+        codes = random_bytes(seed, stream, N * K // 2, sub=expert).reshape(N, K // 2)
+        sc = to_f16_bits(uniform(seed, stream + 1, N * K // 32, INT4_SCALE_LO, INT4_SCALE_HI, sub=expert))
+        return codes, sc.reshape(N, K // 32)
+    if wl.weight_format == "nvfp4":
+        codes = random_bytes(seed, stream, N * K // 2, sub=expert).reshape(N, K // 2)
+        sc = uniform_uint(seed, stream + 1, N * K // 16, NVFP4_SCALE_CODE_LO, NVFP4_SCALE_CODE_HI, sub=expert)
+        return codes, sc.astype(np.uint8).reshape(N, K // 16)
     z = normal(seed, stream, N * K, std=wl.weight_std, sub=expert).reshape(N, K)
     return to_f16_bits(z), None
+
+
+# INT4 group-32: binary16 scales uniform in [0.002, 0.004) and zero points uniform in 0..15, so
+# with uniform codes a weight (code - zero) * scale has a standard deviation of about 0.02.
+INT4_SCALE_LO, INT4_SCALE_HI = 0.002, 0.004
+# NVFP4: E4M3 scale codes uniform over 0x28 .. 0x3F (0.25 .. 1.875) and fp32 tensor scales
+# uniform in [0.005, 0.01) per expert (weights of standard deviation about 0.02).
+NVFP4_SCALE_CODE_LO, NVFP4_SCALE_CODE_HI = 0x28, 0x3F
+NVFP4_TENSOR_SCALE_LO, NVFP4_TENSOR_SCALE_HI = 0.005, 0.01
+
+
+def make_expert_extra(wl: Workload, which: str, expert: int, seed: int = 0):
+    """INT4 group-32: the zero points of one expert's matrix ([N][ceil(K/64)] bytes, group 2j in
+    the low nibble); NVFP4: its tensor scale (float32 scalar); None for other formats."""
+    H, I = wl.hidden, wl.inter
+    N, K = (I, H) if which in ("gate", "up") else (H, I)
+    if wl.weight_format == "int4g32":
+        g = K // 32
+        z = uniform_uint(seed, STREAM_ZERO[which], N * g, 0, 15, sub=expert).reshape(N, g)
+        if g % 2:
+            z = np.concatenate([z, np.zeros((N, 1), np.int64)], axis=1)
+        return (z[:, 0::2] | (z[:, 1::2] << 4)).astype(np.uint8)
+    if wl.weight_format == "nvfp4":
+        return np.float32(uniform(seed, STREAM_TENSOR_SCALE[which], 1, NVFP4_TENSOR_SCALE_LO, NVFP4_TENSOR_SCALE_HI,
+                                  sub=expert)[0])
+    return None
 
 
 def make_dense_fp16(wl: Workload, seed: int = 0):
@@ -220,27 +270,38 @@ def make_layer(wl: Workload, T: int, seed: int = 0, experts=None) -> LayerInputs
         up = np.ascontiguousarray(u.reshape(E2, I, H))
         down = np.ascontiguousarray(d.reshape(H, E2, I).transpose(1, 0, 2))
         return LayerInputs(wl, T, x, None, None, gate, None, up, None, down, None)
+    shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    extras = None
     if wl.weight_format == "mxfp4":
-        shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
         codes = {k: np.zeros((E2, n, kk // 2), np.uint8) for k, (n, kk) in shapes.items()}
         scales = {k: np.zeros((E2, n, kk // 32), np.uint8) for k, (n, kk) in shapes.items()}
+    elif wl.weight_format == "int4g32":
+        codes = {k: np.zeros((E2, n, kk // 2), np.uint8) for k, (n, kk) in shapes.items()}
+        scales = {k: np.zeros((E2, n, kk // 32), np.uint16) for k, (n, kk) in shapes.items()}
+        extras = {k: np.zeros((E2, n, (kk // 32 + 1) // 2), np.uint8) for k, (n, kk) in shapes.items()}
+    elif wl.weight_format == "nvfp4":
+        codes = {k: np.zeros((E2, n, kk // 2), np.uint8) for k, (n, kk) in shapes.items()}
+        scales = {k: np.zeros((E2, n, kk // 16), np.uint8) for k, (n, kk) in shapes.items()}
+        extras = {k: np.zeros(E2, np.float32) for k in shapes}
     else:
-        shapes = {"gate": (I, H), "up": (I, H), "down": (H, I)}
         codes = {k: np.zeros((E2, n, kk), np.uint16) for k, (n, kk) in shapes.items()}
         scales = {k: None for k in shapes}
+
     def fill(job):
         e, k = job
         c, s = make_expert_matrix(wl, k, e, seed)
         codes[k][e] = c
         if s is not None:
             scales[k][e] = s
+        if extras is not None:
+            extras[k][e] = make_expert_extra(wl, k, e, seed)
 
     jobs = [(e, k) for e in (range(E2) if experts is None else experts) for k in shapes]
     # every (expert, matrix) has its own generator key, so the order of the jobs does not matter
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
         list(ex.map(fill, jobs))
     return LayerInputs(wl, T, x, router, bias, codes["gate"], scales["gate"], codes["up"], scales["up"],
-                       codes["down"], scales["down"])
+                       codes["down"], scales["down"], extras)
 
 
 def to_torch(L: LayerInputs, device) -> dict:
@@ -267,6 +328,11 @@ def to_torch(L: LayerInputs, device) -> dict:
     if L.wl.weight_format == "fp16":
         out.update(gate=t(L.gate_codes).view(torch.float16), up=t(L.up_codes).view(torch.float16),
                    down=t(L.down_codes).view(torch.float16), gate_scales=None, up_scales=None, down_scales=None)
+    elif L.extras is not None:
+        out.update(gate=t(L.gate_codes), up=t(L.up_codes), down=t(L.down_codes),
+                   gate_scales=t(L.gate_scales.view(np.uint8)), up_scales=t(L.up_scales.view(np.uint8)),
+                   down_scales=t(L.down_scales.view(np.uint8)),
+                   extras={k: t(v) for k, v in L.extras.items()})
     else:
         out.update(gate=t(L.gate_codes), up=t(L.up_codes), down=t(L.down_codes), gate_scales=t(L.gate_scales),
                    up_scales=t(L.up_scales), down_scales=t(L.down_scales))

@@ -22,7 +22,7 @@ import numpy as np
 import scipy.special
 
 import synth
-from oracle import ExpertWeights, X_BF16, X_FP16, W_MXFP4, W_FP16
+from oracle import ExpertWeights, X_BF16, X_FP16, W_MXFP4, W_FP16, W_INT4_G32, W_NVFP4
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -73,11 +73,37 @@ def np_act(x_bits: np.ndarray, fmt: int) -> np.ndarray:
     return (x_bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+E4M3_REF = np.array([minifloat(c, 4, 3, 7, False) for c in range(256)])  # 0x7F / 0xFF (NaN) unused
+
+
+def np_decode_int4(codes, scales16, zeros):
+    """[N][K/2] unsigned codes, [N][K/32] binary16 scale bits, [N][ceil(K/64)] packed zero points
+    -> [N][K] float64 (code - zero) * scale, group g = k // 32."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    q = np.stack([codes & 0x0F, codes >> 4], axis=-1).reshape(N, K).astype(np.int64)
+    z = np.stack([zeros & 0x0F, zeros >> 4], axis=-1).reshape(N, -1)[:, :K // 32].astype(np.int64)
+    s = np.ascontiguousarray(scales16).view(np.float16).astype(np.float64)
+    return (q - np.repeat(z, 32, axis=1)) * np.repeat(s, 32, axis=1)
+
+
+def np_decode_nvfp4(codes, scales, ts):
+    """[N][K/2] E2M1 codes, [N][K/16] E4M3 scale codes, tensor scale -> [N][K] float64."""
+    N, K = codes.shape[0], codes.shape[1] * 2
+    c = np.stack([codes & 0x0F, codes >> 4], axis=-1).reshape(N, K)
+    return E2M1_REF[c] * np.repeat(E4M3_REF[scales], 16, axis=1) * float(ts)
+
+
 def np_weights(L):
     """Dense float64 [E'][N][K] gate, up, down for synth.LayerInputs L."""
     if L.wl.weight_format == "mxfp4":
         dec = lambda c, s: np.stack([np_decode(c[e], s[e]) for e in range(c.shape[0])])
         return dec(L.gate_codes, L.gate_scales), dec(L.up_codes, L.up_scales), dec(L.down_codes, L.down_scales)
+    if L.wl.weight_format == "int4g32":
+        dec = lambda c, s, z: np.stack([np_decode_int4(c[e], s[e], z[e]) for e in range(c.shape[0])])
+        return tuple(dec(getattr(L, m + "_codes"), getattr(L, m + "_scales"), L.extras[m]) for m in ("gate", "up", "down"))
+    if L.wl.weight_format == "nvfp4":
+        dec = lambda c, s, t: np.stack([np_decode_nvfp4(c[e], s[e], t[e]) for e in range(c.shape[0])])
+        return tuple(dec(getattr(L, m + "_codes"), getattr(L, m + "_scales"), L.extras[m]) for m in ("gate", "up", "down"))
     f = lambda c: np.ascontiguousarray(c).view(np.float16).astype(np.float64)
     return f(L.gate_codes), f(L.up_codes), f(L.down_codes)
 
@@ -114,7 +140,7 @@ def close(a, b, rel=1e-10, what=""):
 
 def small_layer(T=6, H=64, E=5, k=2, S=0, I=96, seed=3, zipf=0.0, router_std=0.3, fmt="mxfp4", scale=(118, 127)):
     wl = synth.custom(hidden=H, n_routed=E, top_k=k, n_shared=S, inter=I, weight_format=fmt,
-                      act_dtype="bf16" if fmt == "mxfp4" else "fp16", router_std=router_std, zipf_s=zipf,
+                      act_dtype="fp16" if fmt == "fp16" else "bf16", router_std=router_std, zipf_s=zipf,
                       weight_std=0.05, scale_lo=scale[0], scale_hi=scale[1])
     return synth.make_layer(wl, T, seed=seed)
 
@@ -484,6 +510,111 @@ def check_router_sigmoid_bias_selects_only(o):
 
 
 # ------------------------------------------------------------------------------------------------
+# Other weight codecs: Cascadia's group-32 INT4 and NVFP4
+# ------------------------------------------------------------------------------------------------
+def check_int4g32_storage(o):
+    """4 + 16/32 + 4/32 bits per weight: with Cascadia's shapes (hidden 6144, expert width 3072,
+    8 experts per row, 64 sparse layers) that is the page's 16.76 GB of active expert weights per
+    token; an 8-bit zero point (4.75 bits) or none (4.5) would give 17.21 or 16.31 GB."""
+    g = golden("cascadia_int4.json")
+    bpw = o.int4g32_bits_per_weight()
+    assert bpw == 4.625
+    weights = g["sparse_layers"] * g["experts_per_row"] * 3 * g["hidden"] * g["expert_inter"]
+    gb = lambda b: round(weights * b / 8 / 1e9, 2)
+    assert gb(bpw) == g["active_expert_gb_per_token"]
+    assert gb(4.0 + g["scale_bits"] / g["group"]) != g["active_expert_gb_per_token"]
+    assert gb(4.0 + (g["scale_bits"] + 8) / g["group"]) != g["active_expert_gb_per_token"]
+
+
+def check_int4g32_decode(o):
+    """(code - zero) * scale for every code x every zero point under normal, subnormal, negative and
+    largest binary16 scales, against numpy's own unpacking and float16 conversion; odd group counts
+    (a half-used last zero-point byte) and strided rows."""
+    sc = np.array([0.0029296875, 1.0, -2.5, 6.1e-5, 5.96e-8, 65504.0, -0.0, 3.0517578e-05], np.float16)
+    q = np.arange(16)
+    N, K = 16 * 16, 32 * len(sc)                       # row = (code, zero); group g uses scale g
+    codes = np.zeros((N, K), np.uint8)
+    zeros = np.zeros((N, len(sc)), np.uint8)
+    for i, (c, z) in enumerate((c, z) for c in q for z in q):
+        codes[i] = c
+        zeros[i] = z
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    zp = (zeros[:, 0::2] | (zeros[:, 1::2] << 4)).astype(np.uint8)
+    s16 = np.tile(sc.view(np.uint16), (N, 1))
+    W = ExpertWeights(W_INT4_G32, packed[None], s16[None], packed[None], s16[None], packed[None], s16[None],
+                      {"gate": zp[None], "up": zp[None], "down": zp[None]})  # only the gate is read
+    ref = np_decode_int4(packed, s16, zp)
+    for n in range(0, N, 7):
+        for k in range(0, K, 5):
+            v = o.weight(W, "gate", 0, n, k)
+            assert v == ref[n, k] or (np.isnan(v) and np.isnan(ref[n, k])), (n, k, v, ref[n, k])
+    # a synthetic layer: odd group count (K = 96 -> 3 groups), every element
+    L = small_layer(T=3, H=96, E=2, k=1, I=64, fmt="int4g32")
+    Wl = ExpertWeights.from_layer(L)
+    Wg, Wu, Wd = np_weights(L)
+    for e in range(2):
+        for n in range(0, 64, 3):
+            for k in range(96):
+                assert o.weight(Wl, "gate", e, n, k) == Wg[e, n, k]
+                assert o.weight(Wl, "up", e, n, k) == Wu[e, n, k]
+        for n in range(0, 96, 5):
+            for k in range(64):
+                assert o.weight(Wl, "down", e, n, k) == Wd[e, n, k]
+
+
+def check_nvfp4_format(o):
+    """NVFP4: 4.5 bits per weight before the tensor scale (page); every E2M1 code under every
+    non-NaN E4M3 scale code times a tensor scale, against the minifloat reference; a synthetic
+    layer's every element against numpy."""
+    g = golden("nvfp4_format.json")
+    assert o.nvfp4_bits_per_weight() == g["bits_per_weight"]
+    assert g["element_bits"] + 8 / g["block"] == g["bits_per_weight"]
+    scodes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    N, K = 16, 16 * len(scodes)
+    codes = np.repeat(np.arange(16, dtype=np.uint8)[:, None], K, axis=1)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.tile(scodes, (N, 1))
+    ts = np.array([0.3125], np.float32)
+    W = ExpertWeights(W_NVFP4, packed[None], scales[None], packed[None], scales[None], packed[None], scales[None],
+                      {"gate": ts, "up": ts, "down": ts})
+    ref = np_decode_nvfp4(packed, scales, ts[0])
+    for n in range(N):
+        for k in range(0, K, 3):
+            assert o.weight(W, "gate", 0, n, k) == ref[n, k], (n, k)
+    L = small_layer(T=3, H=64, E=2, k=1, I=96, fmt="nvfp4")
+    Wl = ExpertWeights.from_layer(L)
+    Wg, Wu, Wd = np_weights(L)
+    for e in range(2):
+        for n in range(0, 96, 7):
+            for k in range(64):
+                assert o.weight(Wl, "gate", e, n, k) == Wg[e, n, k] and o.weight(Wl, "up", e, n, k) == Wu[e, n, k]
+        for n in range(0, 64, 5):
+            for k in range(96):
+                assert o.weight(Wl, "down", e, n, k) == Wd[e, n, k]
+
+
+def check_codec_layers_vs_numpy(o):
+    """The whole oracle layer with INT4 group-32 and NVFP4 experts against numpy routing and a
+    per-token expert mixture over the numpy-decoded weights (one shared expert included)."""
+    for fmt in ("int4g32", "nvfp4"):
+        T, H, E, k, S, I = 7, 64, 5, 2, 1, 96
+        L = small_layer(T=T, H=H, E=E, k=k, S=S, I=I, fmt=fmt)
+        out = o.layer(L)
+        xf = X_BF16
+        _, p, order = np_route(L.x, xf, L.router, L.bias, k)
+        Wg, Wu, Wd = np_weights(L)
+        X = np_act(L.x, xf)
+        ref = np.zeros((T, H))
+        for t in range(T):
+            sel = order[t, :k]
+            w = p[t, sel] / p[t, sel].sum()
+            for j, e in enumerate(list(sel) + list(range(E, E + S))):
+                ref[t] += (w[j] if j < k else 1.0) * np_expert(Wg[e], Wu[e], Wd[e], X[t:t + 1])[0]
+        keep = out["route"]["near_tie"] == 0
+        close(out["y"][keep], ref[keep], 1e-10, f"layer {fmt}")
+
+
+# ------------------------------------------------------------------------------------------------
 # FP16 range management (Cascadia Sec. 3.3, Eq. 1)
 # ------------------------------------------------------------------------------------------------
 def check_eq1_row_factor(o):
@@ -718,6 +849,7 @@ ALL_CHECKS = [
     check_bucket, check_bucket_invalid,
     check_expert_apply_vs_numpy, check_layer_vs_numpy, check_layer_forms, check_single_expert_swiglu,
     check_combine, check_dense_slices, check_eq1_row_factor, check_eq1_restores_plain_layer,
+    check_int4g32_storage, check_int4g32_decode, check_nvfp4_format, check_codec_layers_vs_numpy,
     check_mx_tables, check_mx_encode_nearest, check_mx_scale_rule, check_mx_quantize_fp8_vs_torch,
     check_mx_quantize_blocks, check_expert_ffn_mx_vs_numpy,
 ]

@@ -30,6 +30,15 @@ MUTANTS = {
     "sigmoid of the negated logit": ("sc[e] = 1.0 / (1.0 + exp(-acc));", "sc[e] = 1.0 / (1.0 + exp(acc));"),
     "shared weight fixed at 1": ("weights[(int64_t)t * k_total + top_k + s] = shared_weight;",
                                  "weights[(int64_t)t * k_total + top_k + s] = 1.0;"),
+    "int4 zero-point nibbles swapped": ("const int zero = (g % 2 == 0) ? (zrow[g / 2] & 0x0F) : (zrow[g / 2] >> 4);",
+                                        "const int zero = (g % 2 == 0) ? (zrow[g / 2] >> 4) : (zrow[g / 2] & 0x0F);"),
+    "int4 zero point not subtracted": ("return (double)(code - zero) * orc_f16(sbits);", "return (double)code * orc_f16(sbits);"),
+    "int4 scale bytes big-endian": ("const uint16_t sbits = (uint16_t)(srow[2 * g] | (srow[2 * g + 1] << 8));",
+                                    "const uint16_t sbits = (uint16_t)(srow[2 * g + 1] | (srow[2 * g] << 8));"),
+    "int4 groups of 64": ("const int g = k / 32;\n    const uint16_t", "const int g = k / 64;\n    const uint16_t"),
+    "nvfp4 blocks of 32": ("orc_mx_value(ORC_MX_FP8_E4M3, srow[k / 16])", "orc_mx_value(ORC_MX_FP8_E4M3, srow[k / 32])"),
+    "nvfp4 tensor scale dropped": (" * (double)p->tensor_scale[e];", ";"),
+    "int4 storage without zero points": ("return (32.0 * 4.0 + 16.0 + 4.0) / 32.0;", "return (32.0 * 4.0 + 16.0) / 32.0;"),
     "attenuation not applied": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",
                                 "hs[(int64_t)i * I + n] = orc_silu(g) * u;"),
     "attenuation applied to the gate": ("hs[(int64_t)i * I + n] = orc_silu(g) * (u * up_scale);",

@@ -3,6 +3,8 @@
  * (gfx950).  Four calls make one layer: moe_route -> moe_bucket -> moe_expert_ffn -> moe_combine.
  *
  * Sources (cited by page title and section; the pages print no code):
+ *  [NV]  same post and section: NVFP4 also stores E2M1 values, with an E4M3 scale per 16 values
+ *        and a second, tensor-wide scale.
  *  [MX]  "DeepSeek-V4-Flash on a four-GPU Ampere workstation" (FreeToken blog post), section
  *        "MXFP4 is not NVFP4, and the difference matters on Ampere": packed E2M1 codes with one
  *        unsigned E8M0 scale per 32 values, decoded weight v(c) * 2^(e-127), 4.25 bits/weight,
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024  /* routed experts E, and buckets / experts E' of the later calls */
 #define MOE_MAX_SLOTS_PER_TOKEN 256  /* top_k + n_shared */
 
@@ -62,7 +64,7 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_FP16 = 1 } moe_act_dtype;
-typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP16 = 1 } moe_w_format;
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP16 = 1, MOE_W_INT4_G32 = 2, MOE_W_NVFP4 = 3 } moe_w_format;
 
 /* One projection of every expert: logical [n_experts][N][K], K contiguous within a row [MX].
  *  MXFP4: `w` holds two E2M1 codes per byte, element k of a row in byte k/2 with even k in the
@@ -72,6 +74,17 @@ typedef enum { MOE_W_MXFP4 = 0, MOE_W_FP16 = 1 } moe_w_format;
  *         supported (every decoded value is then finite in fp32 and bf16); at 253 and 254 the
  *         largest magnitudes overflow bf16, and 255 is outside the contract.
  *  FP16:  `w` holds IEEE binary16 values; `scales` must be NULL.
+ *  INT4_G32 [C31] (Cascadia Sec. 3.1 and 3.5): `w` holds unsigned 4-bit codes packed as for
+ *         MXFP4; group g = k/32 of a row has a binary16 scale (little-endian bytes 2g, 2g+1 of the
+ *         scale row) and an unsigned 4-bit zero point (zero row byte g/2, even g in the low
+ *         nibble); decoded weight = (code - zero) * scale (4.625 bits per weight).
+ *  NVFP4 [NV] (FreeToken post, "MXFP4 is not NVFP4"): `w` holds E2M1 codes packed as for MXFP4;
+ *         block b = k/16 has an E4M3 scale byte (byte b of the scale row; the two NaN codes are
+ *         outside the contract) and every expert one fp32 tensor scale; decoded weight =
+ *         v(code) * e4m3(scale) * tensor_scale[e] (4.5 bits per weight plus the tensor scale).
+ *  INT4_G32 and NVFP4 run on the K-split kernels with bf16 activations; their weights are exact
+ *  MFMA operands (INT4 as a bf16 high + low pair, NVFP4 in one bf16), the NVFP4 tensor scale
+ *  multiplies the fp32 sums.
  *  Strides are in bytes between consecutive experts / rows, so a projection may be a slice of a
  *  larger matrix [C34] -- e.g. columns [j*I, (j+1)*I) of a dense [H][8*I] down projection have
  *  w = base + j*I*(bytes per element), w_expert_stride = I*(bytes per element),
@@ -84,6 +97,9 @@ typedef struct {
   const uint8_t *scales;
   int64_t w_expert_stride, w_row_stride;
   int64_t s_expert_stride, s_row_stride;
+  const uint8_t *zeros;        /* INT4_G32 zero points (NULL for the other formats) */
+  int64_t z_expert_stride, z_row_stride;
+  const float *tensor_scale;   /* NVFP4: [n_experts] fp32 (NULL for the other formats) */
 } moe_proj;
 
 /* All expert weights of a layer [C31].  gate and up: N = inter, K = hidden; down: N = hidden,

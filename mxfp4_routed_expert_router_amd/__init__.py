@@ -26,7 +26,8 @@ ROOT = os.path.dirname(PKG)
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 MOE_ACT_BF16, MOE_ACT_FP16 = 0, 1
-MOE_W_MXFP4, MOE_W_FP16 = 0, 1
+MOE_W_MXFP4, MOE_W_FP16, MOE_W_INT4_G32, MOE_W_NVFP4 = 0, 1, 2, 3
+W_FORMATS = {"mxfp4": MOE_W_MXFP4, "fp16": MOE_W_FP16, "int4g32": MOE_W_INT4_G32, "nvfp4": MOE_W_NVFP4}
 MOE_MX_FP8_E4M3, MOE_MX_FP4_E2M1, MOE_MX_FP6_E2M3 = 1, 2, 3
 MX_FORMATS = {"fp8": MOE_MX_FP8_E4M3, "fp4": MOE_MX_FP4_E2M1, "fp6": MOE_MX_FP6_E2M3}
 
@@ -43,7 +44,9 @@ class MoEError(RuntimeError):
 class moe_proj(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("w_expert_stride", ctypes.c_int64), ("w_row_stride", ctypes.c_int64),
-                ("s_expert_stride", ctypes.c_int64), ("s_row_stride", ctypes.c_int64)]
+                ("s_expert_stride", ctypes.c_int64), ("s_row_stride", ctypes.c_int64),
+                ("zeros", ctypes.c_void_p), ("z_expert_stride", ctypes.c_int64), ("z_row_stride", ctypes.c_int64),
+                ("tensor_scale", ctypes.c_void_p)]
 
 
 class moe_expert_weights(ctypes.Structure):
@@ -142,16 +145,25 @@ class ExpertWeights:
 
     MXFP4: gate/up codes uint8 [E'][I][H/2], scales uint8 [E'][I][H/32]; down codes [E'][H][I/2],
     scales [E'][H][I/32].  FP16: gate/up float16 [E'][I][H], down [E'][H][I], scales None.
+    INT4_G32 (fmt="int4g32"): codes as MXFP4, scales [E'][N][K/32] binary16 bits as uint8 pairs
+    ([E'][N][K/16] uint8), extras {"gate"/"up"/"down": zero points uint8 [E'][N][ceil(K/64)]}.
+    NVFP4 (fmt="nvfp4"): codes as MXFP4, scales uint8 E4M3 [E'][N][K/16], extras {matrix: fp32
+    tensor scales [E']}.
     Any strided view whose last dimension is contiguous is accepted (slices of a larger matrix)."""
 
-    def __init__(self, gate, gate_scales, up, up_scales, down, down_scales):
-        fmt = MOE_W_FP16 if gate.dtype == torch.float16 else MOE_W_MXFP4
+    def __init__(self, gate, gate_scales, up, up_scales, down, down_scales, fmt=None, extras=None):
+        if fmt is None:
+            fmt = MOE_W_FP16 if gate.dtype == torch.float16 else MOE_W_MXFP4
+        elif isinstance(fmt, str):
+            fmt = W_FORMATS[fmt]
+        extras = dict(extras or {})
+        self.extras = extras
         self.tensors = (gate, gate_scales, up, up_scales, down, down_scales)
         E2, I = gate.shape[0], gate.shape[1]
         H = down.shape[1]
         self.fmt, self.n_experts, self.hidden, self.inter = fmt, E2, H, I
 
-        def proj(c, s):
+        def proj(c, s, ex):
             p = moe_proj()
             p.w = c.data_ptr()
             es = c.element_size()
@@ -160,11 +172,19 @@ class ExpertWeights:
                 raise ValueError("weight rows must be contiguous")
             if s is not None:
                 p.scales = s.data_ptr()
-                p.s_expert_stride, p.s_row_stride = s.stride(0), s.stride(1)
+                ss = s.element_size()
+                p.s_expert_stride, p.s_row_stride = s.stride(0) * ss, s.stride(1) * ss
+            if ex is not None and fmt == MOE_W_INT4_G32:
+                p.zeros = ex.data_ptr()
+                p.z_expert_stride, p.z_row_stride = ex.stride(0), ex.stride(1)
+            if ex is not None and fmt == MOE_W_NVFP4:
+                if ex.dtype != torch.float32 or not ex.is_contiguous():
+                    raise ValueError("NVFP4 tensor scales must be a contiguous float32 tensor")
+                p.tensor_scale = ex.data_ptr()
             return p
 
-        self.c = moe_expert_weights(fmt, E2, H, I, proj(gate, gate_scales), proj(up, up_scales),
-                                    proj(down, down_scales))
+        self.c = moe_expert_weights(fmt, E2, H, I, proj(gate, gate_scales, extras.get("gate")),
+                                    proj(up, up_scales, extras.get("up")), proj(down, down_scales, extras.get("down")))
 
     @property
     def device(self):

@@ -17,10 +17,29 @@ inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+inline bool known_format(int f) {
+  return f == MOE_W_MXFP4 || f == MOE_W_FP16 || f == MOE_W_INT4_G32 || f == MOE_W_NVFP4;
+}
 
 // Checks of one projection; K is its reduction dimension.
 moe_status check_proj(const moe_proj& p, moe_w_format fmt, int n_experts, int N, int K) {
   if (!p.w) return MOE_ERR_NULL;
+  if (fmt == MOE_W_INT4_G32 || fmt == MOE_W_NVFP4) {
+    // 16 code bytes are one INT4 group or two NVFP4 blocks: a base or stride off that grid starts
+    // inside one, and the group and block scales are sliced with the codes
+    if (!p.scales || (fmt == MOE_W_INT4_G32 && !p.zeros) || (fmt == MOE_W_NVFP4 && !p.tensor_scale))
+      return MOE_ERR_NULL;
+    if (K % 32 != 0) return MOE_ERR_BLOCK;
+    const int64_t srow = fmt == MOE_W_INT4_G32 ? 2 * (K / 32) : K / 16;
+    if (p.w_row_stride < K / 2 || p.s_row_stride < srow || p.w_expert_stride < 0 || p.s_expert_stride < 0)
+      return MOE_ERR_SHAPE;
+    if (fmt == MOE_W_INT4_G32 && (p.z_row_stride < (K / 32 + 1) / 2 || p.z_expert_stride < 0)) return MOE_ERR_SHAPE;
+    if (!al16(p.w) || p.w_row_stride % 16 != 0 || p.w_expert_stride % 16 != 0) return MOE_ERR_BLOCK;
+    if (fmt == MOE_W_NVFP4 && !al4(p.tensor_scale)) return MOE_ERR_ALIGN;
+    (void)n_experts;
+    (void)N;
+    return MOE_OK;
+  }
   if (fmt == MOE_W_MXFP4) {
     if (!p.scales) return MOE_ERR_NULL;
     if (K % 32 != 0) return MOE_ERR_BLOCK;
@@ -55,6 +74,10 @@ moe::ProjDev dev(const moe_proj& p) {
   d.wr = p.w_row_stride;
   d.se = p.s_expert_stride;
   d.sr = p.s_row_stride;
+  d.z = p.zeros;
+  d.ze = p.z_expert_stride;
+  d.zr = p.z_row_stride;
+  d.ts = p.tensor_scale;
   return d;
 }
 
@@ -191,11 +214,11 @@ moe_status check_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_total, c
                      void** table) {
   if (!W) return MOE_ERR_NULL;
   if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_SHAPE;
-  if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
+  if (!known_format(W->fmt)) return MOE_ERR_DTYPE;
   if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
   if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
   if ((int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
-  if ((W->fmt == MOE_W_MXFP4) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
+  if ((W->fmt != MOE_W_FP16) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
   if ((need_x && !x) || !offsets || !sorted_slot || (need_y && !y_slots)) return MOE_ERR_NULL;
   const int H = W->hidden, I = W->inter;
   moe_status st;
@@ -298,9 +321,9 @@ moe_status moe_expert_ffn_f16(const void* x, moe_act_dtype x_dtype, int T, int k
   if (!W) return MOE_ERR_NULL;
   if (T < 0 || k_total < 1 || k_total > MOE_MAX_SLOTS_PER_TOKEN || (int64_t)T * k_total > INT_MAX) return MOE_ERR_SHAPE;
   if (attenuation_log2 < 0 || attenuation_log2 > MOE_MAX_ATTENUATION_LOG2) return MOE_ERR_SHAPE;
-  if (W->fmt != MOE_W_MXFP4 && W->fmt != MOE_W_FP16) return MOE_ERR_DTYPE;
+  if (!known_format(W->fmt)) return MOE_ERR_DTYPE;
   if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
-  if ((W->fmt == MOE_W_MXFP4) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
+  if ((W->fmt != MOE_W_FP16) != (x_dtype == MOE_ACT_BF16)) return MOE_ERR_DTYPE;
   if (W->n_experts < 1 || W->n_experts > MOE_MAX_EXPERTS || W->hidden < 1 || W->inter < 1) return MOE_ERR_SHAPE;
   if (!x || !offsets || !sorted_slot || !y_slots) return MOE_ERR_NULL;
   const int H = W->hidden, I = W->inter;

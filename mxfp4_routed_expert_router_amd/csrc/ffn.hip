@@ -105,8 +105,27 @@ struct Op<MOE_W_FP16> {
   }
 };
 
-// Raw weight data of one lane for one chunk and one 16-row tile: the 16-byte MXFP4 block and its
-// scale, or 4 x 16 bytes of fp16.
+// Cascadia's group-32 INT4 and NVFP4 weights run on the bf16 MFMA like MXFP4.
+template <>
+struct Op<MOE_W_INT4_G32> : Op<MOE_W_MXFP4> {};
+template <>
+struct Op<MOE_W_NVFP4> : Op<MOE_W_MXFP4> {};
+
+// Decoded A operands of one MFMA step: NP planes whose sum is the exact weight.  INT4 group-32
+// weights (code - zero) * scale carry up to 15 significant bits, so they take a bf16 high and a
+// bf16 low plane (two MFMAs); every other format is exact in one operand.
+template <int FMT>
+struct Planes {
+  static constexpr int n = FMT == MOE_W_INT4_G32 ? 2 : 1;
+};
+template <int FMT>
+struct Dec {
+  typename Op<FMT>::V p[Planes<FMT>::n];
+};
+
+// Raw weight data of one lane for one chunk and one 16-row tile: the 16-byte block of 32 codes
+// and its scale data (MXFP4: the E8M0 byte; INT4: the group's binary16 scale and zero point;
+// NVFP4: the E4M3 scales of its two 16-value blocks), or 4 x 16 bytes of fp16.
 template <int FMT>
 struct RawW;
 template <>
@@ -118,11 +137,29 @@ template <>
 struct RawW<MOE_W_FP16> {
   u32x4 q[4];
 };
+template <>
+struct RawW<MOE_W_INT4_G32> {
+  u32x4 q;
+  float scale, zs;  // zs = -zero * scale (exact: 4 x 11 significant bits)
+};
+template <>
+struct RawW<MOE_W_NVFP4> {
+  u32x4 q;
+  float s0, s1;
+};
 
-// Load lane's raw weights: row pointer `row` (already offset to expert and row), its scale row,
-// k = this lane's block start; ok = row and block inside the matrix.
+// E4M3 (bias 7, subnormals at exponent field 0; the NaN codes are outside the contract) -> fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 15u, fr = c & 7u;
+  const float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (fr << 20)) : (float)fr * 0.001953125f;  // fr * 2^-9
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Load lane's raw weights: row pointer `row` (already offset to expert and row), its scale row
+// and (INT4) zero-point row, k = this lane's block start; ok = row and block inside the matrix.
 template <int FMT>
-__device__ __forceinline__ RawW<FMT> load_w(const uint8_t* row, const uint8_t* srow, int k, bool ok) {
+__device__ __forceinline__ RawW<FMT> load_w(const uint8_t* row, const uint8_t* srow, const uint8_t* zrow, int k,
+                                            bool ok) {
   RawW<FMT> r;
   if constexpr (FMT == MOE_W_MXFP4) {
     if (ok) {
@@ -132,6 +169,28 @@ __device__ __forceinline__ RawW<FMT> load_w(const uint8_t* row, const uint8_t* s
       r.q = u32x4{0, 0, 0, 0};
       r.e = 127;
     }
+  } else if constexpr (FMT == MOE_W_INT4_G32) {
+    if (ok) {
+      const int g = k >> 5;
+      r.q = ld16(row + (k >> 1));
+      const uint32_t sb = (uint32_t)srow[2 * g] | ((uint32_t)srow[2 * g + 1] << 8);
+      r.scale = (float)bitcast<_Float16>((uint16_t)sb);
+      const uint32_t z = (zrow[g >> 1] >> (4 * (g & 1))) & 15u;
+      r.zs = -(float)z * r.scale;
+    } else {
+      r.q = u32x4{0, 0, 0, 0};
+      r.scale = 0.0f;
+      r.zs = 0.0f;
+    }
+  } else if constexpr (FMT == MOE_W_NVFP4) {
+    if (ok) {
+      r.q = ld16(row + (k >> 1));
+      r.s0 = e4m3_to_f32(srow[k >> 4]);
+      r.s1 = e4m3_to_f32(srow[(k >> 4) + 1]);
+    } else {
+      r.q = u32x4{0, 0, 0, 0};
+      r.s0 = r.s1 = 0.0f;
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) r.q[s] = ok ? ld16(row + 2 * (k + 8 * s)) : u32x4{0, 0, 0, 0};
@@ -139,13 +198,58 @@ __device__ __forceinline__ RawW<FMT> load_w(const uint8_t* row, const uint8_t* s
   return r;
 }
 
+// Two fp32 values whose low 16 bits are zero (at most 8 significant bits) -> a packed bf16 pair.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+// MFMA operands for step s of a lane's block: codes 8s .. 8s+7 (dword s).
 template <int FMT>
-__device__ __forceinline__ typename Op<FMT>::V decode_step(const RawW<FMT>& r, int s) {
+__device__ __forceinline__ Dec<FMT> decode_step(const RawW<FMT>& r, int s) {
+  Dec<FMT> d;
   if constexpr (FMT == MOE_W_MXFP4) {
-    return decode8_bf16(r.q[s], e8m0_to_f32(r.e));
+    d.p[0] = decode8_bf16(r.q[s], e8m0_to_f32(r.e));
+  } else if constexpr (FMT == MOE_W_INT4_G32) {
+    // (code - zero) * scale = fma(code, scale, -zero * scale), exact in fp32 (at most 15
+    // significant bits); truncating to bf16 keeps its top 8 bits, the remainder (at most 7 more)
+    // is exact in bf16 too.
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[2], h[2], l[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t c = (r.q[s] >> (8 * i + 4 * j)) & 15u;
+        v[j] = __builtin_fmaf((float)c, r.scale, r.zs);
+        h[j] = __uint_as_float(__float_as_uint(v[j]) & 0xFFFF0000u);
+        l[j] = v[j] - h[j];
+      }
+      hi[i] = pack_bf16_exact(h[0], h[1]);
+      lo[i] = pack_bf16_exact(l[0], l[1]);
+    }
+    d.p[0] = bitcast<bf16x8>(u32x4{hi[0], hi[1], hi[2], hi[3]});
+    d.p[1] = bitcast<bf16x8>(u32x4{lo[0], lo[1], lo[2], lo[3]});
+  } else if constexpr (FMT == MOE_W_NVFP4) {
+    // exact E2M1 values times the block's E4M3 scale: at most 2 x 4 = 6 significant bits, inside
+    // bf16's range, so exact in bf16
+    const float sc = s < 2 ? r.s0 : r.s1;
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q[s], 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q[s], 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q[s], 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.q[s], 1.0f, 3);
+    d.p[0] = bitcast<bf16x8>(u32x4{pack_bf16_exact(v0[0] * sc, v0[1] * sc), pack_bf16_exact(v1[0] * sc, v1[1] * sc),
+                                   pack_bf16_exact(v2[0] * sc, v2[1] * sc), pack_bf16_exact(v3[0] * sc, v3[1] * sc)});
   } else {
-    return bitcast<f16x8>(r.q[s]);
+    d.p[0] = bitcast<f16x8>(r.q[s]);
   }
+  return d;
+}
+
+// The NVFP4 tensor scale of expert e of a projection (applied to the fp32 sums); 1 otherwise.
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const ProjDev& p, int e) {
+  if constexpr (FMT == MOE_W_NVFP4) return p.ts[e];
+  return 1.0f;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -185,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     xrow[mt] = x + (int64_t)(ok ? s / k_total : 0) * H;
   }
   // A sources: weight rows n0 + rt*16 + l16 of expert e
-  const uint8_t *grow[RT], *urow[RT], *gsrow[RT], *usrow[RT];
+  const uint8_t *grow[RT], *urow[RT], *gsrow[RT], *usrow[RT], *gzrow[RT], *uzrow[RT];
   bool row_ok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -196,6 +300,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     urow[rt] = up.w + (int64_t)ti.e * up.we + (int64_t)nn * up.wr;
     gsrow[rt] = gate.s ? gate.s + (int64_t)ti.e * gate.se + (int64_t)nn * gate.sr : nullptr;
     usrow[rt] = up.s ? up.s + (int64_t)ti.e * up.se + (int64_t)nn * up.sr : nullptr;
+    gzrow[rt] = gate.z ? gate.z + (int64_t)ti.e * gate.ze + (int64_t)nn * gate.zr : nullptr;
+    uzrow[rt] = up.z ? up.z + (int64_t)ti.e * up.ze + (int64_t)nn * up.zr : nullptr;
   }
 
   const int n_chunks = (H + 127) >> 7;
@@ -229,8 +335,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     const int k = c0 * 128 + 32 * lq;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      wg[rt] = load_w<FMT>(grow[rt], gsrow[rt], k, row_ok[rt] && k < H);
-      wu[rt] = load_w<FMT>(urow[rt], usrow[rt], k, row_ok[rt] && k < H);
+      wg[rt] = load_w<FMT>(grow[rt], gsrow[rt], gzrow[rt], k, row_ok[rt] && k < H);
+      wu[rt] = load_w<FMT>(urow[rt], usrow[rt], uzrow[rt], k, row_ok[rt] && k < H);
     }
     load_x(k, xb);
   }
@@ -242,8 +348,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
       const int kn = k + 128;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        ng[rt] = load_w<FMT>(grow[rt], gsrow[rt], kn, row_ok[rt] && kn < H);
-        nu[rt] = load_w<FMT>(urow[rt], usrow[rt], kn, row_ok[rt] && kn < H);
+        ng[rt] = load_w<FMT>(grow[rt], gsrow[rt], gzrow[rt], kn, row_ok[rt] && kn < H);
+        nu[rt] = load_w<FMT>(urow[rt], usrow[rt], uzrow[rt], kn, row_ok[rt] && kn < H);
       }
       load_x(kn, nx);
     }
@@ -251,13 +357,15 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const V ag = decode_step<FMT>(wg[rt], s);
-        const V au = decode_step<FMT>(wu[rt], s);
+        const Dec<FMT> ag = decode_step<FMT>(wg[rt], s);
+        const Dec<FMT> au = decode_step<FMT>(wu[rt], s);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          accg[mt][rt] = Op<FMT>::mfma(ag, xb[mt][s], accg[mt][rt]);
-          accu[mt][rt] = Op<FMT>::mfma(au, xb[mt][s], accu[mt][rt]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int p = 0; p < Planes<FMT>::n; ++p) {
+            accg[mt][rt] = Op<FMT>::mfma(ag.p[p], xb[mt][s], accg[mt][rt]);
+            accu[mt][rt] = Op<FMT>::mfma(au.p[p], xb[mt][s], accu[mt][rt]);
+          }
       }
     }
     if (c + 1 < c1) {
@@ -294,6 +402,8 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_kernel(
         g += s_red[w][rt][0][q];
         u += s_red[w][rt][1][q];
       }
+      g *= tensor_scale<FMT>(gate, ti.e);
+      u *= tensor_scale<FMT>(up, ti.e);
       const int n = n0 + rt * 16 + row, m = mt * 16 + tok;
       if (n < I && m < ti.nr) {
         float h = (g / (1.0f + expf(-g))) * (u * u_scale);
@@ -339,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     hrow_hi[mt] = h_hi + r * I;
     hrow_lo[mt] = h_lo + r * I;
   }
-  const uint8_t *drow[RT], *dsrow[RT];
+  const uint8_t *drow[RT], *dsrow[RT], *dzrow[RT];
   bool row_ok[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -348,6 +458,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     const int nn = row_ok[rt] ? n : 0;
     drow[rt] = down.w + (int64_t)ti.e * down.we + (int64_t)nn * down.wr;
     dsrow[rt] = down.s ? down.s + (int64_t)ti.e * down.se + (int64_t)nn * down.sr : nullptr;
+    dzrow[rt] = down.z ? down.z + (int64_t)ti.e * down.ze + (int64_t)nn * down.zr : nullptr;
   }
 
   const int n_chunks = (I + 127) >> 7;
@@ -379,7 +490,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
   if (c0 < c1) {
     const int k = c0 * 128 + 32 * lq;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) wd[rt] = load_w<FMT>(drow[rt], dsrow[rt], k, row_ok[rt] && k < I);
+    for (int rt = 0; rt < RT; ++rt) wd[rt] = load_w<FMT>(drow[rt], dsrow[rt], dzrow[rt], k, row_ok[rt] && k < I);
     load_h(k, bh, bl);
   }
   for (int c = c0; c < c1; ++c) {
@@ -389,19 +500,21 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
     if (c + 1 < c1) {
       const int kn = k + 128;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) nd[rt] = load_w<FMT>(drow[rt], dsrow[rt], kn, row_ok[rt] && kn < I);
+      for (int rt = 0; rt < RT; ++rt) nd[rt] = load_w<FMT>(drow[rt], dsrow[rt], dzrow[rt], kn, row_ok[rt] && kn < I);
       load_h(kn, nh, nl);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const V a = decode_step<FMT>(wd[rt], s);
+        const Dec<FMT> a = decode_step<FMT>(wd[rt], s);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][rt] = Op<FMT>::mfma(a, bh[mt][s], acc[mt][rt]);
-          acc[mt][rt] = Op<FMT>::mfma(a, bl[mt][s], acc[mt][rt]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int p = 0; p < Planes<FMT>::n; ++p) {
+            acc[mt][rt] = Op<FMT>::mfma(a.p[p], bh[mt][s], acc[mt][rt]);
+            acc[mt][rt] = Op<FMT>::mfma(a.p[p], bl[mt][s], acc[mt][rt]);
+          }
       }
     }
     if (c + 1 < c1) {
@@ -431,6 +544,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_kernel(
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += s_red[w][rt][q];
+      v *= tensor_scale<FMT>(down, ti.e);
       const int n = n0 + rt * 16 + row, m = mt * 16 + tok;
       if (n < H && m < ti.nr) {
         const int s = sorted_slot[ti.r0 + m];
@@ -1799,6 +1913,12 @@ hipError_t launch_ffn_range(const void* x, int T, int k_total, int fmt, int n_ex
   if (fmt == MOE_W_FP16)
     return ffn_range_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale,
                                      y16, stream);
+  if (fmt == MOE_W_INT4_G32)
+    return ffn_range_fmt<MOE_W_INT4_G32>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles,
+                                         u_scale, y16, stream);
+  if (fmt == MOE_W_NVFP4)
+    return ffn_range_fmt<MOE_W_NVFP4>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles,
+                                      u_scale, y16, stream);
   return ffn_range_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, down, sorted_slot, h_hi, h_lo, tiles, u_scale,
                                     y16, stream);
 }
@@ -1853,6 +1973,10 @@ hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_e
   }
   if (fmt == MOE_W_FP16)
     return gateup_fmt<MOE_W_FP16>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+  if (fmt == MOE_W_INT4_G32)
+    return gateup_fmt<MOE_W_INT4_G32>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
+  if (fmt == MOE_W_NVFP4)
+    return gateup_fmt<MOE_W_NVFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   return gateup_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
 }
 
@@ -1868,6 +1992,10 @@ hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big,
   }
   if (fmt == MOE_W_FP16)
     return down_fmt<MOE_W_FP16>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+  if (fmt == MOE_W_INT4_G32)
+    return down_fmt<MOE_W_INT4_G32>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+  if (fmt == MOE_W_NVFP4)
+    return down_fmt<MOE_W_NVFP4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   return down_fmt<MOE_W_MXFP4>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
 }
 

@@ -32,6 +32,9 @@ struct ProjDev {
   const uint8_t* w;
   const uint8_t* s;
   int64_t we, wr, se, sr;
+  const uint8_t* z;  // INT4 group-32 zero points
+  int64_t ze, zr;
+  const float* ts;   // NVFP4 tensor scales [n_experts]
 };
 // Tile plan of one expert-FFN call: 16*mt sorted rows per tile, `tiles` entries in the tile table
 // (an upper bound, padded to a multiple of the XCD count).

@@ -314,7 +314,7 @@ def to_torch(L: LayerInputs, device) -> dict:
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     act = torch.bfloat16 if L.wl.act_dtype == "bf16" else torch.float16
-    out = {"x": t(L.x).view(act), "router": t(L.router), "bias": t(L.bias)}
+    out = {"x": t(L.x).view(act), "router": t(L.router), "bias": t(L.bias), "weight_format": L.wl.weight_format}
     if L.wl.dense_slices:
         E2, I, H = L.gate_codes.shape
         g = t(L.gate_codes.reshape(E2 * I, H)).view(torch.float16)

@@ -35,7 +35,8 @@ def require_gpu():
 
 
 def expert_weights(t: dict) -> moe.ExpertWeights:
-    return moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+    return moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"],
+                             fmt=t.get("weight_format"), extras=t.get("extras"))
 
 
 def x_fmt(wl) -> int:

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
     assert {"moe_route", "moe_bucket", "moe_expert_ffn", "moe_combine"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for s in range(9):
         assert L.moe_status_str(s)
 
@@ -308,3 +308,43 @@ def test_sigmoid_route_validation():
     assert r(g=float("nan")) == SHAPE and r(sw=float("inf")) == SHAPE
     assert r(x=None) == NULL
     assert r(x=fake(8)) == ALIGN
+
+
+def codec_weights(fmt, E=4, H=64, I=96):
+    W = m.moe_expert_weights()
+    W.fmt, W.n_experts, W.hidden, W.inter = fmt, E, H, I
+    for name, (N, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        p = getattr(W, name)
+        p.w = P + 0x10000
+        p.scales = P + 0x20000
+        p.w_row_stride, p.w_expert_stride = K // 2, N * K // 2
+        srow = 2 * (K // 32) if fmt == m.MOE_W_INT4_G32 else K // 16
+        p.s_row_stride, p.s_expert_stride = srow, N * srow
+        if fmt == m.MOE_W_INT4_G32:
+            p.zeros = P + 0x30000
+            p.z_row_stride, p.z_expert_stride = (K // 32 + 1) // 2, N * ((K // 32 + 1) // 2)
+        else:
+            p.tensor_scale = P + 0x40000
+    return W
+
+
+def test_codec_validation():
+    """INT4 group-32 and NVFP4 weights: bf16 activations, their scale data required, 32-value
+    groups (16 code bytes) never cut."""
+    for fmt in (m.MOE_W_INT4_G32, m.MOE_W_NVFP4):
+        W = codec_weights(fmt)
+        assert ffn(W, xdt=1) == DTYPE
+        W = codec_weights(fmt); W.gate.scales = None
+        assert ffn(W) == NULL
+        W = codec_weights(fmt, H=48)
+        assert ffn(W) == BLOCK
+        W = codec_weights(fmt); W.up.w = P + 0x10008
+        assert ffn(W) == BLOCK
+        W = codec_weights(fmt); W.down.s_row_stride = 1
+        assert ffn(W) == SHAPE
+    W = codec_weights(m.MOE_W_INT4_G32); W.gate.zeros = None
+    assert ffn(W) == NULL
+    W = codec_weights(m.MOE_W_NVFP4); W.down.tensor_scale = None
+    assert ffn(W) == NULL
+    W = codec_weights(m.MOE_W_NVFP4); W.down.tensor_scale = P + 0x40002
+    assert ffn(W) == ALIGN

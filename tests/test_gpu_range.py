@@ -84,8 +84,9 @@ def test_range_needs_attenuation(orc):
     L = host_layer("decode", 8)
     ys0, y0, ref0, _ = run_range(orc, L, 0)
     assert np.nanmax(np.abs(ref0)) > F16_MAX
-    # past the binary16 rounding point 65520 by more than the kernel's own fp32 error
-    big = np.abs(ref0) > 65520.0 * (1.0 + 1e-3)
+    # past the binary16 rounding point 65520 by more than the path's own error (h is rounded to
+    # binary16 on the way: about 3e-3 x RMS of E, a few hundred here, against a 2% margin of 1310)
+    big = np.abs(ref0) > 65520.0 * 1.02
     assert big.any() and not np.any(np.isfinite(ys0[big]))
     note(f"  A = 1: {int(big.sum())} slot values past the binary16 range, all non-finite on the GPU")
     ys4, _, _, _ = run_range(orc, L, 4)

@@ -176,6 +176,24 @@ moe_status moe_pad_rows(const int32_t *n_rows, int T_shape, int k_total, int32_t
                         void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * moe_route_bucket -- moe_route, then moe_bucket of its ids over n_buckets = E + n_shared, then
+ * (W non-NULL) moe_expert_ffn_plan into ffn_workspace, with the same results bit for bit, in fewer
+ * launches: for T * (top_k + n_shared) <= 2048 the selection kernel's last workgroup does the
+ * bucketing and the tile table (two launches in all instead of four).  Arguments as for those
+ * calls; W->n_experts must equal E + n_shared; ffn_workspace then is the workspace that the
+ * following moe_expert_ffn_gateup / moe_expert_ffn_down calls use.  workspace:
+ * moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared) bytes, 16-byte aligned (it holds
+ * the router's partial sums, a counter the kernels reset themselves, and the bucketing's scratch).
+ * Errors: as for the three calls. */
+size_t moe_route_bucket_workspace_bytes(int T, int H, int E, int top_k, int n_shared);
+moe_status moe_route_bucket(const void *x, moe_act_dtype x_dtype, int T, int H, const float *w_router,
+                            const float *logit_bias, int E, int top_k, int n_shared, int32_t *ids,
+                            float *weights, float *probs, int32_t *counts, int32_t *offsets,
+                            int32_t *sorted_slot, int32_t *slot_pos, const moe_expert_weights *W,
+                            void *ffn_workspace, size_t ffn_workspace_bytes, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * moe_bucket -- group slots by expert (the fused path runs only the selected experts' work
  * [C31]).  Slot s = t*k_total + j.
  *   counts[b]      number of slots with ids[s] == b                         ([n_buckets])

@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_bytes.restype = st; L.moe_route_workspace_bytes.argtypes = [i, i, i]
         L.moe_route.restype = i
         L.moe_route.argtypes = [vp, i, i, i, vp, vp, i, i, i, vp, vp, vp, vp, st, vp]
+        L.moe_route_bucket_workspace_bytes.restype = st
+        L.moe_route_bucket_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.moe_route_bucket.restype = i
+        L.moe_route_bucket.argtypes = [vp, i, i, i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(moe_expert_weights), vp, st, vp, st, vp]
         L.moe_route_sigmoid.restype = i
         L.moe_route_sigmoid.argtypes = [vp, i, i, i, vp, vp, i, i, i, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                                         vp, st, vp]
@@ -224,6 +229,28 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, top_k: int, logit_bias: O
                            _ptr(ids), _ptr(w), _ptr(probs), _ptr(ws), 0 if ws is None else ws.numel(),
                            _stream(dev)), "moe_route")
     return ids, w, probs
+
+
+def moe_route_bucket_workspace_bytes(T: int, H: int, E: int, top_k: int, n_shared: int = 0) -> int:
+    return lib().moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared)
+
+
+def moe_route_bucket(x: torch.Tensor, w_router: torch.Tensor, top_k: int, logit_bias: Optional[torch.Tensor],
+                     n_shared: int, ids: torch.Tensor, weights: torch.Tensor, buckets: "Buckets",
+                     W: Optional[ExpertWeights] = None, ffn_workspace: Optional[torch.Tensor] = None,
+                     probs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> None:
+    """moe_route + moe_bucket (+ moe_expert_ffn_plan into ffn_workspace when W is given) in one call,
+    into the caller's buffers."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    need = moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared)
+    ws = workspace if workspace is not None else _workspace(need, x.device)
+    _check(lib().moe_route_bucket(_ptr(x), _act_dtype(x), T, H, _ptr(w_router), _ptr(logit_bias), E, top_k, n_shared,
+                                  _ptr(ids), _ptr(weights), _ptr(probs), _ptr(buckets.counts), _ptr(buckets.offsets),
+                                  _ptr(buckets.sorted_slot), _ptr(buckets.slot_pos),
+                                  None if W is None else ctypes.byref(W.c), _ptr(ffn_workspace),
+                                  0 if ffn_workspace is None else ffn_workspace.numel(), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(x.device)), "moe_route_bucket")
 
 
 def moe_route_sigmoid(x: torch.Tensor, w_router: torch.Tensor, top_k: int,
@@ -470,7 +497,7 @@ class MoELayer:
         else:
             self.ids = torch.empty((T, kt), dtype=torch.int32, device=dev)
             self.weights = torch.empty((T, kt), dtype=torch.float32, device=dev)
-            self.route_ws = _workspace(moe_route_workspace_bytes(T, H, E), dev)
+            self.route_ws = _workspace(moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared), dev)
         n = T * kt
         self.buckets = Buckets(torch.empty(W.n_experts, dtype=torch.int32, device=dev),
                                torch.empty(W.n_experts + 1, dtype=torch.int32, device=dev),
@@ -483,6 +510,14 @@ class MoELayer:
         self.y = torch.empty((T, H), dtype=torch.float32, device=dev)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if not self.dense and self.mx is None:
+            # route, bucket and tile plan in one call, then the two FFN phases
+            moe_route_bucket(x, self.w_router, self.top_k, self.logit_bias, self.n_shared, self.ids, self.weights,
+                             self.buckets, self.W, self.ffn_ws, workspace=self.route_ws)
+            moe_expert_ffn_gateup(x, self.W, self.buckets.offsets, self.buckets.sorted_slot, self.k_total, self.ffn_ws)
+            moe_expert_ffn_down(self.T, self.W, self.buckets.offsets, self.buckets.sorted_slot, self.k_total,
+                                self.ffn_ws, self.y_slots)
+            return moe_combine(self.y_slots, self.weights, out=self.y)
         if not self.dense:
             moe_route(x, self.w_router, self.top_k, self.logit_bias, self.n_shared,
                       out=(self.ids, self.weights, None), workspace=self.route_ws)
@@ -575,7 +610,7 @@ class FixedShapeLayer:
         return self.y[:T]
 
 
-__all__ = ["moe_route", "moe_route_sigmoid", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
+__all__ = ["moe_route", "moe_route_sigmoid", "moe_route_bucket", "moe_route_bucket_workspace_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
            "moe_expert_ffn_f16_workspace_bytes", "moe_combine_restore", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
            "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
            "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",

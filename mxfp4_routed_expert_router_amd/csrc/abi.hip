@@ -555,3 +555,69 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int n_
 }
 
 }  // extern "C"
+
+extern "C" {
+
+// ---------------------------------------------------------------------------------------------
+// moe_route_bucket.  Workspace: router partial sums | ticket (256 bytes) | bucketing workspace.
+size_t moe_route_bucket_workspace_bytes(int T, int H, int E, int top_k, int n_shared) {
+  if (T <= 0 || H <= 0 || E <= 0 || top_k < 1 || n_shared < 0) return 0;
+  const int64_t n_slots = (int64_t)T * (top_k + n_shared);
+  if (n_slots > INT_MAX) return 0;
+  return moe_route_workspace_bytes(T, H, E) + 256 +
+         round_up(moe_bucket_workspace_bytes((int)n_slots, E + n_shared), 256);
+}
+
+moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, const float* w_router,
+                            const float* logit_bias, int E, int top_k, int n_shared, int32_t* ids, float* weights,
+                            float* probs, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
+                            const moe_expert_weights* W, void* ffn_workspace, size_t ffn_workspace_bytes,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (T == 0) return MOE_OK;
+  if (T < 0 || H < 1 || E < 1 || E > MOE_MAX_EXPERTS || n_shared < 0 || E + n_shared > MOE_MAX_EXPERTS)
+    return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_ACT_BF16 && x_dtype != MOE_ACT_FP16) return MOE_ERR_DTYPE;
+  if (top_k < 1 || top_k > E || top_k + n_shared > MOE_MAX_SLOTS_PER_TOKEN) return MOE_ERR_TOPK;
+  const int k_total = top_k + n_shared, n_buckets = E + n_shared;
+  if ((int64_t)T * k_total > INT_MAX || (int64_t)T * E > INT_MAX) return MOE_ERR_SHAPE;
+  if (!x || !w_router || !ids || !weights || !counts || !offsets || !sorted_slot) return MOE_ERR_NULL;
+  if (!al16(x) || !al4(w_router) || !al4(ids) || !al4(weights) || (probs && !al4(probs)) ||
+      (logit_bias && !al4(logit_bias)) || !al4(counts) || !al4(offsets) || !al4(sorted_slot) ||
+      (slot_pos && !al4(slot_pos)))
+    return MOE_ERR_ALIGN;
+  void* table = nullptr;
+  moe::FfnPlan pl{};
+  if (W) {  // the tile table goes where moe_expert_ffn_plan would write it
+    if (W->n_experts != n_buckets) return MOE_ERR_SHAPE;
+    uint16_t *h_hi, *h_lo;
+    const moe_act_dtype xdt = W->fmt == MOE_W_FP16 ? MOE_ACT_FP16 : MOE_ACT_BF16;
+    const moe_status st = check_ffn(nullptr, xdt, T, k_total, W, offsets, offsets, nullptr, false, false,
+                                    ffn_workspace, ffn_workspace_bytes, &h_hi, &h_lo, &table);
+    if (st != MOE_OK) return st;
+    pl = moe::ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total));
+  }
+  const size_t need = moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  uint8_t* ws = (uint8_t*)workspace;
+  float* partial = (float*)ws;
+  const size_t rws = moe_route_workspace_bytes(T, H, E);
+  uint32_t* ticket = (uint32_t*)(ws + rws);
+  int32_t* bws = (int32_t*)(ws + rws + 256);
+  const int splits = moe::route_splits(T, H, E);
+  hipStream_t st = (hipStream_t)stream;
+  if (moe::route_bucket_fusable(T, k_total, n_buckets))
+    return hip_status(moe::launch_route_bucket(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k,
+                                               n_shared, ids, weights, probs, partial, splits, ticket, n_buckets,
+                                               counts, offsets, sorted_slot, slot_pos, table, 16 * pl.mt, pl.tiles,
+                                               st));
+  hipError_t err = moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k, n_shared, ids,
+                                     weights, probs, partial, splits, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_bucket(ids, T * k_total, n_buckets, counts, offsets, sorted_slot, slot_pos, bws, st);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  if (!W) return MOE_OK;
+  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total), offsets, table, st));
+}
+
+}  // extern "C"

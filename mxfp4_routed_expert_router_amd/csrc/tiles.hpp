@@ -42,6 +42,52 @@ __device__ __forceinline__ void xcd_work(int b, int n_nblk, int& tile, int& nblk
   nblk = slot % n_nblk;
 }
 
+// The tile table built by one workgroup from bucket offsets held in LDS (off[e] = first sorted row
+// of expert e, e < n_experts; `total` = valid rows), with the same entries as ffn_tiles_kernel:
+// each expert's ceil(n_e / rows_per_tile) tiles in expert order, then empty entries up to
+// n_entries.  scratch: (blockDim / 64 + 1) ints of LDS; ends with a barrier.
+__device__ inline void tiles_from_offsets_block(const int* off, int total, int n_experts, int n_rows_max,
+                                                int rows_per_tile, int n_entries, TileEntry* __restrict__ table,
+                                                int* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int per = (n_experts + blockDim.x - 1) / blockDim.x;  // consecutive experts per thread (<= 2)
+  const int e0 = tid * per;
+  int a[2] = {0, 0}, n[2] = {0, 0}, cnt[2] = {0, 0}, mine = 0;
+  for (int i = 0; i < per && i < 2; ++i) {
+    const int e = e0 + i;
+    if (e < n_experts) {
+      a[i] = min(max(off[e], 0), n_rows_max);
+      const int b = min(max(e + 1 < n_experts ? off[e + 1] : total, 0), n_rows_max);
+      n[i] = max(b - a[i], 0);
+      cnt[i] = (n[i] + rows_per_tile - 1) / rows_per_tile;
+      mine += cnt[i];
+    }
+  }
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int v = scratch[w];
+      scratch[w] = run;
+      run += v;
+    }
+    scratch[nwaves] = run;
+  }
+  __syncthreads();
+  int first = scratch[wave] + incl - mine;
+  for (int i = 0; i < per && i < 2; ++i) {
+    for (int p = 0; p < cnt[i] && first + p < n_entries; ++p) {
+      const int r0 = a[i] + p * rows_per_tile;
+      table[first + p] = TileEntry{e0 + i, r0, min(rows_per_tile, a[i] + n[i] - r0), 0};
+    }
+    first += cnt[i];
+  }
+  for (int t = scratch[nwaves] + tid; t < n_entries; t += blockDim.x) table[t] = TileEntry{0, 0, 0, 0};
+  __syncthreads();
+}
+
 // Upper bound of the number of tiles: A active experts hold at least one row each, so
 // sum_e ceil(n_e / R) <= A + (rows - A) / R with A <= min(n_experts, rows).
 inline int64_t max_tiles(int64_t rows, int n_experts, int rows_per_tile) {

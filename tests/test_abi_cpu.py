@@ -348,3 +348,22 @@ def test_codec_validation():
     assert ffn(W) == NULL
     W = codec_weights(m.MOE_W_NVFP4); W.down.tensor_scale = P + 0x40002
     assert ffn(W) == ALIGN
+
+
+def test_route_bucket_validation():
+    L = m.lib()
+    need = L.moe_route_bucket_workspace_bytes(4, 64, 8, 2, 0)
+    assert need >= L.moe_route_workspace_bytes(4, 64, 8) + 4
+    W = weights(E=8)
+
+    def rb(T=4, E=8, k=2, S=0, Wp=None, ws=fake(0x8000), wsb=need, fws=fake(0x40000), fwsb=1 << 24, ids=fake(0x200)):
+        return L.moe_route_bucket(fake(), 0, T, 64, fake(0x100), None, E, k, S, ids, fake(0x300), None,
+                                  fake(0x400), fake(0x500), fake(0x600), None, Wp, fws, fwsb, ws, wsb, None)
+
+    assert L.moe_route_bucket(None, 0, 0, 64, None, None, 8, 2, 0, None, None, None, None, None, None, None, None,
+                              None, 0, None, 0, None) == OK
+    assert rb(k=0) == TOPK and rb(E=0) == SHAPE
+    assert rb(ids=None) == NULL and rb(ids=fake(0x202)) == ALIGN
+    assert rb(wsb=need - 1) == WORKSPACE
+    assert rb(Wp=ctypes.byref(weights(E=9))) == SHAPE            # n_experts must be E + n_shared
+    assert rb(Wp=ctypes.byref(W), fwsb=16) == WORKSPACE          # the FFN workspace holds the tile table

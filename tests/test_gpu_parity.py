@@ -497,3 +497,50 @@ def test_graph_replay_equals_eager(name, T):
         got = sync_np(layer.y)
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {r}"
         assert float(other) == float(other)
+
+
+# ------------------------------------------------------------------------------------------------
+# moe_route_bucket (router + bucketing + tile plan in one call) against the separate calls
+# ------------------------------------------------------------------------------------------------
+RB_CASES = [("tiny", 16), ("decode", 1), ("decode", 8), ("sweep", 176), ("sweep", 255), ("sweep", 256),
+            ("sweep", 300), ("prefill", 8192)]
+
+
+@pytest.mark.parametrize("name,T", RB_CASES, ids=[f"{n}-T{t}" for n, t in RB_CASES])
+def test_route_bucket_equals_separate_calls(name, T):
+    """Same ids, weights, probabilities, bucket arrays and tile table bit for bit, and the same
+    expert-FFN output, from one moe_route_bucket call as from moe_route -> moe_bucket ->
+    moe_expert_ffn_plan: through the fused two-launch path up to 2048 slots (sweep T = 255 and
+    256 end at the boundary) and the separate kernels above it."""
+    wl = synth.WORKLOADS[name]
+    note(f"route_bucket {name} T={T}")
+    import dataclasses
+    base = host_layer(name, {"sweep": 176, "decode": 8, "tiny": 16, "prefill": 8192}[name])
+    L = dataclasses.replace(base, T=T, x=synth.make_x(wl, T))  # the workload's weights, T new tokens
+    t = synth.to_torch(L, DEV)
+    W = expert_weights(t)
+    E, k, S = wl.n_routed, wl.top_k, wl.n_shared
+    kt = k + S
+    ids_a, w_a, p_a = moe.moe_route(t["x"], t["router"], k, t["bias"], S, want_probs=True)
+    b_a = moe.moe_bucket(ids_a, wl.n_experts)
+    ws_a = torch.empty(moe.moe_expert_ffn_workspace_bytes(T, kt, W), dtype=torch.uint8, device=DEV)
+    moe.moe_expert_ffn_plan(T, W, b_a.offsets, kt, ws_a)
+    ids_b = torch.full_like(ids_a, -7)
+    w_b = torch.full_like(w_a, -7.0)
+    p_b = torch.full_like(p_a, -7.0)
+    b_b = moe.Buckets(*(torch.full_like(v, -7) for v in (b_a.counts, b_a.offsets, b_a.sorted_slot, b_a.slot_pos)))
+    ws_b = torch.zeros_like(ws_a)
+    for rep in range(2):  # the second call reuses the workspace (its counter was reset by the first)
+        moe.moe_route_bucket(t["x"], t["router"], k, t["bias"], S, ids_b, w_b, b_b, W, ws_b, probs=p_b)
+        for a, b in ((ids_a, ids_b), (w_a, w_b), (p_a, p_b), (b_a.counts, b_b.counts), (b_a.offsets, b_b.offsets),
+                     (b_a.sorted_slot, b_b.sorted_slot), (b_a.slot_pos, b_b.slot_pos)):
+            assert np.array_equal(sync_np(a.view(torch.int32)), sync_np(b.view(torch.int32))), rep
+    n_tab = ws_a.numel()
+    plane = 2 * ((T * kt * W.inter * 2 + 255) // 256 * 256)
+    assert np.array_equal(sync_np(ws_a[plane:]), sync_np(ws_b[plane:]))   # the tile tables
+    moe.moe_expert_ffn_gateup(t["x"], W, b_a.offsets, b_a.sorted_slot, kt, ws_b)
+    yb = moe.moe_expert_ffn_down(T, W, b_a.offsets, b_a.sorted_slot, kt, ws_b,
+                                 torch.empty((T * kt, W.hidden), dtype=torch.float32, device=DEV))
+    ya = moe.moe_expert_ffn(t["x"], W, b_a.offsets, b_a.sorted_slot, kt)
+    assert np.array_equal(sync_np(ya).view(np.uint32), sync_np(yb).view(np.uint32))
+    assert n_tab > plane

@@ -4,17 +4,20 @@
 Workload: the concurrency-sweep MoE layer -- hidden 7168, 256 routed experts, top-8, expert SwiGLU
 intermediate 2048, MXFP4 expert weights (codes uniform, E8M0 in [118, 127]), bf16 activations
 ~N(0,1), router weights ~N(0, 1/7168) so logits are ~N(0,1); seeded synthetic inputs (seed 0).
-One step = one layer call on T tokens (default 176): moe_route -> moe_bucket -> expert FFN
-(tile plan, gate/up phase, down phase) -> moe_combine, inputs resident in HBM.  Weight sets are rotated so
-that the bytes touched between two visits of one set exceed the 256 MB Infinity Cache.
+One step = one layer call on T tokens (default 176): moe_route_bucket (router, bucketing and the
+expert FFN's tile plan) -> moe_expert_ffn_gateup -> moe_expert_ffn_down -> moe_combine, inputs resident
+in HBM.  Weight sets are rotated so that the bytes touched between two visits of one set exceed the
+256 MB Infinity Cache (a one-set control is reported where rotation applies).
 
 Each T is timed twice: eager (the library calls issued from Python, HIP events around the steps and
 between the calls) and replayed from HIP graphs that hold one layer call each (the headline: the
-host's launch work is then out of the loop, which matters at small T).
+host's launch work is then out of the loop, which matters at small T); the graph pass also gives
+the per-step p10 / median / p90.
 
 Prints one JSON line: tokens/s (value, graph replay), ms per layer call, the gate/up kernel's
-roofline (HIP-event duration and algorithmic bytes), the per-T sweep T = 1..176, and the fp64 CPU
-oracle timed on a bounded token sample.
+roofline (HIP-event duration and algorithmic bytes), the per-T sweep T = 1..176, a measured
+read-stream peak beside the nominal 8 TB/s, the prefill layer (T = 8192, exact and MX-FP6 modes,
+fraction of the MXFP4 MFMA peak), and the fp64 CPU oracle timed on bounded samples.
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ def parse():
                     help="measure another layer workload instead and print its own JSON line: the decode "
                          "layer (hidden 4096, 128 experts, top-8, I 1536, MXFP4; T = 1, 8, 32, 64) or the "
                          "dense FFN as 8 all-active FP16 slices (hidden 4096, I 16384; T = 1, 16, 128)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave the prefill object (T=8192, exact and MX-FP6 expert FFN) out of the default line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain elementwise copy (torch.neg, fp32) of this many MiB three times, "
                          "for scaling memory counters, and exit")
@@ -69,6 +74,7 @@ class Runner:
         self.moe, self.sets, self.T, self.top_k, self.n_shared = moe, sets, T, top_k, n_shared
         self.mx = mx
         self.fixed = fixed_routing  # dense slices: ids [t][j] = j, weights 1, no router call
+        self.fused = mx is None and not fixed_routing
         self.kt = top_k + n_shared
         self.n_experts = n_experts
         n = T * self.kt
@@ -78,7 +84,8 @@ class Runner:
         if fixed_routing:
             self.ids.copy_(torch.arange(self.kt, dtype=torch.int32, device=dev).expand(T, self.kt))
             self.w.fill_(1.0)
-        self.route_ws = None if fixed_routing else self._ws(moe.moe_route_workspace_bytes(T, H, n_experts - n_shared))
+        self.route_ws = None if fixed_routing else self._ws(
+            moe.moe_route_bucket_workspace_bytes(T, H, n_experts - n_shared, top_k, n_shared))
         self.b = moe.Buckets(torch.empty(n_experts, dtype=torch.int32, device=dev),
                              torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
                              torch.empty(n, dtype=torch.int32, device=dev), None)
@@ -96,6 +103,22 @@ class Runner:
     def step(self, i, events=None):
         m, s = self.moe, self.sets[i % len(self.sets)]
         rec = (lambda k: events[k].record()) if events is not None else (lambda k: None)
+        if self.fused:
+            # router + bucketing + tile plan in one call (two launches), then gate/up, down, combine
+            rec(0)
+            m.moe_route_bucket(s["x"][:self.T], s["router"], self.top_k, s["bias"], self.n_shared, self.ids, self.w,
+                               self.b, s["W"], self.ffn_ws, workspace=self.route_ws)
+            rec(1)
+            rec(2)
+            rec(3)
+            m.moe_expert_ffn_gateup(s["x"][:self.T], s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws)
+            rec(4)
+            m.moe_expert_ffn_down(self.T, s["W"], self.b.offsets, self.b.sorted_slot, self.kt, self.ffn_ws,
+                                  self.y_slots)
+            rec(5)
+            m.moe_combine(self.y_slots, self.w, out=self.y)
+            rec(6)
+            return
         rec(0)
         if not self.fixed:
             m.moe_route(s["x"][:self.T], s["router"], self.top_k, s["bias"], self.n_shared,
@@ -139,8 +162,9 @@ def time_steps(runner, steps, warmup):
     for i in range(steps):
         runner.step(i, evs[i])
     torch.cuda.synchronize()
-    names = ["route", "bucket", "ffn_plan", "ffn_gateup", "ffn_down", "combine"]
-    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    names = (["route_bucket_plan", None, None, "ffn_gateup", "ffn_down", "combine"] if runner.fused else
+             ["route", "bucket", "ffn_plan", "ffn_gateup", "ffn_down", "combine"])
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names) if n}
     return total_ms, per
 
 
@@ -171,8 +195,18 @@ def time_graph(runner, steps, warmup):
         graphs[i % len(graphs)].replay()
     end.record()
     torch.cuda.synchronize()
+    mean_ms = start.elapsed_time(end) / steps
+    # a second pass with an event between consecutive replays: the per-step distribution
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
     del graphs
-    return start.elapsed_time(end) / steps
+    return mean_ms, {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
 
 
 def active_experts(runner):
@@ -248,16 +282,23 @@ def main():
         steps = args.steps if T == args.tokens else args.sweep_steps
         warm = args.warmup if T == args.tokens else min(args.warmup, 5)
         eager_ms, per = time_steps(runner, steps, warm)
-        graph_ms = time_graph(runner, steps, warm)
+        graph_ms, dist = time_graph(runner, steps, warm)
         ms = graph_ms
         A = active_experts(runner)
         n_slots = T * k
         w_bytes = A * expert_bytes
         gateup_bytes = A * 2 * H * I * MXFP4_BYTES_PER_WEIGHT + n_slots * (2 * H + 4 * I)
-        results[T] = dict(T=T, ms=ms, eager_ms=eager_ms, per=per, active=A, weight_bytes=w_bytes,
+        results[T] = dict(T=T, ms=ms, eager_ms=eager_ms, per=per, dist=dist, active=A, weight_bytes=w_bytes,
                           gateup_bytes=gateup_bytes, rotation_sets=len(sets), steps=steps)
+        if len(sets) > 1:
+            # control: the same calls on one weight set, which then stays in the Infinity Cache
+            runner.sets = sets[:1]
+            results[T]["no_rotation_ms"] = time_graph(runner, steps, warm)[0]
         del runner, sets
         torch.cuda.empty_cache()
+
+    print("bench: read-stream peak", file=sys.stderr, flush=True)
+    read_peak = read_stream_peak()
 
     head = results[args.tokens]
     t_gu = head["per"]["ffn_gateup"] / 1e3
@@ -281,8 +322,11 @@ def main():
                    "weights": "mxfp4 (E2M1 + E8M0/32)", "activations": "bf16", "output": "fp32",
                    "parallelism": "single GPU", "timing": "HIP graph replay of whole layer calls"},
         "eager_ms_per_step": head["eager_ms"],
+        "ms_per_step_p10_median_p90": [head["dist"]["p10"], head["dist"]["median"], head["dist"]["p90"]],
         "weight_GBps": head["weight_bytes"] / (head["ms"] / 1e3) / 1e9,
         "weight_frac_of_hbm_peak": head["weight_bytes"] / (head["ms"] / 1e3) / HBM_PEAK,
+        "read_stream_peak_GBps": read_peak / 1e9,
+        "weight_frac_of_read_stream_peak": head["weight_bytes"] / (head["ms"] / 1e3) / read_peak,
         "active_experts": head["active"],
         "rotation_sets": head["rotation_sets"],
         "per_call_ms": {kk: round(v, 5) for kk, v in head["per"].items()},
@@ -290,21 +334,59 @@ def main():
                      "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK, "traffic": traffic,
+                     "traffic_source": ("stored rocprofv3 --pmc record (FETCH_SIZE + WRITE_SIZE per launch, "
+                                        "profiles/ffn_gateup_T176_counters.json), valid for the current ffn.hip "
+                                        "source" if traffic is not None else
+                                        "none: the stored counter record predates the current ffn.hip source"),
+                     "frac_of_read_stream_peak": achieved / read_peak,
                      "algorithmic_bytes_per_launch": head["gateup_bytes"], "launch_ms": head["per"]["ffn_gateup"]},
         "sweep": [{"T": r["T"], "us_per_layer": r["ms"] * 1e3, "eager_us_per_layer": r["eager_ms"] * 1e3,
+                   "us_p10_median_p90": [r["dist"]["p10"] * 1e3, r["dist"]["median"] * 1e3, r["dist"]["p90"] * 1e3],
                    "tokens_per_s": r["T"] / (r["ms"] / 1e3),
                    "active_experts": r["active"], "weight_GBps": r["weight_bytes"] / (r["ms"] / 1e3) / 1e9,
                    "weight_frac_of_hbm_peak": r["weight_bytes"] / (r["ms"] / 1e3) / HBM_PEAK,
                    "gateup_us": r["per"]["ffn_gateup"] * 1e3, "down_us": r["per"]["ffn_down"] * 1e3,
-                   "rotation_sets": r["rotation_sets"]} for r in (results[T] for T in Ts)],
+                   "rotation_sets": r["rotation_sets"],
+                   **({"no_rotation_us_per_layer": r["no_rotation_ms"] * 1e3} if "no_rotation_ms" in r else {})}
+                  for r in (results[T] for T in Ts)],
         "input_generation_s": gen_s,
     }
+    del base
+    torch.cuda.empty_cache()
+    pre_L = None
+    if not args.no_prefill:
+        print("bench: prefill", file=sys.stderr, flush=True)
+        out["prefill"], pre_L = prefill_measure(max(2, args.warmup // 3), 5)
     if not args.no_cpu:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens, pre_L)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def read_stream_peak(gib=4, reps=5):
+    """Bytes/s of a plain streaming read of a large fp32 buffer (row sums of 4096 consecutive
+    values: every row one contiguous 16 KB read, best of reps) -- the practical read bandwidth this
+    chip shows in this process, beside the nominal 8 TB/s.  (A single whole-buffer torch.sum reads
+    slower, about 4 TB/s: its reduction tree, not memory, limits it.)"""
+    import torch
+    n = (gib << 30) // 4
+    buf = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    rows = buf.view(-1, 4096)
+    rows.sum(1)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        rows.sum(1)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, n * 4 / (a.elapsed_time(b) / 1e3))
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def side_run(args):
@@ -345,10 +427,11 @@ def side_run(args):
         sets = make_sets(T)
         runner = Runner(moe, sets, T, k, 0, E, H, I, fixed_routing=dense)
         eager_ms, per = time_steps(runner, args.sweep_steps, min(args.warmup, 5))
-        ms = time_graph(runner, args.sweep_steps, min(args.warmup, 5))
+        ms, dist = time_graph(runner, args.sweep_steps, min(args.warmup, 5))
         A = E if dense else active_experts(runner)
         wb = A * expert_bytes
         lines.append({"T": T, "us_per_layer": ms * 1e3, "eager_us_per_layer": eager_ms * 1e3,
+                      "us_p10_median_p90": [dist["p10"] * 1e3, dist["median"] * 1e3, dist["p90"] * 1e3],
                       "tokens_per_s": T / (ms / 1e3), "active_experts": A, "weight_GBps": wb / (ms / 1e3) / 1e9,
                       "weight_frac_of_hbm_peak": wb / (ms / 1e3) / HBM_PEAK,
                       "per_call_us": {kk: round(v * 1e3, 2) for kk, v in per.items()},
@@ -365,57 +448,83 @@ def side_run(args):
     print(json.dumps(out), flush=True)
 
 
-def prefill_run(args):
-    """The prefill layer (one weight set: its 6 GB of expert weights exceed the Infinity Cache many
-    times over).  Exact mode: weights decoded to bf16 in registers, bf16 MFMA with fp32
-    accumulation, h as a bf16 hi + lo pair (two MFMAs per down product)."""
-    import torch
+def prefill_inputs():
+    """The prefill layer's inputs on the GPU (one weight set: its 6 GB of expert weights exceed the
+    Infinity Cache many times over)."""
     import synth
     import mxfp4_routed_expert_router_amd as moe
     moe.lib()
     wl = synth.WORKLOADS["prefill"]
+    t0 = time.time()
+    L = synth.make_layer(wl, wl.tokens[0])
+    t = synth.to_torch(L, "cuda:0")
+    W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+    return wl, [{"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t}], time.time() - t0, L
+
+
+def prefill_mode(wl, sets, mx, steps, warmup):
+    """One prefill mode (exact: mx None; else the MX activation format) -> timing record."""
+    import mxfp4_routed_expert_router_amd as moe
     T = wl.tokens[0]
     H, I, E, k, S = wl.hidden, wl.inter, wl.n_routed, wl.top_k, wl.n_shared
-    t0 = time.time()
-    L = synth.make_layer(wl, T)
-    t = synth.to_torch(L, "cuda:0")
-    gen_s = time.time() - t0
-    W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
-    sets = [{"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t}]
-    runner = Runner(moe, sets, T, k, S, E + S, H, I, mx=args.mx)
-    ms, per = time_steps(runner, args.steps, args.warmup)
+    runner = Runner(moe, sets, T, k, S, E + S, H, I, mx=mx)
+    ms, per = time_steps(runner, steps, warmup)
     counts = runner.b.counts.cpu()
-    A = int((counts > 0).sum().item())
     kt = k + S
     ffn_flops = 6.0 * H * I * T * kt
-    router_flops = 2.0 * T * H * E
-    bf16_peak = 2.5e15
-    ffn_s = (per["ffn_plan"] + per["ffn_gateup"] + per["ffn_down"]) / 1e3
+    ffn_ms = sum(per.get(kk, 0.0) for kk in ("ffn_plan", "ffn_gateup", "ffn_down")) if mx is not None else \
+        per["ffn_gateup"] + per["ffn_down"]
+    rec = {"mode": "exact" if mx is None else f"mx_{mx}", "ms_per_layer": ms, "tokens_per_s": T / (ms / 1e3),
+           "ffn_ms": ffn_ms, "ffn_tflops": ffn_flops / (ffn_ms / 1e3) / 1e12,
+           "frac_of_bf16_mfma_peak": ffn_flops / (ffn_ms / 1e3) / 2.5e15,
+           "frac_of_mxfp4_mfma_peak": ffn_flops / (ffn_ms / 1e3) / 10.1e15,
+           "active_experts": int((counts > 0).sum().item()), "max_rows_per_expert": int(counts.max().item()),
+           "per_call_ms": {kk: round(v, 4) for kk, v in per.items()}}
+    if mx is None:
+        rec["gateup_tflops"] = 4.0 * H * I * T * kt / (per["ffn_gateup"] / 1e3) / 1e12
+        rec["down_tflops"] = 2.0 * H * I * T * kt / (per["ffn_down"] / 1e3) / 1e12
+    else:
+        rec["per_call_ms"]["ffn_mx"] = rec["per_call_ms"].pop("ffn_plan")
+        for kk in ("ffn_gateup", "ffn_down"):  # one call: its kernels are split by the profiler only
+            rec["per_call_ms"].pop(kk)
+    del runner
+    return rec
+
+
+def prefill_measure(warmup, steps):
+    """The prefill object of the default line: T = 8192, exact mode and MX mode with MXFP6
+    activations, FFN time and the fraction of the MXFP4 MFMA peak (10.1 PFLOP/s)."""
+    import torch
+    wl, sets, gen_s, L = prefill_inputs()
+    out = {"workload": f"moe_layer_prefill_H{wl.hidden}_E{wl.n_routed}+{wl.n_shared}_top{wl.top_k}_I{wl.inter}"
+                       f"_mxfp4_T{wl.tokens[0]}", "input_generation_s": gen_s}
+    for mx in (None, "fp6"):
+        out["exact" if mx is None else f"mx_{mx}"] = prefill_mode(wl, sets, mx, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    return out, L
+
+
+def prefill_run(args):
+    """The prefill layer alone (its own JSON line).  Exact mode: weights decoded to bf16 in
+    registers, bf16 MFMA with fp32 accumulation, h as a bf16 hi + lo pair (two MFMAs per down
+    product); MX mode with --mx."""
+    wl, sets, gen_s, _ = prefill_inputs()
+    T = wl.tokens[0]
+    H, I, E, k, S = wl.hidden, wl.inter, wl.n_routed, wl.top_k, wl.n_shared
+    rec = prefill_mode(wl, sets, args.mx, args.steps, args.warmup)
     mode = "exact mode" if args.mx is None else f"MX mode, {args.mx} activations"
     out = {
         "metric": f"prefill MoE-layer tokens/s and MFMA utilisation ({mode})",
-        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True,
+        "value": rec["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_layer"], "higher_is_better": True,
         "dtype": "bf16" if args.mx is None else f"fp4 weights x {args.mx} activations", "data": "synthetic",
         "config": {"workload": f"moe_layer_prefill_H{H}_E{E}+{S}_top{k}_I{I}_mxfp4_T{T}", "tokens": T,
-                   "zipf_s": wl.zipf_s, "mode": "exact" if args.mx is None else f"mx_{args.mx}"},
-        "active_experts": A, "max_rows_per_expert": int(counts.max().item()),
-        "per_call_ms": {kk: round(v, 4) for kk, v in per.items()},
-        "ffn_ms": ffn_s * 1e3,
-        "ffn_tflops": ffn_flops / ffn_s / 1e12,
-        "frac_of_bf16_mfma_peak": ffn_flops / ffn_s / bf16_peak,
-        "frac_of_mxfp4_mfma_peak": ffn_flops / ffn_s / 10.1e15,
-        "layer_flops": ffn_flops + router_flops,
+                   "zipf_s": wl.zipf_s, "mode": rec["mode"]},
+        "layer_flops": 6.0 * H * I * T * (k + S) + 2.0 * T * H * E,
         "input_generation_s": gen_s,
     }
-    if args.mx is None:
-        gu_s, dn_s = per["ffn_gateup"] / 1e3, per["ffn_down"] / 1e3
-        out["gateup_tflops"] = 4.0 * H * I * T * kt / gu_s / 1e12
-        out["down_tflops"] = 2.0 * H * I * T * kt / dn_s / 1e12
-    else:
-        out["per_call_ms"]["ffn_mx"] = out["per_call_ms"].pop("ffn_plan")
-        for kk in ("ffn_gateup", "ffn_down"):  # one call: its kernels are split by the profiler only
-            out["per_call_ms"].pop(kk)
+    out.update({kk: v for kk, v in rec.items() if kk not in ("mode", "ms_per_layer", "tokens_per_s")})
     print(json.dumps(out), flush=True)
 
 
@@ -432,19 +541,81 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}), flush=True)
 
 
-def cpu_baseline(L, T, n):
-    """The fp64 oracle (as it stands) on the first n tokens of the same batch, run as one layer call
-    of n tokens: route, bucket, grouped expert FFN, combine."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(L, T, n, pre=None):
+    """The fp64 oracle as it stands, timed on the host cores (OpenMP over its default thread count,
+    plus one single-thread run).  `value`: the first n tokens of the benchmark's own T-token batch
+    run as one n-token layer call (route, bucket, grouped expert FFN, combine).  `runs`: the other
+    layer workloads -- the tiny layer (median of 5, all threads and one thread), the decode layer at
+    T = 8, the dense FFN as 8 all-active FP16 slices at T = 1, and the prefill layer, whose routing
+    and bucketing run on all 8192 tokens while its expert FFN runs on 8 tokens and is extrapolated
+    per token to the batch (labelled as such)."""
     import dataclasses
+    import statistics
+    import numpy as np
     import oracle
+    import synth
     o = oracle.load()
+    threads = o.num_threads()
     sub = dataclasses.replace(L, T=n, x=L.x[:n])
     t0 = time.perf_counter()
     o.layer(sub)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": o.num_threads(), "kind": "oracle",
+    runs = []
+
+    def timed(fn, reps=1):
+        ts = []
+        for _ in range(reps):
+            a = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - a)
+        return statistics.median(ts)
+
+    tiny = synth.make_layer(synth.WORKLOADS["tiny"], 16)
+    t_all = timed(lambda: o.layer(tiny), 5)
+    o.set_num_threads(1)
+    t_one = timed(lambda: o.layer(tiny), 5)
+    o.set_num_threads(threads)
+    runs.append({"workload": "tiny T=16", "s_per_layer": t_all, "tokens_per_s": 16 / t_all, "threads": threads,
+                 "stat": "median of 5"})
+    runs.append({"workload": "tiny T=16", "s_per_layer": t_one, "tokens_per_s": 16 / t_one, "threads": 1,
+                 "stat": "median of 5"})
+    dec = synth.make_layer(synth.WORKLOADS["decode"], 8)
+    t_dec = timed(lambda: o.layer(dec))
+    runs.append({"workload": "decode T=8", "s_per_layer": t_dec, "tokens_per_s": 8 / t_dec, "threads": threads})
+    dense = synth.make_layer(synth.WORKLOADS["dense_slices"], 1)
+    t_den = timed(lambda: o.layer(dense))
+    runs.append({"workload": "dense_slices T=1", "s_per_layer": t_den, "tokens_per_s": 1 / t_den,
+                 "threads": threads})
+    wl = synth.WORKLOADS["prefill"]
+    if pre is None:
+        pre = synth.make_layer(wl, wl.tokens[0])
+    a = time.perf_counter()
+    r = o.route(pre.x, oracle.X_BF16, pre.router, pre.bias, wl.top_k, wl.n_shared)
+    o.bucket(r["ids"], wl.n_experts)
+    t_rb = time.perf_counter() - a
+    mask = np.zeros(pre.T, np.uint8)
+    mask[np.linspace(0, pre.T - 1, 8).astype(int)] = 1
+    t_ffn8 = timed(lambda: o.layer(pre, token_mask=mask))
+    runs.append({"workload": "prefill T=8192 route + bucket (all tokens)", "s": t_rb, "threads": threads})
+    runs.append({"workload": "prefill T=8192 whole layer", "extrapolated": True,
+                 "s_per_layer": t_rb + (t_ffn8 - t_rb) * pre.T / 8, "threads": threads,
+                 "how": "route + bucket measured on all 8192 tokens; expert FFN and combine measured on 8 spread "
+                        "tokens (that call also re-routes all tokens) and scaled by 8192 / 8"})
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {T}-token batch as one {n}-token layer call (route, bucket, expert FFN, "
-                      f"combine in fp64); {dt:.1f} s"}
+                      f"combine in fp64); {dt:.1f} s",
+            "cpu_model": cpu_model(), "hardware_threads": os.cpu_count(), "runs": runs}
 
 
 if __name__ == "__main__":

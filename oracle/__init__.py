@@ -117,6 +117,7 @@ class Oracle:
         lib.orc_mxfp4_bytes.restype = ctypes.c_int64
         lib.orc_mxfp4_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
         lib.orc_num_threads.restype = i; lib.orc_num_threads.argtypes = []
+        lib.orc_set_num_threads.restype = None; lib.orc_set_num_threads.argtypes = [i]
         lib.orc_route.restype = None
         lib.orc_route.argtypes = [vp, i, i, i, vp, vp, i, i, i, d, vp, vp, vp, vp, vp]
         lib.orc_route_sigmoid.restype = None
@@ -166,6 +167,7 @@ class Oracle:
     def nvfp4_bits_per_weight(self) -> float: return self.lib.orc_nvfp4_bits_per_weight()
     def mxfp4_bytes(self, n_rows: int, k: int) -> int: return self.lib.orc_mxfp4_bytes(n_rows, k)
     def num_threads(self) -> int: return self.lib.orc_num_threads()
+    def set_num_threads(self, n: int) -> None: self.lib.orc_set_num_threads(n)
 
     def weight(self, W: "ExpertWeights", which: str, e: int, n: int, k: int) -> float:
         """Decoded element (n, k) of expert e's projection which in {gate, up, down}."""

@@ -119,6 +119,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Thread count for the following calls (timing only: results do not depend on it). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Router: logits, softmax, top-k, renormalise, append shared experts                         */
 /* ------------------------------------------------------------------------------------------ */

@@ -145,6 +145,7 @@ void orc_mxfp4_decode_matrix(const uint8_t *codes, const uint8_t *scales, int n_
                              double *out);
 double orc_silu(double z);
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

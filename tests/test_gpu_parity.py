@@ -523,7 +523,8 @@ def test_route_bucket_equals_separate_calls(name, T):
     kt = k + S
     ids_a, w_a, p_a = moe.moe_route(t["x"], t["router"], k, t["bias"], S, want_probs=True)
     b_a = moe.moe_bucket(ids_a, wl.n_experts)
-    ws_a = torch.empty(moe.moe_expert_ffn_workspace_bytes(T, kt, W), dtype=torch.uint8, device=DEV)
+    # zero-filled, so that the padding past the tile table compares equal too
+    ws_a = torch.zeros(moe.moe_expert_ffn_workspace_bytes(T, kt, W), dtype=torch.uint8, device=DEV)
     moe.moe_expert_ffn_plan(T, W, b_a.offsets, kt, ws_a)
     ids_b = torch.full_like(ids_a, -7)
     w_b = torch.full_like(w_a, -7.0)

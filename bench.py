@@ -7,7 +7,10 @@ intermediate 2048, MXFP4 expert weights (codes uniform, E8M0 in [118, 127]), bf1
 One step = one layer call on T tokens (default 176): moe_route_bucket (router, bucketing and the
 expert FFN's tile plan) -> moe_expert_ffn_gateup -> moe_expert_ffn_down -> moe_combine, inputs resident
 in HBM.  Weight sets are rotated so that the bytes touched between two visits of one set exceed the
-256 MB Infinity Cache (a one-set control is reported where rotation applies).
+256 MB Infinity Cache (a one-set control is reported where rotation applies).  The rotated copies
+are made once and, like every other buffer, freed only after the last GPU measurement: device memory
+freed during the run is cleared by the driver in the background, and that traffic slowed the
+kernels timed in the next seconds by about 3%.
 
 Each T is timed twice: eager (the library calls issued from Python, HIP events around the steps and
 between the calls) and replayed from HIP graphs that hold one layer call each (the headline: the
@@ -260,24 +263,16 @@ def main():
     gen_s = time.time() - t0
     expert_bytes = 3 * H * I * MXFP4_BYTES_PER_WEIGHT
 
-    def make_sets(T):
+    def n_sets(T):
         # enough independent copies (router + weights) that one pass over them exceeds 4x the cache
         a = E * (1.0 - (1.0 - k / E) ** T)
-        r = max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes + 4 * H * E))))
-        sets = []
-        for j in range(r):
-            if j == 0:
-                t = base
-            else:
-                t = {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base.items()}
-            W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
-            sets.append({"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t})
-        return sets
+        return max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes + 4 * H * E))))
 
+    pool = weight_pool(moe, base, max(n_sets(T) for T in Ts))
     results = {}
     for T in Ts:
         print(f"bench: T={T}", file=sys.stderr, flush=True)
-        sets = make_sets(T)
+        sets = pool[:n_sets(T)]
         runner = Runner(moe, sets, T, k, 0, E, H, I)
         steps = args.steps if T == args.tokens else args.sweep_steps
         warm = args.warmup if T == args.tokens else min(args.warmup, 5)
@@ -295,10 +290,9 @@ def main():
             runner.sets = sets[:1]
             results[T]["no_rotation_ms"] = time_graph(runner, steps, warm)[0]
         del runner, sets
-        torch.cuda.empty_cache()
 
     print("bench: read-stream peak", file=sys.stderr, flush=True)
-    read_peak = read_stream_peak()
+    read_peak, read_buf = read_stream_peak()
 
     head = results[args.tokens]
     t_gu = head["per"]["ffn_gateup"] / 1e3
@@ -351,12 +345,14 @@ def main():
                   for r in (results[T] for T in Ts)],
         "input_generation_s": gen_s,
     }
-    del base
-    torch.cuda.empty_cache()
     pre_L = None
     if not args.no_prefill:
         print("bench: prefill", file=sys.stderr, flush=True)
         out["prefill"], pre_L = prefill_measure(max(2, args.warmup // 3), 5)
+    # nothing is freed before the last GPU measurement: the driver clears freed device memory in
+    # the background, and that traffic slows the kernels measured next (about 3% for several
+    # seconds after freeing the rotated weight sets)
+    del pool, base, read_buf
     if not args.no_cpu:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(L, args.tokens, args.cpu_tokens, pre_L)
@@ -365,11 +361,28 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def weight_pool(moe, base, n, fix=None):
+    """n weight sets: the inputs `base` and n - 1 copies of them, allocated once and kept until the
+    measurements end (fix(t) adjusts a copy's views, e.g. the dense slices)."""
+    sets = []
+    for j in range(n):
+        if j == 0:
+            t = base
+        else:
+            t = {kk: (v.clone() if hasattr(v, "clone") else v) for kk, v in base.items()}
+            if fix is not None:
+                fix(t)
+        W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
+        sets.append({"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t})
+    return sets
+
+
 def read_stream_peak(gib=4, reps=5):
     """Bytes/s of a plain streaming read of a large fp32 buffer (row sums of 4096 consecutive
     values: every row one contiguous 16 KB read, best of reps) -- the practical read bandwidth this
     chip shows in this process, beside the nominal 8 TB/s.  (A single whole-buffer torch.sum reads
-    slower, about 4 TB/s: its reduction tree, not memory, limits it.)"""
+    slower, about 4 TB/s: its reduction tree, not memory, limits it.)  Returns the buffer too, for
+    the caller to free once nothing else is timed."""
     import torch
     n = (gib << 30) // 4
     buf = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -384,9 +397,7 @@ def read_stream_peak(gib=4, reps=5):
         b.record()
         torch.cuda.synchronize()
         best = max(best, n * 4 / (a.elapsed_time(b) / 1e3))
-    del buf
-    torch.cuda.empty_cache()
-    return best
+    return best, buf
 
 
 def side_run(args):
@@ -407,24 +418,20 @@ def side_run(args):
     gen_s = time.time() - t0
     expert_bytes = 3 * H * I * (2.0 if dense else MXFP4_BYTES_PER_WEIGHT)
 
-    def make_sets(T):
+    def n_sets(T):
         a = E if dense else E * (1.0 - (1.0 - k / E) ** T)
-        r = max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes))))
-        sets = []
-        for j in range(r):
-            t = base if j == 0 else {kk: (v.clone() if isinstance(v, torch.Tensor) else v) for kk, v in base.items()}
-            if dense and j > 0:  # keep the slice views over the copied dense matrices
-                E2 = wl.n_experts
-                t["gate"], t["up"] = t["dense_gate"].view(E2, I, H), t["dense_up"].view(E2, I, H)
-                t["down"] = t["dense_down"].as_strided((E2, H, I), (I, E2 * I, 1))
-            W = moe.ExpertWeights(t["gate"], t["gate_scales"], t["up"], t["up_scales"], t["down"], t["down_scales"])
-            sets.append({"x": t["x"], "router": t["router"], "bias": t["bias"], "W": W, "t": t})
-        return sets
+        return max(1, min(16, math.ceil(4 * INFINITY_CACHE / (a * expert_bytes))))
 
+    def slices(t):  # keep the slice views over the copied dense matrices
+        E2 = wl.n_experts
+        t["gate"], t["up"] = t["dense_gate"].view(E2, I, H), t["dense_up"].view(E2, I, H)
+        t["down"] = t["dense_down"].as_strided((E2, H, I), (I, E2 * I, 1))
+
+    pool = weight_pool(moe, base, max(n_sets(T) for T in Ts), slices if dense else None)
     lines = []
     for T in Ts:
         print(f"bench {name}: T={T}", file=sys.stderr, flush=True)
-        sets = make_sets(T)
+        sets = pool[:n_sets(T)]
         runner = Runner(moe, sets, T, k, 0, E, H, I, fixed_routing=dense)
         eager_ms, per = time_steps(runner, args.sweep_steps, min(args.warmup, 5))
         ms, dist = time_graph(runner, args.sweep_steps, min(args.warmup, 5))
@@ -437,7 +444,6 @@ def side_run(args):
                       "per_call_us": {kk: round(v * 1e3, 2) for kk, v in per.items()},
                       "rotation_sets": len(sets)})
         del runner, sets
-        torch.cuda.empty_cache()
     wdesc = "fp16 (8 all-active slices of one dense FFN)" if dense else "mxfp4 (E2M1 + E8M0/32)"
     out = {"metric": f"{name} MoE-layer tokens/s and HBM GB/s on expert weights (side measurement)",
            "n_gpus": 1, "data": "synthetic", "higher_is_better": True,
@@ -501,7 +507,6 @@ def prefill_measure(warmup, steps):
     for mx in (None, "fp6"):
         out["exact" if mx is None else f"mx_{mx}"] = prefill_mode(wl, sets, mx, steps, warmup)
     del sets
-    torch.cuda.empty_cache()
     return out, L
 
 

@@ -177,13 +177,13 @@ moe_status moe_pad_rows(const int32_t *n_rows, int T_shape, int k_total, int32_t
 
 /* ---------------------------------------------------------------------------------------------
  * moe_route_bucket -- moe_route, then moe_bucket of its ids over n_buckets = E + n_shared, then
- * (W non-NULL) moe_expert_ffn_plan into ffn_workspace, with the same results bit for bit, in fewer
- * launches: for T * (top_k + n_shared) <= 2048 the selection kernel's last workgroup does the
- * bucketing and the tile table (two launches in all instead of four).  Arguments as for those
- * calls; W->n_experts must equal E + n_shared; ffn_workspace then is the workspace that the
- * following moe_expert_ffn_gateup / moe_expert_ffn_down calls use.  workspace:
+ * (W non-NULL) moe_expert_ffn_plan into ffn_workspace, with the same results bit for bit: for
+ * T <= 8 in two launches instead of four (one workgroup selects, buckets and writes the tile
+ * table), for larger T as the separate kernels.  Arguments as for those calls; W->n_experts must
+ * equal E + n_shared; ffn_workspace then is the workspace that the following
+ * moe_expert_ffn_gateup / moe_expert_ffn_down calls use.  workspace:
  * moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared) bytes, 16-byte aligned (it holds
- * the router's partial sums, a counter the kernels reset themselves, and the bucketing's scratch).
+ * the router's partial sums and the bucketing's scratch).
  * Errors: as for the three calls. */
 size_t moe_route_bucket_workspace_bytes(int T, int H, int E, int top_k, int n_shared);
 moe_status moe_route_bucket(const void *x, moe_act_dtype x_dtype, int T, int H, const float *w_router,

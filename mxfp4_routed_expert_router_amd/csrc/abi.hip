@@ -559,13 +559,12 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int n_
 extern "C" {
 
 // ---------------------------------------------------------------------------------------------
-// moe_route_bucket.  Workspace: router partial sums | ticket (256 bytes) | bucketing workspace.
+// moe_route_bucket.  Workspace: router partial sums | bucketing workspace.
 size_t moe_route_bucket_workspace_bytes(int T, int H, int E, int top_k, int n_shared) {
   if (T <= 0 || H <= 0 || E <= 0 || top_k < 1 || n_shared < 0) return 0;
   const int64_t n_slots = (int64_t)T * (top_k + n_shared);
   if (n_slots > INT_MAX) return 0;
-  return moe_route_workspace_bytes(T, H, E) + 256 +
-         round_up(moe_bucket_workspace_bytes((int)n_slots, E + n_shared), 256);
+  return moe_route_workspace_bytes(T, H, E) + round_up(moe_bucket_workspace_bytes((int)n_slots, E + n_shared), 256);
 }
 
 moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, const float* w_router,
@@ -602,15 +601,13 @@ moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, 
   uint8_t* ws = (uint8_t*)workspace;
   float* partial = (float*)ws;
   const size_t rws = moe_route_workspace_bytes(T, H, E);
-  uint32_t* ticket = (uint32_t*)(ws + rws);
-  int32_t* bws = (int32_t*)(ws + rws + 256);
+  int32_t* bws = (int32_t*)(ws + rws);
   const int splits = moe::route_splits(T, H, E);
   hipStream_t st = (hipStream_t)stream;
   if (moe::route_bucket_fusable(T, k_total, n_buckets))
     return hip_status(moe::launch_route_bucket(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k,
-                                               n_shared, ids, weights, probs, partial, splits, ticket, n_buckets,
-                                               counts, offsets, sorted_slot, slot_pos, table, 16 * pl.mt, pl.tiles,
-                                               st));
+                                               n_shared, ids, weights, probs, partial, splits, n_buckets, counts,
+                                               offsets, sorted_slot, slot_pos, table, 16 * pl.mt, pl.tiles, st));
   hipError_t err = moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k, n_shared, ids,
                                      weights, probs, partial, splits, st);
   if (err != hipSuccess) return MOE_ERR_HIP;

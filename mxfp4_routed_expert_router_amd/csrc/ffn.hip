@@ -604,6 +604,10 @@ __device__ __forceinline__ void run_pipeline_impl(int c0, int c1, Load& load, Co
 constexpr int kMaxChunksPerWave = 64;  // K share of one wave <= 8192
 // Scale table of one wave: [pairs][cpw dwords]
 __host__ __device__ constexpr int stab_bytes(int pairs, int cpw) { return pairs * cpw * 4; }
+// Row stride (dwords) of the row-split kernels' scale tables: odd, so that the 16 rows a wave's
+// lanes read at once fall on 16 different LDS banks (with n_chunks dwords per row, e.g. 16 or 56,
+// they shared 2 or 4 banks, and each read waited on 8- or 4-way bank conflicts).
+__host__ __device__ constexpr int rows_stab_stride(int n_chunks) { return n_chunks | 1; }
 
 // Fills a wave's scale table: NM matrices of `total` units each; unit f of matrix m is read by
 // ld(m, f) (which must read nothing for f >= total) and written by st(m, f, v).  PER units of every
@@ -922,7 +926,8 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
   const int n_chunks = H >> 7, n_steps = (n_chunks + 1) >> 1;
 
   uint8_t* xs = lds;  // [2][kGuXStage]
-  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kGuXStage + wave * stab_bytes(NP, n_chunks));
+  const int sstr = rows_stab_stride(n_chunks);
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kGuXStage + wave * stab_bytes(NP, sstr));
 
   // Activations: thread q = 64*wave + lane moves 16-byte column q%16 of token q/16, both chunks of
   // a step (4 waves), or of token q/32, chunk (q/16)%2 (8 waves).  Padded tokens get an
@@ -994,8 +999,8 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float sg = e8m0_to_f32(sc[4 * n_chunks * (0 * 16 * RT + rt * 16 + l16)]);
-      const float su = e8m0_to_f32(sc[4 * n_chunks * (1 * 16 * RT + rt * 16 + l16)]);
+      const float sg = e8m0_to_f32(sc[4 * sstr * (0 * 16 * RT + rt * 16 + l16)]);
+      const float su = e8m0_to_f32(sc[4 * sstr * (1 * 16 * RT + rt * 16 + l16)]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const V ag = decode8_bf16(d.q[0][rt][j][k], sg), au = decode8_bf16(d.q[1][rt][j][k], su);
@@ -1045,7 +1050,12 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
             const int r = f / upr, u = f - r * upr;
             return bld16(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * (m ? up.sr : gate.sr)) + 16u * u : kOutOfRange);
           },
-          [&](int m, int f, const u32x4& v) { *reinterpret_cast<u32x4*>(stab + m * rows * n_chunks + 4 * f) = v; });
+          [&](int m, int f, const u32x4& v) {
+            const int r = f / upr, u = f - r * upr;
+            uint32_t* d = stab + (m * rows + r) * sstr + 4 * u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = v[i];
+          });
     } else {
       const int total = rows * n_chunks;
       fill_table<NM, 4, uint32_t>(
@@ -1054,7 +1064,10 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
             const int r = f / n_chunks, j = f - r * n_chunks;
             return bld4(sr[m], f < total ? (uint32_t)(min(n0 + r, I - 1) * (m ? up.sr : gate.sr)) + 4u * j : kOutOfRange);
           },
-          [&](int m, int f, uint32_t v) { stab[m * rows * n_chunks + f] = v; });
+          [&](int m, int f, uint32_t v) {
+            const int r = f / n_chunks, j = f - r * n_chunks;
+            stab[(m * rows + r) * sstr + j] = v;
+          });
     }
   }
   put_x(0, X[0]);
@@ -1155,7 +1168,8 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
   const int n_chunks = I >> 7, n_pairs = (n_chunks + 1) >> 1;
 
   uint8_t* xs = lds;  // [2][kStage]
-  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kStage + wave * stab_bytes(NP, n_chunks));
+  const int sstr = rows_stab_stride(n_chunks);
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + 2 * kStage + wave * stab_bytes(NP, sstr));
 
   // h lane-load i: q = 64 * (NW * i + wave) + lane covers 16-byte column q % 16 of chunk (q / 16) % 2
   // of the pair, token (q / 32) % 16 and plane q / 512 (uniform over a wave's load).
@@ -1211,7 +1225,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
       const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * c + lq;
       float scale[HT];
 #pragma unroll
-      for (int r = 0; r < HT; ++r) scale[r] = e8m0_to_f32(sc[4 * n_chunks * ((HT * th + r) * 16 + l16)]);
+      for (int r = 0; r < HT; ++r) scale[r] = e8m0_to_f32(sc[4 * sstr * ((HT * th + r) * 16 + l16)]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const V bh = *reinterpret_cast<const V*>(st + 16 * k);
@@ -1262,7 +1276,12 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
             const int r = f / upr, u = f - r * upr;
             return bld16(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 16u * u : kOutOfRange);
           },
-          [&](int, int f, const u32x4& v) { *reinterpret_cast<u32x4*>(stab + 4 * f) = v; });
+          [&](int, int f, const u32x4& v) {
+            const int r = f / upr, u = f - r * upr;
+            uint32_t* d = stab + r * sstr + 4 * u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = v[i];
+          });
     } else {
       const int total = NP * n_chunks;
       fill_table<1, 8, uint32_t>(
@@ -1271,7 +1290,10 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
             const int r = f / n_chunks, j = f - r * n_chunks;
             return bld4(sr, f < total ? (uint32_t)(min(n0 + r, H - 1) * down.sr) + 4u * j : kOutOfRange);
           },
-          [&](int, int f, uint32_t v) { stab[f] = v; });
+          [&](int, int f, uint32_t v) {
+            const int r = f / n_chunks, j = f - r * n_chunks;
+            stab[r * sstr + j] = v;
+          });
     }
   }
   put_h(0, Hc[0]);
@@ -1756,7 +1778,9 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 // streams; below that the K-split kernels spread each expert over more workgroups.
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
-size_t gateup_rows_lds(int H, int rt, int nw) { return 2 * (size_t)kGuXStage + nw * (size_t)stab_bytes(2 * 16 * rt, H / 128); }
+size_t gateup_rows_lds(int H, int rt, int nw) {
+  return 2 * (size_t)kGuXStage + nw * (size_t)stab_bytes(2 * 16 * rt, rows_stab_stride(H / 128));
+}
 // Gate/up row-split workgroups: one 16-row tile of each matrix per wave and 8 waves sharing each
 // x stage, or 4 waves when 8-wave row blocks would give fewer than kGuSmallBlocks workgroups
 // (measured on the sweep workload, 8 waves: T = 176 685 -> 667 us, T = 128 673 -> 657 us,
@@ -1770,7 +1794,7 @@ constexpr int kGuNW = 8, kGuNWSmall = 4;
 constexpr int kDnNW = 8, kDnNWSmall = 4;
 constexpr int64_t kDnSmallBlocks = 4096;
 size_t down_rows_lds(int I, int nw) {
-  return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, I / 128);
+  return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, rows_stab_stride(I / 128));
 }
 
 template <int FMT, int MT>

@@ -19,14 +19,14 @@ hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_
                         float routed_scale = 1.0f, float shared_weight = 1.0f);
 
 // Router, bucketing and (table != NULL) the expert FFN's tile table in two launches (logits, then
-// selection with the last workgroup bucketing), for calls route_bucket_fusable() accepts.  ticket:
-// a device uint32 the two kernels use (zeroed by the first).
+// one workgroup that selects, buckets and plans), for the small calls route_bucket_fusable()
+// accepts (at most 8 tokens).
 bool route_bucket_fusable(int T, int k_total, int n_buckets);
 hipError_t launch_route_bucket(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias,
                                int E, int top_k, int n_shared, int32_t* ids, float* weights, float* probs,
-                               float* partial, int splits, uint32_t* ticket, int n_buckets, int32_t* counts,
-                               int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* table,
-                               int rows_per_tile, int64_t n_entries, hipStream_t stream);
+                               float* partial, int splits, int n_buckets, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slot, int32_t* slot_pos, void* table, int rows_per_tile,
+                               int64_t n_entries, hipStream_t stream);
 
 // ---- fixed row shapes: zero routing weights and invalid ids on rows past the device row count ----
 hipError_t launch_pad_rows(const int32_t* n_rows, int T_shape, int k_total, int32_t* ids, float* weights,

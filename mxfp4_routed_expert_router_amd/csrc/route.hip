@@ -40,13 +40,11 @@ constexpr int route_ku() { return MT == 1 ? 8 : 4; }
 
 // MT: 16-token tiles per wave (more than one when T is large: each router-weight fragment, and its
 // three-way split, then serves MT token tiles, which cuts the weight re-reads through L2).
-// ticket (or NULL): the fused selection kernel's counter, zeroed here by the first wave.
 template <int XF16, int VEC, int MT>
 __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ w, int E, int ks_per_split,
-                                                          float* __restrict__ partial, uint32_t* __restrict__ ticket) {
+                                                          float* __restrict__ partial) {
   const int lane = threadIdx.x, l16 = lane & 15, lq = lane >> 4;
-  if (ticket && lane == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *ticket = 0u;
   const int e = blockIdx.x * 16 + l16;
   const int split = blockIdx.z;
   const int nks = (H + 31) / 32;
@@ -342,16 +340,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
                               shared_weight, t);
 }
 
-// The router's selection, the bucketing and the expert FFN's tile table in one launch, for calls
-// of at most kFusedChunks * kBucketChunk slots: each workgroup of 8 waves selects 8 tokens; the
-// last workgroup to finish (an atomic ticket after a device-scope release of its ids) acquires
-// every workgroup's ids and runs the whole bucketing, then builds the tile table from the bucket
-// offsets.  The ticket counter is zeroed by the logits kernel that precedes this one on the
-// stream, and again by the last workgroup.
+// The router's selection, the bucketing and the expert FFN's tile table in one workgroup, for calls
+// of at most kFusedTokens tokens: wave t selects token t, and after a barrier (which makes the
+// workgroup's ids visible to all its waves) the workgroup buckets the slots and builds the tile
+// table from the bucket offsets.  (With several selection workgroups the bucketing would wait for
+// all of them behind a device-scope release, an atomic ticket and an acquire; measured on the
+// sweep layer, that tail was slower than the separate bucketing and plan launches at 32 tokens and
+// more, and no faster below, so larger calls take the separate kernels.)
+constexpr int kFusedTokens = kBucketChunk / 64;
 struct FusedTail {
   int n_buckets;
   int32_t *counts, *offsets, *sorted_slot, *slot_pos;
-  uint32_t* ticket;
   TileEntry* table;  // NULL: no tile table
   int rows_per_tile, n_entries;
 };
@@ -362,24 +361,17 @@ __global__ __launch_bounds__(kBucketChunk) void route_select_bucket_kernel(
     int n_shared, int32_t* __restrict__ ids, float* __restrict__ weights, float* __restrict__ probs,
     float routed_scale, float shared_weight, FusedTail ft) {
   extern __shared__ int lds[];
-  __shared__ int s_last;
-  const int t = blockIdx.x * (kBucketChunk / 64) + (threadIdx.x >> 6);
+  const int t = threadIdx.x >> 6;  // one workgroup: T <= kFusedTokens
   if (t < T)
     select_token<VPL, VEC, SIG>(partial, splits, T, E, bias, top_k, n_shared, ids, weights, probs, routed_scale,
                                 shared_weight, t);
-  __threadfence();  // release: this workgroup's ids and weights, device-wide
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(ft.ticket, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;  // uniform over the workgroup
-  __threadfence();      // acquire: every other workgroup's ids
   const int n_slots = T * (top_k + n_shared);
   const int total = bucket_fused_block(ids, n_slots, ft.n_buckets, ft.counts, ft.offsets, ft.sorted_slot,
                                        ft.slot_pos, lds);
   if (ft.table)
     tiles_from_offsets_block(fused_base(lds, ft.n_buckets), total, ft.n_buckets, n_slots, ft.rows_per_tile,
                              ft.n_entries, ft.table, lds);
-  if (threadIdx.x == 0) *ft.ticket = 0u;
 }
 }  // namespace
 
@@ -406,28 +398,27 @@ int route_splits(int T, int H, int E) {
 }
 
 template <int XF16, int VEC>
-void launch_logits(const void* x, int T, int H, const float* w, int E, int splits, float* partial, hipStream_t st,
-                   uint32_t* ticket) {
+void launch_logits(const void* x, int T, int H, const float* w, int E, int splits, float* partial, hipStream_t st) {
   const int nks = (H + 31) / 32;
   const int per = (nks + splits - 1) / splits;
   const int mt = route_mt(T, E);
   const dim3 g((E + 15) / 16, (T + 16 * mt - 1) / (16 * mt), splits);
   const uint16_t* xx = (const uint16_t*)x;
-  if (mt == 4) route_logits_kernel<XF16, VEC, 4><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial, ticket);
-  else if (mt == 2) route_logits_kernel<XF16, VEC, 2><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial, ticket);
-  else route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial, ticket);
+  if (mt == 4) route_logits_kernel<XF16, VEC, 4><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else if (mt == 2) route_logits_kernel<XF16, VEC, 2><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
+  else route_logits_kernel<XF16, VEC, 1><<<g, 64, 0, st>>>(xx, T, H, w, E, per, partial);
 }
 
 // Logits for every form of the router call.
 hipError_t launch_route_logits(const void* x, int x_fp16, int T, int H, const float* w_router, int E, float* partial,
-                               int splits, hipStream_t stream, uint32_t* ticket) {
+                               int splits, hipStream_t stream) {
   const bool vec = ((uintptr_t)w_router % 16 == 0) && (H % 8 == 0);
   if (x_fp16) {
-    if (vec) launch_logits<1, 1>(x, T, H, w_router, E, splits, partial, stream, ticket);
-    else launch_logits<1, 0>(x, T, H, w_router, E, splits, partial, stream, ticket);
+    if (vec) launch_logits<1, 1>(x, T, H, w_router, E, splits, partial, stream);
+    else launch_logits<1, 0>(x, T, H, w_router, E, splits, partial, stream);
   } else {
-    if (vec) launch_logits<0, 1>(x, T, H, w_router, E, splits, partial, stream, ticket);
-    else launch_logits<0, 0>(x, T, H, w_router, E, splits, partial, stream, ticket);
+    if (vec) launch_logits<0, 1>(x, T, H, w_router, E, splits, partial, stream);
+    else launch_logits<0, 0>(x, T, H, w_router, E, splits, partial, stream);
   }
   return hipGetLastError();
 }
@@ -435,7 +426,7 @@ hipError_t launch_route_logits(const void* x, int x_fp16, int T, int H, const fl
 hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias, int E,
                         int top_k, int n_shared, int32_t* ids, float* weights, float* probs, float* partial,
                         int splits, hipStream_t stream, bool sigmoid, float routed_scale, float shared_weight) {
-  hipError_t err = launch_route_logits(x, x_fp16, T, H, w_router, E, partial, splits, stream, nullptr);
+  hipError_t err = launch_route_logits(x, x_fp16, T, H, w_router, E, partial, splits, stream);
   if (err != hipSuccess) return err;
   dim3 g2((T + 3) / 4);
   const int vpl = (E + 63) / 64;
@@ -468,20 +459,20 @@ hipError_t launch_route(const void* x, int x_fp16, int T, int H, const float* w_
 }
 
 bool route_bucket_fusable(int T, int k_total, int n_buckets) {
-  return (int64_t)T * k_total <= (int64_t)kFusedChunks * kBucketChunk && n_buckets <= MOE_MAX_EXPERTS;
+  return T <= kFusedTokens && (int64_t)T * k_total <= (int64_t)kFusedChunks * kBucketChunk &&
+         n_buckets <= MOE_MAX_EXPERTS;
 }
 
 hipError_t launch_route_bucket(const void* x, int x_fp16, int T, int H, const float* w_router, const float* bias,
                                int E, int top_k, int n_shared, int32_t* ids, float* weights, float* probs,
-                               float* partial, int splits, uint32_t* ticket, int n_buckets, int32_t* counts,
-                               int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* table,
-                               int rows_per_tile, int64_t n_entries, hipStream_t stream) {
-  hipError_t err = launch_route_logits(x, x_fp16, T, H, w_router, E, partial, splits, stream, ticket);
+                               float* partial, int splits, int n_buckets, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_slot, int32_t* slot_pos, void* table, int rows_per_tile,
+                               int64_t n_entries, hipStream_t stream) {
+  if (!route_bucket_fusable(T, top_k + n_shared, n_buckets)) return hipErrorInvalidValue;
+  hipError_t err = launch_route_logits(x, x_fp16, T, H, w_router, E, partial, splits, stream);
   if (err != hipSuccess) return err;
-  FusedTail ft{n_buckets, counts, offsets, sorted_slot, slot_pos, ticket, (TileEntry*)table, rows_per_tile,
-               (int)n_entries};
-  constexpr int kTok = kBucketChunk / 64;
-  const dim3 g((T + kTok - 1) / kTok);
+  FusedTail ft{n_buckets, counts, offsets, sorted_slot, slot_pos, (TileEntry*)table, rows_per_tile, (int)n_entries};
+  const dim3 g(1);
   const size_t lds = sizeof(int) * bucket_fused_lds_ints(n_buckets);
   const int vpl = (E + 63) / 64;
 #define MOE_FSEL(V)                                                                                            \

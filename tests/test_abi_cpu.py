@@ -353,7 +353,9 @@ def test_codec_validation():
 def test_route_bucket_validation():
     L = m.lib()
     need = L.moe_route_bucket_workspace_bytes(4, 64, 8, 2, 0)
-    assert need >= L.moe_route_workspace_bytes(4, 64, 8) + 4
+    assert need >= L.moe_route_workspace_bytes(4, 64, 8)
+    big = L.moe_route_bucket_workspace_bytes(3000, 64, 8, 2, 0)  # router partials + bucketing scratch
+    assert big >= L.moe_route_workspace_bytes(3000, 64, 8) + L.moe_bucket_workspace_bytes(6000, 8)
     W = weights(E=8)
 
     def rb(T=4, E=8, k=2, S=0, Wp=None, ws=fake(0x8000), wsb=need, fws=fake(0x40000), fwsb=1 << 24, ids=fake(0x200)):

@@ -502,16 +502,17 @@ def test_graph_replay_equals_eager(name, T):
 # ------------------------------------------------------------------------------------------------
 # moe_route_bucket (router + bucketing + tile plan in one call) against the separate calls
 # ------------------------------------------------------------------------------------------------
-RB_CASES = [("tiny", 16), ("decode", 1), ("decode", 8), ("sweep", 176), ("sweep", 255), ("sweep", 256),
-            ("sweep", 300), ("prefill", 8192)]
+RB_CASES = [("tiny", 16), ("decode", 1), ("decode", 8), ("sweep", 1), ("sweep", 5), ("sweep", 8), ("sweep", 9),
+            ("sweep", 176), ("sweep", 300), ("prefill", 8), ("prefill", 8192)]
 
 
 @pytest.mark.parametrize("name,T", RB_CASES, ids=[f"{n}-T{t}" for n, t in RB_CASES])
 def test_route_bucket_equals_separate_calls(name, T):
     """Same ids, weights, probabilities, bucket arrays and tile table bit for bit, and the same
     expert-FFN output, from one moe_route_bucket call as from moe_route -> moe_bucket ->
-    moe_expert_ffn_plan: through the fused two-launch path up to 2048 slots (sweep T = 255 and
-    256 end at the boundary) and the separate kernels above it."""
+    moe_expert_ffn_plan: through the two-launch path (one selecting and bucketing workgroup) up to
+    8 tokens -- sweep T = 8 and 9 sit on either side of the boundary, prefill T = 8 adds a shared
+    expert -- and the separate kernels above it."""
     wl = synth.WORKLOADS[name]
     note(f"route_bucket {name} T={T}")
     import dataclasses
@@ -531,7 +532,7 @@ def test_route_bucket_equals_separate_calls(name, T):
     p_b = torch.full_like(p_a, -7.0)
     b_b = moe.Buckets(*(torch.full_like(v, -7) for v in (b_a.counts, b_a.offsets, b_a.sorted_slot, b_a.slot_pos)))
     ws_b = torch.zeros_like(ws_a)
-    for rep in range(2):  # the second call reuses the workspace (its counter was reset by the first)
+    for rep in range(2):  # the second call reuses the workspace
         moe.moe_route_bucket(t["x"], t["router"], k, t["bias"], S, ids_b, w_b, b_b, W, ws_b, probs=p_b)
         for a, b in ((ids_a, ids_b), (w_a, w_b), (p_a, p_b), (b_a.counts, b_b.counts), (b_a.offsets, b_b.offsets),
                      (b_a.sorted_slot, b_b.sorted_slot), (b_a.slot_pos, b_b.slot_pos)):

@@ -61,9 +61,9 @@ moe_status check_proj(const moe_proj& p, moe_w_format fmt, int n_experts, int N,
 }
 
 moe::ProjDev dev(const moe_proj& p);
-// The FFN's tile-size choice, derived from the weights description alone (see ffn_big_tiles).
-bool big_tiles(const moe_expert_weights* W, int T, int k_total) {
-  return moe::ffn_big_tiles(W->fmt, T, k_total, W->hidden, W->inter, dev(W->gate), dev(W->up), dev(W->down));
+// The FFN's kernel-choice flags, derived from the weights description alone (see ffn_plan_opts).
+int plan_opts(const moe_expert_weights* W, int T, int k_total) {
+  return moe::ffn_plan_opts(W->fmt, T, k_total, W->hidden, W->inter, dev(W->gate), dev(W->up), dev(W->down));
 }
 
 moe::ProjDev dev(const moe_proj& p) {
@@ -199,7 +199,7 @@ size_t moe_expert_ffn_workspace_bytes(int T, int k_total, const moe_expert_weigh
   // h as a high plane and a low plane of 16-bit values, one row of `inter` per sorted slot,
   // then the tile table shared by the two phases
   const size_t plane = round_up(sizeof(uint16_t) * (size_t)T * (size_t)k_total * (size_t)W->inter, 256);
-  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts, big_tiles(W, T, k_total)), 256);
+  return 2 * plane + round_up(moe::ffn_table_bytes(T, k_total, W->n_experts, plan_opts(W, T, k_total)), 256);
 }
 
 }  // extern "C"
@@ -254,7 +254,7 @@ moe_status moe_expert_ffn_plan(moe_act_dtype x_dtype, int T, int k_total, const 
   moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, offsets, nullptr, false, false, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total), offsets, table,
+  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, plan_opts(W, T, k_total), offsets, table,
                                          (hipStream_t)stream));
 }
 
@@ -267,7 +267,7 @@ moe_status moe_expert_ffn_gateup(const void* x, moe_act_dtype x_dtype, int T, in
   moe_status st = check_ffn(x, x_dtype, T, k_total, W, offsets, sorted_slot, nullptr, true, false, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, big_tiles(W, T, k_total), W->hidden,
+  return hip_status(moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, plan_opts(W, T, k_total), W->hidden,
                                            W->inter, dev(W->gate),
                                            dev(W->up), sorted_slot, h_hi, h_lo, table, (hipStream_t)stream));
 }
@@ -281,7 +281,7 @@ moe_status moe_expert_ffn_down(moe_act_dtype x_dtype, int T, int k_total, const 
   moe_status st = check_ffn(nullptr, x_dtype, T, k_total, W, offsets, sorted_slot, y_slots, false, true, workspace,
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, big_tiles(W, T, k_total), W->hidden,
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, plan_opts(W, T, k_total), W->hidden,
                                          W->inter, dev(W->down),
                                          sorted_slot, y_slots, h_hi, h_lo, table, (hipStream_t)stream));
 }
@@ -296,13 +296,13 @@ moe_status moe_expert_ffn(const void* x, moe_act_dtype x_dtype, int T, int k_tot
                             workspace_bytes, &h_hi, &h_lo, &table);
   if (st != MOE_OK) return st;
   const int H = W->hidden, I = W->inter;
-  const bool big = big_tiles(W, T, k_total);
-  hipError_t err = moe::launch_ffn_plan(T, k_total, W->n_experts, big, offsets, table, (hipStream_t)stream);
+  const int opts = plan_opts(W, T, k_total);
+  hipError_t err = moe::launch_ffn_plan(T, k_total, W->n_experts, opts, offsets, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, big, H, I, dev(W->gate), dev(W->up), sorted_slot,
+  err = moe::launch_ffn_gateup(x, T, k_total, W->fmt, W->n_experts, opts, H, I, dev(W->gate), dev(W->up), sorted_slot,
                                h_hi, h_lo, table, (hipStream_t)stream);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, big, H, I, dev(W->down), sorted_slot, y_slots,
+  return hip_status(moe::launch_ffn_down(T, k_total, W->fmt, W->n_experts, opts, H, I, dev(W->down), sorted_slot, y_slots,
                                          h_hi, h_lo, table, (hipStream_t)stream));
 }
 
@@ -593,7 +593,7 @@ moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, 
     const moe_status st = check_ffn(nullptr, xdt, T, k_total, W, offsets, offsets, nullptr, false, false,
                                     ffn_workspace, ffn_workspace_bytes, &h_hi, &h_lo, &table);
     if (st != MOE_OK) return st;
-    pl = moe::ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total));
+    pl = moe::ffn_plan(T, k_total, W->n_experts, plan_opts(W, T, k_total));
   }
   const size_t need = moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
@@ -607,14 +607,14 @@ moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, 
   if (moe::route_bucket_fusable(T, k_total, n_buckets))
     return hip_status(moe::launch_route_bucket(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k,
                                                n_shared, ids, weights, probs, partial, splits, n_buckets, counts,
-                                               offsets, sorted_slot, slot_pos, table, 16 * pl.mt, pl.tiles, st));
+                                               offsets, sorted_slot, slot_pos, table, pl.rpt, pl.tiles, st));
   hipError_t err = moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k, n_shared, ids,
                                      weights, probs, partial, splits, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
   err = moe::launch_bucket(ids, T * k_total, n_buckets, counts, offsets, sorted_slot, slot_pos, bws, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
   if (!W) return MOE_OK;
-  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, big_tiles(W, T, k_total), offsets, table, st));
+  return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, plan_opts(W, T, k_total), offsets, table, st));
 }
 
 }  // extern "C"

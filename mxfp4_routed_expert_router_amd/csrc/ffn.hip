@@ -885,6 +885,224 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------
+// Down for tiny calls (at most kTinyT tokens, so no tile has more rows than that): each wave owns
+// 16 rows of H over the whole reduction dimension (no cross-wave sums) and issues every load it
+// needs at once -- its share of the tile's h rows straight into LDS (buffer loads with the LDS
+// destination, so they hold no registers), then its rows' block scales, then all of their weight
+// chunks -- so a wave waits for one memory round trip instead of one per pair of chunks.  MFMA
+// columns past the tile's rows take zeros (those lanes read no LDS).
+// ------------------------------------------------------------------------------------------------
+constexpr int kTinyNC = 16, kTinyNW = 4;  // (kTinyT: launch.hpp)
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    float* __restrict__ y_slots) {
+  typedef bf16x8 V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [plane][kTinyT][I] bf16
+  int tile, nblk;
+  xcd_work(blockIdx.x, n_nblk, tile, nblk);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, kTinyT);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = (nblk * kTinyNW + wave) * 16;
+  const int ex = __builtin_amdgcn_readfirstlane(ti.e);
+  const int nc = I >> 7;  // chunks of 128 along I, at most kTinyNC
+
+  // h rows of the tile: piece f of a plane (16 bytes) is column f % (I/8) of row f / (I/8); the
+  // LDS copy holds them in that order, so each wave's load instruction fills 1 KB of LDS in lane
+  // order.  Rows past the tile's (and pieces past the plane) read nothing.
+  const int hp = I >> 3, per_plane = kTinyT * hp;
+  const __amdgpu_buffer_rsrc_t hr[2] = {make_rsrc(h_hi, (int64_t)n_slots * I * 2), make_rsrc(h_lo, (int64_t)n_slots * I * 2)};
+#pragma unroll
+  for (int plane = 0; plane < 2; ++plane)
+#pragma unroll
+    for (int j = 0; j < kTinyT * kTinyNC * 16 / (kTinyNW * 64); ++j) {
+      const int fw = 256 * j + 64 * wave;  // the wave's first piece (uniform)
+      if (fw < per_plane) {
+        const int f = fw + lane, t = f / hp, col = f - t * hp;
+        const uint32_t off = t < ti.nr ? (uint32_t)(ti.r0 + t) * (uint32_t)I * 2u + 16u * col : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr[plane], (lds_void*)(lds + plane * per_plane * 16 + 16 * fw), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
+  const int row = min(n0 + l16, H - 1);
+  // the row's block scales, 16 bytes per load (scale rows 16-byte aligned, I / 32 a multiple of
+  // 16): block 4c + lq of chunk c is byte lq of dword c
+  u32x4 sv[kTinyNC / 4];
+#pragma unroll
+  for (int u = 0; u < kTinyNC / 4; ++u) sv[u] = bld16(sr, 16 * u < I / 32 ? (uint32_t)(row * down.sr) + 16u * u : kOutOfRange);
+  u32x4 q[kTinyNC];
+  const uint32_t coff = (uint32_t)(row * down.wr) + 16u * lq;
+#pragma unroll
+  for (int c = 0; c < kTinyNC; ++c) q[c] = bld16(wr, c < nc ? coff + 64u * c : kOutOfRange);
+  __syncthreads();  // the h pieces of every wave are in LDS
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool tok = l16 < ti.nr;
+  const uint8_t* hb = lds + (l16 < kTinyT ? l16 : 0) * I * 2 + 64 * lq;
+#pragma unroll
+  for (int c = 0; c < kTinyNC; ++c) {
+    if (c < nc) {  // uniform
+      const float scale = e8m0_to_f32((sv[c >> 2][c & 3] >> (8 * lq)) & 0xFFu);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const V a = decode8_bf16(q[c][s4], scale);
+        V bh = V{}, bl = V{};
+        if (tok) {
+          bh = *reinterpret_cast<const V*>(hb + 256 * c + 16 * s4);
+          bl = *reinterpret_cast<const V*>(hb + per_plane * 16 + 256 * c + 16 * s4);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane (token l16, quarter lq) holds rows n0 + 4 lq .. + 3 of its token
+  if (tok) {
+    const int sl = sorted_slot[ti.r0 + l16];
+    const int n = n0 + 4 * lq;
+    if (sl >= 0 && sl < n_slots) {
+      float* dst = y_slots + (int64_t)sl * H + n;
+      if ((H & 3) == 0 && n + 3 < H) {
+        *reinterpret_cast<f32x4*>(dst) = acc;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < H) dst[i] = acc[i];
+      }
+    }
+  }
+}
+
+// Gate/up for the same tiny calls: the K-split streaming structure (four waves share a 16-row block
+// of each of gate and up, each over a quarter of K, and meet in LDS for SwiGLU), with the whole of
+// x -- at most kTinyT rows -- staged once in LDS by buffer loads with the LDS destination, and the
+// weights kTinyDepth chunks deep in registers.  The streaming kernel's activation registers (four
+// 16-byte loads per chunk) become LDS reads, which leaves room for the deeper weight pipeline.
+constexpr int kTinyDepth = 4, kTinyGuT = 2;
+
+__global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
+    const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+  constexpr int NW = kTinyNW, D = kTinyDepth;
+  typedef bf16x8 V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // x [T][H] | scale tables | sums
+  const int n_slots = T * k_total;
+  int tile, nblk;
+  xcd_work(blockIdx.x, n_nblk, tile, nblk);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, kTinyT);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = nblk * 16;
+  const int e = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = H >> 7, cpw = (n_chunks + NW - 1) / NW;
+  const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
+
+  // x: piece f (16 bytes) = token f / (H/8), column f % (H/8), at LDS byte 16 f; T * H / 8 is a
+  // multiple of 64 (H % 512 == 0), so every load instruction fills 1 KB inside the x region
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
+  const int n_x = T * (H >> 3);
+  for (int fw = 64 * wave; fw < n_x; fw += 64 * NW)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(lds + 16 * fw), 16, 16u * (uint32_t)(fw + lane), 0, 0, 0);
+
+  const __amdgpu_buffer_rsrc_t wr[2] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
+                                        make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
+  const __amdgpu_buffer_rsrc_t sr[2] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
+                                        make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
+  const int row = min(n0 + l16, I - 1);  // rows past I repeat the last row; never stored
+  const uint32_t coff[2] = {(uint32_t)(row * gate.wr) + 16u * lq, (uint32_t)(row * up.wr) + 16u * lq};
+  u32x4 q[D][2];
+  auto load = [&](int c, u32x4 (&d)[2]) {  // chunks past the wave's share read nothing
+#pragma unroll
+    for (int m = 0; m < 2; ++m) d[m] = bld16(wr[m], c < c1 ? coff[m] + 64u * c : kOutOfRange);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(c0 + d, q[d]);
+
+  // scale table of the wave's share: dword (m * 16 + r) * cpw + j holds the four block scales of
+  // chunk c0 + j of row n0 + r of matrix m (gate, up)
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + (size_t)T * H * 2 + wave * stab_bytes(32, cpw));
+  {
+    const int total = 16 * cpw;
+    fill_table<2, 4, uint32_t>(
+        total, lane,
+        [&](int m, int f) {
+          const int r = f / cpw, j = f - r * cpw;
+          const int n = min(n0 + r, I - 1), c = min(c0 + j, n_chunks - 1);
+          return bld4(sr[m], f < total ? (uint32_t)(n * (m ? up.sr : gate.sr)) + 4u * c : kOutOfRange);
+        },
+        [&](int m, int f, uint32_t v) { stab[m * total + f] = v; });
+  }
+  // the token of this lane's MFMA column (a row of the tile), or -1 past the tile's rows
+  int tok = -1;
+  if (l16 < ti.nr) {
+    const int sl = sorted_slot[ti.r0 + l16];
+    if (sl >= 0 && sl < n_slots) tok = sl / k_total;
+  }
+  const uint8_t* xrow = lds + (size_t)(tok > 0 ? tok : 0) * H * 2 + 64 * lq;
+  __syncthreads();  // x in LDS
+
+  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int c, const u32x4 (&d)[2]) {
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
+    const float sg = e8m0_to_f32(sc[4 * cpw * l16]);
+    const float su = e8m0_to_f32(sc[4 * cpw * (16 + l16)]);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      V b = V{};
+      if (tok >= 0) b = *reinterpret_cast<const V*>(xrow + 256 * c + 16 * s4);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(d[0][s4], sg), b, accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(d[1][s4], su), b, accu, 0, 0, 0);
+    }
+  };
+  // ring of D register sets: chunk c in set (c - c0) % D, refilled with chunk c + D once used
+  for (int c = c0; c < c1; c += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c + d < c1) compute(c + d, q[d]);  // uniform
+      load(c + d + D, q[d]);
+    }
+  }
+
+  // cross-wave sums of the K shares, then SwiGLU
+  float* red = reinterpret_cast<float*>(lds + (size_t)T * H * 2 + NW * stab_bytes(32, cpw));  // [NW][2][256]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[(wave * 2 + 0) * 256 + lane * 4 + i] = accg[i];
+    red[(wave * 2 + 1) * 256 + lane * 4 + i] = accu[i];
+  }
+  __syncthreads();
+  {
+    const int o = threadIdx.x;  // one (row, token) per thread: 256 = 16 rows x 16 tokens
+    const int rr = o & 15, tt = o >> 4;
+    const int qq = (16 * (rr >> 2) + tt) * 4 + (rr & 3);
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      g += red[(w * 2 + 0) * 256 + qq];
+      u += red[(w * 2 + 1) * 256 + qq];
+    }
+    const int n = n0 + rr;
+    if (n < I && tt < ti.nr) {
+      const float h = (g / (1.0f + expf(-g))) * u;
+      uint16_t hi, lo;
+      Op<MOE_W_MXFP4>::split(h, hi, lo);
+      const int64_t idx = (int64_t)(ti.r0 + tt) * I + n;
+      h_hi[idx] = hi;
+      h_lo[idx] = lo;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Row-split streaming variants (many active experts).  The waves of a workgroup (4 or 8) own
 // different weight rows, each over the whole reduction dimension, so no cross-wave reduction is
 // needed; the activation (or h) chunk of the tile's tokens is shared: each wave loads a part of
@@ -1806,7 +2024,17 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
   const bool small = pl.tiles * nb8 < kGuSmallBlocks;
   const int nw = small ? kGuNWSmall : kGuNW;
   const int nb_rows = (I + 16 * nw - 1) / (16 * nw);
-  if (MT == 1 && streamable && gateup_rows_lds(H, 1, nw) <= kMaxLds && pl.tiles * nb8 >= kRowsMinBlocks) {
+  const int tiny_cpw = (H / 128 + kTinyNW - 1) / kTinyNW;
+  const size_t tiny_lds = (size_t)T * H * 2 + (size_t)kTinyNW * stab_bytes(32, tiny_cpw) + (size_t)kTinyNW * 2 * 256 * 4;
+  // (pl.tiny: T <= kTinyT.)  Measured on the sweep layer against the streaming kernel: T = 1 31.3 ->
+  // 29.4 us, T = 2 56.5 -> 52.8 us, but T = 4 105 -> 109 us (x for 4 tokens takes 56 KB of LDS per
+  // workgroup and halves the workgroups per CU), so up to kTinyGuT tokens.
+  if (MT == 1 && streamable && pl.tiny && T <= kTinyGuT && H % 512 == 0 && tiny_lds <= kMaxLds) {
+    const int nb = (I + 15) / 16;
+    const size_t lds = tiny_lds;
+    ffn_gateup_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, lds, stream>>>(
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
+  } else if (MT == 1 && streamable && gateup_rows_lds(H, 1, nw) <= kMaxLds && pl.tiles * nb8 >= kRowsMinBlocks) {
     const dim3 grid((unsigned)(pl.tiles * nb_rows));
     if (small)
       ffn_gateup_rows_kernel<kGuNWSmall, 1><<<grid, kGuNWSmall * 64, gateup_rows_lds(H, 1, nw), stream>>>(
@@ -1834,7 +2062,11 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const bool small = pl.tiles * nb8 < kDnSmallBlocks;
   const int nw = small ? kDnNWSmall : kDnNW;
   const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
-  if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
+  if (MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
+    const int nb = H / (16 * kTinyNW);
+    ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2, stream>>>(
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
+  } else if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
     const dim3 grid((unsigned)(pl.tiles * nb_rows));
     if (small)
       ffn_down_lines_kernel<kDnNWSmall><<<grid, kDnNWSmall * 64, down_rows_lds(I, nw), stream>>>(
@@ -1879,7 +2111,7 @@ hipError_t ffn_range_fmt(const FfnPlan& pl, const void* x, int T, int k_total, i
   }
 }
 
-// The tile kernels (planned only when ffn_big_tiles() holds for the call).
+// The tile kernels (planned only when ffn_plan_opts() gives kPlanBig for the call).
 template <int FMT>
 hipError_t gateup_tile(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                        const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
@@ -1929,8 +2161,8 @@ hipError_t launch_ffn_range(const void* x, int T, int k_total, int fmt, int n_ex
                             ProjDev up, ProjDev down, const int32_t* offsets, const int32_t* sorted_slot,
                             uint16_t* h_hi, uint16_t* h_lo, void* table, int att_log2, uint16_t* y16,
                             hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts, false);
-  hipError_t err = launch_ffn_plan(T, k_total, n_experts, false, offsets, table, stream);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, 0);
+  hipError_t err = launch_ffn_plan(T, k_total, n_experts, 0, offsets, table, stream);
   if (err != hipSuccess) return err;
   const float u_scale = ldexpf(1.0f, -att_log2);
   const TileEntry* tiles = (const TileEntry*)table;
@@ -1947,27 +2179,35 @@ hipError_t launch_ffn_range(const void* x, int T, int k_total, int fmt, int n_ex
                                     y16, stream);
 }
 
-bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
-                   const ProjDev& down) {
-  return (fmt == MOE_W_MXFP4 || fmt == MOE_W_FP16) && stream_ok(gate, H, I) && stream_ok(up, H, I) && stream_ok(down, I, H) &&
-         (int64_t)T * H * 2 < INT32_MAX && (int64_t)T * k_total * I * 2 < INT32_MAX;
+int ffn_plan_opts(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
+                  const ProjDev& down) {
+  const bool offs = (int64_t)T * H * 2 < INT32_MAX && (int64_t)T * k_total * I * 2 < INT32_MAX;
+  const bool streams = stream_ok(gate, H, I) && stream_ok(up, H, I) && stream_ok(down, I, H) && offs;
+  int opts = 0;
+  if ((fmt == MOE_W_MXFP4 || fmt == MOE_W_FP16) && streams) opts |= kPlanBig;
+  if (fmt == MOE_W_MXFP4 && streams && T <= kTinyT && I <= 128 * kTinyNC && I % 512 == 0 && H % (16 * kTinyNW) == 0 &&
+      (down.sr & 15) == 0 && (down.se & 15) == 0 && ((uintptr_t)down.s & 15) == 0)
+    opts |= kPlanTiny;
+  return opts;
 }
 
-FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big) {
+FfnPlan ffn_plan(int T, int k_total, int n_experts, int opts) {
   // Tokens per tile from the mean rows per active expert (known on the host without a sync).
   const int64_t rows = (int64_t)T * k_total;
   const int64_t active = rows < n_experts ? rows : n_experts;
   const double mean = (double)rows / (double)(active > 0 ? active : 1);
   FfnPlan p;
   p.n_experts = n_experts;
-  p.tile = big && mean > 32.0;  // 16 * kTileMT-token tiles on the tile kernels
+  p.tile = (opts & kPlanBig) && mean > 32.0;  // 16 * kTileMT-token tiles on the tile kernels
+  p.tiny = !p.tile && (opts & kPlanTiny) && T <= kTinyT;
   p.mt = p.tile ? kTileMT : (mean <= 16.0 ? 1 : (mean <= 32.0 ? 2 : 4));
-  p.tiles = (max_tiles(rows, n_experts, 16 * p.mt) + kXcds - 1) / kXcds * kXcds;
+  p.rpt = p.tiny ? kTinyT : 16 * p.mt;
+  p.tiles = (max_tiles(rows, n_experts, p.rpt) + kXcds - 1) / kXcds * kXcds;
   return p;
 }
 
-size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big) {
-  return (size_t)ffn_plan(T, k_total, n_experts, big).tiles * sizeof(TileEntry);
+size_t ffn_table_bytes(int T, int k_total, int n_experts, int opts) {
+  return (size_t)ffn_plan(T, k_total, n_experts, opts).tiles * sizeof(TileEntry);
 }
 
 hipError_t launch_ffn_tiles(const int32_t* offsets, int n_experts, int n_rows, int rows_per_tile, int64_t n_entries,
@@ -1977,18 +2217,17 @@ hipError_t launch_ffn_tiles(const int32_t* offsets, int n_experts, int n_rows, i
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, int opts, const int32_t* offsets, void* table,
                            hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
-  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, 16 * pl.mt, (int)pl.tiles,
-                                           (TileEntry*)table);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, opts);
+  ffn_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, n_experts, T * k_total, pl.rpt, (int)pl.tiles, (TileEntry*)table);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, bool big, int H, int I,
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int opts, int H, int I,
                              ProjDev gate, ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
                              const void* table, hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, opts);
   const TileEntry* tiles = (const TileEntry*)table;
   if (pl.tile) {
     if (fmt == MOE_W_FP16)
@@ -2004,10 +2243,10 @@ hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_e
   return gateup_fmt<MOE_W_MXFP4>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
 }
 
-hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big, int H, int I, ProjDev down,
+hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int opts, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream) {
-  const FfnPlan pl = ffn_plan(T, k_total, n_experts, big);
+  const FfnPlan pl = ffn_plan(T, k_total, n_experts, opts);
   const TileEntry* tiles = (const TileEntry*)table;
   if (pl.tile) {
     if (fmt == MOE_W_FP16)

@@ -49,29 +49,37 @@ struct ProjDev {
 // Tile plan of one expert-FFN call: 16*mt sorted rows per tile, `tiles` entries in the tile table
 // (an upper bound, padded to a multiple of the XCD count).
 struct FfnPlan {
-  int mt;  // 16*mt sorted rows (tokens) per tile
+  int mt;   // token tiles of 16 per MFMA column block (the kernels' MT)
+  int rpt;  // sorted rows (tokens) per tile: 16 * mt, or kTinyT for the tiny down kernel
   int64_t tiles;
   int n_experts;
   bool tile;  // the tile kernels (MXFP4, many rows per expert)
+  bool tiny;  // the tiny down kernel (at most kTinyT tokens)
 };
-// Whether calls with many rows per expert may use the 128-token tile kernels (MXFP4, whole
-// 128-wide chunks, aligned scale rows, 32-bit offsets).  The three FFN entry points and the
-// workspace query must agree, so they all derive it from the same weights description.
-bool ffn_big_tiles(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
-                   const ProjDev& down);
-FfnPlan ffn_plan(int T, int k_total, int n_experts, bool big);
-size_t ffn_table_bytes(int T, int k_total, int n_experts, bool big);
+constexpr int kTinyT = 4;  // tokens of a call the tiny down kernel takes (at most kTinyT rows per tile)
+// Kernel choices that depend on the weights description, as flags for ffn_plan: kPlanBig -- calls
+// with many rows per expert may use the 128-token tile kernels (MXFP4 or FP16, whole 128-wide
+// chunks, aligned scale rows, 32-bit offsets); kPlanTiny -- calls of at most kTinyT tokens may use
+// the tiny down kernel (MXFP4, I a multiple of 512 up to 2048, H a multiple of 64, 16-byte
+// aligned scale rows).  The
+// FFN entry points and the workspace query must agree, so they all derive the flags from the same
+// weights description.
+constexpr int kPlanBig = 1, kPlanTiny = 2;
+int ffn_plan_opts(int fmt, int T, int k_total, int H, int I, const ProjDev& gate, const ProjDev& up,
+                  const ProjDev& down);
+FfnPlan ffn_plan(int T, int k_total, int n_experts, int opts);
+size_t ffn_table_bytes(int T, int k_total, int n_experts, int opts);
 // The tile table of `rows_per_tile`-row tiles for the bucket offsets (entries up to n_entries).
 hipError_t launch_ffn_tiles(const int32_t* offsets, int n_experts, int n_rows, int rows_per_tile, int64_t n_entries,
                             void* table, hipStream_t stream);
 // The plan builds the tile table in `table`; the gate/up phase reads it and writes h; the down
 // phase reads both.
-hipError_t launch_ffn_plan(int T, int k_total, int n_experts, bool big, const int32_t* offsets, void* table,
+hipError_t launch_ffn_plan(int T, int k_total, int n_experts, int opts, const int32_t* offsets, void* table,
                            hipStream_t stream);
-hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, bool big, int H, int I,
+hipError_t launch_ffn_gateup(const void* x, int T, int k_total, int fmt, int n_experts, int opts, int H, int I,
                              ProjDev gate, ProjDev up, const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo,
                              const void* table, hipStream_t stream);
-hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, bool big, int H, int I, ProjDev down,
+hipError_t launch_ffn_down(int T, int k_total, int fmt, int n_experts, int opts, int H, int I, ProjDev down,
                            const int32_t* sorted_slot, float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo,
                            const void* table, hipStream_t stream);
 

@@ -229,6 +229,23 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     # the same tile kernels on FP16 weights: ragged tiles, 3 and 5 chunks of 128
     (300, 384, 640, 3, 2, "fp16", "routed"),
     (200, 128, 256, 4, 1, "fp16", "one-expert"),
+    # at most 4 tokens: the tiny kernels (4-row tiles; down: whole-K rows per wave, h in LDS;
+    # gate/up for up to 2 tokens and H a multiple of 512: x in LDS, a 4-deep weight ring) at 1 to
+    # 16 chunks of 128 per wave; an expert chosen twice per token (8 rows: two tiles); I not a
+    # multiple of 512, H not a multiple of 64 and I above 2048 (the K-split kernels instead)
+    (1, 512, 512, 8, 4, "mxfp4", "routed"),
+    (2, 1024, 1024, 16, 4, "mxfp4", "duplicate"),
+    (2, 1536, 512, 4, 1, "mxfp4", "one-expert"),
+    (4, 1536, 512, 4, 1, "mxfp4", "one-expert"),
+    (2, 2560, 1536, 6, 2, "mxfp4", "routed"),
+    (1, 128, 512, 8, 4, "mxfp4", "routed"),
+    (2, 256, 1536, 8, 3, "mxfp4", "routed"),
+    (3, 192, 2048, 16, 4, "mxfp4", "routed"),
+    (4, 64, 512, 4, 4, "mxfp4", "duplicate"),
+    (4, 128, 1024, 4, 1, "mxfp4", "one-expert"),
+    (2, 128, 384, 8, 2, "mxfp4", "routed"),
+    (4, 96, 512, 4, 2, "mxfp4", "routed"),
+    (4, 128, 2560, 8, 2, "mxfp4", "routed"),
 ]
 
 
@@ -243,6 +260,8 @@ def test_expert_ffn_edges(orc, case):
         ids = orc.route(L.x, x_fmt(wl), L.router, L.bias, k)["ids"]
     elif pattern == "one-expert":
         ids = np.full((T, 1), 2, np.int32)
+    elif pattern == "duplicate":
+        ids = np.tile(np.array([0, 0, 1, 2][:k], np.int32), (T, 1))
     else:
         ids = np.tile(np.array([0, 2], np.int32), (T, 1))
     err = ffn_vs_oracle(orc, L, ids)

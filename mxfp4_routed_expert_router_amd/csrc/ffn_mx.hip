@@ -549,10 +549,12 @@ template <int F, bool GU>
 __global__ __launch_bounds__(kMxNW * 64, 2) void ffn_mx_kernel(
     const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_s, int n_act_rows, int k_total, int K, int N,
     ProjDev w0, ProjDev w1, const TileEntry* __restrict__ tiles, int n_experts,
-    const int32_t* __restrict__ sorted_slot, int n_slots, int n_nblk, int n_nblk_pad, uint8_t* __restrict__ h_codes,
+    const int32_t* __restrict__ sorted_slot, int n_slots, int n_nblk, int n_items, uint8_t* __restrict__ h_codes,
     uint8_t* __restrict__ h_scales, float* __restrict__ y_slots) {
-  const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
-  if (nblk >= n_nblk) return;
+  // two workgroups per CU: a chunk of 64 items is what one XCD holds at once
+  const int item = grouped_item(blockIdx.x, 2 * kCusPerXcd);
+  if (item >= n_items) return;
+  const int tile = item / n_nblk, nblk = item - tile * n_nblk;
   const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, kMxTok);
   if (ti.nr <= 0) return;
   // 16-token column tiles computed: the rows of the tile rounded up to 32
@@ -596,18 +598,21 @@ hipError_t ffn_mx_fmt(const MxFfnArgs& a, hipStream_t stream) {
   err = launch_ffn_tiles(a.offsets, a.n_experts, n_slots, kMxTok, tiles, a.table, stream);
   if (err != hipSuccess) return err;
   const size_t lds = (size_t)MxTile<F>::kLds;
+  constexpr int64_t kGroup = (int64_t)kXcds * 2 * kCusPerXcd;  // grid granule of the grouped item map
   {
-    const int nb = (a.I + kMxNW * 32 - 1) / (kMxNW * 32), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-    ffn_mx_kernel<F, true><<<dim3((unsigned)(tiles * nbp)), kMxNW * 64, lds, stream>>>(
+    const int nb = (a.I + kMxNW * 32 - 1) / (kMxNW * 32);
+    const int64_t items = tiles * nb;
+    ffn_mx_kernel<F, true><<<dim3((unsigned)((items + kGroup - 1) / kGroup * kGroup)), kMxNW * 64, lds, stream>>>(
         a.xq, a.xs, a.T, a.k_total, a.H, a.I, a.gate, a.up, (const TileEntry*)a.table, a.n_experts,
-        a.sorted_slot, n_slots, nb, nbp, a.hq, a.hs, nullptr);
+        a.sorted_slot, n_slots, nb, (int)items, a.hq, a.hs, nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   {
-    const int nb = (a.H + kMxNW * 64 - 1) / (kMxNW * 64), nbp = (nb + kXcds - 1) / kXcds * kXcds;
-    ffn_mx_kernel<F, false><<<dim3((unsigned)(tiles * nbp)), kMxNW * 64, lds, stream>>>(
+    const int nb = (a.H + kMxNW * 64 - 1) / (kMxNW * 64);
+    const int64_t items = tiles * nb;
+    ffn_mx_kernel<F, false><<<dim3((unsigned)((items + kGroup - 1) / kGroup * kGroup)), kMxNW * 64, lds, stream>>>(
         a.hq, a.hs, n_slots, a.k_total, a.I, a.H, a.down, a.down, (const TileEntry*)a.table, a.n_experts,
-        a.sorted_slot, n_slots, nb, nbp, nullptr, nullptr, a.y_slots);
+        a.sorted_slot, n_slots, nb, (int)items, nullptr, nullptr, a.y_slots);
   }
   return hipGetLastError();
 }

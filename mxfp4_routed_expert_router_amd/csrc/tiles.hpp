@@ -42,6 +42,19 @@ __device__ __forceinline__ void xcd_work(int b, int n_nblk, int& tile, int& nblk
   nblk = slot % n_nblk;
 }
 
+// Work item of workgroup b in a grouped schedule: items are numbered tile-major (item = tile * n_nblk
+// + nblk) and cut into chunks of `chunk` consecutive items, chunk c running on XCD c % 8.  With
+// `chunk` = the workgroups one XCD holds at once, the workgroups of a chunk are dispatched together
+// and stay in step, so that they share in that XCD's L2 the activation rows of their tiles (all
+// n-blocks of a tile are in one chunk when n_nblk divides it) and the weight slices of the tiles of
+// one expert -- instead of each n-block fetching every tile's activations into its own XCD.  The
+// grid holds a multiple of 8 * chunk workgroups, which makes the map a permutation.
+constexpr int kCusPerXcd = 32;
+__device__ __forceinline__ int grouped_item(int b, int chunk) {
+  const int xcd = b % kXcds, q = b / kXcds;
+  return ((q / chunk) * kXcds + xcd) * chunk + q % chunk;
+}
+
 // The tile table built by one workgroup from bucket offsets held in LDS (off[e] = first sorted row
 // of expert e, e < n_experts; `total` = valid rows), with the same entries as ffn_tiles_kernel:
 // each expert's ceil(n_e / rows_per_tile) tiles in expert order, then empty entries up to

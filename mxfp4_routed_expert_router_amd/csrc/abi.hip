@@ -611,9 +611,14 @@ moe_status moe_route_bucket(const void* x, moe_act_dtype x_dtype, int T, int H, 
   hipError_t err = moe::launch_route(x, x_dtype == MOE_ACT_FP16, T, H, w_router, logit_bias, E, top_k, n_shared, ids,
                                      weights, probs, partial, splits, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_bucket(ids, T * k_total, n_buckets, counts, offsets, sorted_slot, slot_pos, bws, st);
+  if (!W) {
+    err = moe::launch_bucket(ids, T * k_total, n_buckets, counts, offsets, sorted_slot, slot_pos, bws, st);
+    return err != hipSuccess ? MOE_ERR_HIP : MOE_OK;
+  }
+  err = moe::launch_bucket_plan(ids, T * k_total, n_buckets, counts, offsets, sorted_slot, slot_pos, bws, table,
+                                pl.rpt, pl.tiles, st);
   if (err != hipSuccess) return MOE_ERR_HIP;
-  if (!W) return MOE_OK;
+  if (moe::bucket_plans_inline(T * k_total)) return MOE_OK;
   return hip_status(moe::launch_ffn_plan(T, k_total, W->n_experts, plan_opts(W, T, k_total), offsets, table, st));
 }
 

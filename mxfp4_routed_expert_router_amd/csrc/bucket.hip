@@ -10,6 +10,7 @@
 //   up to 4 chunks : bucket_fused_kernel does rank + scan + scatter in one workgroup;
 //   more chunks    : bucket_rank_kernel -> bucket_scan_kernel -> bucket_scatter_kernel.
 #include "bucket.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
@@ -22,6 +23,18 @@ __global__ __launch_bounds__(kBucketChunk) void bucket_fused_kernel(const int32_
                                                                      int32_t* __restrict__ slot_pos) {
   extern __shared__ int lds[];
   bucket_fused_block(ids, n_slots, n_buckets, counts, offsets, sorted_slot, slot_pos, lds);
+}
+
+// bucket_fused_kernel followed, in the same workgroup, by the expert FFN's tile table built from the
+// offsets it leaves in LDS (saves the plan launch).
+__global__ __launch_bounds__(kBucketChunk) void bucket_fused_plan_kernel(
+    const int32_t* __restrict__ ids, int n_slots, int n_buckets, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_pos,
+    TileEntry* __restrict__ table, int rows_per_tile, int n_entries) {
+  extern __shared__ int lds[];
+  const int total = bucket_fused_block(ids, n_slots, n_buckets, counts, offsets, sorted_slot, slot_pos, lds);
+  tiles_from_offsets_block(fused_base(lds, n_buckets), total, n_buckets, n_slots, rows_per_tile, n_entries, table,
+                           lds);
 }
 
 // ws layout: rank [n_slots] | chunk table [n_chunks][n_buckets] (counts, then bases in place)
@@ -106,6 +119,21 @@ hipError_t launch_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t
   if (err != hipSuccess) return err;
   bucket_scatter_kernel<<<n_chunks, kBucketChunk, 0, stream>>>(ids, n_slots, n_buckets, rank, table, offsets,
                                                                sorted_slot, slot_pos);
+  return hipGetLastError();
+}
+
+static_assert(2 * kBucketChunk >= MOE_MAX_EXPERTS, "tiles_from_offsets_block covers two experts per thread");
+bool bucket_plans_inline(int n_slots) { return (n_slots + kBucketChunk - 1) / kBucketChunk <= kFusedChunks; }
+
+hipError_t launch_bucket_plan(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_slot, int32_t* slot_pos, int32_t* ws, void* table, int rows_per_tile,
+                              int64_t n_entries, hipStream_t stream) {
+  if (!bucket_plans_inline(n_slots))
+    return launch_bucket(ids, n_slots, n_buckets, counts, offsets, sorted_slot, slot_pos, ws, stream);
+  const size_t lds = sizeof(int) * bucket_fused_lds_ints(n_buckets);
+  bucket_fused_plan_kernel<<<1, kBucketChunk, lds, stream>>>(ids, n_slots, n_buckets, counts, offsets, sorted_slot,
+                                                             slot_pos, (TileEntry*)table, rows_per_tile,
+                                                             (int)n_entries);
   return hipGetLastError();
 }
 

@@ -36,6 +36,14 @@ hipError_t launch_pad_rows(const int32_t* n_rows, int T_shape, int k_total, int3
 constexpr int kBucketChunk = 512;
 hipError_t launch_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,
                          int32_t* sorted_slot, int32_t* slot_pos, int32_t* ws, hipStream_t stream);
+// Whether launch_bucket_plan builds the tile table inside the bucketing launch (one workgroup holds
+// all of the slots); otherwise the caller runs the plan launch after it.
+bool bucket_plans_inline(int n_slots);
+// launch_bucket, and for bucket_plans_inline(n_slots) the expert FFN's tile table (n_entries
+// entries of rows_per_tile rows, the entries of ffn_tiles_kernel) from the offsets it just built.
+hipError_t launch_bucket_plan(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_slot, int32_t* slot_pos, int32_t* ws, void* table, int rows_per_tile,
+                              int64_t n_entries, hipStream_t stream);
 
 // ---- expert FFN ----
 struct ProjDev {

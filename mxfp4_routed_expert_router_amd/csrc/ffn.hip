@@ -1636,7 +1636,7 @@ template <int FMT, int NW, int RT, int MT>
 __global__ __launch_bounds__(NW * 64, FMT == MOE_W_MXFP4 ? 2 : 1) void ffn_gateup_tile_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
-    int n_items, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+    int n_nblk_pad, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   constexpr int NM = 2, NTOK = 16 * MT;
   constexpr int kStage = NTOK * kTileRow;
   constexpr int LPT = NTOK * 16 / (64 * NW);  // 16-byte lane-loads of x per thread per chunk
@@ -1644,9 +1644,8 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_MXFP4 ? 2 : 1) void ffn_gateu
   typedef typename Op<FMT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_slots = T * k_total;
-  const int g = grouped_item(blockIdx.x, 2 * kCusPerXcd);  // two workgroups per CU
-  if (g >= n_items) return;
-  const int tile = g / n_nblk, nblk = g - tile * n_nblk;
+  const int tile = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - tile * n_nblk_pad;
+  if (nblk >= n_nblk) return;
   const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, NTOK);
   if (ti.nr <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1802,16 +1801,15 @@ template <int FMT, int NW>
 __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
-    int n_items, float* __restrict__ y_slots) {
+    int n_nblk_pad, float* __restrict__ y_slots) {
   constexpr int RT = 2, MT = kDnTileMT, NTOK = 16 * MT;
   constexpr int HALVES = kTileMT / kDnTileMT;     // work items per tile
   constexpr int kStage = 2 * NTOK * kTileRow;     // hi plane, then lo plane
   constexpr int LPT = 2 * NTOK * 16 / (64 * NW);  // 16-byte lane-loads of h per thread per chunk
   typedef typename Op<FMT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int g = grouped_item(blockIdx.x, 2 * kCusPerXcd);  // two workgroups per CU
-  if (g >= n_items) return;
-  const int item = g / n_nblk, nblk = g - item * n_nblk;
+  const int item = blockIdx.x / n_nblk_pad, nblk = blockIdx.x - item * n_nblk_pad;
+  if (nblk >= n_nblk) return;
   TileInfo ti = get_tile(tiles, item / HALVES, n_experts, n_slots, NTOK * HALVES);
   {  // this item's part of the tile's rows
     const int skip = (item % HALVES) * NTOK;
@@ -2113,30 +2111,25 @@ hipError_t ffn_range_fmt(const FfnPlan& pl, const void* x, int T, int k_total, i
   }
 }
 
-// The tile kernels (planned only when ffn_plan_opts() gives kPlanBig for the call), on the grouped
-// work map: a chunk of 64 items (two workgroups per CU over one XCD) covers all n-blocks of a tile
-// or two, so that the tile's activations and the expert's weights are shared in that XCD's L2.
-constexpr int64_t kTileGroup = (int64_t)kXcds * 2 * kCusPerXcd;
+// The tile kernels (planned only when ffn_plan_opts() gives kPlanBig for the call).
 template <int FMT>
 hipError_t gateup_tile(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                        const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                        hipStream_t stream) {
-  const int nb = (I + 16 * kTileRT * kNW - 1) / (16 * kTileRT * kNW);
-  const int64_t items = (int64_t)pl.tiles * nb, grid = (items + kTileGroup - 1) / kTileGroup * kTileGroup;
-  ffn_gateup_tile_kernel<FMT, kNW, kTileRT, kTileMT><<<dim3((unsigned)grid), kNW * 64,
+  const int nb = (I + 16 * kTileRT * kNW - 1) / (16 * kTileRT * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+  ffn_gateup_tile_kernel<FMT, kNW, kTileRT, kTileMT><<<dim3((unsigned)(pl.tiles * nbp)), kNW * 64,
                                                  2 * kTileMT * 16 * kTileRow, stream>>>(
-      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, (int)items, h_hi, h_lo);
+      (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, nbp, h_hi, h_lo);
   return hipGetLastError();
 }
 template <int FMT>
 hipError_t down_tile(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
                      float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
-  const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW);
-  const int64_t items = (int64_t)pl.tiles * (kTileMT / kDnTileMT) * nb;
-  const int64_t grid = (items + kTileGroup - 1) / kTileGroup * kTileGroup;
-  ffn_down_tile_kernel<FMT, kNW><<<dim3((unsigned)grid), kNW * 64, 2 * 2 * kDnTileMT * 16 * kTileRow, stream>>>(
-      h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, (int)items, y_slots);
+  const int nb = (H + 16 * 2 * kNW - 1) / (16 * 2 * kNW), nbp = (nb + kXcds - 1) / kXcds * kXcds;
+  ffn_down_tile_kernel<FMT, kNW><<<dim3((unsigned)(pl.tiles * (kTileMT / kDnTileMT) * nbp)), kNW * 64,
+                              2 * 2 * kDnTileMT * 16 * kTileRow, stream>>>(
+      h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, nbp, y_slots);
   return hipGetLastError();
 }
 

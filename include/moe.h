@@ -179,7 +179,8 @@ moe_status moe_pad_rows(const int32_t *n_rows, int T_shape, int k_total, int32_t
  * moe_route_bucket -- moe_route, then moe_bucket of its ids over n_buckets = E + n_shared, then
  * (W non-NULL) moe_expert_ffn_plan into ffn_workspace, with the same results bit for bit: for
  * T <= 8 in two launches instead of four (one workgroup selects, buckets and writes the tile
- * table), for larger T as the separate kernels.  Arguments as for those calls; W->n_experts must
+ * table), up to 2048 slots in three (the bucketing workgroup also writes the tile table), beyond
+ * that as the separate kernels.  Arguments as for those calls; W->n_experts must
  * equal E + n_shared; ffn_workspace then is the workspace that the following
  * moe_expert_ffn_gateup / moe_expert_ffn_down calls use.  workspace:
  * moe_route_bucket_workspace_bytes(T, H, E, top_k, n_shared) bytes, 16-byte aligned (it holds

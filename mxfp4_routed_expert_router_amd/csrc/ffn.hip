@@ -1167,13 +1167,14 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
                                          make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
   const __amdgpu_buffer_rsrc_t sr[NM] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
                                          make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
-  uint32_t coff[NM][RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = min(n0 + rt * 16 + l16, I - 1);
-    coff[0][rt] = (uint32_t)(n * gate.wr) + 16u * lq;
-    coff[1][rt] = (uint32_t)(n * up.wr) + 16u * lq;
-  }
+  // Weights come as whole lines: a load instruction covers 8 rows x the 128 bytes of a step (lane:
+  // row lr of the 8, 16-byte piece lc; pieces 0-3 are the step's first chunk, 4-7 its second),
+  // with the nontemporal hint.  Rows past I fall past the buffer's range and read zeros.  Each
+  // 16-row tile is turned into MFMA layout through the wave's 512-byte LDS slot, 8 rows at a time.
+  const int lr = lane >> 3, lc = lane & 7;
+  const bool lsecond = lc >= 4;  // the lane's piece is in the step's second chunk
+  const uint32_t lbase[NM] = {(uint32_t)((n0 + lr) * gate.wr) + 16u * lc, (uint32_t)((n0 + lr) * up.wr) + 16u * lc};
+  uint8_t* const tslot = lds + 2 * kGuXStage + NW * stab_bytes(NP, sstr) + wave * 512;
 
   f32x4 accg[RT], accu[RT];
 #pragma unroll
@@ -1183,18 +1184,45 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
   }
 
   struct Step {
-    u32x4 q[NM][RT][2];  // [matrix][row tile][chunk of the step]
+    u32x4 q[NM][RT][2];  // [matrix][row tile][8-row group]: whole lines of the step
   };
-  // (the second chunk of the last step of an odd chunk count reads nothing)
+  // (a piece of a missing second chunk of the last step reads nothing)
   auto load = [&](int s, Step& d) {
-    const bool two = 2 * s + 1 < n_chunks;
+    const bool in = 2 * s + (lsecond ? 1 : 0) < n_chunks;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int m = 0; m < NM; ++m) {
+      const int64_t wrm = m ? up.wr : gate.wr;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        d.q[m][rt][0] = bld16(wr[m], coff[m][rt] + 128u * s);
-        d.q[m][rt][1] = bld16(wr[m], two ? coff[m][rt] + 128u * s + 64u : kOutOfRange);
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          d.q[m][rt][g] = bld16nt(wr[m], in ? lbase[m] + (uint32_t)((16 * rt + 8 * g) * wrm) + 128u * s : kOutOfRange);
+    }
+  };
+  // chunk j of row tile rt of matrix m in MFMA layout (lane: row l16, the chunk's piece lq), in two
+  // rounds through the 512-byte slot: round g holds rows 8g .. 8g + 7 (piece c of slot row w at
+  // 64 w + 16 (c ^ ((w >> 1) & 3))), which the lanes of those rows read.  Lanes read what other
+  // lanes wrote: wavefront-scope fences and wave barriers keep the compiler's order (a wave's LDS
+  // operations run in order).
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto mfma_layout = [&](const Step& d, int m, int rt, int j) -> u32x4 {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (lsecond == (j == 1))
+        *reinterpret_cast<u32x4*>(tslot + 64 * lr + 16 * ((lc & 3) ^ ((lr >> 1) & 3))) = d.q[m][rt][g];
+      wave_sync();
+      if ((l16 >> 3) == g) {
+        const int w = l16 & 7;
+        v = *reinterpret_cast<const u32x4*>(tslot + 64 * w + 16 * (lq ^ ((w >> 1) & 3)));
       }
+      wave_sync();
+    }
+    return v;
   };
   // Activations are fetched two steps ahead, like the weights: X[s % 2] holds step s's chunks
   // until they are written to their stage, then is refilled with step s + 2's.
@@ -1219,11 +1247,17 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_gateup_rows_kern
     for (int rt = 0; rt < RT; ++rt) {
       const float sg = e8m0_to_f32(sc[4 * sstr * (0 * 16 * RT + rt * 16 + l16)]);
       const float su = e8m0_to_f32(sc[4 * sstr * (1 * 16 * RT + rt * 16 + l16)]);
+      {
+        const u32x4 w = mfma_layout(d, 0, rt, j);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const V ag = decode8_bf16(d.q[0][rt][j][k], sg), au = decode8_bf16(d.q[1][rt][j][k], su);
-        accg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, xb[k], accg[rt], 0, 0, 0);
-        accu[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au, xb[k], accu[rt], 0, 0, 0);
+        for (int k = 0; k < 4; ++k)
+          accg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(w[k], sg), xb[k], accg[rt], 0, 0, 0);
+      }
+      {
+        const u32x4 w = mfma_layout(d, 1, rt, j);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          accu[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(w[k], su), xb[k], accu[rt], 0, 0, 0);
       }
     }
   };
@@ -1407,23 +1441,54 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
-  uint32_t coff[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) coff[rt] = (uint32_t)(min(n0 + rt * 16 + l16, H - 1) * down.wr) + 16u * lq;
+  // Weights come as whole lines: a load instruction covers 8 rows x the 128 bytes of a pair (lane:
+  // row lr of the 8, 16-byte piece lc; pieces 0-3 are the pair's first chunk, 4-7 its second), with
+  // the nontemporal hint.  Rows past H fall past the buffer's range and read zeros.  Each row tile
+  // is turned into MFMA layout through the wave's 1 KB LDS slot, one chunk at a time.
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t lbase = (uint32_t)((n0 + lr) * down.wr) + 16u * lc;
+  const bool lsecond = lc >= 4;  // the lane's piece is in the pair's second chunk
+  uint8_t* const tslot = lds + 2 * kStage + NW * stab_bytes(NP, rows_stab_stride(n_chunks)) + wave * 1024;
   f32x4 acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   struct Half {
-    u32x4 q[HT][2];  // [row tile of the half][chunk of the pair]
+    u32x4 q[HT][2];  // [row tile of the half][8-row group]: whole lines of the pair
   };
-  // pair p, half th: row tiles HT * th .. HT * th + HT - 1, chunks 2p and 2p + 1
+  // pair p, half th: row tiles HT * th .. HT * th + HT - 1, chunks 2p and 2p + 1 (a piece of a
+  // missing second chunk reads nothing)
   auto load = [&](int p, int th, Half& d) {
+    const bool in = 2 * p + (lsecond ? 1 : 0) < n_chunks;
 #pragma unroll
     for (int r = 0; r < HT; ++r)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        d.q[r][j] = bld16(wr, 2 * p + j < n_chunks ? coff[HT * th + r] + 64u * (2 * p + j) : kOutOfRange);
+      for (int g = 0; g < 2; ++g)
+        d.q[r][g] = bld16nt(wr, in ? lbase + (uint32_t)((16 * (HT * th + r) + 8 * g) * down.wr) + 128u * p
+                                   : kOutOfRange);
+  };
+  // chunk j of row tile r of d in MFMA layout (lane: row l16, the chunk's 16-byte piece lq),
+  // through the wave's slot (piece c of slot row w at 64 w + 16 (c ^ ((w >> 1) & 3)): the 8 rows
+  // a read pass touches sit on distinct banks).  A lane reads what other lanes of its wave wrote:
+  // wavefront-scope fences and wave barriers keep the compiler from moving the read above the
+  // writes or the next writes above the read (a wave's LDS operations run in order, so no wait
+  // is needed in hardware).
+  auto mfma_layout = [&](const Half& d, int r, int j) -> u32x4 {
+    if (lsecond == (j == 1)) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int w = 8 * g + lr;
+        *reinterpret_cast<u32x4*>(tslot + 64 * w + 16 * ((lc & 3) ^ ((w >> 1) & 3))) = d.q[r][g];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tslot + 64 * l16 + 16 * (lq ^ ((l16 >> 1) & 3)));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return v;
   };
   auto fetch_h = [&](int p, u32x4 (&r)[LPT]) {
 #pragma unroll
@@ -1444,13 +1509,16 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
       float scale[HT];
 #pragma unroll
       for (int r = 0; r < HT; ++r) scale[r] = e8m0_to_f32(sc[4 * sstr * ((HT * th + r) * 16 + l16)]);
+      u32x4 w[HT];
+#pragma unroll
+      for (int r = 0; r < HT; ++r) w[r] = mfma_layout(d, r, j);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const V bh = *reinterpret_cast<const V*>(st + 16 * k);
         const V bl = *reinterpret_cast<const V*>(st + 16 * kRow + 16 * k);
 #pragma unroll
         for (int r = 0; r < HT; ++r) {
-          const V a = decode8_bf16(d.q[r][j][k], scale[r]);
+          const V a = decode8_bf16(w[r][k], scale[r]);
           acc[HT * th + r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[HT * th + r], 0, 0, 0);
           acc[HT * th + r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[HT * th + r], 0, 0, 0);
         }
@@ -1996,8 +2064,8 @@ void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, Pro
 // streams; below that the K-split kernels spread each expert over more workgroups.
 constexpr int64_t kRowsMinBlocks = 1024;
 constexpr size_t kMaxLds = 160 * 1024;
-size_t gateup_rows_lds(int H, int rt, int nw) {
-  return 2 * (size_t)kGuXStage + nw * (size_t)stab_bytes(2 * 16 * rt, rows_stab_stride(H / 128));
+size_t gateup_rows_lds(int H, int rt, int nw) {  // x ring, scale tables, a 512-byte transposition slot per wave
+  return 2 * (size_t)kGuXStage + nw * (size_t)stab_bytes(2 * 16 * rt, rows_stab_stride(H / 128)) + nw * 512;
 }
 // Gate/up row-split workgroups: one 16-row tile of each matrix per wave and 8 waves sharing each
 // x stage, or 4 waves when 8-wave row blocks would give fewer than kGuSmallBlocks workgroups
@@ -2011,8 +2079,8 @@ constexpr int kGuNW = 8, kGuNWSmall = 4;
 // T = 64 321 -> 318 us; from T = 128 on, 8 waves are as fast or faster: T = 176 372 against 383 us).
 constexpr int kDnNW = 8, kDnNWSmall = 4;
 constexpr int64_t kDnSmallBlocks = 4096;
-size_t down_rows_lds(int I, int nw) {
-  return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, rows_stab_stride(I / 128));
+size_t down_rows_lds(int I, int nw) {  // h ring, scale tables, a 1 KB transposition slot per wave
+  return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, rows_stab_stride(I / 128)) + nw * 1024;
 }
 
 template <int FMT, int MT>

@@ -125,6 +125,12 @@ __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 // With a wave-uniform offset part in an SGPR (added to the per-lane offset).
+// A 16-byte buffer load with the nontemporal hint (streamed data, read once): with whole 128-byte
+// lines per instruction (8 lanes per row) it reads HBM about 10% faster than plain loads; with
+// partial lines it is slower.
+__device__ __forceinline__ u32x4 bld16nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 __device__ __forceinline__ u32x4 bld16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }

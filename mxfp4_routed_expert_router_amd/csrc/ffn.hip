@@ -2073,12 +2073,11 @@ size_t gateup_rows_lds(int H, int rt, int nw) {  // x ring, scale tables, a 512-
 // T = 64 600 -> 595 us, T = 8 153 -> 159 us; two tiles per wave were slower at every T).
 constexpr int64_t kGuSmallBlocks = 4096;
 constexpr int kGuNW = 8, kGuNWSmall = 4;
-// Waves per down workgroup (they share each h stage): 8, or 4 when 8-wave row blocks would give
-// fewer than kDnSmallBlocks workgroups -- then smaller workgroups fill the chip better (measured on
-// the sweep workload with the whole-line kernel, 4 waves: T = 8 91 -> 84 us, T = 32 236 -> 229 us,
-// T = 64 321 -> 318 us; from T = 128 on, 8 waves are as fast or faster: T = 176 372 against 383 us).
-constexpr int kDnNW = 8, kDnNWSmall = 4;
-constexpr int64_t kDnSmallBlocks = 4096;
+// Waves per down workgroup (they share each h stage): 8 at every T.  (With 64-byte half-line
+// loads, 4-wave workgroups were faster below 4,096 eight-wave blocks: T = 32 236 -> 229 us.  With
+// whole-line loads 8 waves are faster throughout, side by side: T = 8 88.5 -> 87.2 us, T = 32
+// 228 -> 218 us, T = 88 346 -> 326 us.)
+constexpr int kDnNW = 8;
 size_t down_rows_lds(int I, int nw) {  // h ring, scale tables, a 1 KB transposition slot per wave
   return 2 * (size_t)DnStage::kBytes + nw * (size_t)stab_bytes(16 * kRowsRT2, rows_stab_stride(I / 128)) + nw * 1024;
 }
@@ -2126,22 +2125,17 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
                    hipStream_t stream) {
   const int n_slots = T * k_total;
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
-  const int nb8 = (H + 16 * kRowsRT2 * kDnNW - 1) / (16 * kRowsRT2 * kDnNW);
-  const bool small = pl.tiles * nb8 < kDnSmallBlocks;
-  const int nw = small ? kDnNWSmall : kDnNW;
+  const int nw = kDnNW;
   const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
   if (MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
     const int nb = H / (16 * kTinyNW);
     ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2, stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
-  } else if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 2) {
-    const dim3 grid((unsigned)(pl.tiles * nb_rows));
-    if (small)
-      ffn_down_lines_kernel<kDnNWSmall><<<grid, kDnNWSmall * 64, down_rows_lds(I, nw), stream>>>(
-          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
-    else
-      ffn_down_lines_kernel<kDnNW><<<grid, kDnNW * 64, down_rows_lds(I, nw), stream>>>(
-          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
+  } else if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 4) {
+    // (kRowsMinBlocks / 4 eight-wave blocks: the 2,048 waves that kRowsMinBlocks / 2 four-wave
+    // blocks gave before the down kernel dropped its 4-wave form)
+    ffn_down_lines_kernel<kDnNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I, nw), stream>>>(
+        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
   } else if (streamable) {
     launch_down_stream<MT, kStRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {

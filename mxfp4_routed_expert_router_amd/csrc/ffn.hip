@@ -937,11 +937,39 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
   u32x4 sv[kTinyNC / 4];
 #pragma unroll
   for (int u = 0; u < kTinyNC / 4; ++u) sv[u] = bld16(sr, 16 * u < I / 32 ? (uint32_t)(row * down.sr) + 16u * u : kOutOfRange);
+  // the weights as whole lines (nontemporal): load 2p + g covers rows n0 + 8g .. + 7 x the 128
+  // bytes of chunks 2p and 2p + 1 (lane: row lr of the 8, piece lc; pieces 4-7 are the second
+  // chunk); rows past H fall past the buffer's range and read zeros
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t lbase = (uint32_t)((n0 + lr) * down.wr) + 16u * lc;
   u32x4 q[kTinyNC];
-  const uint32_t coff = (uint32_t)(row * down.wr) + 16u * lq;
 #pragma unroll
-  for (int c = 0; c < kTinyNC; ++c) q[c] = bld16(wr, c < nc ? coff + 64u * c : kOutOfRange);
+  for (int c = 0; c < kTinyNC; ++c) {
+    const int p = c >> 1, g = c & 1;
+    q[c] = bld16nt(wr, 2 * p + (lc >> 2) < nc ? lbase + (uint32_t)(8 * g * down.wr) + 128u * p : kOutOfRange);
+  }
   __syncthreads();  // the h pieces of every wave are in LDS
+  // chunk c of the wave's 16 rows in MFMA layout (lane: row l16, the chunk's piece lq) through the
+  // wave's 1 KB slot after the h copy, as in the row-split down kernel
+  uint8_t* const tslot = lds + 2 * per_plane * 16 + wave * 1024;
+  auto mfma_layout = [&](int c) -> u32x4 {
+    const int p = c >> 1, j = c & 1;
+    if ((lc >> 2) == j) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int w = 8 * g + lr;
+        *reinterpret_cast<u32x4*>(tslot + 64 * w + 16 * ((lc & 3) ^ ((w >> 1) & 3))) = q[2 * p + g];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tslot + 64 * l16 + 16 * (lq ^ ((l16 >> 1) & 3)));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return v;
+  };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool tok = l16 < ti.nr;
@@ -950,9 +978,10 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
   for (int c = 0; c < kTinyNC; ++c) {
     if (c < nc) {  // uniform
       const float scale = e8m0_to_f32((sv[c >> 2][c & 3] >> (8 * lq)) & 0xFFu);
+      const u32x4 w = mfma_layout(c);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const V a = decode8_bf16(q[c][s4], scale);
+        const V a = decode8_bf16(w[s4], scale);
         V bh = V{}, bl = V{};
         if (tok) {
           bh = *reinterpret_cast<const V*>(hb + 256 * c + 16 * s4);
@@ -986,6 +1015,8 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
 // weights kTinyDepth chunks deep in registers.  The streaming kernel's activation registers (four
 // 16-byte loads per chunk) become LDS reads, which leaves room for the deeper weight pipeline.
 constexpr int kTinyDepth = 4, kTinyGuT = 2;
+// K share (chunks of 128) of one tiny gate/up wave: a quarter of K rounded up to whole pairs
+__host__ __device__ constexpr int tiny_gateup_cpw(int H) { return ((H / 128 + kTinyNW - 1) / kTinyNW + 1) & ~1; }
 
 __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
     const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
@@ -1003,7 +1034,7 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
   const int l16 = lane & 15, lq = lane >> 4;
   const int n0 = nblk * 16;
   const int e = __builtin_amdgcn_readfirstlane(ti.e);
-  const int n_chunks = H >> 7, cpw = (n_chunks + NW - 1) / NW;
+  const int n_chunks = H >> 7, cpw = tiny_gateup_cpw(H);  // an even share: whole chunk pairs
   const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
 
   // x: piece f (16 bytes) = token f / (H/8), column f % (H/8), at LDS byte 16 f; T * H / 8 is a
@@ -1017,15 +1048,26 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
                                         make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
   const __amdgpu_buffer_rsrc_t sr[2] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
                                         make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
-  const int row = min(n0 + l16, I - 1);  // rows past I repeat the last row; never stored
-  const uint32_t coff[2] = {(uint32_t)(row * gate.wr) + 16u * lq, (uint32_t)(row * up.wr) + 16u * lq};
-  u32x4 q[D][2];
-  auto load = [&](int c, u32x4 (&d)[2]) {  // chunks past the wave's share read nothing
+  // The weights as whole lines (nontemporal), a chunk pair per register set: load g of matrix m
+  // covers rows n0 + 8g .. + 7 x the 128 bytes of chunks 2p and 2p + 1 (lane: row lr of the 8,
+  // piece lc; pieces 4-7 are the second chunk).  Pieces past the wave's share, and rows past I
+  // (past the buffer's range), read nothing.
+  constexpr int DP = D / 2;  // chunk pairs in flight
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t lbase[2] = {(uint32_t)((n0 + lr) * gate.wr) + 16u * lc, (uint32_t)((n0 + lr) * up.wr) + 16u * lc};
+  u32x4 q[DP][2][2];  // [set][matrix][8-row group]
+  auto load = [&](int p, u32x4 (&d)[2][2]) {
+    const bool in = 2 * p + (lc >> 2) < c1;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) d[m] = bld16(wr[m], c < c1 ? coff[m] + 64u * c : kOutOfRange);
+    for (int m = 0; m < 2; ++m) {
+      const int64_t wrm = m ? up.wr : gate.wr;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) d[m][g] = bld16nt(wr[m], in ? lbase[m] + (uint32_t)(8 * g * wrm) + 128u * p : kOutOfRange);
+    }
   };
+  const int p0 = c0 >> 1, p1 = (c1 + 1) >> 1;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(c0 + d, q[d]);
+  for (int d = 0; d < DP; ++d) load(p0 + d, q[d]);
 
   // scale table of the wave's share: dword (m * 16 + r) * cpw + j holds the four block scales of
   // chunk c0 + j of row n0 + r of matrix m (gate, up)
@@ -1050,25 +1092,49 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
   const uint8_t* xrow = lds + (size_t)(tok > 0 ? tok : 0) * H * 2 + 64 * lq;
   __syncthreads();  // x in LDS
 
+  // chunk j of a matrix's 16 rows in MFMA layout (lane: row l16, the chunk's piece lq) through the
+  // wave's 1 KB slot after the reduction area, as in the row-split down kernel
+  uint8_t* const tslot = lds + (size_t)T * H * 2 + NW * stab_bytes(32, cpw) + NW * 2 * 256 * 4 + wave * 1024;
+  auto mfma_layout = [&](const u32x4 (&dm)[2], int j) -> u32x4 {
+    if ((lc >> 2) == j) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int w = 8 * g + lr;
+        *reinterpret_cast<u32x4*>(tslot + 64 * w + 16 * ((lc & 3) ^ ((w >> 1) & 3))) = dm[g];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tslot + 64 * l16 + 16 * (lq ^ ((l16 >> 1) & 3)));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return v;
+  };
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int c, const u32x4 (&d)[2]) {
+  auto compute = [&](int c, const u32x4 (&d)[2][2]) {  // chunk c of the pair held in d
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
     const float sg = e8m0_to_f32(sc[4 * cpw * l16]);
     const float su = e8m0_to_f32(sc[4 * cpw * (16 + l16)]);
+    const u32x4 wg = mfma_layout(d[0], c & 1), wu = mfma_layout(d[1], c & 1);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       V b = V{};
       if (tok >= 0) b = *reinterpret_cast<const V*>(xrow + 256 * c + 16 * s4);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(d[0][s4], sg), b, accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(d[1][s4], su), b, accu, 0, 0, 0);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wg[s4], sg), b, accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wu[s4], su), b, accu, 0, 0, 0);
     }
   };
-  // ring of D register sets: chunk c in set (c - c0) % D, refilled with chunk c + D once used
-  for (int c = c0; c < c1; c += D) {
+  // ring of DP register sets: pair p in set (p - p0) % DP, refilled with pair p + DP once used
+  for (int p = p0; p < p1; p += DP) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (c + d < c1) compute(c + d, q[d]);  // uniform
-      load(c + d + D, q[d]);
+    for (int d = 0; d < DP; ++d) {
+      if (p + d < p1) {  // uniform
+        compute(2 * (p + d), q[d]);
+        if (2 * (p + d) + 1 < c1) compute(2 * (p + d) + 1, q[d]);
+      }
+      load(p + d + DP, q[d]);
     }
   }
 
@@ -2091,8 +2157,9 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
   const bool small = pl.tiles * nb8 < kGuSmallBlocks;
   const int nw = small ? kGuNWSmall : kGuNW;
   const int nb_rows = (I + 16 * nw - 1) / (16 * nw);
-  const int tiny_cpw = (H / 128 + kTinyNW - 1) / kTinyNW;
-  const size_t tiny_lds = (size_t)T * H * 2 + (size_t)kTinyNW * stab_bytes(32, tiny_cpw) + (size_t)kTinyNW * 2 * 256 * 4;
+  const int tiny_cpw = tiny_gateup_cpw(H);
+  const size_t tiny_lds = (size_t)T * H * 2 + (size_t)kTinyNW * stab_bytes(32, tiny_cpw) + (size_t)kTinyNW * 2 * 256 * 4 +
+                          (size_t)kTinyNW * 1024;  // x, scale tables, reduction, transposition slots
   // (pl.tiny: T <= kTinyT.)  Measured on the sweep layer against the streaming kernel: T = 1 31.3 ->
   // 29.4 us, T = 2 56.5 -> 52.8 us, but T = 4 105 -> 109 us (x for 4 tokens takes 56 KB of LDS per
   // workgroup and halves the workgroups per CU), so up to kTinyGuT tokens.
@@ -2129,7 +2196,8 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
   if (MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
     const int nb = H / (16 * kTinyNW);
-    ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2, stream>>>(
+    ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2 + kTinyNW * 1024,
+                           stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
   } else if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 4) {
     // (kRowsMinBlocks / 4 eight-wave blocks: the 2,048 waves that kRowsMinBlocks / 2 four-wave

@@ -230,8 +230,9 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     (300, 384, 640, 3, 2, "fp16", "routed"),
     (200, 128, 256, 4, 1, "fp16", "one-expert"),
     # at most 4 tokens: the tiny kernels (4-row tiles; down: whole-K rows per wave, h in LDS;
-    # gate/up for up to 2 tokens and H a multiple of 512: x in LDS, a 4-deep weight ring) at 1 to
-    # 16 chunks of 128 per wave; an expert chosen twice per token (8 rows: two tiles); I not a
+    # gate/up for up to 2 tokens and H a multiple of 512: x in LDS, weights two chunk pairs deep, a
+    # wave's K share rounded to whole pairs, so that H = 512 and 1536 leave the last waves empty) at
+    # 1 to 16 chunks of 128 per wave; an expert chosen twice per token (8 rows: two tiles); I not a
     # multiple of 512, H not a multiple of 64 and I above 2048 (the K-split kernels instead)
     (1, 512, 512, 8, 4, "mxfp4", "routed"),
     (2, 1024, 1024, 16, 4, "mxfp4", "duplicate"),

@@ -292,7 +292,7 @@ def main():
         del runner, sets
 
     print("bench: read-stream peak", file=sys.stderr, flush=True)
-    read_peak, read_buf = read_stream_peak()
+    read_peak, plain_read, read_buf = read_stream_peak()
 
     head = results[args.tokens]
     t_gu = head["per"]["ffn_gateup"] / 1e3
@@ -320,6 +320,7 @@ def main():
         "weight_GBps": head["weight_bytes"] / (head["ms"] / 1e3) / 1e9,
         "weight_frac_of_hbm_peak": head["weight_bytes"] / (head["ms"] / 1e3) / HBM_PEAK,
         "read_stream_peak_GBps": read_peak / 1e9,
+        "plain_read_GBps": plain_read / 1e9,
         "weight_frac_of_read_stream_peak": head["weight_bytes"] / (head["ms"] / 1e3) / read_peak,
         "active_experts": head["active"],
         "rotation_sets": head["rotation_sets"],
@@ -378,26 +379,39 @@ def weight_pool(moe, base, n, fix=None):
 
 
 def read_stream_peak(gib=4, reps=5):
-    """Bytes/s of a plain streaming read of a large fp32 buffer (row sums of 4096 consecutive
-    values: every row one contiguous 16 KB read, best of reps) -- the practical read bandwidth this
-    chip shows in this process, beside the nominal 8 TB/s.  (A single whole-buffer torch.sum reads
-    slower, about 4 TB/s: its reduction tree, not memory, limits it.)  Returns the buffer too, for
-    the caller to free once nothing else is timed."""
+    """Practical read bandwidth of this chip in this process, beside the nominal 8 TB/s, in two forms
+    over one 4 GiB buffer (best of reps each):
+      line -- moe_stream_read: the library's streaming read with 16-byte nontemporal loads covering
+              whole 128-byte lines per wave load, the shape the streaming FFN kernels read their
+              weights in; this is the peak the kernels are compared with;
+      plain -- torch row sums of 4096 consecutive fp32 values (every row one contiguous 16 KB
+              read), an ordinary cached read.
+    (A single whole-buffer torch.sum reads slower, about 4 TB/s: its reduction tree, not memory,
+    limits it.)  Returns (line, plain, buffer); the caller frees the buffer once nothing else is
+    timed."""
     import torch
+    import mxfp4_routed_expert_router_amd as moe
     n = (gib << 30) // 4
     buf = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     rows = buf.view(-1, 4096)
-    rows.sum(1)
-    torch.cuda.synchronize()
-    best = 0.0
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        rows.sum(1)
-        b.record()
+
+    def best_of(fn):
+        fn()
         torch.cuda.synchronize()
-        best = max(best, n * 4 / (a.elapsed_time(b) / 1e3))
-    return best, buf
+        best = 0.0
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, n * 4 / (a.elapsed_time(b) / 1e3))
+        return best
+
+    line = best_of(lambda: moe.moe_stream_read(buf, sink))
+    plain = best_of(lambda: rows.sum(1))
+    return line, plain, buf
 
 
 def side_run(args):

@@ -390,6 +390,17 @@ moe_status moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int n_
                              int64_t code_row_stride, int64_t scale_row_stride, uint16_t *out,
                              void *stream);
 
+/* moe_stream_read -- a measurement utility, not a step of the layer: reads `bytes` of device memory
+ * at `buf` once, with 16-byte nontemporal loads in which consecutive lanes take consecutive 16-byte
+ * pieces (every wave load covers whole 128-byte lines, the shape in which the streaming FFN
+ * kernels read their weights), and folds them into a checksum.  Timed over a buffer much larger
+ * than the caches, it gives the practical HBM read rate that those kernels are compared with.
+ *   buf device memory, 16-byte aligned, read only; bytes a multiple of 16 (0 is a no-op);
+ *   sink one device uint32, written only when the checksum takes one fixed value, so its
+ *   contents are meaningless (it exists so that the loads cannot be removed).
+ * Errors: NULL, ALIGN (buf or bytes), HIP. */
+moe_status moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Short text for a status code (host, static storage). */
 const char *moe_status_str(moe_status status);
 /* MOE_ABI_VERSION of the built library. */

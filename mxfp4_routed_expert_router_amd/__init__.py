@@ -116,6 +116,8 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.moe_expert_ffn_mx.restype = i
         L.moe_expert_ffn_mx.argtypes = [vp, i, i, i, ctypes.POINTER(moe_expert_weights), i, vp, vp, vp, vp, st, vp]
+        L.moe_stream_read.restype = i
+        L.moe_stream_read.argtypes = [vp, st, vp, vp]
         _lib = L
     return _lib
 
@@ -427,6 +429,16 @@ def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor
     return out
 
 
+def moe_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of the contiguous device tensor `buf` once with whole-line nontemporal loads
+    (a measurement utility: timing it over a buffer far larger than the caches gives the practical
+    HBM read rate).  `sink` is a one-element int32 device tensor whose contents are meaningless."""
+    if not buf.is_contiguous() or sink.numel() < 1 or sink.dtype != torch.int32:
+        raise ValueError("moe_stream_read: needs a contiguous buffer and an int32 sink")
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf.device)),
+           "moe_stream_read")
+
+
 def _mx_fmt(fmt) -> int:
     return MX_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
 
@@ -613,7 +625,7 @@ class FixedShapeLayer:
 __all__ = ["moe_route", "moe_route_sigmoid", "moe_route_bucket", "moe_route_bucket_workspace_bytes", "moe_bucket", "moe_expert_ffn", "moe_expert_ffn_static", "moe_expert_ffn_f16",
            "moe_expert_ffn_f16_workspace_bytes", "moe_combine_restore", "moe_expert_ffn_plan", "moe_expert_ffn_gateup",
            "moe_expert_ffn_down", "moe_combine", "moe_mxfp4_dequant", "moe_mx_quantize", "moe_mx_row_bytes",
-           "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_expert_ffn_mx_workspace_layout",
+           "moe_expert_ffn_mx", "moe_expert_ffn_mx_workspace_bytes", "moe_stream_read", "moe_expert_ffn_mx_workspace_layout",
            "moe_route_workspace_bytes", "moe_bucket_workspace_bytes", "moe_expert_ffn_workspace_bytes",
            "moe_row_shape", "moe_pad_rows", "ExpertWeights", "Buckets", "MoELayer", "FixedShapeLayer", "MoEError",
            "lib"]

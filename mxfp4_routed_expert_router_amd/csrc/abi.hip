@@ -554,6 +554,13 @@ moe_status moe_mxfp4_dequant(const uint8_t* codes, const uint8_t* scales, int n_
                                         (hipStream_t)stream));
 }
 
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!buf || !sink) return MOE_ERR_NULL;
+  if (!al16(buf) || bytes % 16 != 0) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_stream_read(buf, (uint64_t)bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 extern "C" {

@@ -32,6 +32,9 @@ hipError_t launch_route_bucket(const void* x, int x_fp16, int T, int H, const fl
 hipError_t launch_pad_rows(const int32_t* n_rows, int T_shape, int k_total, int32_t* ids, float* weights,
                            hipStream_t stream);
 
+// ---- streaming-read probe (a measurement utility) ----
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // ---- bucketing ----
 constexpr int kBucketChunk = 512;
 hipError_t launch_bucket(const int32_t* ids, int n_slots, int n_buckets, int32_t* counts, int32_t* offsets,

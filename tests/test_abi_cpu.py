@@ -232,6 +232,15 @@ def test_combine_and_dequant_validation():
     assert L.moe_mxfp4_dequant(None, fake(0x100), 3, 64, 32, 2, fake(0x200), None) == NULL
 
 
+def test_stream_read_validation():
+    L = m.lib()
+    assert L.moe_stream_read(None, 0, None, None) == OK           # nothing to read
+    assert L.moe_stream_read(None, 64, fake(), None) == NULL
+    assert L.moe_stream_read(fake(), 64, None, None) == NULL
+    assert L.moe_stream_read(fake(8), 64, fake(0x100), None) == ALIGN
+    assert L.moe_stream_read(fake(), 40, fake(0x100), None) == ALIGN
+
+
 def test_workspace_queries_are_host_only():
     L = m.lib()
     assert L.moe_route_workspace_bytes(0, 64, 8) == 0

@@ -66,6 +66,25 @@ def test_dequant_strided_rows(orc):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("where", ["first", "inner", "last"])
+def test_stream_read_reaches_every_piece(where):
+    """moe_stream_read (a measurement utility) reads the whole buffer: one 16-byte piece holds the
+    value that makes the checksum write the sink, placed at the first piece, inside a later
+    workgroup's 64 KB chunk (4096 pieces) or at the very last piece of a ragged size; every other
+    piece is zero, so the sink holds that value exactly when that piece was read."""
+    magic = 0x9E3779B9
+    n16 = 4096 * 1024 + 1003                             # 1024 whole chunks plus a ragged tail
+    idx = {"first": 0, "inner": 4096 * 517 + 2049, "last": n16 - 1}[where]
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.moe_stream_read(buf, sink)
+    assert int(sync_np(sink)[0]) == 0                    # all-zero buffer: nothing written
+    buf[4 * idx] = np.int64(magic).astype(np.int32).item()
+    moe.moe_stream_read(buf, sink)
+    assert int(sync_np(sink)[0]) & 0xFFFFFFFF == magic
+    note(f"stream read: piece {idx} of {n16} reached")
+
+
 # ------------------------------------------------------------------------------------------------
 # router
 # ------------------------------------------------------------------------------------------------

@@ -3,6 +3,7 @@
 #pragma once
 #include "common.hpp"
 #include "launch.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
@@ -161,6 +162,93 @@ __device__ inline int bucket_fused_block(const int32_t* __restrict__ ids, int n_
     if (s < n_slots && s >= total) sorted_slot[s] = -1;
   }
   return total;
+}
+
+// Calls of at most kSmallSlots slots, ids already in LDS: the bucketing and the tile table without
+// histograms, with work that does not grow with the slot count.  Slot s (key k_s: its expert, or
+// n_buckets when dropped) goes to position #{j : (k_j, j) < (k_s, s)}, the stable counting sort of
+// the general path; the eight waves count over eight slots each and wave 0 adds the parts.  The
+// keys in sorted order then give everything else: wave 0 walks the sorted positions (an expert's
+// first row is where the key changes, a ballot finds the next such row, a DPP scan of the tile
+// counts places each expert's tiles, in expert order as in tiles_from_offsets_block), and every
+// bucket b takes offset = #{keys < b} and count = #{keys < b + 1} - offset by binary search.
+// sids: the n_slots ids in LDS; tmp: kSmallLdsInts ints of LDS.  Workgroup of kBucketChunk threads.
+constexpr int kSmallSlots = 64;
+constexpr int kSmallLdsInts = kBucketWaves * kSmallSlots + kSmallSlots;
+static_assert(kBucketWaves * 8 >= kSmallSlots, "eight slots per wave cover the small calls");
+__device__ inline void bucket_small_block(const int* sids, int n_slots, int n_buckets, int32_t* __restrict__ counts,
+                                          int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+                                          int32_t* __restrict__ slot_pos, TileEntry* __restrict__ table,
+                                          int rows_per_tile, int n_entries, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* part = tmp;                          // [kBucketWaves][64] partial positions
+  int* sk = tmp + kBucketWaves * kSmallSlots;  // [64] keys in sorted order
+  auto key = [&](int j) {
+    const int id = sids[j];
+    return (id < 0 || id >= n_buckets) ? n_buckets : id;
+  };
+  if (8 * wave < n_slots) {  // uniform
+    const int ks = lane < n_slots ? key(lane) : n_buckets;
+    int r = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 8 * wave + jj;
+      if (j < n_slots) {  // uniform
+        const int kj = key(j);
+        r += (kj < ks) | ((kj == ks) & (j < lane));
+      }
+    }
+    part[wave * kSmallSlots + lane] = r;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool in = lane < n_slots;
+    const int ks = in ? key(lane) : n_buckets;
+    int pos = 0;
+#pragma unroll
+    for (int w = 0; w < kBucketWaves; ++w)
+      if (8 * w < n_slots) pos += part[w * kSmallSlots + lane];  // uniform condition
+    const bool valid = in && ks < n_buckets;
+    const int total = __popcll(__ballot(valid));
+    if (valid) {
+      sorted_slot[pos] = lane;
+      if (slot_pos) slot_pos[lane] = pos;
+    } else if (in && slot_pos) {
+      slot_pos[lane] = -1;
+    }
+    if (lane >= total && in) sorted_slot[lane] = -1;
+    if (lane == 0) offsets[n_buckets] = total;
+    if (in) sk[pos] = ks;  // pos runs over 0 .. n_slots - 1, dropped slots after the valid ones
+    if (table) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const bool row = lane < total;  // sorted position `lane` holds a valid row
+      const int kp = row ? sk[lane] : 0;
+      const bool first = row && (lane == 0 || sk[lane - 1] != kp);
+      const uint64_t fm = __ballot(first);
+      const uint64_t later = lane == 63 ? 0ull : fm & (~0ull << (lane + 1));
+      const int next = later ? __builtin_ctzll(later) : total;
+      const int cnt = next - lane;  // rows of expert kp (at its first row)
+      const int ntl = first ? (cnt + rows_per_tile - 1) / rows_per_tile : 0;
+      const int incl = (int)wave_incl_scan_dpp((uint32_t)ntl);
+      const int all_tiles = __builtin_amdgcn_readlane(incl, 63);
+      for (int q = 0; q < ntl && incl - ntl + q < n_entries; ++q)
+        table[incl - ntl + q] = TileEntry{kp, lane + q * rows_per_tile, min(rows_per_tile, cnt - q * rows_per_tile), 0};
+      for (int t = all_tiles + lane; t < n_entries; t += 64) table[t] = TileEntry{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();  // sk complete
+  for (int b = tid; b < n_buckets; b += blockDim.x) {
+    int lo = 0, hi = 0;  // #{keys < b}, #{keys < b + 1}
+#pragma unroll
+    for (int step = kSmallSlots; step > 0; step >>= 1) {
+      if (lo + step <= n_slots && sk[lo + step - 1] < b) lo += step;
+      if (hi + step <= n_slots && sk[hi + step - 1] <= b) hi += step;
+    }
+    counts[b] = hi - lo;
+    offsets[b] = lo;
+  }
 }
 
 }  // namespace moe

@@ -100,6 +100,18 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 #undef MOE_DPP_ADD
   return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
 }
+// Inclusive prefix sum over the lanes of a wave in DPP steps (within rows of 16, then across rows).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t u) {
+#define MOE_DPP_SCAN(C, R) u += dpp_u32<C, R>(0u, u)
+  MOE_DPP_SCAN(kDppRowShr1, 0xF);
+  MOE_DPP_SCAN(kDppRowShr2, 0xF);
+  MOE_DPP_SCAN(kDppRowShr4, 0xF);
+  MOE_DPP_SCAN(kDppRowShr8, 0xF);
+  MOE_DPP_SCAN(kDppRowBcast15, 0xA);
+  MOE_DPP_SCAN(kDppRowBcast31, 0xC);
+#undef MOE_DPP_SCAN
+  return u;
+}
 // Maximum of an unsigned 32-bit value over the wave, returned uniform.
 __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t u) {
 #define MOE_DPP_MAXU(C, R) u = max(u, dpp_u32<C, R>(u, u))

@@ -19,7 +19,7 @@
 namespace moe {
 
 namespace {
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 
 // Round to nearest even (v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ bf16x8 to_bf16x8_rne(const float (&v)[8]) {
@@ -60,9 +60,11 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int ks = ks0; ks < ks1; ks += kU) {
-    float wv[kU][8];
-    uint16_t xv[kU][MT][8];
+  // kG groups of kU k-steps are loaded before any of them is used (two with one token tile: the
+  // 14 k-steps of a small call's slice in one memory round trip; separate arrays keep them in
+  // registers)
+  constexpr int kG = MT == 1 ? 2 : 1;
+  auto load_group = [&](int ks, float (&wv)[kU][8], uint16_t (&xv)[kU][MT][8]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       // k-steps past the slice reload the slice's last step and are skipped below
@@ -89,6 +91,8 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
         }
       }
     }
+  };
+  auto compute_group = [&](int ks, float (&wv)[kU][8], uint16_t (&xv)[kU][MT][8]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (ks + u >= ks1) break;  // uniform
@@ -136,6 +140,20 @@ __global__ __launch_bounds__(64) void route_logits_kernel(const uint16_t* __rest
         }
       }
     }
+  };
+  for (int ks = ks0; ks < ks1; ks += kG * kU) {
+    float wa[kU][8];
+    uint16_t xa[kU][MT][8];
+    load_group(ks, wa, xa);
+    if constexpr (kG == 2) {
+      float wb[kU][8];
+      uint16_t xb[kU][MT][8];
+      if (ks + kU < ks1) load_group(ks + kU, wb, xb);  // uniform
+      compute_group(ks, wa, xa);
+      if (ks + kU < ks1) compute_group(ks + kU, wb, xb);
+    } else {
+      compute_group(ks, wa, xa);
+    }
   }
   // D: lane holds experts 16*blockIdx.x + 4*lq + i of token l16 of each token tile
 #pragma unroll
@@ -165,35 +183,42 @@ __device__ __forceinline__ void select_token(const float* __restrict__ partial, 
                                              const float* __restrict__ bias, int top_k, int n_shared,
                                              int32_t* __restrict__ ids, float* __restrict__ weights,
                                              float* __restrict__ probs, float routed_scale, float shared_weight,
-                                             int t) {
+                                             int t, int* lds_ids = nullptr) {
   const int lane = threadIdx.x & 63;
   const int e0 = VPL * lane;
   float L[VPL];
-  // Sum the hidden-dimension slices in slice order (all loads issued together).  A lane past E
-  // reads the last valid lane's values and discards them.
-  float part[kMaxSplits][VPL];
+  // Sum the hidden-dimension slices in slice order, kSplitChunk slices at a time (the loads of a
+  // chunk issued together: all of them with at most 4 experts per lane).  A lane past E reads the
+  // last valid lane's values and discards them.
+  constexpr int kSplitChunk = VPL <= 4 ? kMaxSplits : 16;
 #pragma unroll
-  for (int q = 0; q < kMaxSplits; ++q) {
-    if (VEC) {
-      const float* src = partial + ((int64_t)min(q, splits - 1) * T + t) * E + min(e0, E - VPL);
-      typedef float fv __attribute__((ext_vector_type(VPL)));
-      fv val;
-      __builtin_memcpy(&val, __builtin_assume_aligned(src, VPL >= 4 ? 16 : 4 * VPL), 4 * VPL);  // workspace: 16-byte aligned
+  for (int v = 0; v < VPL; ++v) L[v] = 0.0f;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) part[q][v] = (q < splits && e0 < E) ? val[v] : 0.0f;
-    } else {
+  for (int q0 = 0; q0 < kMaxSplits; q0 += kSplitChunk) {
+    if (q0 >= splits) break;  // uniform
+    float part[kSplitChunk][VPL];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = e0 + v;
-        part[q][v] = (q < splits && e < E) ? partial[((int64_t)q * T + t) * E + e] : 0.0f;
+    for (int qq = 0; qq < kSplitChunk; ++qq) {
+      const int q = q0 + qq;
+      if (VEC) {
+        const float* src = partial + ((int64_t)min(q, splits - 1) * T + t) * E + min(e0, E - VPL);
+        typedef float fv __attribute__((ext_vector_type(VPL)));
+        fv val;
+        __builtin_memcpy(&val, __builtin_assume_aligned(src, VPL >= 4 ? 16 : 4 * VPL), 4 * VPL);  // workspace: 16-byte aligned
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) part[qq][v] = (q < splits && e0 < E) ? val[v] : 0.0f;
+      } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const int e = e0 + v;
+          part[qq][v] = (q < splits && e < E) ? partial[((int64_t)q * T + t) * E + e] : 0.0f;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    L[v] = 0.0f;
+    for (int v = 0; v < VPL; ++v)
 #pragma unroll
-    for (int q = 0; q < kMaxSplits; ++q) L[v] += part[q][v];
+      for (int qq = 0; qq < kSplitChunk; ++qq) L[v] += part[qq][v];
   }
   if constexpr (SIG) {
     // scores, and the selection keys score + bias; the winner of a round reads its score from the
@@ -247,6 +272,7 @@ __device__ __forceinline__ void select_token(const float* __restrict__ partial, 
       if (j >= k_total) break;
       const bool routed = j < top_k;
       ids[(int64_t)t * k_total + j] = routed ? my_id[z] : E + (j - top_k);
+      if (lds_ids) lds_ids[t * k_total + j] = routed ? my_id[z] : E + (j - top_k);
       weights[(int64_t)t * k_total + j] = routed ? routed_scale * (my_p[z] / psum) : shared_weight;
     }
     return;
@@ -271,44 +297,65 @@ __device__ __forceinline__ void select_token(const float* __restrict__ partial, 
       if (e < E) probs[(int64_t)t * E + e] = expf(L[v] - mx) / den;
     }
   }
-  // k rounds of wave argmax over (logit desc, index asc): the largest order key of the logits
-  // (one 32-bit DPP maximum), then the lowest index holding it -- expert e = VPL lane + v, so per
-  // v the lowest lane with a match (a ballot), then the smallest of those VPL indices.  Taken and
-  // padded experts carry key 0, below every logit's key.  The winner of round j is kept by lane
-  // j % 64 in register q = j / 64 (k_total <= MOE_MAX_SLOTS_PER_TOKEN = 4 * 64).
-  uint32_t kh[VPL];
+  // k rounds of wave argmax over (logit desc, index asc).  Each lane first sorts its VPL
+  // (order key, expert) pairs, descending by key and, among equal keys, ascending by expert (a
+  // stable exchange network on keys that start in expert order); a round is then one 32-bit DPP
+  // maximum of the lanes' heads, one ballot for the lowest lane holding it (lanes hold ascending
+  // experts, so that is the lowest index with the largest key), a read of that lane's head expert,
+  // and the winning lane dropping its head.  Padded experts carry key 0, below every logit's key.
+  // The winner of round j is kept by lane j % 64 in register q = j / 64 (k_total <=
+  // MOE_MAX_SLOTS_PER_TOKEN = 4 * 64); the probabilities and their sum follow the rounds.
+  uint32_t sk[VPL];
+  int si[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) kh[v] = (e0 + v < E) ? f32_order_key(L[v]) : 0u;
-  float psum = 0.0f;
+  for (int v = 0; v < VPL; ++v) {
+    sk[v] = (e0 + v < E) ? f32_order_key(L[v]) : 0u;
+    si[v] = e0 + v;
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+#pragma unroll
+    for (int v = VPL - 1; v > i; --v)
+      if (sk[v] > sk[v - 1]) {
+        const uint32_t tk = sk[v];
+        sk[v] = sk[v - 1];
+        sk[v - 1] = tk;
+        const int ti = si[v];
+        si[v] = si[v - 1];
+        si[v - 1] = ti;
+      }
   int my_id[4] = {0, 0, 0, 0};
-  float my_p[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t my_key[4] = {0u, 0u, 0u, 0u};
   for (int j = 0; j < top_k; ++j) {
-    uint32_t m = kh[0];
+    const uint32_t m = wave_max_u32_dpp(sk[0]);
+    const int wl = __builtin_ffsll((long long)__ballot(sk[0] == m)) - 1;  // uniform
+    const int bi = __builtin_amdgcn_readlane(si[0], wl);
+    if (lane == wl) {
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) m = max(m, kh[v]);
-    m = wave_max_u32_dpp(m);
-    int bi = INT_MAX;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const uint64_t b = __ballot(kh[v] == m);
-      if (b) bi = min(bi, VPL * (__builtin_ffsll((long long)b) - 1) + v);
+      for (int v = 0; v + 1 < VPL; ++v) {
+        sk[v] = sk[v + 1];
+        si[v] = si[v + 1];
+      }
+      sk[VPL - 1] = 0u;
     }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (e0 + v == bi) kh[v] = 0u;
-    const float bv = f32_from_order_key(m);
-    const float p = expf(bv - mx) / den;
-    psum += p;
     if ((j & 63) == lane) {
       const int q = j >> 6;
 #pragma unroll
       for (int z = 0; z < 4; ++z)
         if (z == q) {
           my_id[z] = bi;
-          my_p[z] = p;
+          my_key[z] = m;
         }
     }
   }
+  float my_p[4];
+  float psum_l = 0.0f;
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    my_p[z] = (lane + 64 * z < top_k) ? expf(f32_from_order_key(my_key[z]) - mx) / den : 0.0f;
+    psum_l += my_p[z];
+  }
+  const float psum = wave_sum_dpp(psum_l);
   const int k_total = top_k + n_shared;
 #pragma unroll
   for (int z = 0; z < 4; ++z) {
@@ -324,6 +371,7 @@ __device__ __forceinline__ void select_token(const float* __restrict__ partial, 
       wgt = 1.0f;
     }
     ids[(int64_t)t * k_total + j] = id;
+    if (lds_ids) lds_ids[t * k_total + j] = id;
     weights[(int64_t)t * k_total + j] = wgt;
   }
 }
@@ -362,11 +410,17 @@ __global__ __launch_bounds__(kBucketChunk) void route_select_bucket_kernel(
     float routed_scale, float shared_weight, FusedTail ft) {
   extern __shared__ int lds[];
   const int t = threadIdx.x >> 6;  // one workgroup: T <= kFusedTokens
+  const int n_slots = T * (top_k + n_shared);
+  const bool small = n_slots <= kSmallSlots;  // uniform: the ids stay in LDS for the small path
   if (t < T)
     select_token<VPL, VEC, SIG>(partial, splits, T, E, bias, top_k, n_shared, ids, weights, probs, routed_scale,
-                                shared_weight, t);
+                                shared_weight, t, small ? lds : nullptr);
   __syncthreads();
-  const int n_slots = T * (top_k + n_shared);
+  if (small) {
+    bucket_small_block(lds, n_slots, ft.n_buckets, ft.counts, ft.offsets, ft.sorted_slot, ft.slot_pos, ft.table,
+                       ft.rows_per_tile, ft.n_entries, lds + kSmallSlots);
+    return;
+  }
   const int total = bucket_fused_block(ids, n_slots, ft.n_buckets, ft.counts, ft.offsets, ft.sorted_slot,
                                        ft.slot_pos, lds);
   if (ft.table)
@@ -473,7 +527,7 @@ hipError_t launch_route_bucket(const void* x, int x_fp16, int T, int H, const fl
   if (err != hipSuccess) return err;
   FusedTail ft{n_buckets, counts, offsets, sorted_slot, slot_pos, (TileEntry*)table, rows_per_tile, (int)n_entries};
   const dim3 g(1);
-  const size_t lds = sizeof(int) * bucket_fused_lds_ints(n_buckets);
+  const size_t lds = sizeof(int) * std::max<size_t>(bucket_fused_lds_ints(n_buckets), kSmallSlots + kSmallLdsInts);
   const int vpl = (E + 63) / 64;
 #define MOE_FSEL(V)                                                                                            \
   {                                                                                                            \

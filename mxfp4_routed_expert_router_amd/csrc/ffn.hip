@@ -1168,6 +1168,169 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
   }
 }
 
+// Gate/up of the K-split calls with one token tile (too few tiles for the row-split kernels, more
+// tokens than the tiny kernel stages, e.g. 3 to about 10 tokens of the sweep layer): the tiny
+// kernel's structure -- four waves share a 16-row block of each of gate and up, each over a
+// quarter of K in whole chunk pairs, and meet in LDS for SwiGLU; weights as whole 128-byte lines
+// with the nontemporal hint, turned into MFMA layout through a per-wave LDS slot -- with the
+// tile's activations read per chunk pair from global memory (the tokens' rows stay in L2) into the
+// same register ring as the weights, DP chunk pairs deep.  (Against the K-split kernel with
+// half-line loads, side by side: sweep T = 4 180.5 -> 175.5 us, T = 8 265.2 -> 259.3 us.)
+template <int DP>
+__global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_split_lines_kernel(
+    const uint16_t* __restrict__ x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
+    const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+  constexpr int NW = kTinyNW;
+  typedef bf16x8 V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // scale tables | sums | slots
+  const int n_slots = T * k_total;
+  int tile, nblk;
+  xcd_work(blockIdx.x, n_nblk, tile, nblk);
+  const TileInfo ti = get_tile(tiles, tile, n_experts, n_slots, 16);
+  if (ti.nr <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int n0 = nblk * 16;
+  const int e = __builtin_amdgcn_readfirstlane(ti.e);
+  const int n_chunks = H >> 7, cpw = tiny_gateup_cpw(H);  // an even share: whole chunk pairs
+  const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
+
+  // the x row of this lane's MFMA column (a row of the tile), quarter lq of each chunk; columns
+  // past the tile's rows take an offset past the descriptor's range (zeros, no memory access)
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)T * H * 2);
+  uint32_t xoff = kOutOfRange;
+  if (l16 < ti.nr) {
+    const int sl = sorted_slot[ti.r0 + l16];
+    if (sl >= 0 && sl < n_slots) xoff = (uint32_t)(sl / k_total) * (uint32_t)H * 2u + 64u * lq;
+  }
+  const __amdgpu_buffer_rsrc_t wr[2] = {make_rsrc(gate.w + (int64_t)e * gate.we, (int64_t)(I - 1) * gate.wr + H / 2),
+                                        make_rsrc(up.w + (int64_t)e * up.we, (int64_t)(I - 1) * up.wr + H / 2)};
+  const __amdgpu_buffer_rsrc_t sr[2] = {make_rsrc(gate.s + (int64_t)e * gate.se, (int64_t)(I - 1) * gate.sr + H / 32),
+                                        make_rsrc(up.s + (int64_t)e * up.se, (int64_t)(I - 1) * up.sr + H / 32)};
+  // load g of matrix m covers rows n0 + 8g .. + 7 x the 128 bytes of chunks 2p and 2p + 1 (lane:
+  // row lr of the 8, piece lc; pieces 4-7 are the second chunk); pieces past the wave's share and
+  // rows past I (past the buffer's range) read nothing
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t lbase[2] = {(uint32_t)((n0 + lr) * gate.wr) + 16u * lc, (uint32_t)((n0 + lr) * up.wr) + 16u * lc};
+  u32x4 q[DP][2][2];   // [set][matrix][8-row group]
+  u32x4 xq[DP][2][4];  // [set][chunk of the pair][k-step]
+  auto load = [&](int p, u32x4 (&d)[2][2], u32x4 (&dx)[2][4]) {
+    const bool in = 2 * p + (lc >> 2) < c1;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int64_t wrm = m ? up.wr : gate.wr;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) d[m][g] = bld16nt(wr[m], in ? lbase[m] + (uint32_t)(8 * g * wrm) + 128u * p : kOutOfRange);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * p + j;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) dx[j][s4] = bld16(xr, c < c1 ? xoff + 256u * c + 16u * s4 : kOutOfRange);
+    }
+  };
+  const int p0 = c0 >> 1, p1 = (c1 + 1) >> 1;
+#pragma unroll
+  for (int d = 0; d < DP; ++d) load(p0 + d, q[d], xq[d]);
+
+  // scale table of the wave's share: dword (m * 16 + r) * cpw + j holds the four block scales of
+  // chunk c0 + j of row n0 + r of matrix m (gate, up)
+  uint32_t* stab = reinterpret_cast<uint32_t*>(lds + wave * stab_bytes(32, cpw));
+  {
+    const int total = 16 * cpw;
+    fill_table<2, 4, uint32_t>(
+        total, lane,
+        [&](int m, int f) {
+          const int r = f / cpw, j = f - r * cpw;
+          const int n = min(n0 + r, I - 1), c = min(c0 + j, n_chunks - 1);
+          return bld4(sr[m], f < total ? (uint32_t)(n * (m ? up.sr : gate.sr)) + 4u * c : kOutOfRange);
+        },
+        [&](int m, int f, uint32_t v) { stab[m * total + f] = v; });
+  }
+
+  // chunk j of a matrix's 16 rows in MFMA layout (lane: row l16, the chunk's piece lq) through the
+  // wave's 1 KB slot after the reduction area
+  uint8_t* const tslot = lds + NW * stab_bytes(32, cpw) + NW * 2 * 256 * 4 + wave * 1024;
+  auto mfma_layout = [&](const u32x4 (&dm)[2], int j) -> u32x4 {
+    if ((lc >> 2) == j) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int w = 8 * g + lr;
+        *reinterpret_cast<u32x4*>(tslot + 64 * w + 16 * ((lc & 3) ^ ((w >> 1) & 3))) = dm[g];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tslot + 64 * l16 + 16 * (lq ^ ((l16 >> 1) & 3)));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return v;
+  };
+  f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int c, const u32x4 (&d)[2][2], const u32x4 (&dx)[2][4]) {  // chunk c of the pair in d
+    const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
+    const float sg = e8m0_to_f32(sc[4 * cpw * l16]);
+    const float su = e8m0_to_f32(sc[4 * cpw * (16 + l16)]);
+    const u32x4 wg = mfma_layout(d[0], c & 1), wu = mfma_layout(d[1], c & 1);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const V b = bitcast<V>(dx[c & 1][s4]);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wg[s4], sg), b, accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wu[s4], su), b, accu, 0, 0, 0);
+    }
+  };
+  // ring of DP register sets: pair p in set (p - p0) % DP, refilled with pair p + DP once used
+  for (int p = p0; p < p1; p += DP) {
+#pragma unroll
+    for (int d = 0; d < DP; ++d) {
+      if (p + d < p1) {  // uniform
+        compute(2 * (p + d), q[d], xq[d]);
+        if (2 * (p + d) + 1 < c1) compute(2 * (p + d) + 1, q[d], xq[d]);
+      }
+      load(p + d + DP, q[d], xq[d]);
+    }
+  }
+
+  // cross-wave sums of the K shares, then SwiGLU
+  float* red = reinterpret_cast<float*>(lds + NW * stab_bytes(32, cpw));  // [NW][2][256]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[(wave * 2 + 0) * 256 + lane * 4 + i] = accg[i];
+    red[(wave * 2 + 1) * 256 + lane * 4 + i] = accu[i];
+  }
+  __syncthreads();
+  {
+    const int o = threadIdx.x;  // one (row, token) per thread: 256 = 16 rows x 16 tokens
+    const int rr = o & 15, tt = o >> 4;
+    const int qq = (16 * (rr >> 2) + tt) * 4 + (rr & 3);
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      g += red[(w * 2 + 0) * 256 + qq];
+      u += red[(w * 2 + 1) * 256 + qq];
+    }
+    const int n = n0 + rr;
+    if (n < I && tt < ti.nr) {
+      const float h = (g / (1.0f + expf(-g))) * u;
+      uint16_t hi, lo;
+      Op<MOE_W_MXFP4>::split(h, hi, lo);
+      const int64_t idx = (int64_t)(ti.r0 + tt) * I + n;
+      h_hi[idx] = hi;
+      h_lo[idx] = lo;
+    }
+  }
+}
+size_t gateup_split_lines_lds(int H) {  // scale tables, reduction, transposition slots
+  return (size_t)kTinyNW * stab_bytes(32, tiny_gateup_cpw(H)) + (size_t)kTinyNW * 2 * 256 * 4 + (size_t)kTinyNW * 1024;
+}
+// One chunk pair in flight per wave: 100 registers and five waves per SIMD were faster than two
+// pairs at 156 registers and three waves (side by side, sweep T = 4 182 -> 175 us, decode workload
+// T = 8 136 -> 129 us, sweep T = 8 unchanged).
+constexpr int kSplitLinesDP = 1;
+
 // ------------------------------------------------------------------------------------------------
 // Row-split streaming variants (many active experts).  The waves of a workgroup (4 or 8) own
 // different weight rows, each over the whole reduction dimension, so no cross-wave reduction is
@@ -2176,6 +2339,11 @@ hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H
     else
       ffn_gateup_rows_kernel<kGuNW, 1><<<grid, kGuNW * 64, gateup_rows_lds(H, 1, nw), stream>>>(
           (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb_rows, h_hi, h_lo);
+  } else if (MT == 1 && streamable) {
+    const int nb = (I + 15) / 16;
+    ffn_gateup_split_lines_kernel<kSplitLinesDP><<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64,
+                                                   gateup_split_lines_lds(H), stream>>>(
+        (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
   } else if (streamable) {
     launch_gateup_stream<MT, kStRT1>(pl, x, T, k_total, H, I, gate, up, sorted_slot, h_hi, h_lo, tiles, stream);
   } else {

@@ -775,13 +775,22 @@ __global__ __launch_bounds__(NW * 64) void ffn_gateup_stream_kernel(
   }
 }
 
-template <int NW, int MT, int RT>
+// FMT: MXFP4 (one 16-byte load of 32 codes per row and chunk, decoded with the block scale; K
+// permuted within a chunk so that lane quarter lq holds values 32 lq .. + 31, as in the gate/up
+// kernel) or FP16 (four 16-byte loads per row and chunk in the matrix core's own K order: k-step
+// s, quarter lq takes values 32 s + 8 lq .. + 7, so one load covers 64 contiguous bytes of 16
+// rows; no scales).  The h planes follow the same K order.
+template <int FMT, int NW, int MT, int RT>
 __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
     float* __restrict__ y_slots) {
   constexpr int NP = RT * 16;  // rows of the row block
-  typedef bf16x8 V;
+  constexpr bool MX = FMT == MOE_W_MXFP4;
+  constexpr int WQ = MX ? 1 : 4;
+  constexpr uint32_t kCW = MX ? 64u : 256u;
+  constexpr uint32_t kHQ = MX ? 64u : 16u, kHS = MX ? 16u : 64u;
+  typedef typename Op<FMT>::V V;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int tile, nblk;
   xcd_work(blockIdx.x, n_nblk, tile, nblk);
@@ -798,10 +807,12 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + l16;
-    hoff[mt] = m < ti.nr ? (uint32_t)(ti.r0 + m) * (uint32_t)I * 2u + 64u * lq : kOutOfRange;
+    hoff[mt] = m < ti.nr ? (uint32_t)(ti.r0 + m) * (uint32_t)I * 2u + kHQ * lq : kOutOfRange;
   }
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + I / 2);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(down.s + (int64_t)ex * down.se, (int64_t)(H - 1) * down.sr + I / 32);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(down.w + (int64_t)ex * down.we, (int64_t)(H - 1) * down.wr + (MX ? I / 2 : (int64_t)I * 2));
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(MX ? down.s + (int64_t)ex * down.se : nullptr, MX ? (int64_t)(H - 1) * down.sr + I / 32 : 0);
   uint32_t coff[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) coff[rt] = (uint32_t)(min(n0 + rt * 16 + l16, H - 1) * down.wr) + 16u * lq;
@@ -811,6 +822,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
   const int c0 = wave * cpw, c1 = min(c0 + cpw, n_chunks);
   uint32_t* stab = reinterpret_cast<uint32_t*>(lds + wave * stab_bytes(NP, cpw));
   auto fill = [&]() {  // as in gate/up
+    if constexpr (!MX) return;
     const int total = NP * cpw;
     fill_table<1, 8, uint32_t>(
         total, lane,
@@ -828,32 +840,37 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
     for (int rt = 0; rt < RT; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   struct Chunk {
-    u32x4 q[RT];
+    u32x4 q[RT][WQ];
     V hi[MT][4], lo[MT][4];
   };
   auto load = [&](int c, Chunk& d) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) d.q[rt] = bld16(wr, coff[rt] + 64u * c);
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int w = 0; w < WQ; ++w) d.q[rt][w] = bld16(wr, coff[rt] + kCW * c + 64u * w);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        d.hi[mt][s] = bitcast<V>(bld16(hr_hi, hoff[mt] + 256u * c + 16u * s));
-        d.lo[mt][s] = bitcast<V>(bld16(hr_lo, hoff[mt] + 256u * c + 16u * s));
+        d.hi[mt][s] = bitcast<V>(bld16(hr_hi, hoff[mt] + 256u * c + kHS * s));
+        d.lo[mt][s] = bitcast<V>(bld16(hr_lo, hoff[mt] + 256u * c + kHS * s));
       }
   };
   auto compute = [&](int c, const Chunk& d) {
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float scale = e8m0_to_f32(sc[4 * cpw * (rt * 16 + l16)]);
+      float scale = 1.0f;
+      if constexpr (MX) scale = e8m0_to_f32(sc[4 * cpw * (rt * 16 + l16)]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const V a = decode8_bf16(d.q[rt][s], scale);
+        V a;
+        if constexpr (MX) a = decode8_bf16(d.q[rt][0][s], scale);
+        else a = bitcast<V>(d.q[rt][s]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, d.hi[mt][s], acc[mt][rt], 0, 0, 0);
-          acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, d.lo[mt][s], acc[mt][rt], 0, 0, 0);
+          acc[mt][rt] = Op<FMT>::mfma(a, d.hi[mt][s], acc[mt][rt]);
+          acc[mt][rt] = Op<FMT>::mfma(a, d.lo[mt][s], acc[mt][rt]);
         }
       }
     }
@@ -2264,6 +2281,11 @@ inline bool stream_ok(const ProjDev& p, int K, int64_t rows) {
   return K % 128 == 0 && K <= 4 * 128 * kMaxChunksPerWave && al4(p.s) && p.se % 4 == 0 && p.sr % 4 == 0 &&
          rows * p.wr < INT32_MAX;
 }
+// FP16 weights on the K-split streaming kernels: whole 128-wide chunks, 16-byte aligned rows.
+inline bool stream_ok_f16(const ProjDev& p, int K, int64_t rows) {
+  return K % 128 == 0 && K <= 4 * 128 * kMaxChunksPerWave && ((uintptr_t)p.w & 15u) == 0 && p.wr % 16 == 0 &&
+         p.we % 16 == 0 && rows * p.wr < INT32_MAX;
+}
 
 // K-split streaming kernels: RT 16-row tiles per workgroup (kStRT1 of each matrix for gate/up,
 // kStRT2 for down).  Wider blocks amortise each activation chunk over more weight rows but cost
@@ -2278,14 +2300,14 @@ void launch_gateup_stream(const FfnPlan& pl, const void* x, int T, int k_total, 
   ffn_gateup_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
       (const uint16_t*)x, T, k_total, H, I, gate, up, tiles, pl.n_experts, sorted_slot, nb, h_hi, h_lo);
 }
-template <int MT, int RT>
+template <int FMT, int MT, int RT>
 void launch_down_stream(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev down, const int32_t* sorted_slot,
                         float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                         hipStream_t stream) {
   const int nb = (H + 16 * RT - 1) / (16 * RT);
   const int cpw = (I / 128 + kNW - 1) / kNW;
   const size_t lds = (size_t)kNW * stab_bytes(16 * RT, cpw) + (size_t)kNW * RT * 256 * 4;
-  ffn_down_stream_kernel<kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
+  ffn_down_stream_kernel<FMT, kNW, MT, RT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, lds, stream>>>(
       h_hi, h_lo, T * k_total, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
 }
 
@@ -2315,6 +2337,8 @@ template <int FMT, int MT>
 hipError_t gateup_mt(const FfnPlan& pl, const void* x, int T, int k_total, int H, int I, ProjDev gate, ProjDev up,
                      const int32_t* sorted_slot, uint16_t* h_hi, uint16_t* h_lo, const TileEntry* tiles,
                      hipStream_t stream) {
+  // (FP16 weights take the general kernel here: on the dense slices the K-split streaming form
+  // with FP16 loads was no faster at 1 token and slower at 16, 61.0 -> 64.5 us)
   const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(gate, H, I) && stream_ok(up, H, I) && (int64_t)T * H * 2 < INT32_MAX;
   const int nb8 = (I + 16 * kGuNW - 1) / (16 * kGuNW);
   const bool small = pl.tiles * nb8 < kGuSmallBlocks;
@@ -2359,21 +2383,25 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
                    float* y_slots, const uint16_t* h_hi, const uint16_t* h_lo, const TileEntry* tiles,
                    hipStream_t stream) {
   const int n_slots = T * k_total;
-  const bool streamable = FMT == MOE_W_MXFP4 && stream_ok(down, I, H) && (int64_t)n_slots * I * 2 < INT32_MAX;
+  constexpr bool mx = FMT == MOE_W_MXFP4;  // the tiny and row-split down kernels are MXFP4 only
+  const bool streamable = (mx ? stream_ok(down, I, H) : FMT == MOE_W_FP16 && stream_ok_f16(down, I, H)) &&
+                          (int64_t)n_slots * I * 2 < INT32_MAX;
   const int nw = kDnNW;
   const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
-  if (MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
+  if (mx && MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
     const int nb = H / (16 * kTinyNW);
     ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2 + kTinyNW * 1024,
                            stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
-  } else if (MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 4) {
+  } else if (mx && MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 4) {
     // (kRowsMinBlocks / 4 eight-wave blocks: the 2,048 waves that kRowsMinBlocks / 2 four-wave
     // blocks gave before the down kernel dropped its 4-wave form)
     ffn_down_lines_kernel<kDnNW><<<dim3((unsigned)(pl.tiles * nb_rows)), kDnNW * 64, down_rows_lds(I, nw), stream>>>(
         h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb_rows, y_slots);
-  } else if (streamable) {
-    launch_down_stream<MT, kStRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
+  } else if (streamable && (mx || MT == 1)) {
+    // (FP16 weights with one token tile: dense slices T = 1 35.6 -> 29.1 us, T = 16 unchanged)
+    if constexpr (mx || (FMT == MOE_W_FP16 && MT == 1))
+      launch_down_stream<FMT, MT, kStRT2>(pl, T, k_total, H, I, down, sorted_slot, y_slots, h_hi, h_lo, tiles, stream);
   } else {
     const int nb = (H + 16 * kRT2 - 1) / (16 * kRT2);
     ffn_down_kernel<FMT, kNW, kRT2, MT><<<dim3((unsigned)(pl.tiles * nb)), kNW * 64, 0, stream>>>(

@@ -248,6 +248,10 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     # the same tile kernels on FP16 weights: ragged tiles, 3 and 5 chunks of 128
     (300, 384, 640, 3, 2, "fp16", "routed"),
     (200, 128, 256, 4, 1, "fp16", "one-expert"),
+    # FP16 weights on the K-split streaming kernels (one 16-token tile per expert): 5 and 3 chunks
+    # of 128 (the four waves' K shares 2, 2, 1, 0 and 1, 1, 1, 0), and 9 and 8 chunks
+    (8, 640, 384, 6, 3, "fp16", "routed"),
+    (16, 1152, 1024, 8, 2, "fp16", "routed"),
     # at most 4 tokens: the tiny kernels (4-row tiles; down: whole-K rows per wave, h in LDS;
     # gate/up for up to 2 tokens and H a multiple of 512: x in LDS, weights two chunk pairs deep, a
     # wave's K share rounded to whole pairs, so that H = 512 and 1536 leave the last waves empty) at

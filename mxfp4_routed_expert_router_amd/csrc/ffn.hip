@@ -2195,6 +2195,9 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
       V bh[MT], bl[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        // uniform: 16-token column tiles past the rows hold nothing (prefill layer: down 4.90 ->
+        // 4.66 ms; the same skip in the gate/up tile kernel was slower, 5.66 -> 5.80 ms)
+        if (16 * mt >= ti.nr) break;
         bh[mt] = *reinterpret_cast<const V*>(st + mt * 16 * kTileRow + 16 * k);
         bl[mt] = *reinterpret_cast<const V*>(st + NTOK * kTileRow + mt * 16 * kTileRow + 16 * k);
       }
@@ -2203,6 +2206,7 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_tile_kernel(
         const V a = tile_operand<FMT>(d.w[rt], k, scl[rt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
+          if (16 * mt >= ti.nr) break;
           acc[rt][mt] = Op<FMT>::mfma(a, bh[mt], acc[rt][mt]);
           acc[rt][mt] = Op<FMT>::mfma(a, bl[mt], acc[rt][mt]);
         }

@@ -991,6 +991,9 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool tok = l16 < ti.nr;
   const uint8_t* hb = lds + (l16 < kTinyT ? l16 : 0) * I * 2 + 64 * lq;
+  // B operands: lanes of the tile's rows load them, the other lanes keep what the registers hold
+  // (their output columns are never stored)
+  V bh = V{}, bl = V{};
 #pragma unroll
   for (int c = 0; c < kTinyNC; ++c) {
     if (c < nc) {  // uniform
@@ -999,7 +1002,6 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const V a = decode8_bf16(w[s4], scale);
-        V bh = V{}, bl = V{};
         if (tok) {
           bh = *reinterpret_cast<const V*>(hb + 256 * c + 16 * s4);
           bl = *reinterpret_cast<const V*>(hb + per_plane * 16 + 256 * c + 16 * s4);
@@ -1130,6 +1132,8 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
     return v;
   };
   f32x4 accg = f32x4{0.f, 0.f, 0.f, 0.f}, accu = f32x4{0.f, 0.f, 0.f, 0.f};
+  // B operand: lanes of the tile's rows load it, the others keep zeros (no refill per step)
+  V b = V{};
   auto compute = [&](int c, const u32x4 (&d)[2][2]) {  // chunk c of the pair held in d
     const uint8_t* sc = reinterpret_cast<const uint8_t*>(stab) + 4 * (c - c0) + lq;
     const float sg = e8m0_to_f32(sc[4 * cpw * l16]);
@@ -1137,7 +1141,6 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_gateup_tiny_kernel(
     const u32x4 wg = mfma_layout(d[0], c & 1), wu = mfma_layout(d[1], c & 1);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      V b = V{};
       if (tok >= 0) b = *reinterpret_cast<const V*>(xrow + 256 * c + 16 * s4);
       accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wg[s4], sg), b, accg, 0, 0, 0);
       accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(wu[s4], su), b, accu, 0, 0, 0);

@@ -1892,8 +1892,9 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 4 : 1) void ffn_down_lines_kerne
 // two-stage LDS ring, written right after each step's barrier.  MXFP4 block scales are loaded with
 // the weights (one dword per row and chunk); FP16 weights are four 16-byte loads per row and chunk.  Workgroups are numbered tile-major with the row blocks
 // padded to a multiple of 8, so row block j of every tile runs on XCD j % 8: the tiles of a hot
-// expert that run together read each weight row from one L2.  Sub-tiles past the tile's rows are
-// computed on zero activations (branching around their MFMAs would split the scheduled loop).
+// expert that run together read each weight row from one L2.  Gate/up computes sub-tiles past the
+// tile's rows on zero activations (branching around their MFMAs split its scheduled loop and was
+// slower); the down kernel skips them.
 // ------------------------------------------------------------------------------------------------
 constexpr int kTileMT = 8;                     // 16-token sub-tiles per gate/up tile
 constexpr int kTileRT = 1;                     // 16-row tiles of each matrix per gate/up wave

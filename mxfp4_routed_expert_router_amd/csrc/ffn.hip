@@ -903,15 +903,24 @@ __global__ __launch_bounds__(NW * 64) void ffn_down_stream_kernel(
 
 // ------------------------------------------------------------------------------------------------
 // Down for tiny calls (at most kTinyT tokens, so no tile has more rows than that): each wave owns
-// 16 rows of H over the whole reduction dimension (no cross-wave sums) and issues every load it
-// needs at once -- its share of the tile's h rows straight into LDS (buffer loads with the LDS
-// destination, so they hold no registers), then its rows' block scales, then all of their weight
-// chunks -- so a wave waits for one memory round trip instead of one per pair of chunks.  MFMA
-// columns past the tile's rows take zeros (those lanes read no LDS).
+// 16 rows of H over the whole reduction dimension (no cross-wave sums) and issues its loads ahead
+// of its MFMAs -- its share of the tile's h rows straight into LDS (buffer loads with the LDS
+// destination, so they hold no registers), then its rows' block scales, then its weight chunks
+// (all of them, or the first AHEAD pairs) -- so a wave waits for one memory round trip instead of
+// one per pair of chunks.  The hi and lo planes of h are two sets of MFMA columns (token t in
+// column t and kTinyT + t), one MFMA per weight operand, summed once at the end; columns past the
+// tile's rows take zeros (those lanes read no LDS).
 // ------------------------------------------------------------------------------------------------
 constexpr int kTinyNC = 16, kTinyNW = 4;  // (kTinyT: launch.hpp)
 typedef __attribute__((address_space(3))) void lds_void;
 
+// AHEAD: chunk pairs of weight lines requested before the first MFMA, the next pair requested as
+// each pair's first chunk starts (kTinyNC / 2: all at once).  A CU serves its load requests in
+// order, so with every line requested at once the last workgroup on a CU receives all of its lines
+// at the end and computes all of its chunks after them; requesting a few pairs ahead interleaves
+// the workgroups' lines.  Measured, that paid for calls of one token (one row per tile) and was
+// slower from two tokens on, which keep the one-shot form.
+template <int AHEAD>
 __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int n_slots, int H, int I, ProjDev down,
     const TileEntry* __restrict__ tiles, int n_experts, const int32_t* __restrict__ sorted_slot, int n_nblk,
@@ -960,11 +969,13 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
   const int lr = lane >> 3, lc = lane & 7;
   const uint32_t lbase = (uint32_t)((n0 + lr) * down.wr) + 16u * lc;
   u32x4 q[kTinyNC];
+  auto load_pair = [&](int p) {
 #pragma unroll
-  for (int c = 0; c < kTinyNC; ++c) {
-    const int p = c >> 1, g = c & 1;
-    q[c] = bld16nt(wr, 2 * p + (lc >> 2) < nc ? lbase + (uint32_t)(8 * g * down.wr) + 128u * p : kOutOfRange);
-  }
+    for (int g = 0; g < 2; ++g)
+      q[2 * p + g] = bld16nt(wr, 2 * p + (lc >> 2) < nc ? lbase + (uint32_t)(8 * g * down.wr) + 128u * p : kOutOfRange);
+  };
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p) load_pair(p);
   __syncthreads();  // the h pieces of every wave are in LDS
   // chunk c of the wave's 16 rows in MFMA layout (lane: row l16, the chunk's piece lq) through the
   // wave's 1 KB slot after the h copy, as in the row-split down kernel
@@ -989,31 +1000,33 @@ __global__ __launch_bounds__(kTinyNW * 64) void ffn_down_tiny_kernel(
   };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool tok = l16 < ti.nr;
-  const uint8_t* hb = lds + (l16 < kTinyT ? l16 : 0) * I * 2 + 64 * lq;
-  // B operands: lanes of the tile's rows load them, the other lanes keep what the registers hold
+  static_assert(2 * kTinyT <= 16, "hi and lo columns of every token in one MFMA");
+  const int tcol = l16 < kTinyT ? l16 : l16 - kTinyT;  // token of this lane's column
+  const bool tok = l16 < 2 * kTinyT && tcol < ti.nr;
+  const uint8_t* hb = lds + (l16 < kTinyT ? 0 : per_plane * 16) + (tok ? tcol : 0) * I * 2 + 64 * lq;
+  // B operand: lanes of the tile's rows load it, the other lanes keep what the registers hold
   // (their output columns are never stored)
-  V bh = V{}, bl = V{};
+  V b = V{};
 #pragma unroll
   for (int c = 0; c < kTinyNC; ++c) {
     if (c < nc) {  // uniform
+      if ((c & 1) == 0 && (c >> 1) + AHEAD < kTinyNC / 2) load_pair((c >> 1) + AHEAD);
       const float scale = e8m0_to_f32((sv[c >> 2][c & 3] >> (8 * lq)) & 0xFFu);
       const u32x4 w = mfma_layout(c);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const V a = decode8_bf16(w[s4], scale);
-        if (tok) {
-          bh = *reinterpret_cast<const V*>(hb + 256 * c + 16 * s4);
-          bl = *reinterpret_cast<const V*>(hb + per_plane * 16 + 256 * c + 16 * s4);
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+        if (tok) b = *reinterpret_cast<const V*>(hb + 256 * c + 16 * s4);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8_bf16(w[s4], scale), b, acc, 0, 0, 0);
       }
     }
   }
-  // lane (token l16, quarter lq) holds rows n0 + 4 lq .. + 3 of its token
-  if (tok) {
-    const int sl = sorted_slot[ti.r0 + l16];
+  // lane (column l16, quarter lq) holds rows n0 + 4 lq .. + 3 of its column; the lo column of
+  // token t takes the hi column's sums (the lane kTinyT to its left in the same 16-lane row)
+  static_assert(kTinyT == 4, "the DPP shift below moves columns by kTinyT");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(dpp_u32<kDppRowShr4, 0xF>(0u, __float_as_uint(acc[i])));
+  if (tok && l16 >= kTinyT) {
+    const int sl = sorted_slot[ti.r0 + tcol];
     const int n = n0 + 4 * lq;
     if (sl >= 0 && sl < n_slots) {
       float* dst = y_slots + (int64_t)sl * H + n;
@@ -2398,9 +2411,13 @@ hipError_t down_mt(const FfnPlan& pl, int T, int k_total, int H, int I, ProjDev 
   const int nb_rows = (H + 16 * kRowsRT2 * nw - 1) / (16 * kRowsRT2 * nw);
   if (mx && MT == 1 && streamable && pl.tiny) {  // (the plan holds it only for H a multiple of 16 * kTinyNW)
     const int nb = H / (16 * kTinyNW);
-    ffn_down_tiny_kernel<<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, (size_t)2 * kTinyT * I * 2 + kTinyNW * 1024,
-                           stream>>>(
-        h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
+    const size_t lds = (size_t)2 * kTinyT * I * 2 + kTinyNW * 1024;
+    if (T == 1)
+      ffn_down_tiny_kernel<2><<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, lds, stream>>>(
+          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
+    else
+      ffn_down_tiny_kernel<kTinyNC / 2><<<dim3((unsigned)(pl.tiles * nb)), kTinyNW * 64, lds, stream>>>(
+          h_hi, h_lo, n_slots, H, I, down, tiles, pl.n_experts, sorted_slot, nb, y_slots);
   } else if (mx && MT == 1 && streamable && down_rows_lds(I, nw) <= kMaxLds && pl.tiles * nb_rows >= kRowsMinBlocks / 4) {
     // (kRowsMinBlocks / 4 eight-wave blocks: the 2,048 waves that kRowsMinBlocks / 2 four-wave
     // blocks gave before the down kernel dropped its 4-wave form)

@@ -270,6 +270,9 @@ FFN_EDGE = [  # (T, H, I, E, k, fmt, id pattern)
     (2, 128, 384, 8, 2, "mxfp4", "routed"),
     (4, 96, 512, 4, 2, "mxfp4", "routed"),
     (4, 128, 2560, 8, 2, "mxfp4", "routed"),
+    # the tiny gate/up kernel near its LDS bound: x of two tokens at H = 22528 (88 KB), 44 chunks
+    # of 128 per wave
+    (2, 22528, 256, 4, 2, "mxfp4", "routed"),
 ]
 
 
